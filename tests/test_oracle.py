@@ -1,0 +1,410 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: exact
+rational arithmetic, an independent chunked evaluation, closed forms, or a
+library routine (torch CPU fp64).  ``test_planted_mistakes_are_caught`` plants
+plausible bugs in the oracle and checks that the pins fail on each.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import gdn_oracle as O
+from tests.alt_forms import chunked_form, product_form_exact
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def rel_err(x, r):
+    x, r = np.asarray(x, np.float64), np.asarray(r, np.float64)
+    return float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-300))
+
+
+# ----------------------------------------------------------------- pins
+# Rational unit vectors in R^3 (numerators of Pythagorean quadruples).
+_UNIT3 = [(1, 2, 2, 3), (2, 1, -2, 3), (2, 3, 6, 7), (3, 4, 0, 5), (0, 3, 4, 5), (2, -2, 1, 3), (6, 2, -3, 7)]
+
+
+def pin_exact_product_form(T=6, H_k=2, H_v=4):
+    """Oracle recurrence vs the exact product form (d_k=3 != d_v=2, GQA 2:1)."""
+    dk, dv = 3, 2
+    rng = np.random.default_rng(11)
+    K = [[[Fraction(u[i], u[3]) for i in range(3)] for u in
+          (_UNIT3[(t * 3 + hk * 5) % 7] for t in range(T))] for hk in range(H_k)]
+    Q = [[[Fraction(int(rng.integers(-4, 5)), 4) for _ in range(dk)] for _ in range(T)] for _ in range(H_k)]
+    V = [[[Fraction(int(rng.integers(-6, 7)), 3) for _ in range(dv)] for _ in range(T)] for _ in range(H_v)]
+    alpha = [[Fraction(int(rng.integers(5, 10)), 10) for _ in range(T)] for _ in range(H_v)]
+    beta = [[Fraction(int(rng.integers(1, 5)), 4) for _ in range(T)] for _ in range(H_v)]
+    S0 = [[[Fraction(int(rng.integers(-3, 4)), 2) for _ in range(dk)] for _ in range(dv)] for _ in range(H_v)]
+    scale = Fraction(1, 2)
+    # float copies for the oracle
+    kf = np.array([[[float(x) for x in K[hk][t]] for hk in range(H_k)] for t in range(T)])
+    qf = np.array([[[float(x) for x in Q[hk][t]] for hk in range(H_k)] for t in range(T)])
+    vf = np.array([[[float(x) for x in V[h][t]] for h in range(H_v)] for t in range(T)])
+    gf = np.array([[math.log(alpha[h][t]) for h in range(H_v)] for t in range(T)])
+    bf = np.array([[float(beta[h][t]) for h in range(H_v)] for t in range(T)])
+    S0f = np.array([[[float(x) for x in row] for row in S0[h]] for h in range(H_v)])
+    o, S_T, _ = O.gated_delta_rule(qf, kf, vf, gf, bf, S0f, scale=float(scale))
+    err = 0.0
+    for h in range(H_v):
+        hk = h // (H_v // H_k)
+        o_ex, S_ex = product_form_exact(alpha[h], beta[h], K[hk], V[h], Q[hk], S0[h])
+        o_ex = np.array([[float(x * scale) for x in row] for row in o_ex])
+        S_ex = np.array([[float(x) for x in row] for row in S_ex])
+        err = max(err, rel_err(o[:, h], o_ex), rel_err(S_T[h], S_ex))
+    return err
+
+
+def _rand_seq(rng, T, H_k, H_v, dk, dv, slow=False):
+    q = O.l2norm(rng.standard_normal((T, H_k, dk)))
+    k = O.l2norm(rng.standard_normal((T, H_k, dk)))
+    v = rng.standard_normal((T, H_v, dv))
+    if slow:
+        g = -rng.uniform(0.0, 0.1, (T, H_v))
+    else:
+        g, _ = O.gating(rng.standard_normal((T, H_v)), np.zeros((T, H_v)),
+                        rng.uniform(0, math.log(16), H_v), rng.uniform(-1, 1, H_v))
+    beta = O.sigmoid(rng.standard_normal((T, H_v)))
+    S0 = 0.3 * rng.standard_normal((H_v, dv, dk))
+    return q, k, v, g, beta, S0
+
+
+def pin_chunked_equals_recurrent(T=50, chunk=16, dk=16, dv=12, slow=True):
+    """Oracle token loop vs the chunked WY/UT form (ragged last chunk, S0 != 0)."""
+    rng = np.random.default_rng(5)
+    H_k, H_v = 1, 2
+    q, k, v, g, beta, S0 = _rand_seq(rng, T, H_k, H_v, dk, dv, slow)
+    o, S_T, _ = O.gated_delta_rule(q, k, v, g, beta, S0, scale=0.7)
+    err = 0.0
+    for h in range(H_v):
+        oc, Sc = chunked_form(q[:, 0], k[:, 0], v[:, h], g[:, h], beta[:, h], S0[h], chunk, scale=0.7)
+        err = max(err, rel_err(o[:, h], oc), rel_err(S_T[h], Sc))
+    return err
+
+
+def pin_beta_zero_decay():
+    """beta = 0: S_T = exp(sum g) S0 and o_t = exp(G_t) S0 q_t."""
+    rng = np.random.default_rng(6)
+    T, dk, dv = 40, 8, 5
+    q, k, v, _, _, S0 = _rand_seq(rng, T, 1, 1, dk, dv)
+    g = -rng.uniform(0, 0.05, (T, 1))
+    o, S_T, _ = O.gated_delta_rule(q, k, v, g, np.zeros((T, 1)), S0)
+    G = np.cumsum(g[:, 0])
+    o_ref = np.exp(G)[:, None] * (q[:, 0] @ S0[0].T)
+    return max(rel_err(S_T[0], math.exp(G[-1]) * S0[0]), rel_err(o[:, 0], o_ref))
+
+
+def pin_orthonormal_retrieval():
+    """g = 0, beta = 1, orthonormal keys, S0 = 0: S_T k_j = v_j, and querying
+    with k_j returns v_j for every key already written."""
+    rng = np.random.default_rng(7)
+    T, dk, dv = 10, 12, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Qm[:, :T].T                                           # [T, dk] orthonormal rows
+    v = rng.standard_normal((T, 1, dv))
+    q = np.empty((T, 1, dk))
+    q[:, 0] = keys[rng.integers(0, np.arange(1, T + 1))]          # query a key written so far
+    o, S_T, _ = O.gated_delta_rule(q, keys[:, None], v, np.zeros((T, 1)), np.ones((T, 1)))
+    err = rel_err(S_T[0] @ keys.T, v[:, 0].T)
+    for t in range(T):
+        j = int(np.argmax(np.abs(keys @ q[t, 0])))
+        err = max(err, rel_err(o[t, 0], v[j, 0]))
+    return err
+
+
+def pin_write_invariant():
+    """beta = 1, any g and S0: after token t, S_t k_t = v_t (unit k_t)."""
+    rng = np.random.default_rng(8)
+    T, dk, dv = 20, 8, 6
+    q, k, v, g, _, S0 = _rand_seq(rng, T, 1, 1, dk, dv)
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    _, _, states = O.gated_delta_rule(q, k, v, g, np.ones((T, 1)), S0, keep_states=True)
+    return max(rel_err(states[t][0] @ k[t, 0], v[t, 0]) for t in range(T))
+
+
+def pin_conv_vs_torch():
+    """Oracle conv1d + SiLU vs torch's grouped conv1d (fp64) over state ++ x."""
+    rng = np.random.default_rng(9)
+    T, C, W = 13, 10, 4
+    x, w, b = rng.standard_normal((T, C)), rng.standard_normal((C, W)), rng.standard_normal(C)
+    st = rng.standard_normal((C, W - 1))
+    y, new_state = O.causal_conv1d_silu(x, w, b, st)
+    xe = torch.from_numpy(np.concatenate([st.T, x], 0).T[None])      # [1, C, W-1+T]
+    ref = F.silu(F.conv1d(xe, torch.from_numpy(w)[:, None, :], torch.from_numpy(b), groups=C))[0].T.numpy()
+    err = rel_err(y, ref)
+    full = np.concatenate([st.T, x], 0)
+    return max(err, rel_err(new_state, full[-(W - 1):].T))
+
+
+def pin_gating_vs_torch():
+    rng = np.random.default_rng(10)
+    a, b = 4 * rng.standard_normal((50, 6)), 4 * rng.standard_normal((50, 6))
+    A_log, dtb = rng.uniform(0, math.log(16), 6), rng.uniform(-1, 1, 6)
+    g, beta = O.gating(a, b, A_log, dtb)
+    t = torch.from_numpy
+    g_ref = (-torch.exp(t(A_log)) * F.softplus(t(a) + t(dtb), threshold=50.0)).numpy()
+    return max(rel_err(g, g_ref), rel_err(beta, torch.sigmoid(t(b)).numpy()))
+
+
+def pin_rmsnorm_vs_torch():
+    rng = np.random.default_rng(12)
+    o, z, w = rng.standard_normal((7, 3, 16)), rng.standard_normal((7, 3, 16)), rng.uniform(0.5, 1.5, 16)
+    out = O.gated_rmsnorm(o, z, w, 1e-6)
+    t = torch.from_numpy
+    ref = (F.rms_norm(t(o), (16,), weight=t(w), eps=1e-6) * F.silu(t(z))).numpy()
+    return rel_err(out, ref)
+
+
+def pin_l2norm():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((9, 2, 16)) * 3
+    y = O.l2norm(x, eps=1e-6)
+    n = np.linalg.norm(x, axis=-1)
+    err = rel_err(np.linalg.norm(y, axis=-1), n / np.sqrt(n * n + 1e-6))
+    cos = np.sum(x * y, -1) / (n * np.linalg.norm(y, axis=-1))
+    return max(err, float(np.max(np.abs(cos - 1))))
+
+
+PINS = {
+    "exact_product_form": (pin_exact_product_form, 1e-12),
+    "chunked_equals_recurrent": (pin_chunked_equals_recurrent, 1e-11),
+    "beta_zero_decay": (pin_beta_zero_decay, 1e-12),
+    "orthonormal_retrieval": (pin_orthonormal_retrieval, 1e-12),
+    "write_invariant": (pin_write_invariant, 1e-12),
+    "conv_vs_torch": (pin_conv_vs_torch, 1e-13),
+    "gating_vs_torch": (pin_gating_vs_torch, 1e-13),
+    "rmsnorm_vs_torch": (pin_rmsnorm_vs_torch, 1e-13),
+    "l2norm": (pin_l2norm, 1e-13),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin(name):
+    fn, tol = PINS[name]
+    assert fn() < tol
+
+
+# ------------------------------------------------------- more closed forms
+def test_chunked_form_many_shapes():
+    for T, chunk, dk, dv, slow in [(64, 16, 16, 16, False), (64, 64, 8, 8, True), (1, 16, 4, 4, True),
+                                   (97, 32, 16, 8, True), (130, 64, 12, 12, False)]:
+        assert pin_chunked_equals_recurrent(T, chunk, dk, dv, slow) < 1e-10
+
+
+def test_conv_identity_and_shift_taps():
+    rng = np.random.default_rng(1)
+    T, C, W = 9, 5, 4
+    x, st = rng.standard_normal((T, C)), rng.standard_normal((C, W - 1))
+    for j in range(W):
+        w = np.zeros((C, W))
+        w[:, j] = 1.0
+        y, _ = O.causal_conv1d_silu(x, w, None, st)
+        xe = np.concatenate([st.T, x], 0)
+        shift = W - 1 - j                                   # tap j reads the input `shift` steps back
+        ref = xe[W - 1 - shift: W - 1 - shift + T]
+        assert np.allclose(y, ref * (1 / (1 + np.exp(-ref))), rtol=1e-14, atol=1e-14)
+
+
+def test_conv_short_sequence_keeps_state_tail():
+    rng = np.random.default_rng(2)
+    C, W = 4, 4
+    st = rng.standard_normal((C, W - 1))
+    for T in (0, 1, 2, 3, 5):
+        x = rng.standard_normal((T, C))
+        _, ns = O.causal_conv1d_silu(x, rng.standard_normal((C, W)), None, st)
+        assert np.array_equal(ns, np.concatenate([st.T, x], 0)[-(W - 1):].T)
+
+
+def test_gating_special_values():
+    g, beta = O.gating(np.zeros(3), np.zeros(3), np.zeros(3), np.zeros(3))
+    assert np.allclose(np.exp(g), 0.5, rtol=0, atol=1e-15)        # -softplus(0) = -ln 2
+    assert np.all(beta == 0.5)
+    assert O.softplus(np.array([0.0]))[0] == pytest.approx(math.log(2), abs=1e-16)
+    g, _ = O.gating(np.array([800.0, -800.0]), np.zeros(2), np.zeros(2), np.zeros(2))
+    assert g[0] == -800.0 and -1e-300 < g[1] <= 0.0                # no overflow either way
+
+
+def test_rmsnorm_constant_vector():
+    c, eps = 0.37, 1e-6
+    o = np.full((1, 1, 8), c)
+    out = O.gated_rmsnorm(o, np.full((1, 1, 8), 40.0), np.ones(8), eps)   # silu(40) = 40 to 1e-16
+    assert np.allclose(out, c / math.sqrt(c * c + eps) * 40.0, rtol=1e-14)
+
+
+# --------------------------------------------------------- batch drivers
+DIMS = (2, 4, 8, 8)          # h_k, h_v, d_k, d_v
+C_CH = 2 * 2 * 8 + 4 * 8
+
+
+def _params(rng):
+    return dict(conv_w=0.5 * rng.standard_normal((C_CH, 4)), conv_b=None,
+                A_log=rng.uniform(0, math.log(16), 4), dt_bias=rng.uniform(-1, 1, 4),
+                norm_w=rng.uniform(0.5, 1.5, 8))
+
+
+def _batch(rng, T):
+    return (rng.standard_normal((T, C_CH)), rng.standard_normal((T, 4)), rng.standard_normal((T, 4)),
+            rng.standard_normal((T, 4, 8)))
+
+
+def _pools(rng, n_slots):
+    return rng.standard_normal((n_slots, C_CH, 3)), 0.1 * rng.standard_normal((n_slots, 4, 8, 8))
+
+
+def test_split_prefill_equals_single_pass():
+    rng = np.random.default_rng(20)
+    p = _params(rng)
+    x, a, b, z = _batch(rng, 23)
+    conv, ssm = _pools(rng, 3)
+    one, c1, s1 = O.prefill_batch(x, a, b, z, [0, 23], [1], [1], conv, ssm, p, DIMS)
+    o1, c2, s2 = O.prefill_batch(x[:10], a[:10], b[:10], z[:10], [0, 10], [1], [1], conv, ssm, p, DIMS)
+    o2, c2, s2 = O.prefill_batch(x[10:], a[10:], b[10:], z[10:], [0, 13], [1], [1], c2, s2, p, DIMS)
+    assert rel_err(np.concatenate([o1, o2]), one) < 1e-13
+    assert rel_err(s2, s1) < 1e-13 and np.array_equal(c2, c1)
+
+
+def test_decode_steps_equal_prefill():
+    rng = np.random.default_rng(21)
+    p = _params(rng)
+    x, a, b, z = _batch(rng, 6)
+    conv, ssm = _pools(rng, 2)
+    ref, c_ref, s_ref = O.prefill_batch(x, a, b, z, [0, 6], [1], [1], conv, ssm, p, DIMS)
+    c, s = conv, ssm
+    outs = []
+    for t in range(6):
+        o, c, s = O.decode_batch(x[None, t:t + 1], a[None, t:t + 1], b[None, t:t + 1], z[None, t:t + 1],
+                                 [1], None, c, s, p, DIMS)
+        outs.append(o[0, 0])
+    assert rel_err(np.stack(outs), ref) < 1e-13
+    assert rel_err(s, s_ref) < 1e-13 and np.array_equal(c, c_ref)
+
+
+def test_mtp_snapshots_equal_plain_steps():
+    rng = np.random.default_rng(22)
+    p = _params(rng)
+    n, ts = 2, 3
+    x, a, b = rng.standard_normal((n, ts, C_CH)), rng.standard_normal((n, ts, 4)), rng.standard_normal((n, ts, 4))
+    conv, ssm = _pools(rng, n * (ts + 1))
+    home = np.array([5, 1])
+    outs = np.array([[0, 2, 7], [3, 4, 6]])
+    o, c, s = O.decode_batch(x, a, b, None, home, outs, conv, ssm, p, DIMS)
+    assert np.array_equal(c[home], conv[home]) and np.array_equal(s[home], ssm[home])
+    for i in range(n):
+        for q in range(ts):
+            _, c_ref, s_ref = O.decode_batch(x[i:i + 1, :q + 1], a[i:i + 1, :q + 1], b[i:i + 1, :q + 1], None,
+                                             home[i:i + 1], None, conv, ssm, p, DIMS)
+            assert rel_err(s[outs[i, q]], s_ref[home[i]]) < 1e-13
+            assert np.array_equal(c[outs[i, q]], c_ref[home[i]])
+
+
+def test_permutation_invariance_and_padding():
+    rng = np.random.default_rng(23)
+    p = _params(rng)
+    lens = [5, 0, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x, a, b, z = _batch(rng, cu[-1])
+    conv, ssm = _pools(rng, 6)
+    slots, init = np.array([4, 0, 2, 5]), np.array([1, 0, 0, 1])
+    out, c, s = O.prefill_batch(x, a, b, z, cu, slots, init, conv, ssm, p, DIMS)
+    # empty sequence with has_init=0 stores zero history; untouched slots unchanged
+    assert np.all(c[0] == 0) and np.all(s[0] == 0)
+    for u in (1, 3):
+        assert np.array_equal(c[u], conv[u]) and np.array_equal(s[u], ssm[u])
+    # reorder sequences and relabel slots
+    perm = [2, 0, 3, 1]
+    relabel = np.array([3, 5, 0, 1, 2, 4])
+    segs = [slice(cu[i], cu[i + 1]) for i in perm]
+    cat = lambda arr: np.concatenate([arr[sl] for sl in segs])
+    lens_p = [lens[i] for i in perm]
+    cu_p = np.concatenate([[0], np.cumsum(lens_p)])
+    conv_p, ssm_p = np.empty_like(conv), np.empty_like(ssm)
+    conv_p[relabel], ssm_p[relabel] = conv, ssm
+    out_p, c_p, s_p = O.prefill_batch(cat(x), cat(a), cat(b), cat(z), cu_p, relabel[slots[perm]], init[perm],
+                                      conv_p, ssm_p, p, DIMS)
+    assert np.array_equal(out_p, cat(out))
+    assert np.array_equal(c_p[relabel], c) and np.array_equal(s_p[relabel], s)
+    # padding entry: zero rows, pools untouched
+    out_pad, c_pad, s_pad = O.prefill_batch(x[:5], a[:5], b[:5], z[:5], [0, 5], [-1], [1], conv, ssm, p, DIMS)
+    assert np.all(out_pad == 0) and np.array_equal(c_pad, conv) and np.array_equal(s_pad, ssm)
+
+
+def test_state_copy():
+    pool = np.arange(5 * 3, dtype=np.float64).reshape(5, 3)
+    out = O.state_copy(pool, [0, 3, -1, 2], [4, 1, 2, -1])
+    assert np.array_equal(out[[0, 2, 3]], pool[[0, 2, 3]])
+    assert np.array_equal(out[4], pool[0]) and np.array_equal(out[1], pool[3])
+
+
+# ------------------------------------------------------ planted mistakes
+def _mut_no_decay(S, k, v, q, g, beta, scale):
+    return _orig_step(S, k, v, q, np.zeros_like(g), beta, scale)
+
+
+def _mut_sign(S, k, v, q, g, beta, scale):
+    S = S * np.exp(g)[:, None, None]
+    u = beta[:, None] * (v + np.matmul(S, k[:, :, None])[:, :, 0])
+    S = S + u[:, :, None] * k[:, None, :]
+    return S, scale * np.matmul(S, q[:, :, None])[:, :, 0]
+
+
+def _mut_transpose(S, k, v, q, g, beta, scale):
+    S = S * np.exp(g)[:, None, None]
+    u = beta[:, None] * (v - np.matmul(S.transpose(0, 2, 1), k[:, :, None])[:, :, 0])
+    S = S + u[:, :, None] * k[:, None, :]
+    return S, scale * np.matmul(S, q[:, :, None])[:, :, 0]
+
+
+def _mut_output_before_update(S, k, v, q, g, beta, scale):
+    o = scale * np.matmul(S * np.exp(g)[:, None, None], q[:, :, None])[:, :, 0]
+    S, _ = _orig_step(S, k, v, q, g, beta, scale)
+    return S, o
+
+
+def _mut_decay_after_update(S, k, v, q, g, beta, scale):
+    u = beta[:, None] * (v - np.matmul(S, k[:, :, None])[:, :, 0])
+    S = (S + u[:, :, None] * k[:, None, :]) * np.exp(g)[:, None, None]
+    return S, scale * np.matmul(S, q[:, :, None])[:, :, 0]
+
+
+_orig_step = O.delta_step
+_orig_gating = O.gating
+_orig_conv = O.causal_conv1d_silu
+_orig_qk_head = O.qk_head
+_orig_rms = O.gated_rmsnorm
+
+MUTATIONS = {
+    "no_decay": ("delta_step", _mut_no_decay),
+    "update_sign": ("delta_step", _mut_sign),
+    "transposed_state": ("delta_step", _mut_transpose),
+    "output_before_update": ("delta_step", _mut_output_before_update),
+    "decay_after_update": ("delta_step", _mut_decay_after_update),
+    "gate_bias_sign": ("gating", lambda a, b, A_log, dtb: _orig_gating(a, b, A_log, -np.asarray(dtb))),
+    "beta_not_sigmoid": ("gating", lambda a, b, A_log, dtb: (_orig_gating(a, b, A_log, dtb)[0], np.asarray(b) * 0.5 + 0.5)),
+    "conv_taps_reversed": ("causal_conv1d_silu", lambda x, w, bias=None, state0=None:
+                           _orig_conv(x, np.asarray(w)[:, ::-1], bias, state0)),
+    "head_map_modulo": ("qk_head", lambda h, h_k, h_v: h % h_k),
+    "l2norm_missing_sqrt": ("l2norm", lambda x, eps=O.L2NORM_EPS:
+                            np.asarray(x) / (np.sum(np.asarray(x) ** 2, -1, keepdims=True) + eps)),
+    "rmsnorm_sum_not_mean": ("gated_rmsnorm", lambda o, z, w, eps:
+                             _orig_rms(o, z, w, eps) / math.sqrt(np.asarray(o).shape[-1])),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for p, (pin, tol) in PINS.items():
+        try:
+            if not (pin() < tol):
+                caught.append(p)
+        except (ValueError, IndexError):      # a shape mistake that numpy rejects outright
+            caught.append(p)
+    assert caught, f"planted mistake {name} passes every pin"
