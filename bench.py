@@ -1,0 +1,266 @@
+"""Benchmark of the GDN hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+One step = one pass of the prefill hot path over one batch: causal conv1d +
+SiLU (gdn_conv1d_fwd), gating (gdn_gating), then the chunked gated delta rule
+with fused q/k L2 norm and gated-RMSNorm epilogue (gdn_chunk_prefill), on the
+single-sequence workload: batch 1, T=4096, 16 QK / 32 V heads, d=128, bf16
+activations, fp32 state, chunk 64, synthetic seeded inputs resident in HBM.
+
+Prints ONE JSON line: tokens/s for that step (value), the roofline of the
+dominant kernel (its per-launch time measured with HIP events on the launch
+stream), the decode state-update bandwidth (256 requests x 1 token over a
+512-slot fp32 state pool, pools rotated so states come from HBM), and the
+fp64 CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "GDN prefill tokens/s (MFMA util) + decode state-update GB/s vs HBM peak"
+
+
+def chunk_algorithmic(T: int, n_seq: int, h_k: int, h_v: int, d: int, act_bytes: int, has_init: bool,
+                      chunk: int) -> tuple[float, float]:
+    """Algorithmic bytes and flops of one gdn_chunk_prefill launch.
+
+    Bytes per token: q, k, v rows read once (2*h_k*d + h_v*d activations),
+    g and beta (2*h_v fp32), z read and out written (2*h_v*d activations);
+    per sequence: the fp32 state written (and read when it has history).
+    Flops per chunk and V head (C = chunk, d_k = d_v = d): Gram K K^T and Q K^T
+    (2dC^2 shared by h_v/h_k V heads, triangular), W, Ut and (M o QK^T) U
+    (3dC(C+1)), the UT inverse (C^3/3), and W S^T, Q S^T, K^T U (6Cd^2).
+    """
+    per_tok = (2 * h_k * d + h_v * d) * act_bytes + 2 * h_v * 4 + 2 * h_v * d * act_bytes
+    state = n_seq * h_v * d * d * 4 * (2 if has_init else 1)
+    nbytes = T * per_tok + state
+    C = chunk
+    per_chunk_head = 2 * d * C * C * h_k / h_v + 3 * d * C * (C + 1) + C ** 3 / 3 + 6 * C * d * d
+    flops = (T / C) * h_v * per_chunk_head
+    return float(nbytes), float(flops)
+
+
+def decode_algorithmic(n: int, t_step: int, h_k: int, h_v: int, d: int, act_bytes: int, n_pos_writes: int) -> float:
+    """Bytes of one gdn_recurrent_decode launch: each state read once and written
+    n_pos_writes times, plus per token q/k/v, a/b, z and out."""
+    state = h_v * d * d * 4
+    per_tok = (2 * h_k * d + h_v * d) * act_bytes + 2 * h_v * act_bytes + 2 * h_v * d * act_bytes
+    return float(n * (state * (1 + n_pos_writes) + t_step * per_tok))
+
+
+def device_info() -> dict:
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "cus": p.multi_processor_count, "arch": getattr(p, "gcnArchName", "")}
+
+
+def copy_bandwidth_gbs(torch) -> float:
+    """Measured device-to-device copy bandwidth (read + write bytes / time)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def bench_prefill(args, torch, gdn, gi):
+    case = gi.prefill_case()
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    dev = torch.device("cuda")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    x = bf(case.seq_x(0))
+    a, b, z = bf(case.seq_a(0)), bf(case.seq_b(0)), bf(case.seq_z(0))
+    p = case.params
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log = torch.from_numpy(p.A_log).to(dev)
+    dt_bias = torch.from_numpy(p.dt_bias).to(dev)
+    cu = torch.tensor(case.cu_seqlens, dtype=torch.int32, device=dev)
+    slots = torch.zeros(1, dtype=torch.int32, device=dev)
+    has_init = torch.zeros(1, dtype=torch.uint8, device=dev)
+    conv_pool = torch.zeros((1, d.c_ch, d.conv_w - 1), dtype=torch.bfloat16, device=dev)
+    ssm_pool = torch.zeros((1, d.h_v, d.d_v, d.d_k), dtype=torch.float32, device=dev)
+    T = case.t_total
+    y = torch.empty_like(x)
+    g = torch.empty((T, d.h_v), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(g)
+    o = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        gdn.conv1d_fwd(dims, x, conv_w, cu, slots, conv_pool, has_init, y=y)
+        if e: e[1].record()
+        gdn.gating(a, b, A_log, dt_bias, g=g, beta=beta)
+        if e: e[2].record()
+        gdn.chunk_prefill(dims, y, g, beta, cu, slots, ssm_pool, has_init, case.chunk, 1.0, z, norm_w, 1e-6, o=o)
+        if e: e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in ev]))
+    t_conv, t_gate, t_chunk = ms(0, 1), ms(1, 2), ms(2, 3)
+    t_step = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    nbytes, flops = chunk_algorithmic(T, 1, d.h_k, d.h_v, d.d_k, 2, False, case.chunk)
+    achieved = nbytes / (t_chunk * 1e-3) / 1e9
+    return dict(
+        T=T, wall_s=wall, ms_per_step=wall / args.steps * 1e3, event_ms_per_step=t_step,
+        kernels_ms={"gdn_conv1d_fwd": t_conv, "gdn_gating": t_gate, "gdn_chunk_prefill": t_chunk},
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "chunk_prefill_kernel<bf16,bf16,128,64>", "algorithmic_bytes": nbytes,
+                  "launch_ms": round(t_chunk, 4),
+                  "mfma": {"algorithmic_flops": flops, "achieved_tflops": round(flops / (t_chunk * 1e-3) / 1e12, 2),
+                           "peak_tflops": BF16_PEAK_TFLOPS,
+                           "frac": round(flops / (t_chunk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}},
+        inputs=dict(x=x, a=a, b=b, z=z, case=case))
+
+
+def bench_decode(args, torch, gdn, gi):
+    """256 requests x 1 token, in place, rotating over 3 state pools of 512 slots."""
+    case = gi.decode_case()
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    dev = torch.device("cuda")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(case.seed)
+    pools = []
+    for _ in range(3):
+        ssm = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device=dev, generator=gen) * 0.02
+        conv = torch.randn((case.n_slots, d.c_ch, d.conv_w - 1), device=dev, generator=gen).to(torch.bfloat16)
+        pools.append((ssm, conv))
+    x, a, b, z = bf(case.x()), bf(case.a()), bf(case.b()), bf(case.z())
+    p = case.params
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log = torch.from_numpy(p.A_log).to(dev)
+    dt_bias = torch.from_numpy(p.dt_bias).to(dev)
+    slots = torch.from_numpy(case.slots).to(dev)
+    y = torch.empty_like(x)
+    o = torch.empty((case.n, 1, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+    steps = max(args.steps, 30)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(k, e=None):
+        ssm, conv = pools[k % 3]
+        if e: e[0].record()
+        gdn.conv1d_update(dims, x, conv_w, conv, slots, y=y)
+        if e: e[1].record()
+        gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, None, 1.0, z, norm_w, 1e-6, o=o)
+        if e: e[2].record()
+
+    for k in range(6):
+        step(k)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(k, ev[k])
+    torch.cuda.synchronize()
+    t_conv = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_rec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    nbytes = decode_algorithmic(case.n, 1, d.h_k, d.h_v, d.d_k, 2, 1)
+    gbs = nbytes / (t_rec * 1e-3) / 1e9
+    return {"workload": "decode_256x1", "kernel": "recurrent_kernel<bf16,128>", "launch_ms": round(t_rec, 4),
+            "conv_update_ms": round(t_conv, 4), "algorithmic_bytes": nbytes, "value": round(gbs, 1),
+            "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(case.n / ((t_rec + t_conv) * 1e-3), 1)}
+
+
+def cpu_baseline(inputs) -> dict:
+    """The fp64 oracle on the host, one BLAS thread, on the whole 4096-token
+    sequence (all 32 V heads): conv, gating, recurrence, gated RMSNorm."""
+    from threadpoolctl import threadpool_limits
+    from oracle import gdn_oracle as O
+    case = inputs["case"]
+    d = case.dims
+    p = case.params
+    T = int(os.environ.get("GDN_CPU_BASELINE_TOKENS", case.t_total))
+    x, a, b, z = (case.seq_x(0)[:T], case.seq_a(0)[:T], case.seq_b(0)[:T], case.seq_z(0)[:T])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.layer_sequence(x, a, b, z, p.conv_w, None, p.A_log, p.dt_bias, p.norm_w, None, None,
+                         (d.h_k, d.h_v, d.d_k, d.d_v), 1.0, 1e-6)
+        dt = time.perf_counter() - t0
+    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {T} tokens of the 4096-token sequence, all 32 V heads, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GDN layer's multi-GPU sharding "
+              "is a design, not a measured path", file=sys.stderr)
+        return 2
+
+    import torch
+    import gdn_inputs as gi
+    import gated_deltanet_conv1d_amd as gdn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    gdn.lib()
+    info = device_info()
+    pre = bench_prefill(args, torch, gdn, gi)
+    dec = None if args.no_decode else bench_decode(args, torch, gdn, gi)
+    copy_gbs = copy_bandwidth_gbs(torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(pre["inputs"])
+    T = pre["T"]
+    line = {
+        "metric": METRIC,
+        "value": round(T * args.steps / pre["wall_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_single_4096", "batch": 1, "seq_len": T, "h_k": 16, "h_v": 32,
+                   "head_dim": 128, "conv_w": 4, "chunk": 64, "state": "fp32"},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "kernels_ms": {k: round(v, 4) for k, v in pre["kernels_ms"].items()},
+        "decode": dec,
+        "device": {**info, "copy_gbs": round(copy_gbs, 1)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

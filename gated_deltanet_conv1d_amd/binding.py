@@ -1,0 +1,249 @@
+"""Thin Python binding over libgdn.so (the C ABI declared in include/gdn.h).
+
+Argument marshalling only: every function checks tensor dtypes, devices,
+shapes and contiguity, allocates outputs with torch when the caller passes
+none, and calls the C entry point of the same name on torch's current HIP
+stream.  All arithmetic runs in the HIP kernels behind the ABI.  If the
+library is not built, import succeeds but the first call raises GdnError:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_BF16, GDN_F32 = 0, 1
+_STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE", -4: "GDN_ERR_UNSUPPORTED",
+           -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIGN"}
+
+# Names and signatures of every exported entry point (mirrors include/gdn.h).
+_P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdn_version": (ctypes.c_char_p, []),
+    "gdn_conv1d_fwd": (ctypes.c_int, [_P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P]),
+    "gdn_conv1d_update": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _P]),
+    "gdn_gating": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "gdn_chunk_prefill_workspace_size": (_SZ, [_P, _I32, _I32, _I64, _I32]),
+    "gdn_chunk_prefill": (ctypes.c_int, [_P, _I32, _I32, _I64, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
+                                         _P, _F, _P, _SZ, _P]),
+    "gdn_recurrent_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
+                                            _P, _F, _P]),
+    "gdn_state_copy": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
+}
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+class Dims(NamedTuple):
+    h_k: int = 16
+    h_v: int = 32
+    d_k: int = 128
+    d_v: int = 128
+    conv_w: int = 4
+
+    @property
+    def c_ch(self) -> int:
+        return 2 * self.h_k * self.d_k + self.h_v * self.d_v
+
+
+class _CDims(ctypes.Structure):
+    _fields_ = [("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("conv_w", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so (once) and attach the ABI signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GdnError(f"{LIB_PATH} is not built: run gated_deltanet_conv1d_amd.build.build() first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def version() -> str:
+    return lib().gdn_version().decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = lib().gdn_status_string(rc).decode()
+        raise GdnError(f"{what} failed: {msg} ({rc})")
+
+
+def _cdims(d: Dims) -> ctypes.Structure:
+    return _CDims(*d)
+
+
+def _act(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise GdnError(f"activation dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise GdnError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise GdnError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise GdnError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _shape(t: torch.Tensor, shape, name: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise GdnError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ------------------------------------------------------------------ calls
+def conv1d_fwd(dims: Dims, x, w, cu_seqlens, slots, conv_state, has_init=None, bias=None, y=None):
+    """Causal conv1d + SiLU over a packed varlen batch; updates conv_state in place."""
+    act = _act(x)
+    t_total, n_seq = x.shape[0], slots.shape[0]
+    _shape(x, (t_total, dims.c_ch), "x")
+    _shape(w, (dims.c_ch, dims.conv_w), "w")
+    _shape(cu_seqlens, (n_seq + 1,), "cu_seqlens")
+    if y is None:
+        y = torch.empty_like(x)
+    _check(lib().gdn_conv1d_fwd(ctypes.byref(_cdims(dims)), act, n_seq, t_total, _ptr(x, x.dtype, "x"),
+                                _ptr(w, x.dtype, "w"), _ptr(bias, x.dtype, "bias"),
+                                _ptr(cu_seqlens, torch.int32, "cu_seqlens"), _ptr(slots, torch.int32, "slots"),
+                                _ptr(has_init, torch.uint8, "has_init"), _ptr(conv_state, x.dtype, "conv_state"),
+                                conv_state.shape[0], _ptr(y, x.dtype, "y"), _stream()), "gdn_conv1d_fwd")
+    return y
+
+
+def conv1d_update(dims: Dims, x, w, conv_state, slots, out_slots=None, bias=None, y=None):
+    """Conv for decode / MTP rows [n_seq, t_step, c_ch]; updates the conv pool."""
+    act = _act(x)
+    n_seq, t_step = x.shape[0], x.shape[1]
+    _shape(x, (n_seq, t_step, dims.c_ch), "x")
+    if out_slots is not None:
+        _shape(out_slots, (n_seq, t_step), "out_slots")
+    if y is None:
+        y = torch.empty_like(x)
+    _check(lib().gdn_conv1d_update(ctypes.byref(_cdims(dims)), act, n_seq, t_step, _ptr(x, x.dtype, "x"),
+                                   _ptr(w, x.dtype, "w"), _ptr(bias, x.dtype, "bias"),
+                                   _ptr(conv_state, x.dtype, "conv_state"), conv_state.shape[0],
+                                   _ptr(slots, torch.int32, "slots"), _ptr(out_slots, torch.int32, "out_slots"),
+                                   _ptr(y, x.dtype, "y"), _stream()), "gdn_conv1d_update")
+    return y
+
+
+def gating(a, b, A_log, dt_bias, g=None, beta=None):
+    """g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b); a, b [..., h_v]."""
+    act = _act(a)
+    h_v = a.shape[-1]
+    n = a.numel() // h_v
+    if g is None:
+        g = torch.empty(a.shape, dtype=torch.float32, device=a.device)
+    if beta is None:
+        beta = torch.empty(a.shape, dtype=torch.float32, device=a.device)
+    _check(lib().gdn_gating(act, n, h_v, _ptr(a, a.dtype, "a"), _ptr(b, a.dtype, "b"),
+                            _ptr(A_log, torch.float32, "A_log"), _ptr(dt_bias, torch.float32, "dt_bias"),
+                            _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"), _stream()),
+           "gdn_gating")
+    return g, beta
+
+
+def chunk_prefill_workspace_size(dims: Dims, act: int, n_seq: int, t_total: int, chunk: int) -> int:
+    return int(lib().gdn_chunk_prefill_workspace_size(ctypes.byref(_cdims(dims)), act, n_seq, t_total, chunk))
+
+
+def chunk_prefill(dims: Dims, qkv, g, beta, cu_seqlens, slots, state, has_init=None, chunk: int = 64,
+                  scale: float = 1.0, z=None, norm_w=None, norm_eps: float = 1e-6, o=None, workspace=None):
+    """Chunked gated delta rule over a packed varlen batch; updates state in place."""
+    act = _act(qkv)
+    t_total, n_seq = qkv.shape[0], slots.shape[0]
+    _shape(qkv, (t_total, dims.c_ch), "qkv")
+    _shape(state, (state.shape[0], dims.h_v, dims.d_v, dims.d_k), "state")
+    if o is None:
+        o = torch.empty((t_total, dims.h_v, dims.d_v), dtype=qkv.dtype, device=qkv.device)
+    ws = chunk_prefill_workspace_size(dims, act, n_seq, t_total, chunk)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=qkv.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_chunk_prefill(ctypes.byref(_cdims(dims)), act, n_seq, t_total, chunk, scale,
+                                   _ptr(qkv, qkv.dtype, "qkv"), _ptr(g, torch.float32, "g"),
+                                   _ptr(beta, torch.float32, "beta"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+                                   _ptr(slots, torch.int32, "slots"), _ptr(has_init, torch.uint8, "has_init"),
+                                   _ptr(state, torch.float32, "state"), state.shape[0], _ptr(o, qkv.dtype, "o"),
+                                   _ptr(z, qkv.dtype, "z"), _ptr(norm_w, qkv.dtype, "norm_w"), norm_eps,
+                                   _ptr(workspace, None, "workspace"), ws_bytes, _stream()), "gdn_chunk_prefill")
+    return o
+
+
+def recurrent_decode(dims: Dims, qkv, a, b, A_log, dt_bias, state, slots, out_slots=None, scale: float = 1.0,
+                     z=None, norm_w=None, norm_eps: float = 1e-6, o=None):
+    """Fused recurrent step over request-major rows [n_seq, t_step, ...]."""
+    act = _act(qkv)
+    n_seq, t_step = qkv.shape[0], qkv.shape[1]
+    _shape(qkv, (n_seq, t_step, dims.c_ch), "qkv")
+    _shape(a, (n_seq, t_step, dims.h_v), "a")
+    if out_slots is not None:
+        _shape(out_slots, (n_seq, t_step), "out_slots")
+    if o is None:
+        o = torch.empty((n_seq, t_step, dims.h_v, dims.d_v), dtype=qkv.dtype, device=qkv.device)
+    _check(lib().gdn_recurrent_decode(ctypes.byref(_cdims(dims)), act, n_seq, t_step, scale,
+                                      _ptr(qkv, qkv.dtype, "qkv"), _ptr(a, qkv.dtype, "a"), _ptr(b, qkv.dtype, "b"),
+                                      _ptr(A_log, torch.float32, "A_log"), _ptr(dt_bias, torch.float32, "dt_bias"),
+                                      _ptr(state, torch.float32, "state"), state.shape[0],
+                                      _ptr(slots, torch.int32, "slots"), _ptr(out_slots, torch.int32, "out_slots"),
+                                      _ptr(o, qkv.dtype, "o"), _ptr(z, qkv.dtype, "z"),
+                                      _ptr(norm_w, qkv.dtype, "norm_w"), norm_eps, _stream()),
+           "gdn_recurrent_decode")
+    return o
+
+
+def state_copy(dims: Dims, state, src, dst, conv_state=None):
+    """Bitwise state[dst[i]] <- state[src[i]] (and the conv pool, when given)."""
+    act = GDN_BF16 if conv_state is None else _act(conv_state)
+    _check(lib().gdn_state_copy(ctypes.byref(_cdims(dims)), act, _ptr(state, torch.float32, "state"),
+                                _ptr(conv_state, None, "conv_state"), state.shape[0], _ptr(src, torch.int32, "src"),
+                                _ptr(dst, torch.int32, "dst"), src.shape[0], _stream()), "gdn_state_copy")
+
+
+# ------------------------------------------------------- layer sequences
+def prefill_layer(dims: Dims, x, conv_w, A_log, dt_bias, a, b, cu_seqlens, slots, conv_state, state, has_init=None,
+                  chunk: int = 64, scale: float = 1.0, z=None, norm_w=None, norm_eps: float = 1e-6, conv_b=None):
+    """The prefill hot path as the pages order it: conv1d + SiLU, gating, then
+    the chunked gated delta rule with fused q/k L2 norm and gated RMSNorm.
+    Returns (out, y, g, beta)."""
+    y = conv1d_fwd(dims, x, conv_w, cu_seqlens, slots, conv_state, has_init, conv_b)
+    g, beta = gating(a, b, A_log, dt_bias)
+    out = chunk_prefill(dims, y, g, beta, cu_seqlens, slots, state, has_init, chunk, scale, z, norm_w, norm_eps)
+    return out, y, g, beta
+
+
+def decode_layer(dims: Dims, x, conv_w, A_log, dt_bias, a, b, slots, conv_state, state, out_slots=None,
+                 scale: float = 1.0, z=None, norm_w=None, norm_eps: float = 1e-6, conv_b=None):
+    """The decode / MTP hot path: conv update, then the fused recurrent step.
+    Returns (out, y)."""
+    y = conv1d_update(dims, x, conv_w, conv_state, slots, out_slots, conv_b)
+    out = recurrent_decode(dims, y, a, b, A_log, dt_bias, state, slots, out_slots, scale, z, norm_w, norm_eps)
+    return out, y

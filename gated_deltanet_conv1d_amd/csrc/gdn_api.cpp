@@ -1,0 +1,182 @@
+// C ABI of the GDN hot path: argument validation and kernel dispatch.
+// The calls, shapes and conventions are documented in include/gdn.h.
+// Nothing here allocates, synchronises, or reads device memory.
+#include "../../include/gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "gdn_launch.hpp"
+
+namespace {
+
+using gdn::Shape;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int check_act(int32_t act) { return (act == GDN_BF16 || act == GDN_F32) ? GDN_OK : GDN_ERR_DTYPE; }
+
+// Validate a gdn_dims and turn it into the kernels' Shape.
+int check_dims(const gdn_dims* d, Shape* s) {
+  if (!d) return GDN_ERR_NULL;
+  if (d->h_k <= 0 || d->h_v <= 0 || d->d_k <= 0 || d->d_v <= 0 || d->conv_w <= 0) return GDN_ERR_SHAPE;
+  if (d->h_v % d->h_k != 0) return GDN_ERR_SHAPE;
+  if (d->d_k != d->d_v) return GDN_ERR_UNSUPPORTED;
+  if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return GDN_ERR_UNSUPPORTED;
+  if (d->conv_w < 2 || d->conv_w > 4) return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)2 * d->h_k * d->d_k + (int64_t)d->h_v * d->d_v > (1 << 24)) return GDN_ERR_UNSUPPORTED;
+  *s = Shape{d->h_k, d->h_v, d->d_k, d->conv_w};
+  return GDN_OK;
+}
+
+// All pointers in the list must be non-null.
+template <typename... P>
+int need(P... p) {
+  const void* ptrs[] = {static_cast<const void*>(p)...};
+  for (const void* q : ptrs)
+    if (!q) return GDN_ERR_NULL;
+  return GDN_OK;
+}
+
+// All non-null pointers in the list must be 16-byte aligned.
+template <typename... P>
+int align_ok(P... p) {
+  const void* ptrs[] = {static_cast<const void*>(p)...};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
+inline int from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+#define GDN_TRY(expr)              \
+  do {                             \
+    int rc_ = (expr);              \
+    if (rc_ != GDN_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: invalid or inconsistent size";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown activation dtype";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: size not supported by this build";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: a kernel launch failed";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer not 16-byte aligned";
+  }
+  return "unknown gdn_status";
+}
+
+const char* gdn_version(void) { return "0.1.0"; }
+
+int gdn_conv1d_fwd(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, const void* x, const void* w,
+                   const void* bias, const int32_t* cu_seqlens, const int32_t* slots, const uint8_t* has_init,
+                   void* conv_state, int32_t n_slots, void* y, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq == 0 && t_total > 0) return GDN_ERR_SHAPE;
+  if (n_seq == 0) return GDN_OK;
+  GDN_TRY(need(w, cu_seqlens, slots, conv_state));
+  if (t_total > 0) GDN_TRY(need(x, y));
+  if (x && x == y) return GDN_ERR_SHAPE;
+  GDN_TRY(align_ok(x, w, bias, conv_state, y));
+  gdn::ConvFwdArgs a{s, act == GDN_BF16, n_seq, t_total, x, w, bias, cu_seqlens, slots, has_init,
+                     conv_state, n_slots, y};
+  return from_hip(gdn::launch_conv1d_fwd(a, (hipStream_t)stream));
+}
+
+int gdn_conv1d_update(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step, const void* x, const void* w,
+                      const void* bias, void* conv_state, int32_t n_slots, const int32_t* slots,
+                      const int32_t* out_slots, void* y, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (n_seq < 0 || t_step < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq == 0 || t_step == 0) return GDN_OK;
+  GDN_TRY(need(x, w, conv_state, slots, y));
+  if (x == y) return GDN_ERR_SHAPE;
+  GDN_TRY(align_ok(x, w, bias, conv_state, y));
+  gdn::ConvUpdateArgs a{s, act == GDN_BF16, n_seq, t_step, x, w, bias, conv_state, n_slots, slots, out_slots, y};
+  return from_hip(gdn::launch_conv1d_update(a, (hipStream_t)stream));
+}
+
+int gdn_gating(int32_t act, int64_t n_tokens, int32_t h_v, const void* a, const void* b, const float* A_log,
+               const float* dt_bias, float* g, float* beta, void* stream) {
+  GDN_TRY(check_act(act));
+  if (n_tokens < 0 || h_v <= 0) return GDN_ERR_SHAPE;
+  if (n_tokens == 0) return GDN_OK;
+  GDN_TRY(need(a, b, A_log, dt_bias, g, beta));
+  gdn::GatingArgs args{act == GDN_BF16, n_tokens, h_v, a, b, A_log, dt_bias, g, beta};
+  return from_hip(gdn::launch_gating(args, (hipStream_t)stream));
+}
+
+size_t gdn_chunk_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total,
+                                        int32_t chunk) {
+  Shape s;
+  if (check_dims(dims, &s) != GDN_OK || check_act(act) != GDN_OK || n_seq < 0 || t_total < 0) return 0;
+  return gdn::chunk_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
+}
+
+int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk, float scale,
+                      const void* qkv, const float* g, const float* beta, const int32_t* cu_seqlens,
+                      const int32_t* slots, const uint8_t* has_init, float* state, int32_t n_slots, void* o,
+                      const void* z, const void* norm_w, float norm_eps, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq == 0 && t_total > 0) return GDN_ERR_SHAPE;
+  if (!gdn::chunk_supported(s.d, chunk, act == GDN_BF16)) return GDN_ERR_UNSUPPORTED;
+  if (n_seq == 0) return GDN_OK;
+  GDN_TRY(need(cu_seqlens, slots, state));
+  if (t_total > 0) GDN_TRY(need(qkv, g, beta, o));
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+  GDN_TRY(align_ok(qkv, state, o, z, workspace));
+  const size_t need_ws = gdn::chunk_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
+  if (need_ws > 0 && (!workspace || ws_bytes < need_ws)) return GDN_ERR_WORKSPACE;
+  gdn::ChunkArgs a{s,     act == GDN_BF16, n_seq,  t_total, chunk,  scale,    qkv,      g,         beta,    cu_seqlens,
+                   slots, has_init,        state,  n_slots, o,      z,        norm_w,   norm_eps,  workspace, ws_bytes};
+  return from_hip(gdn::launch_chunk_prefill(a, (hipStream_t)stream));
+}
+
+int gdn_recurrent_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step, float scale,
+                         const void* qkv, const void* a, const void* b, const float* A_log, const float* dt_bias,
+                         float* state, int32_t n_slots, const int32_t* slots, const int32_t* out_slots, void* o,
+                         const void* z, const void* norm_w, float norm_eps, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (n_seq < 0 || t_step < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq == 0 || t_step == 0) return GDN_OK;
+  GDN_TRY(need(qkv, a, b, A_log, dt_bias, state, slots, o));
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+  GDN_TRY(align_ok(qkv, state, o, z));
+  gdn::RecurrentArgs args{s,     act == GDN_BF16, n_seq,   t_step, scale,     qkv, a,      b,       A_log,
+                          dt_bias, state,         n_slots, slots,  out_slots, o,   z,      norm_w, norm_eps};
+  return from_hip(gdn::launch_recurrent(args, (hipStream_t)stream));
+}
+
+int gdn_state_copy(const gdn_dims* dims, int32_t act, float* state, void* conv_state, int32_t n_slots,
+                   const int32_t* src, const int32_t* dst, int32_t n, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (n < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n == 0) return GDN_OK;
+  GDN_TRY(need(state, src, dst));
+  GDN_TRY(align_ok(state, conv_state));
+  gdn::StateCopyArgs a{s, act == GDN_BF16, state, conv_state, n_slots, src, dst, n};
+  return from_hip(gdn::launch_state_copy(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Host-side launchers, one per kernel family.  Each lives in the .hip file of
+// its kernels; gdn_api.cpp validates arguments and then calls these.
+// Arguments are already validated: sizes supported, pointers non-null where required.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct Shape {
+  int h_k, h_v, d, conv_w;  // d = d_k = d_v
+  int c_ch() const { return 2 * h_k * d + h_v * d; }
+};
+
+struct ConvFwdArgs {
+  Shape s;
+  bool bf16;
+  int32_t n_seq;
+  int64_t t_total;
+  const void* x;
+  const void* w;
+  const void* bias;
+  const int32_t* cu_seqlens;
+  const int32_t* slots;
+  const uint8_t* has_init;
+  void* conv_state;
+  int32_t n_slots;
+  void* y;
+};
+hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t st);
+
+struct ConvUpdateArgs {
+  Shape s;
+  bool bf16;
+  int32_t n_seq, t_step;
+  const void* x;
+  const void* w;
+  const void* bias;
+  void* conv_state;
+  int32_t n_slots;
+  const int32_t* slots;
+  const int32_t* out_slots;
+  void* y;
+};
+hipError_t launch_conv1d_update(const ConvUpdateArgs& a, hipStream_t st);
+
+struct GatingArgs {
+  bool bf16;
+  int64_t n_tokens;
+  int32_t h_v;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  float* g;
+  float* beta;
+};
+hipError_t launch_gating(const GatingArgs& a, hipStream_t st);
+
+struct StateCopyArgs {
+  Shape s;
+  bool bf16;
+  float* state;
+  void* conv_state;
+  int32_t n_slots;
+  const int32_t* src;
+  const int32_t* dst;
+  int32_t n;
+};
+hipError_t launch_state_copy(const StateCopyArgs& a, hipStream_t st);
+
+struct RecurrentArgs {
+  Shape s;
+  bool bf16;
+  int32_t n_seq, t_step;
+  float scale;
+  const void* qkv;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  float* state;
+  int32_t n_slots;
+  const int32_t* slots;
+  const int32_t* out_slots;
+  void* o;
+  const void* z;
+  const void* norm_w;
+  float norm_eps;
+};
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t st);
+
+struct ChunkArgs {
+  Shape s;
+  bool bf16;
+  int32_t n_seq;
+  int64_t t_total;
+  int32_t chunk;
+  float scale;
+  const void* qkv;
+  const float* g;
+  const float* beta;
+  const int32_t* cu_seqlens;
+  const int32_t* slots;
+  const uint8_t* has_init;
+  float* state;
+  int32_t n_slots;
+  void* o;
+  const void* z;
+  const void* norm_w;
+  float norm_eps;
+  void* workspace;
+  size_t ws_bytes;
+};
+// True when the chunk kernel has an instantiation for (d, chunk, dtype).
+bool chunk_supported(int d, int chunk, bool bf16);
+size_t chunk_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk);
+hipError_t launch_chunk_prefill(const ChunkArgs& a, hipStream_t st);
+
+}  // namespace gdn

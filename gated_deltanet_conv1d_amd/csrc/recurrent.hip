@@ -1,0 +1,220 @@
+// Fused recurrent GDN step for decode (t_step = 1) and MTP draft tokens
+// (t_step > 1): gating, q/k L2 norm, the token-wise gated delta rule and the
+// gated-RMSNorm epilogue in one kernel.
+//
+// The fused recurrent GDN kernel of LightLLM PR #1184 "[model] support
+// Qwen3next" (Highlights, "Advanced Triton Kernel Optimizations") and the
+// recurrent linear-attention operation of LightLLM #1097 (Highlights,
+// "Specialized Triton Kernels"); per-draft-position states follow the MTP
+// buffers of PR #1184 ("Enhanced Multi-Token Prediction").  Per token, with
+// the state S in R^{d_v x d_k} and row i of S written s_i:
+//   S <- e^g S;  u_i = beta (v_i - s_i.k);  s_i <- s_i + u_i k;  o_i = scale s_i.q
+// and since rows are independent, o_i = scale (e^g (s_i.q) + u_i (k.q)) needs
+// only the two dot products of the decayed old row.
+//
+// HBM design: the step is bound by the fp32 state (64 KiB per head at d=128,
+// read once and written once).  One 256-thread workgroup owns one (request,
+// V head) state; 16 lanes (one DPP row) hold one state row, each lane D/16
+// consecutive-in-16-byte-groups columns, so every state load/store instruction
+// moves 256-byte contiguous row segments.  All D*D/256 values per thread are
+// loaded up front (D/16 rows x D/16 columns) so a workgroup has its whole
+// state in flight before the first reduction.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+struct RowLayout {
+  static constexpr int F = D / 16;               // columns per lane
+  static constexpr int VW = F < 4 ? F : 4;       // floats per vector access
+  static constexpr int NG = F / VW;              // vector groups per lane
+  static constexpr int PASSES = D / 16;          // rows per thread (16 rows per pass)
+  // first column of vector group j for column lane c
+  __device__ static int col(int j, int c) { return j * 16 * VW + VW * c; }
+};
+
+template <int VW>
+__device__ __forceinline__ void ld_f32(const float* p, float* v) {
+  if constexpr (VW == 4) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  } else if constexpr (VW == 2) {
+    float2 a = *reinterpret_cast<const float2*>(p);
+    v[0] = a.x; v[1] = a.y;
+  } else {
+    v[0] = *p;
+  }
+}
+template <int VW>
+__device__ __forceinline__ void st_f32(float* p, const float* v) {
+  if constexpr (VW == 4) *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  else if constexpr (VW == 2) *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  else *p = v[0];
+}
+template <int VW, typename T>
+__device__ __forceinline__ void ld_act(const T* p, float* v) {
+#pragma unroll
+  for (int i = 0; i < VW; ++i) v[i] = to_f32(p[i]);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ a_in, const T* __restrict__ b_in,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float* __restrict__ state, int32_t n_slots,
+    const int32_t* __restrict__ slots, const int32_t* __restrict__ out_slots, T* __restrict__ o,
+    const T* __restrict__ z, const T* __restrict__ norm_w, float norm_eps, float scale, int32_t t_step,
+    int32_t h_k, int32_t h_v) {
+  using L = RowLayout<D>;
+  constexpr int F = L::F, VW = L::VW, NG = L::NG, PASSES = L::PASSES;
+  __shared__ float red[kThreads / 64];
+
+  const int i = blockIdx.x / h_v;
+  const int h = blockIdx.x % h_v;
+  const int hk = h / (h_v / h_k);
+  const int tid = threadIdx.x;
+  const int r16 = tid >> 4;   // row within a pass
+  const int c = tid & 15;     // column lane
+  const int c_ch = 2 * h_k * D + h_v * D;
+  const int32_t slot = slots[i];
+
+  if (!slot_ok(slot, n_slots)) {  // padding request: zero outputs
+    for (int t = 0; t < t_step; ++t)
+      for (int r = tid; r < D; r += kThreads) o[(((int64_t)i * t_step + t) * h_v + h) * D + r] = from_f32<T>(0.0f);
+    return;
+  }
+
+  // ---- whole state into registers
+  float s[PASSES][F];
+  const float* src = state + ((int64_t)slot * h_v + h) * D * D;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+    for (int j = 0; j < NG; ++j) ld_f32<VW>(src + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+
+  const float neg_A = -expf(A_log[h]);
+  const float dtb = dt_bias[h];
+
+  for (int t = 0; t < t_step; ++t) {
+    const int64_t row = (int64_t)i * t_step + t;
+    const T* q_ptr = qkv + row * c_ch + hk * D;
+    const T* k_ptr = qkv + row * c_ch + (h_k + hk) * D;
+    const T* v_ptr = qkv + row * c_ch + 2 * h_k * D + h * D;
+
+    float kv[F], qv[F];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      ld_act<VW>(k_ptr + L::col(j, c), &kv[j * VW]);
+      ld_act<VW>(q_ptr + L::col(j, c), &qv[j * VW]);
+    }
+    float vrow[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) vrow[p] = to_f32(v_ptr[p * 16 + r16]);
+
+    // q, k L2 norm over the head (eps 1e-6 inside the root) and k.q
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < F; ++e) { sk = fmaf(kv[e], kv[e], sk); sq = fmaf(qv[e], qv[e], sq); }
+    sk = group_sum<16>(sk);
+    sq = group_sum<16>(sq);
+    const float rk = rsqrtf(sk + 1e-6f), rq = rsqrtf(sq + 1e-6f);
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < F; ++e) { kv[e] *= rk; qv[e] *= rq; kq = fmaf(kv[e], qv[e], kq); }
+    kq = group_sum<16>(kq);
+
+    // gating
+    const float g = neg_A * softplusf_(to_f32(a_in[row * h_v + h]) + dtb);
+    const float beta = sigmoidf_(to_f32(b_in[row * h_v + h]));
+    const float eg = expf(g);
+
+    float orow[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      float dk = 0.f, dq = 0.f;
+#pragma unroll
+      for (int e = 0; e < F; ++e) { dk = fmaf(s[p][e], kv[e], dk); dq = fmaf(s[p][e], qv[e], dq); }
+      dk = group_sum<16>(dk);
+      dq = group_sum<16>(dq);
+      const float u = beta * (vrow[p] - eg * dk);
+      orow[p] = scale * (eg * dq + u * kq);
+#pragma unroll
+      for (int e = 0; e < F; ++e) s[p][e] = fmaf(eg, s[p][e], u * kv[e]);
+    }
+
+    T* o_ptr = o + (row * h_v + h) * D;
+    if (z) {
+      // gated RMSNorm over d_v: every lane of a row group holds that row's o
+      float ss = 0.f;
+      if (c == 0) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) ss = fmaf(orow[p], orow[p], ss);
+      }
+      ss = wave_sum(ss);
+      if ((tid & 63) == 0) red[tid >> 6] = ss;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
+      __syncthreads();
+      const float rstd = rsqrtf(tot / D + norm_eps);
+      const T* z_ptr = z + (row * h_v + h) * D;
+      if (c == 0) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          const int r = p * 16 + r16;
+          o_ptr[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * siluf_(to_f32(z_ptr[r])));
+        }
+      }
+    } else if (c == 0) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) o_ptr[p * 16 + r16] = from_f32<T>(orow[p]);
+    }
+
+    if (out_slots) {
+      const int32_t d = out_slots[row];
+      if (slot_ok(d, n_slots)) {
+        float* dst = state + ((int64_t)d * h_v + h) * D * D;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+          for (int j = 0; j < NG; ++j) st_f32<VW>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+      }
+    }
+  }
+
+  if (!out_slots) {
+    float* dst = state + ((int64_t)slot * h_v + h) * D * D;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int j = 0; j < NG; ++j) st_f32<VW>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+  }
+}
+
+template <typename T, int D>
+hipError_t impl(const RecurrentArgs& a, hipStream_t st) {
+  if (a.n_seq == 0 || a.t_step == 0) return hipSuccess;
+  hipLaunchKernelGGL((recurrent_kernel<T, D>), dim3((unsigned)((int64_t)a.n_seq * a.s.h_v)), dim3(kThreads), 0, st,
+                     (const T*)a.qkv, (const T*)a.a, (const T*)a.b, a.A_log, a.dt_bias, a.state, a.n_slots, a.slots,
+                     a.out_slots, (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step,
+                     a.s.h_k, a.s.h_v);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t st) {
+  switch (a.s.d) {
+    case 16: return a.bf16 ? impl<bf16, 16>(a, st) : impl<float, 16>(a, st);
+    case 32: return a.bf16 ? impl<bf16, 32>(a, st) : impl<float, 32>(a, st);
+    case 64: return a.bf16 ? impl<bf16, 64>(a, st) : impl<float, 64>(a, st);
+    case 128: return a.bf16 ? impl<bf16, 128>(a, st) : impl<float, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

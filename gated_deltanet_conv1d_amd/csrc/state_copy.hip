@@ -1,0 +1,68 @@
+// Slot-indexed state copy for the MTP commit: pool[dst[i]] <- pool[src[i]],
+// bitwise, for the fp32 recurrent-state pool and the conv-state pool.  This
+// is the buffer copy of LightLLM PR #1184 "[model] support Qwen3next" (review
+// comment on the copy docstring: source and destination indices as 1-D
+// arrays), done here as one HBM-bound kernel of 16-byte vector moves.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kIter = 8;                                     // 16-byte vectors per thread per piece
+constexpr int64_t kPiece = (int64_t)kThreads * kIter * 16;  // bytes per block
+
+// grid: n pairs x (state pieces + conv pieces)
+__global__ __launch_bounds__(kThreads) void state_copy_kernel(
+    uint8_t* __restrict__ state, uint8_t* __restrict__ conv, int64_t state_bytes, int64_t conv_bytes,
+    int32_t n_slots, const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int32_t state_pieces,
+    int32_t pieces) {
+  const int pair = blockIdx.x / pieces;
+  const int piece = blockIdx.x % pieces;
+  const int32_t s = src[pair], d = dst[pair];
+  if (!slot_ok(s, n_slots) || !slot_ok(d, n_slots) || s == d) return;
+  const uint8_t* from;
+  uint8_t* to;
+  int64_t off, bytes;
+  if (piece < state_pieces) {
+    from = state + (int64_t)s * state_bytes;
+    to = state + (int64_t)d * state_bytes;
+    off = (int64_t)piece * kPiece;
+    bytes = state_bytes;
+  } else {
+    if (!conv) return;
+    from = conv + (int64_t)s * conv_bytes;
+    to = conv + (int64_t)d * conv_bytes;
+    off = (int64_t)(piece - state_pieces) * kPiece;
+    bytes = conv_bytes;
+  }
+  uint4 v[kIter];
+#pragma unroll
+  for (int k = 0; k < kIter; ++k) {
+    const int64_t o = off + ((int64_t)k * kThreads + threadIdx.x) * 16;
+    if (o < bytes) v[k] = *reinterpret_cast<const uint4*>(from + o);
+  }
+#pragma unroll
+  for (int k = 0; k < kIter; ++k) {
+    const int64_t o = off + ((int64_t)k * kThreads + threadIdx.x) * 16;
+    if (o < bytes) *reinterpret_cast<uint4*>(to + o) = v[k];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_state_copy(const StateCopyArgs& a, hipStream_t st) {
+  if (a.n == 0) return hipSuccess;
+  const int64_t state_bytes = (int64_t)a.s.h_v * a.s.d * a.s.d * 4;
+  const int64_t conv_bytes = (int64_t)a.s.c_ch() * (a.s.conv_w - 1) * (a.bf16 ? 2 : 4);
+  const int32_t sp = (int32_t)((state_bytes + kPiece - 1) / kPiece);
+  const int32_t cp = a.conv_state ? (int32_t)((conv_bytes + kPiece - 1) / kPiece) : 0;
+  const int32_t pieces = sp + cp;
+  hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((int64_t)a.n * pieces)), dim3(kThreads), 0, st,
+                     (uint8_t*)a.state, (uint8_t*)a.conv_state, state_bytes, conv_bytes, a.n_slots, a.src, a.dst,
+                     sp, pieces);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,120 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+The library must load and export every entry point declared in
+include/gdn.h, and argument validation must return the documented status
+codes before anything touches the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_conv1d_amd as gdn
+from gated_deltanet_conv1d_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return gdn.lib()
+
+
+def D(h_k=16, h_v=32, d=128, w=4):
+    return ctypes.byref(binding._CDims(h_k, h_v, d, d, w))
+
+
+FAKE = 0x1000  # a 16-byte-aligned non-null address; never dereferenced by failing calls
+
+
+def test_exports_every_header_symbol(L):
+    names = header_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in binding.SIGNATURES, n
+
+
+def test_version_and_status_strings(L):
+    assert gdn.version() == "0.1.0"
+    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIGN):
+        assert L.gdn_status_string(code).decode().startswith(binding._STATUS[code])
+
+
+def test_dims_validation(L):
+    args = (0, 1, 8, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1, FAKE + 16, None)
+    assert L.gdn_conv1d_fwd(None, *args) == NULL
+    assert L.gdn_conv1d_fwd(D(h_k=3, h_v=32), *args) == SHAPE          # h_v % h_k
+    assert L.gdn_conv1d_fwd(D(d=96), *args) == UNSUP
+    assert L.gdn_conv1d_fwd(D(w=5), *args) == UNSUP
+    assert L.gdn_conv1d_fwd(D(h_k=0), *args) == SHAPE
+    assert L.gdn_conv1d_fwd(D(), 7, *args[1:]) == DTYPE
+
+
+def test_conv_fwd_argument_errors(L):
+    assert L.gdn_conv1d_fwd(D(), 0, -1, 8, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1, FAKE + 16, None) == SHAPE
+    assert L.gdn_conv1d_fwd(D(), 0, 0, 8, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1, FAKE + 16, None) == SHAPE
+    assert L.gdn_conv1d_fwd(D(), 0, 0, 0, None, None, None, None, None, None, None, 1, None, None) == OK
+    assert L.gdn_conv1d_fwd(D(), 0, 1, 8, None, FAKE, None, FAKE, FAKE, None, FAKE, 1, FAKE + 16, None) == NULL
+    assert L.gdn_conv1d_fwd(D(), 0, 1, 8, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1, FAKE, None) == SHAPE  # y == x
+    assert L.gdn_conv1d_fwd(D(), 0, 1, 8, FAKE + 2, FAKE, None, FAKE, FAKE, None, FAKE, 1, FAKE + 16, None) == ALIGN
+
+
+def test_update_and_gating_errors(L):
+    assert L.gdn_conv1d_update(D(), 0, -1, 1, FAKE, FAKE, None, FAKE, 4, FAKE, None, FAKE + 16, None) == SHAPE
+    assert L.gdn_conv1d_update(D(), 0, 2, 1, None, FAKE, None, FAKE, 4, FAKE, None, FAKE + 16, None) == NULL
+    assert L.gdn_conv1d_update(D(), 0, 0, 1, None, None, None, None, 4, None, None, None, None) == OK
+    assert L.gdn_gating(0, 10, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_gating(2, 10, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == DTYPE
+    assert L.gdn_gating(0, 10, 32, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == NULL
+    assert L.gdn_gating(0, 0, 32, None, None, None, None, None, None, None) == OK
+
+
+def chunk_call(L, dims=None, act=0, n_seq=1, t_total=64, chunk=64, z=None, norm_w=None, eps=1e-6, qkv=FAKE,
+               ws=None, ws_bytes=0):
+    return L.gdn_chunk_prefill(dims or D(), act, n_seq, t_total, chunk, 1.0, qkv, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, 4, FAKE + 16, z, norm_w, eps, ws, ws_bytes, None)
+
+
+def test_chunk_prefill_errors(L):
+    assert chunk_call(L, chunk=48) == UNSUP
+    assert chunk_call(L, chunk=128) == UNSUP
+    assert chunk_call(L, act=1, chunk=64) == UNSUP          # fp32 at d=128 takes chunk <= 32
+    assert chunk_call(L, z=FAKE) == NULL                     # z without norm_w
+    assert chunk_call(L, eps=-1.0) == SHAPE
+    assert chunk_call(L, qkv=None) == NULL
+    assert chunk_call(L, qkv=FAKE + 8) == ALIGN
+    assert chunk_call(L, n_seq=0, t_total=5) == SHAPE
+    assert chunk_call(L, n_seq=0, t_total=0) == OK
+    assert L.gdn_chunk_prefill_workspace_size(D(), 0, 1, 4096, 64) == 0
+
+
+def test_recurrent_and_copy_errors(L):
+    base = (1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE + 16, None, None, 1e-6, None)
+    assert L.gdn_recurrent_decode(D(), 0, -2, 1, *base) == SHAPE
+    assert L.gdn_recurrent_decode(D(), 0, 0, 1, *base) == OK
+    assert L.gdn_recurrent_decode(D(), 0, 2, 1, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, FAKE, None,
+                                  FAKE + 16, None, None, 1e-6, None) == NULL
+    assert L.gdn_recurrent_decode(D(), 0, 2, 1, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None,
+                                  FAKE + 16, FAKE, None, 1e-6, None) == NULL
+    assert L.gdn_state_copy(D(), 0, FAKE, None, 8, FAKE, FAKE, -1, None) == SHAPE
+    assert L.gdn_state_copy(D(), 0, None, None, 8, FAKE, FAKE, 3, None) == NULL
+    assert L.gdn_state_copy(D(), 0, FAKE, FAKE + 4, 8, FAKE, FAKE, 3, None) == ALIGN
+    assert L.gdn_state_copy(D(), 0, None, None, 8, None, None, 0, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, gdn.Dims().c_ch, dtype=torch.bfloat16)
+    with pytest.raises(gdn.GdnError):
+        gdn.conv1d_fwd(gdn.Dims(), x, torch.zeros(gdn.Dims().c_ch, 4, dtype=torch.bfloat16),
+                       torch.tensor([0, 4], dtype=torch.int32), torch.tensor([0], dtype=torch.int32),
+                       torch.zeros(1, gdn.Dims().c_ch, 3, dtype=torch.bfloat16))

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Sizes: small multi-chunk cases with ragged tails are checked element by
+element; the full-size workloads are checked element by element where the
+oracle finishes in seconds (single 4096-token prefill, decode, MTP) and on
+sampled sequences/heads otherwise (the ~271k-token varlen batch).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import gated_deltanet_conv1d_amd as gdn
+from oracle import gdn_oracle as O
+from tests.gpu_cases import TOL, DevPrefill, act_dtype, compare_prefill, dev, host, i32, log, params_dict, rel, u8
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- tiny case
+def test_tiny_case_recurrent_and_chunked():
+    """One sequence, T=64, 1 QK + 1 V head, d=16, fp32, no conv: recurrent and
+    chunked (C=16) outputs and final states against the oracle at 1e-4."""
+    c = gi.tiny_case()
+    dims = gdn.Dims(1, 1, 16, 16, 4)
+    qkv = np.concatenate([c.q[:, 0], c.k[:, 0], c.v[:, 0]], axis=1)          # [64, 48]
+    g_ref, b_ref = O.gating(c.a, c.b, c.A_log, c.dt_bias)
+    o_ref, S_ref, _ = O.gated_delta_rule(O.l2norm(c.q), O.l2norm(c.k), c.v, g_ref, b_ref, None, 1.0)
+
+    # recurrent: one request, 64 tokens, in place
+    state = torch.zeros((1, 1, 16, 16), dtype=torch.float32, device="cuda")
+    o_rec = gdn.recurrent_decode(dims, dev(qkv[None], torch.float32), dev(c.a[None], torch.float32),
+                                 dev(c.b[None], torch.float32), dev(c.A_log, torch.float32),
+                                 dev(c.dt_bias, torch.float32), state, i32([0]))
+    torch.cuda.synchronize()
+    e_rec = rel(host(o_rec[0, :, 0]), o_ref[:, 0])
+    e_rec_s = rel(host(state[0, 0]), S_ref[0])
+
+    # chunked, C = 16
+    state2 = torch.zeros_like(state)
+    g, beta = gdn.gating(dev(c.a, torch.float32), dev(c.b, torch.float32), dev(c.A_log, torch.float32),
+                         dev(c.dt_bias, torch.float32))
+    assert rel(host(g), g_ref) < 1e-6 and rel(host(beta), b_ref) < 1e-6
+    o_chk = gdn.chunk_prefill(dims, dev(qkv, torch.float32), g, beta, i32([0, 64]), i32([0]), state2,
+                              u8([0]), chunk=16)
+    torch.cuda.synchronize()
+    e_chk = rel(host(o_chk[:, 0]), o_ref[:, 0])
+    e_chk_s = rel(host(state2[0, 0]), S_ref[0])
+    log(f"tiny: recurrent o {e_rec:.2e} S {e_rec_s:.2e}; chunked o {e_chk:.2e} S {e_chk_s:.2e}")
+    assert max(e_rec, e_rec_s, e_chk, e_chk_s) < TOL["f32"]
+
+
+# --------------------------------------------------- small varlen prefills
+SMALL_LENGTHS = [1, 3, 17, 64, 65, 200, 0, 130]
+
+
+@pytest.mark.parametrize("act,d,chunk", [("bf16", 128, 64), ("f32", 128, 32), ("bf16", 64, 32), ("f32", 16, 16),
+                                         ("bf16", 32, 16), ("f32", 64, 64)])
+def test_prefill_small_varlen(act, d, chunk):
+    """Several sequences (ragged tails, len 0 and 1, mixed has_init, permuted
+    slots, one padding entry) through conv -> gating -> chunked rule ->
+    gated RMSNorm; outputs, recurrent states and conv states per slot."""
+    dims = gi.Dims(2, 4, d, d, 4)
+    case = gi.varlen_case(seed=11, dims=dims, act=act, lengths=np.array(SMALL_LENGTHS), n_slots=12, chunk=chunk)
+    case.has_init = np.array([1, 0, 1, 1, 0, 1, 0, 1], np.uint8)
+    case.slots[5] = -1                                           # padding entry
+    dp = DevPrefill(case)
+    conv_before = dp.conv_pool.clone()
+    ssm_before = dp.ssm_pool.clone()
+    out, *_ = dp.run()
+    torch.cuda.synchronize()
+    real = [i for i in range(case.n_seq) if case.slots[i] >= 0]
+    w = compare_prefill(dp, out, seqs=real)
+    lo, hi = case.cu_seqlens[5], case.cu_seqlens[6]
+    assert torch.all(out[lo:hi] == 0), "padding rows must be zero"
+    untouched = sorted(set(range(case.n_slots)) - {int(s) for s in case.slots if s >= 0})
+    assert torch.equal(dp.conv_pool[untouched], conv_before[untouched])
+    assert torch.equal(dp.ssm_pool[untouched], ssm_before[untouched])
+    log(f"{act} d={d} C={chunk}: worst out {w['out']:.2e} ssm {w['ssm']:.2e} conv {w['conv']:.1e}")
+    assert w["conv"] == 0.0
+    assert w["out"] < TOL[act] and w["ssm"] < TOL[act]
+
+
+def test_prefill_raw_output_scale():
+    """No epilogue, scale = d^-1/2: raw o against the oracle (bf16)."""
+    dims = gi.Dims(2, 4, 128, 128, 4)
+    case = gi.varlen_case(seed=12, dims=dims, lengths=np.array([100, 70]), n_slots=3)
+    dp = DevPrefill(case, with_z=False)
+    out, *_ = dp.run(scale=128 ** -0.5, epilogue=False)
+    torch.cuda.synchronize()
+    w = compare_prefill(dp, out, scale=128 ** -0.5, epilogue=False)
+    assert w["out"] < TOL["bf16"] and w["ssm"] < TOL["bf16"]
+
+
+# -------------------------------------------------------- full workloads
+def test_prefill_single_4096():
+    """Batch 1, T=4096, 16 QK / 32 V heads, d=128, bf16, C=64, zero initial
+    state: every output and the final state against the oracle."""
+    case = gi.prefill_case()
+    dp = DevPrefill(case)
+    out, *_ = dp.run()
+    torch.cuda.synchronize()
+    w = compare_prefill(dp, out)
+    log(f"prefill 4096: out {w['out']:.2e} ssm {w['ssm']:.2e}")
+    assert w["out"] < TOL["bf16"] and w["ssm"] < TOL["bf16"] and w["conv"] == 0.0
+
+
+def _decode_dev(case: gi.DecodeCase):
+    d = case.dims
+    dt = act_dtype(case.act)
+    conv0 = np.stack([case.slot_conv(s) for s in range(case.n_slots)])
+    ssm_pool = torch.empty((case.n_slots, d.h_v, d.d_v, d.d_k), dtype=torch.float32, device="cuda")
+    for s in range(case.n_slots):
+        ssm_pool[s] = dev(case.slot_ssm(s), torch.float32)
+    return dict(x=dev(case.x(), dt), a=dev(case.a(), dt), b=dev(case.b(), dt), z=dev(case.z(), dt),
+                conv_w=dev(case.params.conv_w, dt), norm_w=dev(case.params.norm_w, dt),
+                A_log=dev(case.params.A_log, torch.float32), dt_bias=dev(case.params.dt_bias, torch.float32),
+                conv_pool=dev(conv0, dt), ssm_pool=ssm_pool, conv0=conv0)
+
+
+def _oracle_decode_seq(case: gi.DecodeCase, x, a, b, z, i, keep_states=False):
+    d = case.dims
+    s = int(case.slots[i])
+    p = case.params
+    return O.layer_sequence(x[i], a[i], b[i], z[i], p.conv_w, None, p.A_log, p.dt_bias, p.norm_w,
+                            case.slot_conv(s), case.slot_ssm(s), (d.h_k, d.h_v, d.d_k, d.d_v), 1.0, 1e-6,
+                            keep_states=keep_states)
+
+
+def test_decode_batched_256():
+    """256 requests x 1 token, 512-slot pools, permuted slot table, in place:
+    outputs and updated states against the oracle; untouched slots bitwise."""
+    case = gi.decode_case()
+    t = _decode_dev(case)
+    dims = gdn.Dims(*case.dims.__dict__.values())
+    ssm_before, conv_before = t["ssm_pool"].clone(), t["conv_pool"].clone()
+    out, _ = gdn.decode_layer(dims, t["x"], t["conv_w"], t["A_log"], t["dt_bias"], t["a"], t["b"], i32(case.slots),
+                              t["conv_pool"], t["ssm_pool"], z=t["z"], norm_w=t["norm_w"])
+    torch.cuda.synchronize()
+    x, a, b, z = case.x(), case.a(), case.b(), case.z()
+    worst_o = worst_s = worst_c = 0.0
+    conv_pool = t["conv_pool"].float().cpu().numpy()
+    for i in range(case.n):
+        r = _oracle_decode_seq(case, x, a, b, z, i)
+        s = int(case.slots[i])
+        got = host(out[i])
+        gs = t["ssm_pool"][s].cpu().numpy()
+        for h in range(case.dims.h_v):
+            worst_o = max(worst_o, rel(got[:, h], r["out"][:, h]))
+            worst_s = max(worst_s, rel(gs[h], r["ssm"][h]))
+        worst_c = max(worst_c, float(np.max(np.abs(conv_pool[s] - r["conv"]))))
+    untouched = sorted(set(range(case.n_slots)) - set(case.slots.tolist()))
+    assert torch.equal(t["ssm_pool"][untouched], ssm_before[untouched])
+    assert torch.equal(t["conv_pool"][untouched], conv_before[untouched])
+    log(f"decode 256: out {worst_o:.2e} ssm {worst_s:.2e} conv {worst_c:.1e}")
+    assert worst_o < TOL["bf16"] and worst_s < TOL["bf16"] and worst_c == 0.0
+
+
+def test_mtp_draft_and_commit():
+    """128 requests x 4 draft tokens: per-position states to their own slots,
+    then the accepted position's state committed with gdn_state_copy.
+    Indexing is bit-exact: a committed slot holds exactly the bytes of the
+    GPU's own position state, accept 0 leaves the home slot untouched, and
+    untouched slots are unchanged; values match the oracle's replay."""
+    case = gi.mtp_case()
+    t = _decode_dev(case)
+    dims = gdn.Dims(*case.dims.__dict__.values())
+    ssm_before, conv_before = t["ssm_pool"].clone(), t["conv_pool"].clone()
+    out, _ = gdn.decode_layer(dims, t["x"], t["conv_w"], t["A_log"], t["dt_bias"], t["a"], t["b"], i32(case.slots),
+                              t["conv_pool"], t["ssm_pool"], out_slots=i32(case.out_slots), z=t["z"],
+                              norm_w=t["norm_w"])
+    torch.cuda.synchronize()
+    # home slots are read-only during the draft step
+    assert torch.equal(t["ssm_pool"][case.slots.tolist()], ssm_before[case.slots.tolist()])
+    assert torch.equal(t["conv_pool"][case.slots.tolist()], conv_before[case.slots.tolist()])
+    pos_ssm = t["ssm_pool"].clone()
+    pos_conv = t["conv_pool"].clone()
+    acc = case.accept
+    sel = acc > 0
+    src = case.out_slots[np.arange(case.n), np.maximum(acc - 1, 0)][sel]
+    dst = case.slots[sel]
+    gdn.state_copy(dims, t["ssm_pool"], i32(src), i32(dst), t["conv_pool"])
+    torch.cuda.synchronize()
+    assert torch.equal(t["ssm_pool"][dst.tolist()], pos_ssm[src.tolist()])
+    assert torch.equal(t["conv_pool"][dst.tolist()], pos_conv[src.tolist()])
+    rejected = case.slots[~sel].tolist()
+    assert torch.equal(t["ssm_pool"][rejected], ssm_before[rejected])
+    # values against the oracle's replay
+    x, a, b, z = case.x(), case.a(), case.b(), case.z()
+    worst_o = worst_s = 0.0
+    ssm_after = t["ssm_pool"].cpu().numpy()
+    for i in range(case.n):
+        r = _oracle_decode_seq(case, x, a, b, z, i, keep_states=True)
+        got = host(out[i])
+        for h in range(case.dims.h_v):
+            worst_o = max(worst_o, rel(got[:, h], r["out"][:, h]))
+        if acc[i] > 0:
+            ref_state = r["ssm_states"][acc[i] - 1]
+            for h in range(case.dims.h_v):
+                worst_s = max(worst_s, rel(ssm_after[case.slots[i], h], ref_state[h]))
+            conv_ref = r["conv_states"][acc[i] - 1]
+            assert np.array_equal(t["conv_pool"][case.slots[i]].float().cpu().numpy(), conv_ref)
+    log(f"mtp: out {worst_o:.2e} committed ssm {worst_s:.2e}; accepted {int(sel.sum())}/{case.n}")
+    assert worst_o < TOL["bf16"] and worst_s < TOL["bf16"]
+
+
+def test_varlen_full_sampled():
+    """64 sequences, ~271k tokens, nonzero initial states, permuted slots:
+    the whole batch runs on the GPU; sampled sequences and heads are checked
+    against the oracle, and every final state is finite."""
+    case = gi.varlen_case()
+    log(f"varlen: {case.n_seq} seqs, {case.t_total} tokens")
+    dp = DevPrefill(case)
+    out, *_ = dp.run()
+    torch.cuda.synchronize()
+    order = np.argsort(case.lengths)
+    seqs = [int(order[0]), int(order[1]), int(order[len(order) // 2]), int(order[-1])]
+    w = compare_prefill(dp, out, seqs=seqs, heads=[0, 1, 14, 31])
+    log(f"varlen sampled: out {w['out']:.2e} ssm {w['ssm']:.2e} conv {w['conv']:.1e}")
+    assert torch.isfinite(dp.ssm_pool[case.slots.tolist()]).all()
+    assert w["out"] < TOL["bf16"] and w["ssm"] < TOL["bf16"] and w["conv"] == 0.0
+
+
+# ------------------------------------------------------------ consistency
+def test_chunked_matches_recurrent_on_gpu():
+    """The same tokens through the chunked kernel and the recurrent kernel."""
+    dims = gi.Dims(2, 4, 128, 128, 4)
+    case = gi.varlen_case(seed=13, dims=dims, lengths=np.array([150]), n_slots=2)
+    dp = DevPrefill(case)
+    ssm0 = dp.ssm_pool.clone()
+    out_c, y, g, beta = dp.run()
+    torch.cuda.synchronize()
+    s = int(case.slots[0])
+    st = ssm0.clone()
+    ddims = gdn.Dims(*dims.__dict__.values())
+    out_r = gdn.recurrent_decode(ddims, y[None], dp.a[None], dp.b[None], dp.A_log, dp.dt_bias, st, i32([s]),
+                                 z=dp.z[None], norm_w=dp.norm_w)
+    torch.cuda.synchronize()
+    e_o = max(rel(host(out_c[:, h]), host(out_r[0, :, h])) for h in range(4))
+    e_s = max(rel(host(dp.ssm_pool[s, h]), host(st[s, h])) for h in range(4))
+    log(f"chunked vs recurrent: out {e_o:.2e} state {e_s:.2e}")
+    assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
+
+
+def test_split_prefill_carries_state():
+    """Prefill of T tokens equals T1 then T2 tokens with the states carried
+    through the slot pools (chunk boundaries differ between the two)."""
+    dims = gi.Dims(2, 4, 128, 128, 4)
+    case = gi.varlen_case(seed=14, dims=dims, lengths=np.array([300]), n_slots=2)
+    dp = DevPrefill(case)
+    conv0, ssm0 = dp.conv_pool.clone(), dp.ssm_pool.clone()
+    out_full, *_ = dp.run()
+    torch.cuda.synchronize()
+    full_ssm, full_conv = dp.ssm_pool.clone(), dp.conv_pool.clone()
+    dp.conv_pool.copy_(conv0)
+    dp.ssm_pool.copy_(ssm0)
+    ddims = dp.dims
+    outs = []
+    for lo, hi in ((0, 100), (100, 300)):
+        o, *_ = gdn.prefill_layer(ddims, dp.x[lo:hi].contiguous(), dp.conv_w, dp.A_log, dp.dt_bias,
+                                  dp.a[lo:hi].contiguous(), dp.b[lo:hi].contiguous(), i32([0, hi - lo]), dp.slots,
+                                  dp.conv_pool, dp.ssm_pool, dp.has_init, 64, 1.0, dp.z[lo:hi].contiguous(),
+                                  dp.norm_w)
+        outs.append(o)
+    torch.cuda.synchronize()
+    split = torch.cat(outs)
+    e_o = max(rel(host(split[:, h]), host(out_full[:, h])) for h in range(4))
+    e_s = rel(host(dp.ssm_pool), host(full_ssm))
+    assert torch.equal(dp.conv_pool, full_conv)
+    log(f"split vs single: out {e_o:.2e} state {e_s:.2e}")
+    assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
+
+
+def test_deterministic():
+    """Two runs on fresh copies give bitwise-identical outputs and states."""
+    dims = gi.Dims(2, 4, 128, 128, 4)
+    case = gi.varlen_case(seed=15, dims=dims, lengths=np.array([77, 190, 64]), n_slots=6)
+    dp = DevPrefill(case)
+    conv0, ssm0 = dp.conv_pool.clone(), dp.ssm_pool.clone()
+    o1, *_ = dp.run()
+    s1, c1 = dp.ssm_pool.clone(), dp.conv_pool.clone()
+    dp.conv_pool.copy_(conv0)
+    dp.ssm_pool.copy_(ssm0)
+    o2, *_ = dp.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, dp.ssm_pool) and torch.equal(c1, dp.conv_pool)
+
+
+def test_state_copy_bitwise_and_skips():
+    dims = gdn.Dims(2, 4, 64, 64, 4)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    state = torch.randn((6, 4, 64, 64), device="cuda", generator=g)
+    conv = torch.randn((6, dims.c_ch, 3), device="cuda", generator=g).to(torch.bfloat16)
+    s0, c0 = state.clone(), conv.clone()
+    gdn.state_copy(dims, state, i32([0, 2, -1, 4, 3]), i32([1, 5, 3, -1, 3]), conv)
+    torch.cuda.synchronize()
+    assert torch.equal(state[1], s0[0]) and torch.equal(state[5], s0[2])
+    assert torch.equal(conv[1], c0[0]) and torch.equal(conv[5], c0[2])
+    for k in (0, 2, 3, 4):
+        assert torch.equal(state[k], s0[k]) and torch.equal(conv[k], c0[k])
