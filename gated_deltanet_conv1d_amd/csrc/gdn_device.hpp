@@ -3,7 +3,7 @@
 // Wave64 everywhere.  Reductions over 16-lane DPP rows use quad_perm /
 // row_half_mirror / row_mirror, so a "row" of 16 lanes can hold one vector
 // of a head split 16 ways.  MFMA helpers cover the 16x16 fp32-accumulator
-// shapes used by the chunked prefill: bf16 16x16x32 / 16x16x16 and fp32 16x16x4.
+// shapes used by the chunked prefill: bf16 16x16x32 and fp32 16x16x4.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -100,14 +100,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 // block of the contraction index: lane group g = l/16 holds contraction
 // indices 4g..4g+3 of that block.  The MFMA only pairs A's and B's slots, so
 // this assignment is consistent for every instruction used here.
-__device__ __forceinline__ void mma_k16(f32x4& acc, const bf16x4& a, const bf16x4& b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
-}
 __device__ __forceinline__ void mma_k32(f32x4& acc, const bf16x4& a0, const bf16x4& a1, const bf16x4& b0,
                                         const bf16x4& b1) {
   bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
   bf16x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+// A lone 16-wide block runs as 16x16x32 with a zero upper half, so every bf16
+// MFMA in a dependent chain has the same shape: chains that mixed 16x16x16 and
+// 16x16x32 bf16 MFMAs on one accumulator gave nondeterministic, wrong results
+// on gfx950 with this toolchain, while each shape alone is exact.
+__device__ __forceinline__ void mma_k16(f32x4& acc, const bf16x4& a, const bf16x4& b) {
+  const bf16x4 zero = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+  mma_k32(acc, a, zero, b, zero);
 }
 __device__ __forceinline__ void mma_k16(f32x4& acc, const f32x4& a, const f32x4& b) {
 #pragma unroll

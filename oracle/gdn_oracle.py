@@ -205,7 +205,8 @@ def gated_rmsnorm(o, z, w, eps):
 
 # ------------------------------------------------------- whole-layer steps
 def layer_sequence(x, a, b, z, conv_w, conv_b, A_log, dt_bias, norm_w, conv_state0, ssm_state0,
-                   dims, scale=1.0, norm_eps=1e-6, heads=None, keep_states=False):
+                   dims, scale=1.0, norm_eps=1e-6, heads=None, keep_states=False, perturb=None,
+                   perturb_qk=None):
     """One sequence through the hot path, in the pages' kernel order:
     causal conv1d + SiLU -> split q/k/v -> L2 norm -> gating -> gated delta
     rule -> gated RMSNorm.
@@ -214,11 +215,24 @@ def layer_sequence(x, a, b, z, conv_w, conv_b, A_log, dt_bias, norm_w, conv_stat
     history).  z None skips the epilogue (out = o).  With keep_states the
     states after every token are returned too (conv windows and recurrent
     states), which is what the MTP draft step stores per position.
+
+    perturb, perturb_qk: optional functions applied to the conv output and
+    to the normalised q and k respectively (e.g. rounding to bf16).  The
+    pages run the conv and the linear-attention operation as separate kernels
+    (LightLLM #1097, "Specialized Triton Kernels"), so the conv output exists
+    as an activation tensor between them; evaluating the layer again with
+    such tensors held at activation precision measures how far one rounding
+    moves a result (its conditioning).  None (the default) is the exact
+    evaluation.
     """
     h_k, h_v, d_k, d_v = dims
     y, conv_T = causal_conv1d_silu(x, conv_w, conv_b, conv_state0)
+    if perturb is not None:
+        y = perturb(y)
     q, k, v = split_qkv(y, h_k, h_v, d_k, d_v)
     q, k = l2norm(q), l2norm(k)
+    if perturb_qk is not None:
+        q, k = perturb_qk(q), perturb_qk(k)
     g, beta = gating(a, b, A_log, dt_bias)
     o, S_T, states = gated_delta_rule(q, k, v, g, beta, ssm_state0, scale, heads, keep_states)
     hs = list(range(h_v)) if heads is None else list(heads)

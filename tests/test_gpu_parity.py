@@ -14,7 +14,8 @@ import torch
 import gdn_inputs as gi
 import gated_deltanet_conv1d_amd as gdn
 from oracle import gdn_oracle as O
-from tests.gpu_cases import TOL, DevPrefill, act_dtype, compare_prefill, dev, host, i32, log, params_dict, rel, u8
+from tests.gpu_cases import (TOL, DevPrefill, Score, act_dtype, compare_prefill, dev, host, i32, log, oracle_prefill_seq,
+                             oracle_with_perturbed, rel, u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,9 +79,9 @@ def test_prefill_small_varlen(act, d, chunk):
     untouched = sorted(set(range(case.n_slots)) - {int(s) for s in case.slots if s >= 0})
     assert torch.equal(dp.conv_pool[untouched], conv_before[untouched])
     assert torch.equal(dp.ssm_pool[untouched], ssm_before[untouched])
-    log(f"{act} d={d} C={chunk}: worst out {w['out']:.2e} ssm {w['ssm']:.2e} conv {w['conv']:.1e}")
+    log(f"{act} d={d} C={chunk}: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
     assert w["conv"] == 0.0
-    assert w["out"] < TOL[act] and w["ssm"] < TOL[act]
+    assert w["out"].ok() and w["ssm"].ok()
 
 
 def test_prefill_raw_output_scale():
@@ -91,7 +92,8 @@ def test_prefill_raw_output_scale():
     out, *_ = dp.run(scale=128 ** -0.5, epilogue=False)
     torch.cuda.synchronize()
     w = compare_prefill(dp, out, scale=128 ** -0.5, epilogue=False)
-    assert w["out"] < TOL["bf16"] and w["ssm"] < TOL["bf16"]
+    log(f"raw output: out [{w['out']}] ssm [{w['ssm']}]")
+    assert w["out"].ok() and w["ssm"].ok()
 
 
 # -------------------------------------------------------- full workloads
@@ -103,8 +105,8 @@ def test_prefill_single_4096():
     out, *_ = dp.run()
     torch.cuda.synchronize()
     w = compare_prefill(dp, out)
-    log(f"prefill 4096: out {w['out']:.2e} ssm {w['ssm']:.2e}")
-    assert w["out"] < TOL["bf16"] and w["ssm"] < TOL["bf16"] and w["conv"] == 0.0
+    log(f"prefill 4096: out [{w['out']}] ssm [{w['ssm']}]")
+    assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
 
 
 def _decode_dev(case: gi.DecodeCase):
@@ -120,13 +122,13 @@ def _decode_dev(case: gi.DecodeCase):
                 conv_pool=dev(conv0, dt), ssm_pool=ssm_pool, conv0=conv0)
 
 
-def _oracle_decode_seq(case: gi.DecodeCase, x, a, b, z, i, keep_states=False):
+def _oracle_decode_seq(case: gi.DecodeCase, x, a, b, z, i, keep_states=False, **pert):
     d = case.dims
     s = int(case.slots[i])
     p = case.params
     return O.layer_sequence(x[i], a[i], b[i], z[i], p.conv_w, None, p.A_log, p.dt_bias, p.norm_w,
                             case.slot_conv(s), case.slot_ssm(s), (d.h_k, d.h_v, d.d_k, d.d_v), 1.0, 1e-6,
-                            keep_states=keep_states)
+                            keep_states=keep_states, **pert)
 
 
 def test_decode_batched_256():
@@ -140,22 +142,23 @@ def test_decode_batched_256():
                               t["conv_pool"], t["ssm_pool"], z=t["z"], norm_w=t["norm_w"])
     torch.cuda.synchronize()
     x, a, b, z = case.x(), case.a(), case.b(), case.z()
-    worst_o = worst_s = worst_c = 0.0
+    so, ss = Score(TOL["bf16"]), Score(TOL["bf16"])
+    worst_c = 0.0
     conv_pool = t["conv_pool"].float().cpu().numpy()
     for i in range(case.n):
-        r = _oracle_decode_seq(case, x, a, b, z, i)
+        r, rts = oracle_with_perturbed(lambda **pe: _oracle_decode_seq(case, x, a, b, z, i, **pe), "bf16")
         s = int(case.slots[i])
         got = host(out[i])
         gs = t["ssm_pool"][s].cpu().numpy()
         for h in range(case.dims.h_v):
-            worst_o = max(worst_o, rel(got[:, h], r["out"][:, h]))
-            worst_s = max(worst_s, rel(gs[h], r["ssm"][h]))
+            so.add(got[:, h], r["out"][:, h], [rt["out"][:, h] for rt in rts])
+            ss.add(gs[h], r["ssm"][h], [rt["ssm"][h] for rt in rts])
         worst_c = max(worst_c, float(np.max(np.abs(conv_pool[s] - r["conv"]))))
     untouched = sorted(set(range(case.n_slots)) - set(case.slots.tolist()))
     assert torch.equal(t["ssm_pool"][untouched], ssm_before[untouched])
     assert torch.equal(t["conv_pool"][untouched], conv_before[untouched])
-    log(f"decode 256: out {worst_o:.2e} ssm {worst_s:.2e} conv {worst_c:.1e}")
-    assert worst_o < TOL["bf16"] and worst_s < TOL["bf16"] and worst_c == 0.0
+    log(f"decode 256: out [{so}] ssm [{ss}] conv {worst_c:.1e}")
+    assert so.ok() and ss.ok() and worst_c == 0.0
 
 
 def test_mtp_draft_and_commit():
@@ -189,21 +192,22 @@ def test_mtp_draft_and_commit():
     assert torch.equal(t["ssm_pool"][rejected], ssm_before[rejected])
     # values against the oracle's replay
     x, a, b, z = case.x(), case.a(), case.b(), case.z()
-    worst_o = worst_s = 0.0
+    so, ss = Score(TOL["bf16"]), Score(TOL["bf16"])
     ssm_after = t["ssm_pool"].cpu().numpy()
     for i in range(case.n):
-        r = _oracle_decode_seq(case, x, a, b, z, i, keep_states=True)
+        r, rts = oracle_with_perturbed(
+            lambda **pe: _oracle_decode_seq(case, x, a, b, z, i, keep_states=True, **pe), "bf16")
         got = host(out[i])
         for h in range(case.dims.h_v):
-            worst_o = max(worst_o, rel(got[:, h], r["out"][:, h]))
+            so.add(got[:, h], r["out"][:, h], [rt["out"][:, h] for rt in rts])
         if acc[i] > 0:
-            ref_state = r["ssm_states"][acc[i] - 1]
+            p = acc[i] - 1
             for h in range(case.dims.h_v):
-                worst_s = max(worst_s, rel(ssm_after[case.slots[i], h], ref_state[h]))
+                ss.add(ssm_after[case.slots[i], h], r["ssm_states"][p][h], [rt["ssm_states"][p][h] for rt in rts])
             conv_ref = r["conv_states"][acc[i] - 1]
             assert np.array_equal(t["conv_pool"][case.slots[i]].float().cpu().numpy(), conv_ref)
-    log(f"mtp: out {worst_o:.2e} committed ssm {worst_s:.2e}; accepted {int(sel.sum())}/{case.n}")
-    assert worst_o < TOL["bf16"] and worst_s < TOL["bf16"]
+    log(f"mtp: out [{so}] committed ssm [{ss}]; accepted {int(sel.sum())}/{case.n}")
+    assert so.ok() and ss.ok()
 
 
 def test_varlen_full_sampled():
@@ -218,14 +222,15 @@ def test_varlen_full_sampled():
     order = np.argsort(case.lengths)
     seqs = [int(order[0]), int(order[1]), int(order[len(order) // 2]), int(order[-1])]
     w = compare_prefill(dp, out, seqs=seqs, heads=[0, 1, 14, 31])
-    log(f"varlen sampled: out {w['out']:.2e} ssm {w['ssm']:.2e} conv {w['conv']:.1e}")
+    log(f"varlen sampled: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
     assert torch.isfinite(dp.ssm_pool[case.slots.tolist()]).all()
-    assert w["out"] < TOL["bf16"] and w["ssm"] < TOL["bf16"] and w["conv"] == 0.0
+    assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
 
 
 # ------------------------------------------------------------ consistency
 def test_chunked_matches_recurrent_on_gpu():
-    """The same tokens through the chunked kernel and the recurrent kernel."""
+    """The same tokens through the chunked kernel and the recurrent kernel:
+    both meet the bound against the oracle, and their states agree."""
     dims = gi.Dims(2, 4, 128, 128, 4)
     case = gi.varlen_case(seed=13, dims=dims, lengths=np.array([150]), n_slots=2)
     dp = DevPrefill(case)
@@ -234,43 +239,47 @@ def test_chunked_matches_recurrent_on_gpu():
     torch.cuda.synchronize()
     s = int(case.slots[0])
     st = ssm0.clone()
-    ddims = gdn.Dims(*dims.__dict__.values())
-    out_r = gdn.recurrent_decode(ddims, y[None], dp.a[None], dp.b[None], dp.A_log, dp.dt_bias, st, i32([s]),
+    out_r = gdn.recurrent_decode(dp.dims, y[None], dp.a[None], dp.b[None], dp.A_log, dp.dt_bias, st, i32([s]),
                                  z=dp.z[None], norm_w=dp.norm_w)
     torch.cuda.synchronize()
-    e_o = max(rel(host(out_c[:, h]), host(out_r[0, :, h])) for h in range(4))
+    r, rts = oracle_with_perturbed(lambda **pe: oracle_prefill_seq(case, 0, **pe), "bf16")
+    sc, sr, st_c, st_r = (Score(TOL["bf16"]) for _ in range(4))
+    for h in range(4):
+        sc.add(host(out_c[:, h]), r["out"][:, h], [rt["out"][:, h] for rt in rts])
+        sr.add(host(out_r[0, :, h]), r["out"][:, h], [rt["out"][:, h] for rt in rts])
+        st_c.add(host(dp.ssm_pool[s, h]), r["ssm"][h], [rt["ssm"][h] for rt in rts])
+        st_r.add(host(st[s, h]), r["ssm"][h], [rt["ssm"][h] for rt in rts])
     e_s = max(rel(host(dp.ssm_pool[s, h]), host(st[s, h])) for h in range(4))
-    log(f"chunked vs recurrent: out {e_o:.2e} state {e_s:.2e}")
-    assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
+    log(f"chunked [{sc}] recurrent [{sr}] states chunked [{st_c}] recurrent [{st_r}] chunked-vs-recurrent {e_s:.2e}")
+    assert sc.ok() and sr.ok() and st_c.ok() and st_r.ok() and e_s < TOL["bf16"]
 
 
 def test_split_prefill_carries_state():
-    """Prefill of T tokens equals T1 then T2 tokens with the states carried
-    through the slot pools (chunk boundaries differ between the two)."""
+    """Prefill of T tokens as T1 then T2 tokens with the states carried through
+    the slot pools (chunk boundaries differ from a single pass) meets the
+    bound against the oracle, and the conv state matches a single pass bitwise."""
     dims = gi.Dims(2, 4, 128, 128, 4)
     case = gi.varlen_case(seed=14, dims=dims, lengths=np.array([300]), n_slots=2)
     dp = DevPrefill(case)
     conv0, ssm0 = dp.conv_pool.clone(), dp.ssm_pool.clone()
-    out_full, *_ = dp.run()
+    dp.run()
     torch.cuda.synchronize()
-    full_ssm, full_conv = dp.ssm_pool.clone(), dp.conv_pool.clone()
+    full_conv = dp.conv_pool.clone()
     dp.conv_pool.copy_(conv0)
     dp.ssm_pool.copy_(ssm0)
-    ddims = dp.dims
     outs = []
     for lo, hi in ((0, 100), (100, 300)):
-        o, *_ = gdn.prefill_layer(ddims, dp.x[lo:hi].contiguous(), dp.conv_w, dp.A_log, dp.dt_bias,
+        o, *_ = gdn.prefill_layer(dp.dims, dp.x[lo:hi].contiguous(), dp.conv_w, dp.A_log, dp.dt_bias,
                                   dp.a[lo:hi].contiguous(), dp.b[lo:hi].contiguous(), i32([0, hi - lo]), dp.slots,
                                   dp.conv_pool, dp.ssm_pool, dp.has_init, 64, 1.0, dp.z[lo:hi].contiguous(),
                                   dp.norm_w)
         outs.append(o)
     torch.cuda.synchronize()
     split = torch.cat(outs)
-    e_o = max(rel(host(split[:, h]), host(out_full[:, h])) for h in range(4))
-    e_s = rel(host(dp.ssm_pool), host(full_ssm))
     assert torch.equal(dp.conv_pool, full_conv)
-    log(f"split vs single: out {e_o:.2e} state {e_s:.2e}")
-    assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
+    w = compare_prefill(dp, split)
+    log(f"split prefill: out [{w['out']}] ssm [{w['ssm']}]")
+    assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
 
 
 def test_deterministic():

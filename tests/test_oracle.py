@@ -408,3 +408,19 @@ def test_planted_mistakes_are_caught(name, monkeypatch):
         except (ValueError, IndexError):      # a shape mistake that numpy rejects outright
             caught.append(p)
     assert caught, f"planted mistake {name} passes every pin"
+
+
+def test_perturbation_hooks_are_neutral_when_identity():
+    """layer_sequence's activation-precision hooks change nothing when they
+    are the identity, and do change the result when they round."""
+    import gdn_inputs as gi
+    rng = np.random.default_rng(30)
+    p = _params(rng)
+    x, a, b, z = _batch(rng, 12)
+    conv, ssm = _pools(rng, 1)
+    args = (x, a, b, z, p["conv_w"], None, p["A_log"], p["dt_bias"], p["norm_w"], conv[0], ssm[0], DIMS)
+    r0 = O.layer_sequence(*args)
+    r1 = O.layer_sequence(*args, perturb=lambda t: t, perturb_qk=lambda t: t)
+    r2 = O.layer_sequence(*args, perturb=gi.round_bf16, perturb_qk=gi.round_bf16)
+    assert np.array_equal(r0["out"], r1["out"]) and np.array_equal(r0["ssm"], r1["ssm"])
+    assert 0 < rel_err(r2["out"], r0["out"]) < 0.1
