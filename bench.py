@@ -60,6 +60,40 @@ def decode_algorithmic(n: int, t_step: int, h_k: int, h_v: int, d: int, act_byte
     return float(n * (state * (1 + n_pos_writes) + t_step * per_tok))
 
 
+def kernel_src_sha() -> str:
+    """Hash of the HIP sources; counter figures apply only to the sources they were taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_deltanet_conv1d_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str, kernels) -> float | None:
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    (profiles/<workload>_traffic.json), summed over `kernels`; None when the kernel
+    sources changed since the counters were taken or a kernel is missing."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("src_sha") != kernel_src_sha():
+        return None
+    per = rec["per_dispatch"]
+    try:
+        return float(sum(per[k]["read_bytes"] + per[k]["write_bytes"] for k in kernels))
+    except KeyError:
+        return None
+
+
+# kernels one gdn_chunk_prefill call launches on the split path
+CHUNK_SPLIT_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64>",
+                       "void split::chunk_state_kernel<__bf16, __bf16, 128, 64>")
+
+
 def device_info() -> dict:
     import torch
     p = torch.cuda.get_device_properties(0)
@@ -134,8 +168,13 @@ def bench_prefill(args, torch, gdn, gi):
         T=T, wall_s=wall, ms_per_step=wall / args.steps * 1e3, event_ms_per_step=t_step,
         kernels_ms={"gdn_conv1d_fwd": t_conv, "gdn_gating": t_gate, "gdn_chunk_prefill": t_chunk},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                  "kernel": "chunk_prefill_kernel<bf16,bf16,128,64>", "algorithmic_bytes": nbytes,
+                  "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)
+                  if os.environ.get("GDN_PREFILL_PATH", "split") == "split" else None,
+                  "kernel": "gdn_chunk_prefill (split path: chunk_index + chunk_prep + chunk_state kernels)"
+                  if os.environ.get("GDN_PREFILL_PATH", "split") == "split"
+                  else "gdn_chunk_prefill (fused path: chunk_prefill_kernel)",
+                  "algorithmic_bytes": nbytes,
                   "launch_ms": round(t_chunk, 4),
                   "mfma": {"algorithmic_flops": flops, "achieved_tflops": round(flops / (t_chunk * 1e-3) / 1e12, 2),
                            "peak_tflops": BF16_PEAK_TFLOPS,

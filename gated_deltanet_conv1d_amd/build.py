@@ -23,8 +23,11 @@ ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc -O3 would otherwise emit packed fp32 math by
 # itself; the kernels are written for scalar fp32 VALU and MFMA.
+# -disable-promote-alloca-to-lds: keep per-thread register arrays (prefetched
+# rows, accumulator tiles) in registers; the kernels size their own LDS.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast",
+             "-mllvm", "-disable-promote-alloca-to-lds"]
 
 
 def _hipcc() -> str:

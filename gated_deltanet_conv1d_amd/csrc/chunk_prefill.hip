@@ -29,6 +29,9 @@
 //    accumulate) in bf16 mode, fp32 16x16x4 in the all-fp32 mode.
 //  * T: 16x16 diagonal blocks by forward substitution in registers, then
 //    off-diagonal blocks by block forward substitution on fp32 MFMA.
+#include <stdlib.h>
+#include <string.h>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -136,55 +139,76 @@ __global__ __launch_bounds__(kChunkThreads<D>) void chunk_prefill_kernel(
       }
     }
 
+  // Each thread owns RPT rows of each of q, k, v (8 elements each) per chunk.
+  // Their raw bits sit in registers: the next chunk's loads are issued as soon
+  // as the current chunk is staged in LDS and land while it is computed.
+  constexpr int RPP = K::THREADS / LPR;     // rows per pass of the workgroup
+  constexpr int RPT = (C + RPP - 1) / RPP;  // rows per thread per kind
+  const int e0 = (tid % LPR) * 8;
+  const int r0 = tid / LPR;
+  const int64_t cols[3] = {(int64_t)hk * D, (int64_t)(h_k + hk) * D, (int64_t)(2 * h_k + h) * D};
+  Raw8<T> pre[3][RPT];
+  float pre_g = 0.f, pre_b = 0.f;
+  // (a macro rather than a lambda: a captured array would be moved to LDS)
+#define GDN_ISSUE_CHUNK_LOADS(cs)                                                         \
+  {                                                                                       \
+    const int nv_ = (int)min((int64_t)C, hi - (cs));                                      \
+    _Pragma("unroll") for (int kind = 0; kind < 3; ++kind)                                \
+    _Pragma("unroll") for (int j = 0; j < RPT; ++j) {                                     \
+      const int r = r0 + j * RPP;                                                         \
+      if (r < nv_) pre[kind][j].load(qkv + ((cs) + r) * c_ch + cols[kind] + e0);          \
+      else pre[kind][j].zero();                                                           \
+    }                                                                                     \
+    if (wave == 0) {                                                                      \
+      pre_g = lane < nv_ ? g_in[((cs) + lane) * h_v + h] : 0.f;                           \
+      pre_b = lane < nv_ ? beta_in[((cs) + lane) * h_v + h] : 0.f;                        \
+    }                                                                                     \
+  }
+  if (lo < hi) GDN_ISSUE_CHUNK_LOADS(lo);
+  Raw8<T> zpre[RPT];
+  float nw[DVT];
+#pragma unroll
+  for (int j = 0; j < DVT; ++j) nw[j] = z ? to_f32(norm_w[16 * (wave * DVT + j) + l16]) : 1.f;
+
   for (int64_t c0 = lo; c0 < hi; c0 += C) {
     const int nvalid = (int)min((int64_t)C, hi - c0);
 
     // ---------------- phase 1: stage q^, k^ (normalised) and v; cumulative gates
     {
-      constexpr int RPP = K::THREADS / LPR;  // rows per pass
-      const int e0 = (tid % LPR) * 8;
-#pragma unroll 1
-      for (int kind = 0; kind < 3; ++kind) {
-        const int64_t col = kind == 0 ? hk * D : (kind == 1 ? (int64_t)(h_k + hk) * D : (int64_t)(2 * h_k + h) * D);
-#pragma unroll 1
-        for (int r = tid / LPR; r < C; r += RPP) {
-          float v[8];
-          if (r < nvalid) {
-            load8(qkv + (c0 + r) * c_ch + col + e0, v);
-          } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.f;
-          }
+      for (int kind = 0; kind < 3; ++kind)
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+          const int r = r0 + j * RPP;
+          float v[8];
+          pre[kind][j].to_f32(v);
           if (kind < 2) {
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
             ss = group_sum<LPR>(ss);
-            const float rn = rsqrtf(ss + 1e-6f);
+            const float rn = fast_rsq(ss + 1e-6f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] *= rn;
           }
-          if (kind == 0) {
-            *reinterpret_cast<FragT*>(sQ + r * LD_D + e0) = FragT{from_f32<Op>(v[0]), from_f32<Op>(v[1]), from_f32<Op>(v[2]), from_f32<Op>(v[3])};
-            *reinterpret_cast<FragT*>(sQ + r * LD_D + e0 + 4) = FragT{from_f32<Op>(v[4]), from_f32<Op>(v[5]), from_f32<Op>(v[6]), from_f32<Op>(v[7])};
-          } else if (kind == 1) {
-            *reinterpret_cast<FragT*>(sK + r * LD_D + e0) = FragT{from_f32<Op>(v[0]), from_f32<Op>(v[1]), from_f32<Op>(v[2]), from_f32<Op>(v[3])};
-            *reinterpret_cast<FragT*>(sK + r * LD_D + e0 + 4) = FragT{from_f32<Op>(v[4]), from_f32<Op>(v[5]), from_f32<Op>(v[6]), from_f32<Op>(v[7])};
+          if (r < C) {
+            if (kind == 0) {
+              *reinterpret_cast<FragT*>(sQ + r * LD_D + e0) = FragT{from_f32<Op>(v[0]), from_f32<Op>(v[1]), from_f32<Op>(v[2]), from_f32<Op>(v[3])};
+              *reinterpret_cast<FragT*>(sQ + r * LD_D + e0 + 4) = FragT{from_f32<Op>(v[4]), from_f32<Op>(v[5]), from_f32<Op>(v[6]), from_f32<Op>(v[7])};
+            } else if (kind == 1) {
+              *reinterpret_cast<FragT*>(sK + r * LD_D + e0) = FragT{from_f32<Op>(v[0]), from_f32<Op>(v[1]), from_f32<Op>(v[2]), from_f32<Op>(v[3])};
+              *reinterpret_cast<FragT*>(sK + r * LD_D + e0 + 4) = FragT{from_f32<Op>(v[4]), from_f32<Op>(v[5]), from_f32<Op>(v[6]), from_f32<Op>(v[7])};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sKT[(e0 + e) * LD_C + r] = from_f32<Op>(v[e]);
-          } else {
+              for (int e = 0; e < 8; ++e) sKT[(e0 + e) * LD_C + r] = from_f32<Op>(v[e]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sVT[(e0 + e) * LD_C + r] = from_f32<Op>(v[e]);
+              for (int e = 0; e < 8; ++e) sVT[(e0 + e) * LD_C + r] = from_f32<Op>(v[e]);
+            }
           }
         }
-      }
       if (wave == 0) {
         // inclusive scan of g over the chunk (padded tokens: g = 0, beta = 0)
-        float gv = 0.f, bv = 0.f;
-        if (lane < nvalid) {
-          gv = g_in[(c0 + lane) * h_v + h];
-          bv = beta_in[(c0 + lane) * h_v + h];
-        }
+        float gv = pre_g;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const float up = __shfl_up(gv, off);
@@ -193,36 +217,61 @@ __global__ __launch_bounds__(kChunkThreads<D>) void chunk_prefill_kernel(
         if (lane < C) {
           sG[lane] = gv;
           sEG[lane] = fast_exp(gv);
-          sB[lane] = bv;
+          sB[lane] = pre_b;
+        }
+      }
+      if (c0 + C < hi) GDN_ISSUE_CHUNK_LOADS(c0 + C);  // next chunk's loads overlap this chunk's compute
+      if (z) {  // this chunk's gate rows, consumed by the epilogue
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+          const int r = r0 + j * RPP;
+          if (r < nvalid) zpre[j].load(z + (c0 + r) * o_ld + h * D + e0);
+          else zpre[j].zero();
         }
       }
     }
     __syncthreads();
 
     // ---------------- phase 2: Gram tiles -> A (fp32, strict lower) and P (lower incl. diagonal)
-    for (int q = wave; q < 2 * CT * CT; q += WAVES) {
-      const bool is_p = q >= CT * CT;
-      const int ti = (q % (CT * CT)) / CT, tj = q % CT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (ti >= tj) {
-        const Op* arow = (is_p ? sQ : sK) + (16 * ti + l16) * LD_D;
-        const Op* brow = sK + (16 * tj + l16) * LD_D;
-        int kb = 0;
-        for (; kb + 1 < NT; kb += 2)
-          mma_k32(acc, lds_frag<Op>(arow + 16 * kb + 4 * g4), lds_frag<Op>(arow + 16 * kb + 16 + 4 * g4),
-                  lds_frag<Op>(brow + 16 * kb + 4 * g4), lds_frag<Op>(brow + 16 * kb + 16 + 4 * g4));
-        if (kb < NT) mma_k16(acc, lds_frag<Op>(arow + 16 * kb + 4 * g4), lds_frag<Op>(brow + 16 * kb + 4 * g4));
-      }
-      const int cc = 16 * tj + l16;
+    {
+      constexpr int NLT = CT * (CT + 1) / 2;  // lower-triangular tiles per matrix
+      constexpr int PER_WAVE = (2 * NLT + WAVES - 1) / WAVES;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * ti + 4 * g4 + i;
-        if (is_p) {
-          const float v = r >= cc ? fast_exp(sG[r] - sG[cc]) * acc[i] : 0.f;
-          sP[r * LD_C + cc] = from_f32<Op>(v);
-        } else {
-          sA[r * LD_F + cc] = r > cc ? sB[r] * fast_exp(sG[r] - sG[cc]) * acc[i] : 0.f;
-          if (ti < tj) sT[r * LD_F + cc] = 0.f;  // upper blocks of T are zero
+      for (int k = 0; k < PER_WAVE; ++k) {
+        const int q = wave + k * WAVES;
+        if (q < 2 * NLT) {
+          const bool is_p = q >= NLT;
+          const int idx = is_p ? q - NLT : q;
+          int ti = 0;
+          while ((ti + 1) * (ti + 2) / 2 <= idx) ++ti;
+          const int tj = idx - ti * (ti + 1) / 2;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const Op* arow = (is_p ? sQ : sK) + (16 * ti + l16) * LD_D;
+          const Op* brow = sK + (16 * tj + l16) * LD_D;
+          int kb = 0;
+#pragma unroll
+          for (; kb + 1 < NT; kb += 2)
+            mma_k32(acc, lds_frag<Op>(arow + 16 * kb + 4 * g4), lds_frag<Op>(arow + 16 * kb + 16 + 4 * g4),
+                    lds_frag<Op>(brow + 16 * kb + 4 * g4), lds_frag<Op>(brow + 16 * kb + 16 + 4 * g4));
+          if (kb < NT) mma_k16(acc, lds_frag<Op>(arow + 16 * kb + 4 * g4), lds_frag<Op>(brow + 16 * kb + 4 * g4));
+          const int cc = 16 * tj + l16;
+          const float gc = sG[cc];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ti + 4 * g4 + i;
+            const float dec = fast_exp(fminf(sG[r] - gc, 0.f));
+            if (is_p) sP[r * LD_C + cc] = from_f32<Op>(r >= cc ? dec * acc[i] : 0.f);
+            else sA[r * LD_F + cc] = r > cc ? sB[r] * dec * acc[i] : 0.f;
+          }
+        }
+      }
+      // upper blocks: A and P are zero there, and so is T
+      for (int e = tid; e < C * C; e += K::THREADS) {
+        const int r = e / C, cc = e % C;
+        if ((r >> 4) < (cc >> 4)) {
+          sA[r * LD_F + cc] = 0.f;
+          sT[r * LD_F + cc] = 0.f;
+          sP[r * LD_C + cc] = from_f32<Op>(0.f);
         }
       }
     }
@@ -398,48 +447,79 @@ __global__ __launch_bounds__(kChunkThreads<D>) void chunk_prefill_kernel(
     }
 
     // ---------------- phase 6: epilogue (scale, optional gated RMSNorm) and store
-    float rstd[CT][4];
-    if (z) {
+    // The output tile is staged in LDS (over the v / A tiles, dead by now) so that
+    // z is read and o written as whole 16-byte row pieces.
+    {
+      T* sZ = reinterpret_cast<T*>(smem + K::VT_OFF);
+      if (z) {
 #pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float ss = 0.f;
-#pragma unroll
-          for (int j = 0; j < DVT; ++j) ss = fmaf(Oacc[mt][j][i], Oacc[mt][j][i], ss);
-          ss = group_sum<16>(ss);
-          if (l16 == 0) sRed[wave * C + 16 * mt + 4 * g4 + i] = ss;
-        }
-      __syncthreads();
-#pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float tot = 0.f;
-#pragma unroll
-          for (int w = 0; w < WAVES; ++w) tot += sRed[w * C + 16 * mt + 4 * g4 + i];
-          rstd[mt][i] = rsqrtf(tot * scale * scale / D + norm_eps);
-        }
-    }
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mt + 4 * g4 + i;
-        if (t < nvalid) {
-          const int64_t row = (c0 + t) * o_ld + h * D;
-#pragma unroll
-          for (int j = 0; j < DVT; ++j) {
-            const int dv = 16 * (wave * DVT + j) + l16;
-            float v = Oacc[mt][j][i] * scale;
-            if (z) v *= rstd[mt][i] * to_f32(norm_w[dv]) * siluf_(to_f32(z[row + dv]));
-            o[row + dv] = from_f32<T>(v);
+        for (int j = 0; j < RPT; ++j) {
+          const int r = r0 + j * RPP;
+          if (r < C) {
+            float v[8];
+            zpre[j].to_f32(v);
+            store8(sZ + r * LD_D + e0, v);
           }
         }
+#pragma unroll
+        for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < DVT; ++j) ss = fmaf(Oacc[mt][j][i], Oacc[mt][j][i], ss);
+            ss = group_sum<16>(ss);
+            if (l16 == 0) sRed[wave * C + 16 * mt + 4 * g4 + i] = ss;
+          }
       }
+      __syncthreads();
+      if (z) {
+        float f[CT][4];
+        float zz[CT][DVT][4];
+#pragma unroll
+        for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * mt + 4 * g4 + i;
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) tot += sRed[w * C + t];
+            f[mt][i] = scale * fast_rsq(tot * scale * scale * (1.0f / D) + norm_eps);
+#pragma unroll
+            for (int j = 0; j < DVT; ++j) zz[mt][j][i] = to_f32(sZ[t * LD_D + 16 * (wave * DVT + j) + l16]);
+          }
+#pragma unroll
+        for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < DVT; ++j)
+              sZ[(16 * mt + 4 * g4 + i) * LD_D + 16 * (wave * DVT + j) + l16] =
+                  from_f32<T>(Oacc[mt][j][i] * f[mt][i] * nw[j] * fast_silu(zz[mt][j][i]));
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < DVT; ++j)
+              sZ[(16 * mt + 4 * g4 + i) * LD_D + 16 * (wave * DVT + j) + l16] = from_f32<T>(Oacc[mt][j][i] * scale);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        const int r = r0 + j * RPP;
+        if (r < nvalid) {
+          float v[8];
+          load8(sZ + r * LD_D + e0, v);
+          store8(o + (c0 + r) * o_ld + h * D + e0, v);
+        }
+      }
+    }
     __syncthreads();  // LDS is rewritten by the next chunk
   }
 
+#undef GDN_ISSUE_CHUNK_LOADS
   // final state back to the slot
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt)
@@ -455,6 +535,7 @@ template <typename T, typename Op, int D, int C>
 hipError_t impl(const ChunkArgs& a, hipStream_t st) {
   using K = Cfg<Op, D, C>;
   static_assert(K::BYTES <= 160 * 1024, "LDS budget");
+  static_assert(C * K::LD_D * (int)sizeof(T) <= K::T_OFF - K::VT_OFF, "output tile fits over the v and A tiles");
   if (a.n_seq == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_prefill_kernel<T, Op, D, C>), dim3((unsigned)((int64_t)a.n_seq * a.s.h_v)),
                      dim3(K::THREADS), 0, st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, a.has_init,
@@ -484,9 +565,26 @@ bool chunk_supported(int d, int chunk, bool bf16) {
   return true;
 }
 
-size_t chunk_workspace_size(const Shape&, bool, int32_t, int64_t, int32_t) { return 0; }
+namespace {
+// Which evaluation runs: GDN_PREFILL_PATH=fused|split (read once), default split.
+bool use_split() {
+  static const int mode = [] {
+    const char* e = getenv("GDN_PREFILL_PATH");
+    return (e && strcmp(e, "fused") == 0) ? 0 : 1;
+  }();
+  return mode == 1;
+}
+}  // namespace
+
+size_t chunk_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk) {
+  return use_split() ? chunk_split_workspace_size(s, bf16, n_seq, t_total, chunk) : 0;
+}
 
 hipError_t launch_chunk_prefill(const ChunkArgs& a, hipStream_t st) {
+  return use_split() ? launch_chunk_split(a, st) : launch_chunk_fused(a, st);
+}
+
+hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t st) {
   switch (a.s.d) {
     case 16: return a.bf16 ? by_chunk<bf16, bf16, 16>(a, st) : by_chunk<float, float, 16>(a, st);
     case 32: return a.bf16 ? by_chunk<bf16, bf16, 32>(a, st) : by_chunk<float, float, 32>(a, st);

@@ -39,7 +39,7 @@ struct Taps {
       float acc = b[i];
 #pragma unroll
       for (int j = 0; j < W; ++j) acc = fmaf(w[j][i], win[j][i], acc);
-      out[i] = siluf_(acc);
+      out[i] = fast_silu(acc);
     }
   }
 };

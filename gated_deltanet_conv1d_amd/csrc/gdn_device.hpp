@@ -67,8 +67,44 @@ __device__ __forceinline__ void load4(const float* p, float* v) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
 }
 
+// Raw bits of 8 consecutive activations, so a load can be issued early and
+// converted later: one 16-byte vector for bf16, two for fp32.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void to_f32(float* v) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  uint4 u[2];
+  __device__ __forceinline__ void load(const float* p) {
+    u[0] = reinterpret_cast<const uint4*>(p)[0];
+    u[1] = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void zero() { u[0] = u[1] = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void to_f32(float* v) const {
+    const uint32_t w[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
+};
+
 // ------------------------------------------------------------------ math
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// Hardware reciprocal and reciprocal square root (about 1 ulp; no denormal
+// fix-up branches): every use has a normal, positive or well-scaled argument.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+// x * sigmoid(x); for x -> -inf the reciprocal of +inf is 0, so the result is -0.
+__device__ __forceinline__ float fast_silu(float x) { return x * fast_rcp(1.0f + fast_exp(-x)); }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
 __device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }

@@ -114,9 +114,15 @@ struct ChunkArgs {
   void* workspace;
   size_t ws_bytes;
 };
-// True when the chunk kernel has an instantiation for (d, chunk, dtype).
+// True when the chunk kernels have an instantiation for (d, chunk, dtype).
 bool chunk_supported(int d, int chunk, bool bf16);
 size_t chunk_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk);
 hipError_t launch_chunk_prefill(const ChunkArgs& a, hipStream_t st);
+// The two evaluations of the chunked form (selected by launch_chunk_prefill):
+// one fused workgroup per (sequence, V head), or a chunk-parallel preparation
+// pass followed by a per-(sequence, V head) state pass through a workspace.
+hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t st);
+size_t chunk_split_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk);
+hipError_t launch_chunk_split(const ChunkArgs& a, hipStream_t st);
 
 }  // namespace gdn

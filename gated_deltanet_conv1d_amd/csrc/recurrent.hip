@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     for (int e = 0; e < F; ++e) { sk = fmaf(kv[e], kv[e], sk); sq = fmaf(qv[e], qv[e], sq); }
     sk = group_sum<16>(sk);
     sq = group_sum<16>(sq);
-    const float rk = rsqrtf(sk + 1e-6f), rq = rsqrtf(sq + 1e-6f);
+    const float rk = fast_rsq(sk + 1e-6f), rq = fast_rsq(sq + 1e-6f);
     float kq = 0.f;
 #pragma unroll
     for (int e = 0; e < F; ++e) { kv[e] *= rk; qv[e] *= rq; kq = fmaf(kv[e], qv[e], kq); }
@@ -160,13 +160,13 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 #pragma unroll
       for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
       __syncthreads();
-      const float rstd = rsqrtf(tot / D + norm_eps);
+      const float rstd = fast_rsq(tot * (1.0f / D) + norm_eps);
       const T* z_ptr = z + (row * h_v + h) * D;
       if (c == 0) {
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
           const int r = p * 16 + r16;
-          o_ptr[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * siluf_(to_f32(z_ptr[r])));
+          o_ptr[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * fast_silu(to_f32(z_ptr[r])));
         }
       }
     } else if (c == 0) {
