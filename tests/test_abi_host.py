@@ -32,7 +32,8 @@ def D(h_k=16, h_v=32, d=128, w=4):
     return ctypes.byref(binding._CDims(h_k, h_v, d, d, w))
 
 
-FAKE = 0x1000  # a 16-byte-aligned non-null address; never dereferenced by failing calls
+FAKE = 0x1000  # a 16-byte-aligned non-null address: every call below must fail validation,
+# so nothing is ever launched with it
 
 
 def test_exports_every_header_symbol(L):
@@ -94,7 +95,21 @@ def test_chunk_prefill_errors(L):
     assert chunk_call(L, qkv=FAKE + 8) == ALIGN
     assert chunk_call(L, n_seq=0, t_total=5) == SHAPE
     assert chunk_call(L, n_seq=0, t_total=0) == OK
-    assert L.gdn_chunk_prefill_workspace_size(D(), 0, 1, 4096, 64) == 0
+
+
+def test_chunk_prefill_workspace(L):
+    ws = L.gdn_chunk_prefill_workspace_size(D(), 0, 1, 4096, 64)
+    if os.environ.get("GDN_PREFILL_PATH") == "fused":
+        assert ws == 0
+        return
+    # split path: a 256-byte-aligned chunk index, then one unit per (chunk, V head)
+    # holding W and Ut (bf16 [C][D]), P (bf16 [C][C]) and G (fp32 [C])
+    unit = 64 * 128 * 2 * 2 + 64 * 64 * 2 + 64 * 4
+    assert ws == 256 + (4096 // 64 + 1) * 32 * unit
+    # (same sizes as the query, so these calls stop at validation and never launch)
+    assert chunk_call(L, t_total=4096) == WS
+    assert chunk_call(L, t_total=4096, ws=FAKE, ws_bytes=ws - 1) == WS
+    assert L.gdn_chunk_prefill_workspace_size(None, 0, 1, 4096, 64) == 0
 
 
 def test_recurrent_and_copy_errors(L):
