@@ -44,7 +44,9 @@ struct Cfg {
   static constexpr int UT_OFF = W_OFF + C * D * (int)sizeof(Op);
   static constexpr int P_OFF = UT_OFF + C * D * (int)sizeof(Op);
   static constexpr int G_OFF = P_OFF + C * C * (int)sizeof(Op);
-  static constexpr int UNIT = G_OFF + C * 4;
+  static constexpr int RQ_OFF = G_OFF + C * 4;   // 1 / sqrt(|q_t|^2 + eps)
+  static constexpr int RK_OFF = RQ_OFF + C * 4;  // 1 / sqrt(|k_t|^2 + eps)
+  static constexpr int UNIT = RK_OFF + C * 4;
   // prep kernel LDS
   static constexpr int PQ = 0;                                     // q^ rows, later W
   static constexpr int PK = PQ + C * LD_D * (int)sizeof(Op);       // k^ rows
@@ -54,13 +56,12 @@ struct Cfg {
   static constexpr int PG = PP + C * LD_C * (int)sizeof(Op);       // G, beta, beta e^G
   static constexpr int PREP_BYTES = PG + 3 * C * 4;
   // state kernel LDS
-  static constexpr int SQ = 0;
-  static constexpr int SK = SQ + C * LD_D * (int)sizeof(Op);
+  static constexpr int SQ = 0;                                     // raw q rows
+  static constexpr int SK = SQ + C * LD_D * (int)sizeof(Op);       // raw k rows
   static constexpr int SW = SK + C * LD_D * (int)sizeof(Op);
   static constexpr int SP = SW + C * LD_D * (int)sizeof(Op);
-  static constexpr int SZ = SP + C * LD_C * (int)sizeof(Op);       // output tile (activation dtype)
-  static constexpr int SG = SZ + C * LD_D * 4;                     // G, e^G
-  static constexpr int SR = SG + 2 * C * 4;                        // [WAVES][C] row sums
+  static constexpr int SG = SP + C * LD_C * (int)sizeof(Op);       // G, e^G r_q, e^(G_n - G) r_k
+  static constexpr int SR = SG + 3 * C * 4;                        // [WAVES][C] row sums
   static constexpr int STATE_BYTES = SR + WAVES * C * 4;
 };
 
@@ -189,6 +190,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
           const float rn = fast_rsq(ss + 1e-6f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] *= rn;
+          if (r < C && tid % LPR == 0) reinterpret_cast<float*>(unit + (kind == 0 ? K::RQ_OFF : K::RK_OFF))[r] = rn;
         }
         if (r < C) {
           Op* dst = (kind == 0 ? sQ : (kind == 1 ? sK : sV)) + r * LD_D + e0;
@@ -345,12 +347,33 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 }
 
 // ----------------------------------------------------------------- state
+// 8 raw activations into LDS unchanged (activation and operand types agree).
+template <typename T>
+__device__ __forceinline__ void raw_store(const Raw8<T>& r, T* dst);
+template <>
+__device__ __forceinline__ void raw_store<bf16>(const Raw8<bf16>& r, bf16* dst) {
+  reinterpret_cast<uint2*>(dst)[0] = make_uint2(r.u.x, r.u.y);
+  reinterpret_cast<uint2*>(dst)[1] = make_uint2(r.u.z, r.u.w);
+}
+template <>
+__device__ __forceinline__ void raw_store<float>(const Raw8<float>& r, float* dst) {
+  reinterpret_cast<uint4*>(dst)[0] = r.u[0];
+  reinterpret_cast<uint4*>(dst)[1] = r.u[1];
+}
+
+// The chain over one sequence's chunks for one V head.  q and k stay raw in LDS:
+// their L2 norms (from the prep pass) are folded into the rows of the products,
+//   diag(r_q) Q S^T  and  (diag(r_k) K)^T U' = K^T (diag(r_k) U'),
+// so staging is a plain copy.  The epilogue works from registers: z arrives in
+// accumulator layout with the prefetch and o leaves straight from the tiles;
+// only the gated RMSNorm's cross-wave row sums go through LDS.
 template <typename T, typename Op, int D, int C>
 __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
     const T* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
     const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws,
     float* __restrict__ state, int32_t n_slots, T* __restrict__ o, const T* __restrict__ z,
     const T* __restrict__ norm_w, float norm_eps, float scale, int64_t t_total, int32_t h_k, int32_t h_v) {
+  static_assert(sizeof(T) == sizeof(Op), "activations are staged unchanged as MFMA operands");
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, DVT = K::DVT, LPR = K::LPR, RPP = K::RPP;
@@ -362,9 +385,9 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
   Op* sK = reinterpret_cast<Op*>(smem + K::SK);
   Op* sW = reinterpret_cast<Op*>(smem + K::SW);
   Op* sP = reinterpret_cast<Op*>(smem + K::SP);
-  T* sZ = reinterpret_cast<T*>(smem + K::SZ);
   float* sG = reinterpret_cast<float*>(smem + K::SG);
-  float* sEG = sG + C;
+  float* sFQ = sG + C;      // e^{G_t} r_q[t]
+  float* sFK = sG + 2 * C;  // e^{G_n - G_t} r_k[t]
   float* sRed = reinterpret_cast<float*>(smem + K::SR);
 
   const int n = blockIdx.x / h_v;
@@ -402,14 +425,15 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
 #pragma unroll
   for (int j = 0; j < DVT; ++j) nw[j] = z ? to_f32(norm_w[16 * (wave * DVT + j) + l16]) : 1.f;
 
-  // operands of the next chunk, prefetched into registers
+  // operands of the next chunk, prefetched into registers in two groups
   const int e0 = (tid % LPR) * 8, r0 = tid / LPR;
   const int64_t col_q = (int64_t)hk * D, col_k = (int64_t)(h_k + hk) * D;
-  Raw8<T> pq[RPT], pk[RPT], pz[RPT];
+  Raw8<T> pq[RPT], pk[RPT];
   Raw8<Op> pw[WPT], pp[PPT];
-  typename Frag<Op>::type put[CT][DVT];
-  float pg = 0.f;
-#define GDN_STATE_PREFETCH(cs, gcx)                                                              \
+  FragT put[CT][DVT];
+  T pz[CT][DVT][4];
+  float pg = 0.f, prq = 0.f, prk = 0.f;
+#define GDN_PREFETCH_A(cs, gcx)                                                                  \
   {                                                                                              \
     const int nv_ = (int)min((int64_t)C, hi - (cs));                                             \
     const unsigned char* unit_ = ws + ((int64_t)(gcx) * h_v + h) * K::UNIT;                      \
@@ -418,9 +442,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
       if (r < nv_) {                                                                             \
         pq[j].load(qkv + ((cs) + r) * c_ch + col_q + e0);                                        \
         pk[j].load(qkv + ((cs) + r) * c_ch + col_k + e0);                                        \
-        if (z) pz[j].load(z + ((cs) + r) * o_ld + h * D + e0); else pz[j].zero();                \
       } else {                                                                                   \
-        pq[j].zero(); pk[j].zero(); pz[j].zero();                                                \
+        pq[j].zero(); pk[j].zero();                                                              \
       }                                                                                          \
     }                                                                                            \
     const Op* w_ = reinterpret_cast<const Op*>(unit_ + K::W_OFF);                                \
@@ -428,6 +451,11 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
       const int e = tid + j * K::THREADS;                                                        \
       if (e < C * D / 8) pw[j].load(w_ + (e / (D / 8)) * D + (e % (D / 8)) * 8); else pw[j].zero(); \
     }                                                                                            \
+  }
+#define GDN_PREFETCH_B(cs, gcx)                                                                  \
+  {                                                                                              \
+    const int nv_ = (int)min((int64_t)C, hi - (cs));                                             \
+    const unsigned char* unit_ = ws + ((int64_t)(gcx) * h_v + h) * K::UNIT;                      \
     const Op* p_ = reinterpret_cast<const Op*>(unit_ + K::P_OFF);                                \
     _Pragma("unroll") for (int j = 0; j < PPT; ++j) {                                            \
       const int e = tid + j * K::THREADS;                                                        \
@@ -437,57 +465,48 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
     _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                            \
     _Pragma("unroll") for (int j = 0; j < DVT; ++j)                                              \
       put[mt][j] = *reinterpret_cast<const FragT*>(u_ + ((mt * NT + wave * DVT + j) * 64 + lane) * 4); \
-    if (wave == 0 && lane < C) pg = reinterpret_cast<const float*>(unit_ + K::G_OFF)[lane];     \
+    if (wave == 0 && lane < C) {                                                                 \
+      pg = reinterpret_cast<const float*>(unit_ + K::G_OFF)[lane];                               \
+      prq = reinterpret_cast<const float*>(unit_ + K::RQ_OFF)[lane];                             \
+      prk = reinterpret_cast<const float*>(unit_ + K::RK_OFF)[lane];                             \
+    }                                                                                            \
+    if (z) {                                                                                     \
+      _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                          \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+        const int t = 16 * mt + 4 * g4 + i;                                                      \
+        _Pragma("unroll") for (int j = 0; j < DVT; ++j)                                          \
+          pz[mt][j][i] = t < nv_ ? z[((cs) + t) * o_ld + h * D + 16 * (wave * DVT + j) + l16]    \
+                                 : from_f32<T>(0.f);                                             \
+      }                                                                                          \
+    }                                                                                            \
   }
-  if (lo < hi) GDN_STATE_PREFETCH(lo, gc0);
+  if (lo < hi) {
+    GDN_PREFETCH_A(lo, gc0);
+    GDN_PREFETCH_B(lo, gc0);
+  }
 
   int32_t gcx = gc0;
   for (int64_t c0 = lo; c0 < hi; c0 += C, ++gcx) {
     const int nvalid = (int)min((int64_t)C, hi - c0);
-    // ---- prefetched registers -> LDS (q^, k^ normalised), Ut -> accumulators
+    const bool more = c0 + C < hi;
+    // ---- prefetched registers -> LDS; Ut -> accumulators; per-token factors
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int r = r0 + j * RPP;
-#pragma unroll
-      for (int kind = 0; kind < 2; ++kind) {
-        float v[8];
-        (kind == 0 ? pq[j] : pk[j]).to_f32(v);
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-        ss = group_sum<LPR>(ss);
-        const float rn = fast_rsq(ss + 1e-6f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= rn;
-        if (r < C) {
-          Op* dst = (kind == 0 ? sQ : sK) + r * LD_D + e0;
-          *reinterpret_cast<FragT*>(dst) = FragT{from_f32<Op>(v[0]), from_f32<Op>(v[1]), from_f32<Op>(v[2]), from_f32<Op>(v[3])};
-          *reinterpret_cast<FragT*>(dst + 4) = FragT{from_f32<Op>(v[4]), from_f32<Op>(v[5]), from_f32<Op>(v[6]), from_f32<Op>(v[7])};
-        }
-      }
       if (r < C) {
-        float v[8];
-        pz[j].to_f32(v);
-        store8(sZ + r * LD_D + e0, v);
+        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&pq[j]), sQ + r * LD_D + e0);
+        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&pk[j]), sK + r * LD_D + e0);
       }
     }
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
       const int e = tid + j * K::THREADS;
-      if (e < C * D / 8) {
-        float v[8];
-        pw[j].to_f32(v);
-        store8(sW + (e / (D / 8)) * LD_D + (e % (D / 8)) * 8, v);
-      }
+      if (e < C * D / 8) raw_store<Op>(pw[j], sW + (e / (D / 8)) * LD_D + (e % (D / 8)) * 8);
     }
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int e = tid + j * K::THREADS;
-      if (e < C * C / 8) {
-        float v[8];
-        pp[j].to_f32(v);
-        store8(sP + (e / (C / 8)) * LD_C + (e % (C / 8)) * 8, v);
-      }
+      if (e < C * C / 8) raw_store<Op>(pp[j], sP + (e / (C / 8)) * LD_C + (e % (C / 8)) * 8);
     }
     f32x4 Uacc[CT][DVT];
 #pragma unroll
@@ -496,14 +515,25 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
       for (int j = 0; j < DVT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Uacc[mt][j][i] = to_f32(put[mt][j][i]);
-    if (wave == 0 && lane < C) {
-      sG[lane] = pg;
-      sEG[lane] = fast_exp(pg);
+    float zz[CT][DVT][4];
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int j = 0; j < DVT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[mt][j][i] = to_f32(pz[mt][j][i]);
+    if (wave == 0) {
+      const float g_last = __shfl(pg, C - 1);
+      if (lane < C) {
+        sG[lane] = pg;
+        sFQ[lane] = fast_exp(pg) * prq;
+        sFK[lane] = fast_exp(g_last - pg) * prk;
+      }
     }
     __syncthreads();
-    if (c0 + C < hi) GDN_STATE_PREFETCH(c0 + C, gcx + 1);
+    if (more) GDN_PREFETCH_A(c0 + C, gcx + 1);
 
-    // ---- U = Ut - W S^T ;  O = diag(e^G) Q S^T
+    // ---- U = Ut - W S^T ;  O = diag(e^G r_q) Q S^T
     FragT Sf[NT][DVT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
@@ -535,10 +565,11 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
           mma_k16(oacc, lds_frag<Op>(qrow + 16 * kb + 4 * g4), Sf[kb][j]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[i] *= sEG[16 * mt + 4 * g4 + i];
+        for (int i = 0; i < 4; ++i) oacc[i] *= sFQ[16 * mt + 4 * g4 + i];
         Oacc[mt][j] = oacc;
       }
     }
+    if (more) GDN_PREFETCH_B(c0 + C, gcx + 1);
     // ---- O += P U
     {
       FragT Uf[CT][DVT];
@@ -560,16 +591,13 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
         }
       }
     }
-    // ---- S^T <- e^{G_n} S^T + K^T diag(e^{G_n - G}) U   (K^T read down k^'s columns)
+    // ---- S^T <- e^{G_n} S^T + K^T diag(e^{G_n - G} r_k) U   (K^T read down k's columns)
     {
-      const float g_last = sG[C - 1];
-      const float eg_last = fast_exp(g_last);
+      const float eg_last = fast_exp(sG[C - 1]);
       FragT Uf[CT][DVT];
 #pragma unroll
       for (int kt = 0; kt < CT; ++kt) {
-        f32x4 d;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = fast_exp(g_last - sG[16 * kt + 4 * g4 + i]);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(sFK + 16 * kt + 4 * g4);
 #pragma unroll
         for (int j = 0; j < DVT; ++j) {
           f32x4 u = Uacc[kt][j];
@@ -597,9 +625,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
       }
     }
 
-    // ---- epilogue: scale, gated RMSNorm over d_v, output staged through LDS
-    // (z is uniform: the two variants keep the element loops branch-free so
-    // their LDS reads issue back to back)
+    // ---- epilogue: scale, gated RMSNorm over d_v, stores from the tiles
+    float f[CT][4];
     if (z) {
 #pragma unroll
       for (int mt = 0; mt < CT; ++mt)
@@ -612,50 +639,43 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
           if (l16 == 0) sRed[wave * C + 16 * mt + 4 * g4 + i] = ss;
         }
       __syncthreads();
-      float f[CT][4];
-      float zz[CT][DVT][4];
 #pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
+      for (int mt = 0; mt < CT; ++mt) {
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * mt + 4 * g4 + i;
-          float tot = 0.f;
+        for (int w = 0; w < WAVES; ++w) {
+          const f32x4 part = *reinterpret_cast<const f32x4*>(sRed + w * C + 16 * mt + 4 * g4);
 #pragma unroll
-          for (int w = 0; w < WAVES; ++w) tot += sRed[w * C + t];
-          f[mt][i] = scale * fast_rsq(tot * scale * scale * (1.0f / D) + norm_eps);
-#pragma unroll
-          for (int j = 0; j < DVT; ++j) zz[mt][j][i] = to_f32(sZ[t * LD_D + 16 * (wave * DVT + j) + l16]);
+          for (int i = 0; i < 4; ++i) tot[i] += part[i];
         }
 #pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < DVT; ++j)
-            sZ[(16 * mt + 4 * g4 + i) * LD_D + 16 * (wave * DVT + j) + l16] =
-                from_f32<T>(Oacc[mt][j][i] * f[mt][i] * nw[j] * fast_silu(zz[mt][j][i]));
+        for (int i = 0; i < 4; ++i) f[mt][i] = scale * fast_rsq(tot[i] * scale * scale * (1.0f / D) + norm_eps);
+      }
     } else {
 #pragma unroll
       for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < DVT; ++j)
-            sZ[(16 * mt + 4 * g4 + i) * LD_D + 16 * (wave * DVT + j) + l16] = from_f32<T>(Oacc[mt][j][i] * scale);
+        for (int i = 0; i < 4; ++i) f[mt][i] = scale;
     }
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int r = r0 + j * RPP;
-      if (r < nvalid) {
-        float v[8];
-        load8(sZ + r * LD_D + e0, v);
-        store8(o + (c0 + r) * o_ld + h * D + e0, v);
+    for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * mt + 4 * g4 + i;
+        if (t < nvalid) {
+          T* orow = o + (c0 + t) * o_ld + h * D;
+#pragma unroll
+          for (int j = 0; j < DVT; ++j) {
+            float v = Oacc[mt][j][i] * f[mt][i];
+            if (z) v *= nw[j] * fast_silu(zz[mt][j][i]);
+            orow[16 * (wave * DVT + j) + l16] = from_f32<T>(v);
+          }
+        }
       }
-    }
     __syncthreads();  // LDS is rewritten by the next chunk
   }
-#undef GDN_STATE_PREFETCH
+#undef GDN_PREFETCH_A
+#undef GDN_PREFETCH_B
 
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt)

@@ -103,8 +103,8 @@ def test_chunk_prefill_workspace(L):
         assert ws == 0
         return
     # split path: a 256-byte-aligned chunk index, then one unit per (chunk, V head)
-    # holding W and Ut (bf16 [C][D]), P (bf16 [C][C]) and G (fp32 [C])
-    unit = 64 * 128 * 2 * 2 + 64 * 64 * 2 + 64 * 4
+    # holding W and Ut (bf16 [C][D]), P (bf16 [C][C]), G and the inverse q/k norms (fp32 [C] each)
+    unit = 64 * 128 * 2 * 2 + 64 * 64 * 2 + 3 * 64 * 4
     assert ws == 256 + (4096 // 64 + 1) * 32 * unit
     # (same sizes as the query, so these calls stop at validation and never launch)
     assert chunk_call(L, t_total=4096) == WS
