@@ -171,7 +171,7 @@ def bench_prefill(args, torch, gdn, gi):
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)
                   if os.environ.get("GDN_PREFILL_PATH", "split") == "split" else None,
-                  "kernel": "gdn_chunk_prefill (split path: chunk_index + chunk_prep + chunk_state kernels)"
+                  "kernel": "gdn_chunk_prefill (split path: chunk_index + chunk_prep + chunk_state + gated_norm kernels)"
                   if os.environ.get("GDN_PREFILL_PATH", "split") == "split"
                   else "gdn_chunk_prefill (fused path: chunk_prefill_kernel)",
                   "algorithmic_bytes": nbytes,

@@ -1,22 +1,33 @@
 // Chunked gated delta rule, split into a chunk-parallel preparation pass and
-// a per-sequence state pass.  Same math as chunk_prefill.hip (the chunked
-// WY / UT form of the gated delta rule over 64-token chunks):
+// a state pass that runs per (sequence, V head, 16-column d_v tile).  Same math
+// as chunk_prefill.hip (the chunked WY / UT form of the gated delta rule):
 //   A = strict-lower(b_i e^{G_i-G_j} k_i.k_j),  T = (I + A)^{-1},
 //   W = T diag(b e^G) K,  Ut = T diag(b) V,  P = M o Q K^T        (no state)
 //   U = Ut - W S0^T,  O = diag(e^G) Q S0^T + P U,
 //   S = e^{G_n} S0 + K^T diag(e^{G_n - G}) U                       (the chain)
 //
-// Why split on MI355X: everything in the first line depends only on the
-// chunk's own tokens, so it runs as one workgroup per (chunk, V head) across
-// the whole GPU (thousands of workgroups, two per CU by LDS), while the serial
-// chain per (sequence, V head) keeps only the three state contractions and
-// the epilogue.  The price is a workspace round trip of W, Ut, P and G
-// (bf16 for the operands: 40 KiB per chunk and head at d = 128, C = 64).
+// Why this shape on MI355X: the first line depends only on the chunk's own
+// tokens, so it runs as one workgroup per (chunk, V head) across the GPU.  In
+// the chain, the rows of S (the d_v index) never mix: every contraction runs
+// over d_k or over tokens.  So one wave owns a 16-wide slice of d_v for all of
+// d_k, holding its S^T slice in MFMA accumulators, and a single 4096-token
+// sequence with 32 V heads already gives 256 independent waves, one per CU,
+// with no LDS and no barrier in the loop.  The prep pass writes every operand
+// the chain reads as ready-made MFMA fragments:
+//   -W and Q' = diag(e^G) Q      (A operands, contraction over d_k)
+//   K'^T = (diag(e^{G_n-G}) K)^T  (A operand, contraction over the chunk)
+//   P                             (A operand, lower triangle)
+//   Ut                            (accumulator layout)
+// so each wave streams them with 16-byte loads one chunk ahead.  The gated
+// RMSNorm needs the whole d_v row, which is spread over the waves of a head:
+// the chain writes scale * O and each tile's sum of squares, and a small
+// elementwise pass finishes the norm in place.
 //
 //   chunk_index_kernel  first global chunk of every sequence (block scan)
-//   chunk_prep_kernel   per (chunk, V head): q/k L2 norm, gates, Gram, T, W, Ut, P
-//   chunk_state_kernel  per (sequence, V head): S^T in MFMA accumulators, the
-//                       chunk loop with prefetched operands, gated-RMSNorm epilogue
+//   chunk_prep_kernel   per (chunk, V head): q/k L2 norm, gates, Gram, T and
+//                       the operand fragments above
+//   chunk_state_kernel  per (sequence, V head, d_v tile): the chunk loop
+//   gated_norm_kernel   per (token, V head): RMSNorm over d_v times w silu(z)
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -39,14 +50,19 @@ struct Cfg {
   static constexpr int LPR = D / 8;    // lanes per row piece of 8 elements
   static constexpr int RPP = THREADS / LPR;
   static constexpr int RPT = (C + RPP - 1) / RPP;
+  // Pair fragments: an A operand tile of 16 rows and a 32-wide step of the
+  // contraction, 8 values per lane (two 16-blocks, 4 each), zero past the end.
+  static constexpr int NPD = (NT + 1) / 2;  // 32-steps over d_k
+  static constexpr int NPC = (CT + 1) / 2;  // 32-steps over the chunk
+  static constexpr int PAIR = 64 * 8;       // elements per pair tile
   // workspace unit per (chunk, V head), bytes
-  static constexpr int W_OFF = 0;
-  static constexpr int UT_OFF = W_OFF + C * D * (int)sizeof(Op);
-  static constexpr int P_OFF = UT_OFF + C * D * (int)sizeof(Op);
-  static constexpr int G_OFF = P_OFF + C * C * (int)sizeof(Op);
-  static constexpr int RQ_OFF = G_OFF + C * 4;   // 1 / sqrt(|q_t|^2 + eps)
-  static constexpr int RK_OFF = RQ_OFF + C * 4;  // 1 / sqrt(|k_t|^2 + eps)
-  static constexpr int UNIT = RK_OFF + C * 4;
+  static constexpr int W_OFF = 0;                                   // -W     [CT][NPD] pairs
+  static constexpr int Q_OFF = W_OFF + CT * NPD * PAIR * (int)sizeof(Op);   // Q'  [CT][NPD]
+  static constexpr int KT_OFF = Q_OFF + CT * NPD * PAIR * (int)sizeof(Op);  // K'^T [NT][NPC]
+  static constexpr int P_OFF = KT_OFF + NT * NPC * PAIR * (int)sizeof(Op);  // P   [CT][NPC]
+  static constexpr int UT_OFF = P_OFF + CT * NPC * PAIR * (int)sizeof(Op);  // Ut  [CT][NT][64][4]
+  static constexpr int F_OFF = UT_OFF + C * D * (int)sizeof(Op);            // e^{G_n}
+  static constexpr int UNIT = (F_OFF + 16 + 255) / 256 * 256;
   // prep kernel LDS
   static constexpr int PQ = 0;                                     // q^ rows, later W
   static constexpr int PK = PQ + C * LD_D * (int)sizeof(Op);       // k^ rows
@@ -55,14 +71,6 @@ struct Cfg {
   static constexpr int PP = PA + C * LD_F * 4;                     // P
   static constexpr int PG = PP + C * LD_C * (int)sizeof(Op);       // G, beta, beta e^G
   static constexpr int PREP_BYTES = PG + 3 * C * 4;
-  // state kernel LDS
-  static constexpr int SQ = 0;                                     // raw q rows
-  static constexpr int SK = SQ + C * LD_D * (int)sizeof(Op);       // raw k rows
-  static constexpr int SW = SK + C * LD_D * (int)sizeof(Op);
-  static constexpr int SP = SW + C * LD_D * (int)sizeof(Op);
-  static constexpr int SG = SP + C * LD_C * (int)sizeof(Op);       // G, e^G r_q, e^(G_n - G) r_k
-  static constexpr int SR = SG + 3 * C * 4;                        // [WAVES][C] row sums
-  static constexpr int STATE_BYTES = SR + WAVES * C * 4;
 };
 
 __device__ __forceinline__ int32_t seq_of_chunk(const int32_t* __restrict__ cstart, int32_t n_seq, int32_t gc) {
@@ -122,6 +130,55 @@ __device__ __forceinline__ typename Frag<Op>::type frag_col(const Op* p, int ld)
   for (int i = 0; i < 4; ++i) r[i] = p[i * ld];
   return r;
 }
+
+template <typename Op>
+__device__ __forceinline__ typename Frag<Op>::type zero_frag() {
+  typename Frag<Op>::type r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = from_f32<Op>(0.f);
+  return r;
+}
+template <typename Op>
+__device__ __forceinline__ typename Frag<Op>::type frag_mul(const typename Frag<Op>::type& a, float f) {
+  typename Frag<Op>::type r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = from_f32<Op>(to_f32(a[i]) * f);
+  return r;
+}
+template <typename Op>
+__device__ __forceinline__ void store_pair(Op* dst, const typename Frag<Op>::type& lo,
+                                           const typename Frag<Op>::type& hi);
+template <>
+__device__ __forceinline__ void store_pair<bf16>(bf16* dst, const bf16x4& lo, const bf16x4& hi) {
+  *reinterpret_cast<bf16x8*>(dst) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <>
+__device__ __forceinline__ void store_pair<float>(float* dst, const f32x4& lo, const f32x4& hi) {
+  reinterpret_cast<f32x4*>(dst)[0] = lo;
+  reinterpret_cast<f32x4*>(dst)[1] = hi;
+}
+
+// A pair fragment in registers: one 16x16x32 bf16 MFMA, or two 16-blocks of
+// 16x16x4 fp32 MFMAs.  B is the two matching 16-blocks in accumulator layout.
+template <typename Op> struct Pair;
+template <> struct Pair<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void mma(f32x4& acc, const bf16x4& b0, const bf16x4& b1) const {
+    const bf16x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, b, acc, 0, 0, 0);
+  }
+};
+template <> struct Pair<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = reinterpret_cast<const f32x4*>(p)[0];
+    hi = reinterpret_cast<const f32x4*>(p)[1];
+  }
+  __device__ __forceinline__ void mma(f32x4& acc, const f32x4& b0, const f32x4& b1) const {
+    mma_k32(acc, lo, hi, b0, b1);
+  }
+};
 
 // ------------------------------------------------------------------ prep
 template <typename T, typename Op, int D, int C>
@@ -190,7 +247,6 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
           const float rn = fast_rsq(ss + 1e-6f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] *= rn;
-          if (r < C && tid % LPR == 0) reinterpret_cast<float*>(unit + (kind == 0 ? K::RQ_OFF : K::RK_OFF))[r] = rn;
         }
         if (r < C) {
           Op* dst = (kind == 0 ? sQ : (kind == 1 ? sK : sV)) + r * LD_D + e0;
@@ -208,8 +264,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         sG[lane] = gv;
         sB[lane] = bv;
         sBE[lane] = bv * fast_exp(gv);
-        reinterpret_cast<float*>(unit + K::G_OFF)[lane] = gv;
       }
+      if (lane == C - 1) reinterpret_cast<float*>(unit + K::F_OFF)[0] = fast_exp(gv);
     }
   }
   __syncthreads();
@@ -256,6 +312,41 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     }
   }
   __syncthreads();
+
+  // ---- Q' = diag(e^G) Q^, K'^T = (diag(e^{G_n - G}) K^)^T and P as pair fragments.
+  // sQ, sK, sP and sG stay unchanged until the W phase, behind later barriers.
+  {
+    constexpr int NPD = K::NPD, NPC = K::NPC, NQ = CT * NPD, NK = NT * NPC, NP = CT * NPC;
+    const float g_n = sG[C - 1];
+    for (int q = wave; q < NQ + NK + NP; q += WAVES) {
+      FragT lo, hi;
+      Op* dst;
+      if (q < NQ) {
+        const int mt = q / NPD, sp = q % NPD, r = 16 * mt + l16;
+        const float f = fast_exp(sG[r]);
+        const Op* src = sQ + r * LD_D + 32 * sp + 4 * g4;
+        lo = frag_mul<Op>(lds_frag<Op>(src), f);
+        hi = 32 * sp + 16 < D ? frag_mul<Op>(lds_frag<Op>(src + 16), f) : zero_frag<Op>();
+        dst = reinterpret_cast<Op*>(unit + K::Q_OFF) + (q * 64 + lane) * 8;
+      } else if (q < NQ + NK) {
+        const int idx = q - NQ, mt = idx / NPC, sp = idx % NPC;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
+          lo[i] = from_f32<Op>(t0 < C ? to_f32(sK[t0 * LD_D + 16 * mt + l16]) * fast_exp(g_n - sG[t0]) : 0.f);
+          hi[i] = from_f32<Op>(t1 < C ? to_f32(sK[t1 * LD_D + 16 * mt + l16]) * fast_exp(g_n - sG[t1]) : 0.f);
+        }
+        dst = reinterpret_cast<Op*>(unit + K::KT_OFF) + (idx * 64 + lane) * 8;
+      } else {
+        const int idx = q - NQ - NK, mt = idx / NPC, sp = idx % NPC;
+        const Op* src = sP + (16 * mt + l16) * LD_C + 32 * sp + 4 * g4;
+        lo = lds_frag<Op>(src);
+        hi = 32 * sp + 16 < C ? lds_frag<Op>(src + 16) : zero_frag<Op>();
+        dst = reinterpret_cast<Op*>(unit + K::P_OFF) + (idx * 64 + lane) * 8;
+      }
+      store_pair<Op>(dst, lo, hi);
+    }
+  }
 
   // ---- T = (I + A)^-1 in place.  (a) diagonal 16x16 blocks, one lane per column
   if (tid < CT * 16) {
@@ -327,93 +418,62 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     }
   }
   __syncthreads();
-  // ---- W and P rows to the workspace, 16-byte pieces
+  // ---- -W as pair fragments (the chain adds -W S^T to Ut)
   {
-    Op* wdst = reinterpret_cast<Op*>(unit + K::W_OFF);
-    for (int e = tid; e < C * D / 8; e += K::THREADS) {
-      const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-      float v[8];
-      load8(sQ + r * LD_D + c8, v);
-      store8(wdst + r * D + c8, v);
-    }
-    Op* pdst = reinterpret_cast<Op*>(unit + K::P_OFF);
-    for (int e = tid; e < C * C / 8; e += K::THREADS) {
-      const int r = e / (C / 8), c8 = (e % (C / 8)) * 8;
-      float v[8];
-      load8(sP + r * LD_C + c8, v);
-      store8(pdst + r * C + c8, v);
+    constexpr int NPD = K::NPD;
+    for (int q = wave; q < CT * NPD; q += WAVES) {
+      const int mt = q / NPD, sp = q % NPD;
+      const Op* src = sQ + (16 * mt + l16) * LD_D + 32 * sp + 4 * g4;
+      const FragT lo = frag_mul<Op>(lds_frag<Op>(src), -1.f);
+      const FragT hi = 32 * sp + 16 < D ? frag_mul<Op>(lds_frag<Op>(src + 16), -1.f) : zero_frag<Op>();
+      store_pair<Op>(reinterpret_cast<Op*>(unit + K::W_OFF) + (q * 64 + lane) * 8, lo, hi);
     }
   }
 }
 
 // ----------------------------------------------------------------- state
-// 8 raw activations into LDS unchanged (activation and operand types agree).
-template <typename T>
-__device__ __forceinline__ void raw_store(const Raw8<T>& r, T* dst);
-template <>
-__device__ __forceinline__ void raw_store<bf16>(const Raw8<bf16>& r, bf16* dst) {
-  reinterpret_cast<uint2*>(dst)[0] = make_uint2(r.u.x, r.u.y);
-  reinterpret_cast<uint2*>(dst)[1] = make_uint2(r.u.z, r.u.w);
-}
-template <>
-__device__ __forceinline__ void raw_store<float>(const Raw8<float>& r, float* dst) {
-  reinterpret_cast<uint4*>(dst)[0] = r.u[0];
-  reinterpret_cast<uint4*>(dst)[1] = r.u[1];
-}
-
-// The chain over one sequence's chunks for one V head.  q and k stay raw in LDS:
-// their L2 norms (from the prep pass) are folded into the rows of the products,
-//   diag(r_q) Q S^T  and  (diag(r_k) K)^T U' = K^T (diag(r_k) U'),
-// so staging is a plain copy.  The epilogue works from registers: z arrives in
-// accumulator layout with the prefetch and o leaves straight from the tiles;
-// only the gated RMSNorm's cross-wave row sums go through LDS.
-template <typename T, typename Op, int D, int C>
-__global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
-    const T* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
-    const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws,
-    float* __restrict__ state, int32_t n_slots, T* __restrict__ o, const T* __restrict__ z,
-    const T* __restrict__ norm_w, float norm_eps, float scale, int64_t t_total, int32_t h_k, int32_t h_v) {
-  static_assert(sizeof(T) == sizeof(Op), "activations are staged unchanged as MFMA operands");
+// One wave: the chain of one sequence's chunks for one V head and NTW 16-wide
+// tiles of d_v.  S^T[d_k][d_v-slice] lives in accumulators (lane: d_k rows
+// 4g..4g+3 of each 16-block, d_v column l16), which is also the B operand
+// layout for every product that contracts over d_k.  Operands of chunk c+1 are
+// loaded right after chunk c consumed the same registers.  Block order puts
+// all tiles of one (sequence, head) on one XCD, so its fragments are fetched
+// into that XCD's L2 once.
+template <typename Op, int D, int C, int NTW>
+__global__ __launch_bounds__(64) void chunk_state_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
+    const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws, float* __restrict__ part,
+    float* __restrict__ state, int32_t n_slots, Op* __restrict__ o, int32_t norm, float scale, int64_t t_total,
+    int32_t n_seq, int32_t h_v) {
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
-  constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, DVT = K::DVT, LPR = K::LPR, RPP = K::RPP;
-  constexpr int RPT = K::RPT, LD_D = K::LD_D, LD_C = K::LD_C;
-  constexpr int WPT = (C * D / 8 + K::THREADS - 1) / K::THREADS;  // W pieces per thread
-  constexpr int PPT = (C * C / 8 + K::THREADS - 1) / K::THREADS;  // P pieces per thread
-  __shared__ __attribute__((aligned(16))) unsigned char smem[K::STATE_BYTES];
-  Op* sQ = reinterpret_cast<Op*>(smem + K::SQ);
-  Op* sK = reinterpret_cast<Op*>(smem + K::SK);
-  Op* sW = reinterpret_cast<Op*>(smem + K::SW);
-  Op* sP = reinterpret_cast<Op*>(smem + K::SP);
-  float* sG = reinterpret_cast<float*>(smem + K::SG);
-  float* sFQ = sG + C;      // e^{G_t} r_q[t]
-  float* sFK = sG + 2 * C;  // e^{G_n - G_t} r_k[t]
-  float* sRed = reinterpret_cast<float*>(smem + K::SR);
-
-  const int n = blockIdx.x / h_v;
-  const int h = blockIdx.x % h_v;
-  const int hk = h / (h_v / h_k);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-  const int c_ch = 2 * h_k * D + h_v * D;
+  constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, NTILE = NT / NTW;
+  const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3, tile = kq % NTILE;
+  const int64_t grp = (int64_t)(kq / NTILE) * 8 + xcd;
+  if (grp >= (int64_t)n_seq * h_v) return;
+  const int n = (int)(grp / h_v), h = (int)(grp % h_v);
+  const int lane = threadIdx.x, g4 = lane >> 4, l16 = lane & 15;
+  const int col0 = h * D + 16 * NTW * tile;  // first output column of this wave
   const int64_t o_ld = (int64_t)h_v * D;
   const int64_t lo = min((int64_t)cu[n], t_total);
   const int64_t hi = min(max((int64_t)cu[n + 1], lo), t_total);
   const int32_t slot = slots[n];
-  if (!slot_ok(slot, n_slots)) {
-    for (int64_t t = lo; t < hi; ++t)
-      for (int r = tid; r < D; r += K::THREADS) o[t * o_ld + h * D + r] = from_f32<T>(0.0f);
+  if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs (and their norm partials)
+    for (int64_t e = lane; e < (hi - lo) * 16 * NTW; e += 64)
+      o[(lo + e / (16 * NTW)) * o_ld + col0 + e % (16 * NTW)] = from_f32<Op>(0.f);
+    if (norm)
+      for (int64_t t = lo + lane; t < hi; t += 64) part[(t * h_v + h) * NT + tile] = 0.f;
     return;
   }
   const bool init = has_init == nullptr || has_init[n] != 0;
   float* st_ptr = state + ((int64_t)slot * h_v + h) * D * D;
-  const int32_t gc0 = cstart[n];
 
-  f32x4 Sacc[NT][DVT];
+  f32x4 Sacc[NT][NTW];
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-    for (int j = 0; j < DVT; ++j) {
-      const int dv = 16 * (wave * DVT + j) + l16;
+    for (int j = 0; j < NTW; ++j) {
+      const int dv = 16 * (NTW * tile + j) + l16;
       if (init) {
         const float4 v = *reinterpret_cast<const float4*>(st_ptr + dv * D + 16 * mt + 4 * g4);
         Sacc[mt][j] = f32x4{v.x, v.y, v.z, v.w};
@@ -421,287 +481,215 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_state_kernel(
         Sacc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-  float nw[DVT];
-#pragma unroll
-  for (int j = 0; j < DVT; ++j) nw[j] = z ? to_f32(norm_w[16 * (wave * DVT + j) + l16]) : 1.f;
 
-  // operands of the next chunk, prefetched into registers in two groups
-  const int e0 = (tid % LPR) * 8, r0 = tid / LPR;
-  const int64_t col_q = (int64_t)hk * D, col_k = (int64_t)(h_k + hk) * D;
-  Raw8<T> pq[RPT], pk[RPT];
-  Raw8<Op> pw[WPT], pp[PPT];
-  FragT put[CT][DVT];
-  T pz[CT][DVT][4];
-  float pg = 0.f, prq = 0.f, prk = 0.f;
-#define GDN_PREFETCH_A(cs, gcx)                                                                  \
-  {                                                                                              \
-    const int nv_ = (int)min((int64_t)C, hi - (cs));                                             \
-    const unsigned char* unit_ = ws + ((int64_t)(gcx) * h_v + h) * K::UNIT;                      \
-    _Pragma("unroll") for (int j = 0; j < RPT; ++j) {                                            \
-      const int r = r0 + j * RPP;                                                                \
-      if (r < nv_) {                                                                             \
-        pq[j].load(qkv + ((cs) + r) * c_ch + col_q + e0);                                        \
-        pk[j].load(qkv + ((cs) + r) * c_ch + col_k + e0);                                        \
-      } else {                                                                                   \
-        pq[j].zero(); pk[j].zero();                                                              \
-      }                                                                                          \
-    }                                                                                            \
-    const Op* w_ = reinterpret_cast<const Op*>(unit_ + K::W_OFF);                                \
-    _Pragma("unroll") for (int j = 0; j < WPT; ++j) {                                            \
-      const int e = tid + j * K::THREADS;                                                        \
-      if (e < C * D / 8) pw[j].load(w_ + (e / (D / 8)) * D + (e % (D / 8)) * 8); else pw[j].zero(); \
-    }                                                                                            \
+  Pair<Op> wn[CT][NPD], qp[CT][NPD], kt[NT][NPC], pp[CT][NPC];
+  FragT ut[CT][NTW];
+  float egn = 0.f;
+#define GDN_LOAD_WU(u)                                                                              \
+  {                                                                                                 \
+    const Op* w_ = reinterpret_cast<const Op*>((u) + K::W_OFF);                                     \
+    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
+    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp) wn[mt][sp].load(w_ + ((mt * NPD + sp) * 64 + lane) * 8); \
+    const Op* u_ = reinterpret_cast<const Op*>((u) + K::UT_OFF);                                    \
+    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
+    _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
+      ut[mt][j] = *reinterpret_cast<const FragT*>(u_ + ((mt * NT + NTW * tile + j) * 64 + lane) * 4); \
   }
-#define GDN_PREFETCH_B(cs, gcx)                                                                  \
-  {                                                                                              \
-    const int nv_ = (int)min((int64_t)C, hi - (cs));                                             \
-    const unsigned char* unit_ = ws + ((int64_t)(gcx) * h_v + h) * K::UNIT;                      \
-    const Op* p_ = reinterpret_cast<const Op*>(unit_ + K::P_OFF);                                \
-    _Pragma("unroll") for (int j = 0; j < PPT; ++j) {                                            \
-      const int e = tid + j * K::THREADS;                                                        \
-      if (e < C * C / 8) pp[j].load(p_ + (e / (C / 8)) * C + (e % (C / 8)) * 8); else pp[j].zero(); \
-    }                                                                                            \
-    const Op* u_ = reinterpret_cast<const Op*>(unit_ + K::UT_OFF);                               \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                            \
-    _Pragma("unroll") for (int j = 0; j < DVT; ++j)                                              \
-      put[mt][j] = *reinterpret_cast<const FragT*>(u_ + ((mt * NT + wave * DVT + j) * 64 + lane) * 4); \
-    if (wave == 0 && lane < C) {                                                                 \
-      pg = reinterpret_cast<const float*>(unit_ + K::G_OFF)[lane];                               \
-      prq = reinterpret_cast<const float*>(unit_ + K::RQ_OFF)[lane];                             \
-      prk = reinterpret_cast<const float*>(unit_ + K::RK_OFF)[lane];                             \
-    }                                                                                            \
-    if (z) {                                                                                     \
-      _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                          \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
-        const int t = 16 * mt + 4 * g4 + i;                                                      \
-        _Pragma("unroll") for (int j = 0; j < DVT; ++j)                                          \
-          pz[mt][j][i] = t < nv_ ? z[((cs) + t) * o_ld + h * D + 16 * (wave * DVT + j) + l16]    \
-                                 : from_f32<T>(0.f);                                             \
-      }                                                                                          \
-    }                                                                                            \
+#define GDN_LOAD_Q(u)                                                                               \
+  {                                                                                                 \
+    const Op* q_ = reinterpret_cast<const Op*>((u) + K::Q_OFF);                                     \
+    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
+    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp) qp[mt][sp].load(q_ + ((mt * NPD + sp) * 64 + lane) * 8); \
   }
+#define GDN_LOAD_P(u)                                                                               \
+  {                                                                                                 \
+    const Op* p_ = reinterpret_cast<const Op*>((u) + K::P_OFF);                                     \
+    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
+    _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                              \
+      if (2 * sp <= mt) pp[mt][sp].load(p_ + ((mt * NPC + sp) * 64 + lane) * 8);                    \
+  }
+#define GDN_LOAD_KT(u)                                                                              \
+  {                                                                                                 \
+    const Op* k_ = reinterpret_cast<const Op*>((u) + K::KT_OFF);                                    \
+    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
+    _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp) kt[mt][sp].load(k_ + ((mt * NPC + sp) * 64 + lane) * 8); \
+    egn = *reinterpret_cast<const float*>((u) + K::F_OFF);                                          \
+  }
+  int32_t gcx = cstart[n];
   if (lo < hi) {
-    GDN_PREFETCH_A(lo, gc0);
-    GDN_PREFETCH_B(lo, gc0);
+    const unsigned char* u0 = ws + ((int64_t)gcx * h_v + h) * K::UNIT;
+    GDN_LOAD_WU(u0);
+    GDN_LOAD_Q(u0);
+    GDN_LOAD_P(u0);
+    GDN_LOAD_KT(u0);
   }
+  const FragT zf = zero_frag<Op>();
 
-  int32_t gcx = gc0;
   for (int64_t c0 = lo; c0 < hi; c0 += C, ++gcx) {
     const int nvalid = (int)min((int64_t)C, hi - c0);
     const bool more = c0 + C < hi;
-    // ---- prefetched registers -> LDS; Ut -> accumulators; per-token factors
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int r = r0 + j * RPP;
-      if (r < C) {
-        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&pq[j]), sQ + r * LD_D + e0);
-        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&pk[j]), sK + r * LD_D + e0);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int e = tid + j * K::THREADS;
-      if (e < C * D / 8) raw_store<Op>(pw[j], sW + (e / (D / 8)) * LD_D + (e % (D / 8)) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int e = tid + j * K::THREADS;
-      if (e < C * C / 8) raw_store<Op>(pp[j], sP + (e / (C / 8)) * LD_C + (e % (C / 8)) * 8);
-    }
-    f32x4 Uacc[CT][DVT];
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-      for (int j = 0; j < DVT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Uacc[mt][j][i] = to_f32(put[mt][j][i]);
-    float zz[CT][DVT][4];
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-      for (int j = 0; j < DVT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zz[mt][j][i] = to_f32(pz[mt][j][i]);
-    if (wave == 0) {
-      const float g_last = __shfl(pg, C - 1);
-      if (lane < C) {
-        sG[lane] = pg;
-        sFQ[lane] = fast_exp(pg) * prq;
-        sFK[lane] = fast_exp(g_last - pg) * prk;
-      }
-    }
-    __syncthreads();
-    if (more) GDN_PREFETCH_A(c0 + C, gcx + 1);
+    const unsigned char* un = ws + ((int64_t)(gcx + 1) * h_v + h) * K::UNIT;  // read only when `more`
 
-    // ---- U = Ut - W S^T ;  O = diag(e^G r_q) Q S^T
-    FragT Sf[NT][DVT];
+    FragT Sf[NT][NTW];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-      for (int j = 0; j < DVT; ++j) Sf[mt][j] = frag_from<Op>(Sacc[mt][j]);
-    f32x4 Oacc[CT][DVT];
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt) {
-      const Op* wrow = sW + (16 * mt + l16) * LD_D;
-      const Op* qrow = sQ + (16 * mt + l16) * LD_D;
-#pragma unroll
-      for (int j = 0; j < DVT; ++j) {
-        f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
-        int kb = 0;
-#pragma unroll
-        for (; kb + 1 < NT; kb += 2) {
-          FragT w0 = lds_frag<Op>(wrow + 16 * kb + 4 * g4), w1 = lds_frag<Op>(wrow + 16 * kb + 16 + 4 * g4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { w0[i] = -w0[i]; w1[i] = -w1[i]; }
-          mma_k32(Uacc[mt][j], w0, w1, Sf[kb][j], Sf[kb + 1][j]);
-          mma_k32(oacc, lds_frag<Op>(qrow + 16 * kb + 4 * g4), lds_frag<Op>(qrow + 16 * kb + 16 + 4 * g4), Sf[kb][j],
-                  Sf[kb + 1][j]);
-        }
-        if (kb < NT) {
-          FragT w0 = lds_frag<Op>(wrow + 16 * kb + 4 * g4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w0[i] = -w0[i];
-          mma_k16(Uacc[mt][j], w0, Sf[kb][j]);
-          mma_k16(oacc, lds_frag<Op>(qrow + 16 * kb + 4 * g4), Sf[kb][j]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[i] *= sFQ[16 * mt + 4 * g4 + i];
-        Oacc[mt][j] = oacc;
-      }
-    }
-    if (more) GDN_PREFETCH_B(c0 + C, gcx + 1);
-    // ---- O += P U
-    {
-      FragT Uf[CT][DVT];
-#pragma unroll
-      for (int kt = 0; kt < CT; ++kt)
-#pragma unroll
-        for (int j = 0; j < DVT; ++j) Uf[kt][j] = frag_from<Op>(Uacc[kt][j]);
-#pragma unroll
-      for (int mt = 0; mt < CT; ++mt) {
-        const Op* prow = sP + (16 * mt + l16) * LD_C;
-#pragma unroll
-        for (int j = 0; j < DVT; ++j) {
-          int kb = 0;
-#pragma unroll
-          for (; kb + 1 <= mt; kb += 2)
-            mma_k32(Oacc[mt][j], lds_frag<Op>(prow + 16 * kb + 4 * g4), lds_frag<Op>(prow + 16 * kb + 16 + 4 * g4),
-                    Uf[kb][j], Uf[kb + 1][j]);
-          if (kb <= mt) mma_k16(Oacc[mt][j], lds_frag<Op>(prow + 16 * kb + 4 * g4), Uf[kb][j]);
-        }
-      }
-    }
-    // ---- S^T <- e^{G_n} S^T + K^T diag(e^{G_n - G} r_k) U   (K^T read down k's columns)
-    {
-      const float eg_last = fast_exp(sG[C - 1]);
-      FragT Uf[CT][DVT];
-#pragma unroll
-      for (int kt = 0; kt < CT; ++kt) {
-        const f32x4 d = *reinterpret_cast<const f32x4*>(sFK + 16 * kt + 4 * g4);
-#pragma unroll
-        for (int j = 0; j < DVT; ++j) {
-          f32x4 u = Uacc[kt][j];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) u[i] *= d[i];
-          Uf[kt][j] = frag_from<Op>(u);
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        FragT ka[CT];
-#pragma unroll
-        for (int kt = 0; kt < CT; ++kt) ka[kt] = frag_col<Op>(sK + (16 * kt + 4 * g4) * LD_D + 16 * mt + l16, LD_D);
-#pragma unroll
-        for (int j = 0; j < DVT; ++j) {
-          f32x4 acc = Sacc[mt][j];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] *= eg_last;
-          int kb = 0;
-#pragma unroll
-          for (; kb + 1 < CT; kb += 2) mma_k32(acc, ka[kb], ka[kb + 1], Uf[kb][j], Uf[kb + 1][j]);
-          if (kb < CT) mma_k16(acc, ka[kb], Uf[kb][j]);
-          Sacc[mt][j] = acc;
-        }
-      }
-    }
+      for (int j = 0; j < NTW; ++j) Sf[mt][j] = frag_from<Op>(Sacc[mt][j]);
 
-    // ---- epilogue: scale, gated RMSNorm over d_v, stores from the tiles
-    float f[CT][4];
-    if (z) {
-#pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float ss = 0.f;
-#pragma unroll
-          for (int j = 0; j < DVT; ++j) ss = fmaf(Oacc[mt][j][i], Oacc[mt][j][i], ss);
-          ss = group_sum<16>(ss);
-          if (l16 == 0) sRed[wave * C + 16 * mt + 4 * g4 + i] = ss;
-        }
-      __syncthreads();
-#pragma unroll
-      for (int mt = 0; mt < CT; ++mt) {
-        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-          const f32x4 part = *reinterpret_cast<const f32x4*>(sRed + w * C + 16 * mt + 4 * g4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tot[i] += part[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[mt][i] = scale * fast_rsq(tot[i] * scale * scale * (1.0f / D) + norm_eps);
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[mt][i] = scale;
-    }
+    // U = Ut - W S^T
+    f32x4 Uacc[CT][NTW];
 #pragma unroll
     for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = to_f32(ut[mt][j][i]);
+#pragma unroll
+        for (int sp = 0; sp < NPD; ++sp) wn[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
+        Uacc[mt][j] = acc;
+      }
+    if (more) GDN_LOAD_WU(un);
+
+    // O = Q' S^T
+    f32x4 Oacc[CT][NTW];
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < NPD; ++sp) qp[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
+        Oacc[mt][j] = acc;
+      }
+    if (more) GDN_LOAD_Q(un);
+
+    // O += P U
+    FragT Uf[CT][NTW];
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) Uf[mt][j] = frag_from<Op>(Uacc[mt][j]);
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int sp = 0; sp < NPC; ++sp)
+          if (2 * sp <= mt) pp[mt][sp].mma(Oacc[mt][j], Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
+    if (more) GDN_LOAD_P(un);
+
+    // S^T <- e^{G_n} S^T + K'^T U
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        f32x4 acc = Sacc[mt][j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= egn;
+#pragma unroll
+        for (int sp = 0; sp < NPC; ++sp) kt[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
+        Sacc[mt][j] = acc;
+      }
+    if (more) GDN_LOAD_KT(un);
+
+    // scale * O out; with the norm, this tile's sum of squares per token
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt) {
+      if (norm) {
+        float ssq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) acc = fmaf(Oacc[mt][j][i] * scale, Oacc[mt][j][i] * scale, acc);
+          ssq[i] = group_sum<16>(acc);
+        }
+        const int t = 16 * mt + 4 * g4 + l16;
+        if (l16 < 4 && t < nvalid)
+          part[((c0 + t) * h_v + h) * NT + tile] = l16 == 0 ? ssq[0] : l16 == 1 ? ssq[1] : l16 == 2 ? ssq[2] : ssq[3];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * mt + 4 * g4 + i;
         if (t < nvalid) {
-          T* orow = o + (c0 + t) * o_ld + h * D;
+          Op* orow = o + (c0 + t) * o_ld + col0;
 #pragma unroll
-          for (int j = 0; j < DVT; ++j) {
-            float v = Oacc[mt][j][i] * f[mt][i];
-            if (z) v *= nw[j] * fast_silu(zz[mt][j][i]);
-            orow[16 * (wave * DVT + j) + l16] = from_f32<T>(v);
-          }
+          for (int j = 0; j < NTW; ++j) orow[16 * j + l16] = from_f32<Op>(Oacc[mt][j][i] * scale);
         }
       }
-    __syncthreads();  // LDS is rewritten by the next chunk
+    }
   }
-#undef GDN_PREFETCH_A
-#undef GDN_PREFETCH_B
+#undef GDN_LOAD_WU
+#undef GDN_LOAD_Q
+#undef GDN_LOAD_P
+#undef GDN_LOAD_KT
 
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-    for (int j = 0; j < DVT; ++j) {
-      const int dv = 16 * (wave * DVT + j) + l16;
+    for (int j = 0; j < NTW; ++j) {
+      const int dv = 16 * (NTW * tile + j) + l16;
       *reinterpret_cast<float4*>(st_ptr + dv * D + 16 * mt + 4 * g4) =
           make_float4(Sacc[mt][j][0], Sacc[mt][j][1], Sacc[mt][j][2], Sacc[mt][j][3]);
     }
+}
+
+// ------------------------------------------------------------------ norm
+// out = o / sqrt(mean_dv(o^2) + eps) * w * silu(z) in place, o = scale * O as
+// the chain wrote it; the mean comes from the chain's per-tile sums in fp32.
+// Tokens outside [cu[0], cu[n_seq]) are left alone, as the chain leaves them.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gated_norm_kernel(T* __restrict__ o, const T* __restrict__ z,
+                                                         const T* __restrict__ norm_w, const float* __restrict__ part,
+                                                         int32_t ntile, const int32_t* __restrict__ cu, int32_t n_seq,
+                                                         int64_t t_total, int32_t h_v, float eps) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR, NT = D / 16;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int e0 = (threadIdx.x % LPR) * 8;
+  const int64_t t = row / h_v;
+  const int64_t t_lo = max((int64_t)cu[0], (int64_t)0), t_hi = min((int64_t)cu[n_seq], t_total);
+  if (t < t_lo || t >= t_hi) return;
+  float tot = 0.f;
+  for (int i = 0; i < ntile; ++i) tot += part[row * NT + i];
+  const float rstd = fast_rsq(tot * (1.0f / D) + eps);
+  float v[8], zz[8], w[8];
+  load8(o + row * D + e0, v);
+  load8(z + row * D + e0, zz);
+  load8(norm_w + e0, w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = v[e] * rstd * w[e] * fast_silu(zz[e]);
+  store8(o + row * D + e0, v);
+}
+
+// Tiles of d_v per wave: one for a single long sequence is the most
+// parallel chain; the per-token partial sums keep room for NT tiles.
+template <typename Op, int D>
+constexpr int kTileW = 1;
+
+// workspace: [chunk index][norm partials fp32 [t_total][h_v][NT]][units]
+inline size_t idx_bytes(int32_t n_seq) { return (((size_t)n_seq + 1) * 4 + 255) / 256 * 256; }
+inline size_t part_bytes(int64_t t_total, int32_t h_v, int nt) {
+  return ((size_t)t_total * h_v * nt * 4 + 255) / 256 * 256;
 }
 
 template <typename T, typename Op, int D, int C>
 size_t ws_bytes(int32_t n_seq, int64_t t_total, int32_t h_v) {
   using K = Cfg<Op, D, C>;
   const int64_t max_chunks = t_total / C + n_seq;
-  const size_t idx = (((size_t)n_seq + 1) * 4 + 255) / 256 * 256;
-  return idx + (size_t)max_chunks * h_v * K::UNIT;
+  return idx_bytes(n_seq) + part_bytes(t_total, h_v, K::NT) + (size_t)max_chunks * h_v * K::UNIT;
 }
 
 template <typename T, typename Op, int D, int C>
 hipError_t run(const ChunkArgs& a, hipStream_t st) {
   using K = Cfg<Op, D, C>;
-  static_assert(K::PREP_BYTES <= 160 * 1024 && K::STATE_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(sizeof(T) == sizeof(Op), "the chain writes O in the activation type");
+  static_assert(K::PREP_BYTES <= 160 * 1024, "LDS budget");
+  constexpr int NTW = kTileW<Op, D>, NTILE = K::NT / NTW;
   if (a.n_seq == 0) return hipSuccess;
   int32_t* cstart = reinterpret_cast<int32_t*>(a.workspace);
-  unsigned char* units = reinterpret_cast<unsigned char*>(a.workspace) + (((size_t)a.n_seq + 1) * 4 + 255) / 256 * 256;
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.workspace) + idx_bytes(a.n_seq));
+  unsigned char* units = reinterpret_cast<unsigned char*>(part) + part_bytes(a.t_total, a.s.h_v, K::NT);
   hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seq, a.t_total, (int32_t)C,
                      cstart);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -712,10 +700,19 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
                        a.s.h_k, a.s.h_v, units);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((chunk_state_kernel<T, Op, D, C>), dim3((unsigned)((int64_t)a.n_seq * a.s.h_v)),
-                     dim3(K::THREADS), 0, st, (const T*)a.qkv, a.cu_seqlens, a.slots, a.has_init, cstart, units,
-                     a.state, a.n_slots, (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.norm_eps, a.scale, a.t_total,
-                     a.s.h_k, a.s.h_v);
+  const int32_t norm = a.z != nullptr;
+  const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
+  hipLaunchKernelGGL((chunk_state_kernel<Op, D, C, NTW>), dim3((unsigned)(groups * NTILE)), dim3(64), 0, st,
+                     a.cu_seqlens, a.slots, a.has_init, cstart, units, part, a.state, a.n_slots, (Op*)a.o, norm,
+                     a.scale, a.t_total, a.n_seq, a.s.h_v);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (norm && a.t_total > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t rows = a.t_total * a.s.h_v;
+    hipLaunchKernelGGL((gated_norm_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       (T*)a.o, (const T*)a.z, (const T*)a.norm_w, part, (int32_t)NTILE, a.cu_seqlens, a.n_seq,
+                       a.t_total, a.s.h_v, a.norm_eps);
+  }
   return hipGetLastError();
 }
 
