@@ -14,14 +14,14 @@
 // sequence with 32 V heads already gives 256 independent waves, one per CU,
 // with no LDS and no barrier in the loop.  The prep pass writes every operand
 // the chain reads as ready-made MFMA fragments:
-//   -W and Q' = diag(e^G) Q      (A operands, contraction over d_k)
-//   K'^T = (diag(e^{G_n-G}) K)^T  (A operand, contraction over the chunk)
-//   P                             (A operand, lower triangle)
+//   -W and Q' = scale diag(e^G) Q (A operands, contraction over d_k)
+//   K'^T = (diag(e^{G_n-G}) K)^T   (A operand, contraction over the chunk)
+//   scale P                        (A operand, lower triangle)
 //   Ut                            (accumulator layout)
 // so each wave streams them with 16-byte loads one chunk ahead.  The gated
 // RMSNorm needs the whole d_v row, which is spread over the waves of a head:
-// the chain writes scale * O and each tile's sum of squares, and a small
-// elementwise pass finishes the norm in place.
+// the chain writes scale * O and a small row-wise pass finishes the norm in
+// place.
 //
 //   chunk_index_kernel  first global chunk of every sequence (block scan)
 //   chunk_prep_kernel   per (chunk, V head): q/k L2 norm, gates, Gram, T and
@@ -185,7 +185,8 @@ template <typename T, typename Op, int D, int C>
 __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     const T* __restrict__ qkv, const float* __restrict__ g_in, const float* __restrict__ beta_in,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const int32_t* __restrict__ cstart,
-    int32_t n_slots, int32_t n_seq, int64_t t_total, int32_t h_k, int32_t h_v, unsigned char* __restrict__ ws) {
+    int32_t n_slots, int32_t n_seq, int64_t t_total, int32_t h_k, int32_t h_v, float scale,
+    unsigned char* __restrict__ ws) {
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   }
   __syncthreads();
 
-  // ---- Q' = diag(e^G) Q^, K'^T = (diag(e^{G_n - G}) K^)^T and P as pair fragments.
+  // ---- Q' = scale diag(e^G) Q^, K'^T = (diag(e^{G_n - G}) K^)^T and scale P as pair fragments.
   // sQ, sK, sP and sG stay unchanged until the W phase, behind later barriers.
   {
     constexpr int NPD = K::NPD, NPC = K::NPC, NQ = CT * NPD, NK = NT * NPC, NP = CT * NPC;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       Op* dst;
       if (q < NQ) {
         const int mt = q / NPD, sp = q % NPD, r = 16 * mt + l16;
-        const float f = fast_exp(sG[r]);
+        const float f = scale * fast_exp(sG[r]);
         const Op* src = sQ + r * LD_D + 32 * sp + 4 * g4;
         lo = frag_mul<Op>(lds_frag<Op>(src), f);
         hi = 32 * sp + 16 < D ? frag_mul<Op>(lds_frag<Op>(src + 16), f) : zero_frag<Op>();
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       } else {
         const int idx = q - NQ - NK, mt = idx / NPC, sp = idx % NPC;
         const Op* src = sP + (16 * mt + l16) * LD_C + 32 * sp + 4 * g4;
-        lo = lds_frag<Op>(src);
-        hi = 32 * sp + 16 < C ? lds_frag<Op>(src + 16) : zero_frag<Op>();
+        lo = frag_mul<Op>(lds_frag<Op>(src), scale);
+        hi = 32 * sp + 16 < C ? frag_mul<Op>(lds_frag<Op>(src + 16), scale) : zero_frag<Op>();
         dst = reinterpret_cast<Op*>(unit + K::P_OFF) + (idx * 64 + lane) * 8;
       }
       store_pair<Op>(dst, lo, hi);
@@ -442,9 +443,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 template <typename Op, int D, int C, int NTW>
 __global__ __launch_bounds__(64) void chunk_state_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
-    const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws, float* __restrict__ part,
-    float* __restrict__ state, int32_t n_slots, Op* __restrict__ o, int32_t norm, float scale, int64_t t_total,
-    int32_t n_seq, int32_t h_v) {
+    const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws, float* __restrict__ state,
+    int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v) {
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, NTILE = NT / NTW;
@@ -458,11 +458,9 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
   const int64_t lo = min((int64_t)cu[n], t_total);
   const int64_t hi = min(max((int64_t)cu[n + 1], lo), t_total);
   const int32_t slot = slots[n];
-  if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs (and their norm partials)
+  if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs
     for (int64_t e = lane; e < (hi - lo) * 16 * NTW; e += 64)
       o[(lo + e / (16 * NTW)) * o_ld + col0 + e % (16 * NTW)] = from_f32<Op>(0.f);
-    if (norm)
-      for (int64_t t = lo + lane; t < hi; t += 64) part[(t * h_v + h) * NT + tile] = 0.f;
     return;
   }
   const bool init = has_init == nullptr || has_init[n] != 0;
@@ -524,11 +522,16 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
     GDN_LOAD_KT(u0);
   }
   const FragT zf = zero_frag<Op>();
+  const int32_t lane_off = (int32_t)(4 * g4 * o_ld) + l16;  // lane's row 4g and column within the tile
 
   for (int64_t c0 = lo; c0 < hi; c0 += C, ++gcx) {
     const int nvalid = (int)min((int64_t)C, hi - c0);
-    const bool more = c0 + C < hi;
-    const unsigned char* un = ws + ((int64_t)(gcx + 1) * h_v + h) * K::UNIT;  // read only when `more`
+    // The next chunk's operands are loaded unconditionally (the last chunk
+    // re-reads its own unit), so the wait counts stay exact: a load under a
+    // branch makes the compiler wait for every load issued after it as well.
+    // Scheduling fences keep each group right after the phase that frees its
+    // registers, a full iteration ahead of its use.
+    const unsigned char* un = ws + ((int64_t)(c0 + C < hi ? gcx + 1 : gcx) * h_v + h) * K::UNIT;
 
     FragT Sf[NT][NTW];
 #pragma unroll
@@ -549,7 +552,9 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
         for (int sp = 0; sp < NPD; ++sp) wn[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
         Uacc[mt][j] = acc;
       }
-    if (more) GDN_LOAD_WU(un);
+    __builtin_amdgcn_sched_barrier(0);
+    GDN_LOAD_WU(un);
+    __builtin_amdgcn_sched_barrier(0);
 
     // O = Q' S^T
     f32x4 Oacc[CT][NTW];
@@ -562,7 +567,9 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
         for (int sp = 0; sp < NPD; ++sp) qp[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
         Oacc[mt][j] = acc;
       }
-    if (more) GDN_LOAD_Q(un);
+    __builtin_amdgcn_sched_barrier(0);
+    GDN_LOAD_Q(un);
+    __builtin_amdgcn_sched_barrier(0);
 
     // O += P U
     FragT Uf[CT][NTW];
@@ -577,7 +584,9 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
 #pragma unroll
         for (int sp = 0; sp < NPC; ++sp)
           if (2 * sp <= mt) pp[mt][sp].mma(Oacc[mt][j], Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
-    if (more) GDN_LOAD_P(un);
+    __builtin_amdgcn_sched_barrier(0);
+    GDN_LOAD_P(un);
+    __builtin_amdgcn_sched_barrier(0);
 
     // S^T <- e^{G_n} S^T + K'^T U
 #pragma unroll
@@ -591,33 +600,32 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
         for (int sp = 0; sp < NPC; ++sp) kt[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
         Sacc[mt][j] = acc;
       }
-    if (more) GDN_LOAD_KT(un);
+    __builtin_amdgcn_sched_barrier(0);
+    GDN_LOAD_KT(un);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // scale * O out; with the norm, this tile's sum of squares per token
+    // O out (the scale is in Q' and P).  Row bases are uniform, the lane part
+    // is loop-invariant; a full chunk stores without per-row guards.
+    if (nvalid == C) {
 #pragma unroll
-    for (int mt = 0; mt < CT; ++mt) {
-      if (norm) {
-        float ssq[4];
+      for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float acc = 0.f;
+          Op* orow = o + (c0 + 16 * mt + i) * o_ld + col0;
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) acc = fmaf(Oacc[mt][j][i] * scale, Oacc[mt][j][i] * scale, acc);
-          ssq[i] = group_sum<16>(acc);
+          for (int j = 0; j < NTW; ++j) orow[lane_off + 16 * j] = from_f32<Op>(Oacc[mt][j][i]);
         }
-        const int t = 16 * mt + 4 * g4 + l16;
-        if (l16 < 4 && t < nvalid)
-          part[((c0 + t) * h_v + h) * NT + tile] = l16 == 0 ? ssq[0] : l16 == 1 ? ssq[1] : l16 == 2 ? ssq[2] : ssq[3];
-      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mt + 4 * g4 + i;
-        if (t < nvalid) {
-          Op* orow = o + (c0 + t) * o_ld + col0;
+      for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) orow[16 * j + l16] = from_f32<Op>(Oacc[mt][j][i] * scale);
+        for (int i = 0; i < 4; ++i) {
+          Op* orow = o + (c0 + 16 * mt + i) * o_ld + col0;
+          if (16 * mt + 4 * g4 + i < nvalid) {
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) orow[lane_off + 16 * j] = from_f32<Op>(Oacc[mt][j][i]);
+          }
         }
-      }
     }
   }
 #undef GDN_LOAD_WU
@@ -637,47 +645,51 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
 
 // ------------------------------------------------------------------ norm
 // out = o / sqrt(mean_dv(o^2) + eps) * w * silu(z) in place, o = scale * O as
-// the chain wrote it; the mean comes from the chain's per-tile sums in fp32.
-// Tokens outside [cu[0], cu[n_seq]) are left alone, as the chain leaves them.
+// the chain wrote it.  D / 8 lanes hold one (token, V head) row.  Tokens
+// outside [cu[0], cu[n_seq]) are left alone, as the chain leaves them.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gated_norm_kernel(T* __restrict__ o, const T* __restrict__ z,
-                                                         const T* __restrict__ norm_w, const float* __restrict__ part,
-                                                         int32_t ntile, const int32_t* __restrict__ cu, int32_t n_seq,
+                                                         const T* __restrict__ norm_w,
+                                                         const int32_t* __restrict__ cu, int32_t n_seq,
                                                          int64_t t_total, int32_t h_v, float eps) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR, NT = D / 16;
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int e0 = (threadIdx.x % LPR) * 8;
   const int64_t t = row / h_v;
   const int64_t t_lo = max((int64_t)cu[0], (int64_t)0), t_hi = min((int64_t)cu[n_seq], t_total);
-  if (t < t_lo || t >= t_hi) return;
-  float tot = 0.f;
-  for (int i = 0; i < ntile; ++i) tot += part[row * NT + i];
-  const float rstd = fast_rsq(tot * (1.0f / D) + eps);
+  const bool live = t >= t_lo && t < t_hi;
   float v[8], zz[8], w[8];
-  load8(o + row * D + e0, v);
-  load8(z + row * D + e0, zz);
-  load8(norm_w + e0, w);
+  if (live) {
+    load8(o + row * D + e0, v);
+    load8(z + row * D + e0, zz);
+    load8(norm_w + e0, w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = zz[e] = w[e] = 0.f;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+  ss = group_sum<LPR>(ss);  // LPR lanes of a row are an aligned group
+  const float rstd = fast_rsq(ss * (1.0f / D) + eps);
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = v[e] * rstd * w[e] * fast_silu(zz[e]);
-  store8(o + row * D + e0, v);
+  if (live) store8(o + row * D + e0, v);
 }
 
 // Tiles of d_v per wave: one for a single long sequence is the most
-// parallel chain; the per-token partial sums keep room for NT tiles.
+// parallel chain.
 template <typename Op, int D>
 constexpr int kTileW = 1;
 
-// workspace: [chunk index][norm partials fp32 [t_total][h_v][NT]][units]
+// workspace: [chunk index][units]
 inline size_t idx_bytes(int32_t n_seq) { return (((size_t)n_seq + 1) * 4 + 255) / 256 * 256; }
-inline size_t part_bytes(int64_t t_total, int32_t h_v, int nt) {
-  return ((size_t)t_total * h_v * nt * 4 + 255) / 256 * 256;
-}
 
 template <typename T, typename Op, int D, int C>
 size_t ws_bytes(int32_t n_seq, int64_t t_total, int32_t h_v) {
   using K = Cfg<Op, D, C>;
   const int64_t max_chunks = t_total / C + n_seq;
-  return idx_bytes(n_seq) + part_bytes(t_total, h_v, K::NT) + (size_t)max_chunks * h_v * K::UNIT;
+  return idx_bytes(n_seq) + (size_t)max_chunks * h_v * K::UNIT;
 }
 
 template <typename T, typename Op, int D, int C>
@@ -688,8 +700,7 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   constexpr int NTW = kTileW<Op, D>, NTILE = K::NT / NTW;
   if (a.n_seq == 0) return hipSuccess;
   int32_t* cstart = reinterpret_cast<int32_t*>(a.workspace);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.workspace) + idx_bytes(a.n_seq));
-  unsigned char* units = reinterpret_cast<unsigned char*>(part) + part_bytes(a.t_total, a.s.h_v, K::NT);
+  unsigned char* units = reinterpret_cast<unsigned char*>(a.workspace) + idx_bytes(a.n_seq);
   hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seq, a.t_total, (int32_t)C,
                      cstart);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -697,21 +708,20 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   if (max_chunks > 0) {
     hipLaunchKernelGGL((chunk_prep_kernel<T, Op, D, C>), dim3((unsigned)(max_chunks * a.s.h_v)), dim3(K::THREADS), 0,
                        st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, cstart, a.n_slots, a.n_seq, a.t_total,
-                       a.s.h_k, a.s.h_v, units);
+                       a.s.h_k, a.s.h_v, a.scale, units);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  const int32_t norm = a.z != nullptr;
   const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
   hipLaunchKernelGGL((chunk_state_kernel<Op, D, C, NTW>), dim3((unsigned)(groups * NTILE)), dim3(64), 0, st,
-                     a.cu_seqlens, a.slots, a.has_init, cstart, units, part, a.state, a.n_slots, (Op*)a.o, norm,
-                     a.scale, a.t_total, a.n_seq, a.s.h_v);
+                     a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state, a.n_slots, (Op*)a.o, a.t_total,
+                     a.n_seq, a.s.h_v);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  if (norm && a.t_total > 0) {
+  if (a.z != nullptr && a.t_total > 0) {
     constexpr int RPB = 256 / (D / 8);
     const int64_t rows = a.t_total * a.s.h_v;
     hipLaunchKernelGGL((gated_norm_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       (T*)a.o, (const T*)a.z, (const T*)a.norm_w, part, (int32_t)NTILE, a.cu_seqlens, a.n_seq,
-                       a.t_total, a.s.h_v, a.norm_eps);
+                       (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.cu_seqlens, a.n_seq, a.t_total, a.s.h_v,
+                       a.norm_eps);
   }
   return hipGetLastError();
 }

@@ -102,12 +102,11 @@ def test_chunk_prefill_workspace(L):
     if os.environ.get("GDN_PREFILL_PATH") == "fused":
         assert ws == 0
         return
-    # split path: a 256-byte-aligned chunk index, the fp32 norm partials per
-    # (token, V head, 16-wide d_v tile), then one 256-byte-aligned unit per
-    # (chunk, V head) holding -W, Q', K'^T, Ut (bf16, C x D each), P (bf16, C x C)
-    # and e^{G_n}
+    # split path: a 256-byte-aligned chunk index, then one 256-byte-aligned unit
+    # per (chunk, V head) holding -W, Q', K'^T, Ut (bf16, C x D each),
+    # P (bf16, C x C) and e^{G_n}
     unit = (4 * 64 * 128 * 2 + 64 * 64 * 2 + 16 + 255) // 256 * 256
-    assert ws == 256 + 4096 * 32 * 8 * 4 + (4096 // 64 + 1) * 32 * unit
+    assert ws == 256 + (4096 // 64 + 1) * 32 * unit
     # (same sizes as the query, so these calls stop at validation and never launch)
     assert chunk_call(L, t_total=4096) == WS
     assert chunk_call(L, t_total=4096, ws=FAKE, ws_bytes=ws - 1) == WS
