@@ -12,22 +12,21 @@
 // over d_k or over tokens.  So one wave owns a 16-wide slice of d_v for all of
 // d_k, holding its S^T slice in MFMA accumulators, and a single 4096-token
 // sequence with 32 V heads already gives 256 independent waves, one per CU,
-// with no LDS and no barrier in the loop.  The prep pass writes every operand
-// the chain reads as ready-made MFMA fragments:
-//   -W and Q' = scale diag(e^G) Q (A operands, contraction over d_k)
+// with no LDS and no barrier in the loop.  The chain keeps only what is
+// serial, U and the state update; it records S at every chunk start (h) and
+// U, and the output O = Q' h^T + P U with its gated RMSNorm is again chunk-
+// parallel.  The prep pass writes every operand as ready-made MFMA fragments:
+//   -W, Q' = scale diag(e^G) Q    (A operands, contraction over d_k)
 //   K'^T = (diag(e^{G_n-G}) K)^T   (A operand, contraction over the chunk)
 //   scale P                        (A operand, lower triangle)
-//   Ut                            (accumulator layout)
-// so each wave streams them with 16-byte loads one chunk ahead.  The gated
-// RMSNorm needs the whole d_v row, which is spread over the waves of a head:
-// the chain writes scale * O and a small row-wise pass finishes the norm in
-// place.
+//   Ut                             (accumulator layout; the chain turns it into U)
+// so every load is a 16- or 8-byte lane-contiguous vector.
 //
 //   chunk_index_kernel  first global chunk of every sequence (block scan)
 //   chunk_prep_kernel   per (chunk, V head): q/k L2 norm, gates, Gram, T and
 //                       the operand fragments above
 //   chunk_state_kernel  per (sequence, V head, d_v tile): the chunk loop
-//   gated_norm_kernel   per (token, V head): RMSNorm over d_v times w silu(z)
+//   chunk_out_kernel    per (chunk, V head): O, gated RMSNorm over d_v, store
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -44,9 +43,6 @@ struct Cfg {
   static constexpr int THREADS = kThreads<D>;
   static constexpr int WAVES = THREADS / 64;
   static constexpr int DVT = NT / WAVES;
-  static constexpr int LD_D = D + 4;   // row stride of [C][D] operand tiles (elements)
-  static constexpr int LD_C = C + 4;   // row stride of [C][C] operand tiles
-  static constexpr int LD_F = C + 4;   // row stride of the fp32 A / T tile
   static constexpr int LPR = D / 8;    // lanes per row piece of 8 elements
   static constexpr int RPP = THREADS / LPR;
   static constexpr int RPT = (C + RPP - 1) / RPP;
@@ -61,16 +57,25 @@ struct Cfg {
   static constexpr int KT_OFF = Q_OFF + CT * NPD * PAIR * (int)sizeof(Op);  // K'^T [NT][NPC]
   static constexpr int P_OFF = KT_OFF + NT * NPC * PAIR * (int)sizeof(Op);  // P   [CT][NPC]
   static constexpr int UT_OFF = P_OFF + CT * NPC * PAIR * (int)sizeof(Op);  // Ut  [CT][NT][64][4]
-  static constexpr int F_OFF = UT_OFF + C * D * (int)sizeof(Op);            // e^{G_n}
+  static constexpr int H_OFF = UT_OFF + C * D * (int)sizeof(Op);            // S^T at chunk start, [NPD][NT] pairs
+  static constexpr int F_OFF = H_OFF + NPD * NT * PAIR * (int)sizeof(Op);   // e^{G_n}
   static constexpr int UNIT = (F_OFF + 16 + 255) / 256 * 256;
-  // prep kernel LDS
-  static constexpr int PQ = 0;                                     // q^ rows, later W
-  static constexpr int PK = PQ + C * LD_D * (int)sizeof(Op);       // k^ rows
-  static constexpr int PV = PK + C * LD_D * (int)sizeof(Op);       // v rows
-  static constexpr int PA = PV + C * LD_D * (int)sizeof(Op);       // fp32 A, then T in place
-  static constexpr int PP = PA + C * LD_F * 4;                     // P
-  static constexpr int PG = PP + C * LD_C * (int)sizeof(Op);       // G, beta, beta e^G
-  static constexpr int PREP_BYTES = PG + 3 * C * 4;
+  // output kernel LDS: the fp32 O tile, row-major
+  static constexpr int LD_O = D + 4;
+  static constexpr int OUT_BYTES = C * LD_O * 4;
+  // prep kernel LDS.  Row strides are padded so the 8-byte fragment reads of
+  // a wave (16 rows x 4 column groups) hit distinct banks.
+  static constexpr int LDR = D + 16;   // raw q, k rows (elements)
+  static constexpr int LDA = C + 16;   // fp32 A, then T in place
+  static constexpr int LDT = C + 8;    // T diag(b e^G r_k) and T diag(b), operand type
+  static constexpr int PQ = 0;
+  static constexpr int PK = PQ + C * LDR * (int)sizeof(Op);
+  static constexpr int PA = PK + C * LDR * (int)sizeof(Op);
+  static constexpr int PS = PA + C * LDA * 4;                      // G, b, r_q, r_k
+  static constexpr bool T_OVER_Q = 2 * LDT <= LDR;                 // the two T copies fit over q
+  static constexpr int PTW = T_OVER_Q ? PQ : PS + 4 * C * 4;
+  static constexpr int PTU = PTW + C * LDT * (int)sizeof(Op);
+  static constexpr int PREP_BYTES = T_OVER_Q ? PS + 4 * C * 4 : PTU + C * LDT * (int)sizeof(Op);
 };
 
 __device__ __forceinline__ int32_t seq_of_chunk(const int32_t* __restrict__ cstart, int32_t n_seq, int32_t gc) {
@@ -164,6 +169,10 @@ template <typename Op> struct Pair;
 template <> struct Pair<bf16> {
   bf16x8 v;
   __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void split(bf16x4& a, bf16x4& b) const {
+    a = bf16x4{v[0], v[1], v[2], v[3]};
+    b = bf16x4{v[4], v[5], v[6], v[7]};
+  }
   __device__ __forceinline__ void mma(f32x4& acc, const bf16x4& b0, const bf16x4& b1) const {
     const bf16x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, b, acc, 0, 0, 0);
@@ -175,31 +184,75 @@ template <> struct Pair<float> {
     lo = reinterpret_cast<const f32x4*>(p)[0];
     hi = reinterpret_cast<const f32x4*>(p)[1];
   }
+  __device__ __forceinline__ void split(f32x4& a, f32x4& b) const {
+    a = lo;
+    b = hi;
+  }
   __device__ __forceinline__ void mma(f32x4& acc, const f32x4& b0, const f32x4& b1) const {
     mma_k32(acc, lo, hi, b0, b1);
   }
 };
 
+// Address of a workspace vector: uniform base plus a 32-bit unsigned byte
+// offset, which lets the compiler use SGPR-base addressing with no 64-bit
+// VALU arithmetic per load.
+template <typename V>
+__device__ __forceinline__ const V* at(const unsigned char* base, uint32_t off) {
+  return reinterpret_cast<const V*>(base + off);
+}
+template <typename V>
+__device__ __forceinline__ V* at(unsigned char* base, uint32_t off) {
+  return reinterpret_cast<V*>(base + off);
+}
+
 // ------------------------------------------------------------------ prep
+// 8 raw activations into LDS unchanged (activation and operand types agree).
+template <typename T>
+__device__ __forceinline__ void raw_store(const Raw8<T>& r, T* dst);
+template <>
+__device__ __forceinline__ void raw_store<bf16>(const Raw8<bf16>& r, bf16* dst) {
+  *reinterpret_cast<uint4*>(dst) = r.u;
+}
+template <>
+__device__ __forceinline__ void raw_store<float>(const Raw8<float>& r, float* dst) {
+  reinterpret_cast<uint4*>(dst)[0] = r.u[0];
+  reinterpret_cast<uint4*>(dst)[1] = r.u[1];
+}
+
+// Per (chunk, V head).  Everything runs on the raw q, k, v of the chunk; the
+// L2 norms enter as per-token factors r = 1/sqrt(|x|^2 + 1e-6):
+//   A_ij  = b_i r_k[i] r_k[j] e^{G_i-G_j} (k_i.k_j), i > j;   T = (I + A)^{-1}
+//   P_ij  = scale r_q[i] r_k[j] e^{G_i-G_j} (q_i.k_j), i >= j
+//   W     = T diag(b e^G r_k) K,   Ut = T diag(b) V
+//   Q'    = diag(scale e^G r_q) Q, K' = diag(e^{G_n-G} r_k) K
+// No fragment is ever read down an LDS column.  P is formed as P^T = K Q^T,
+// whose accumulator layout is P's A-fragment layout; W is formed as
+// W^T = K^T (T diag(..))^T, whose accumulator layout is W's A-fragment layout;
+// K and V blocks reach the column (B operand) layout through one MFMA with an
+// identity operand, which is exact.
 template <typename T, typename Op, int D, int C>
 __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     const T* __restrict__ qkv, const float* __restrict__ g_in, const float* __restrict__ beta_in,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const int32_t* __restrict__ cstart,
     int32_t n_slots, int32_t n_seq, int64_t t_total, int32_t h_k, int32_t h_v, float scale,
     unsigned char* __restrict__ ws) {
+  static_assert(sizeof(T) == sizeof(Op), "raw activations are MFMA operands");
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
-  constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
-  constexpr int LD_D = K::LD_D, LD_C = K::LD_C, LD_F = K::LD_F;
+  constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, DVT = K::DVT, LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
+  constexpr int NPD = K::NPD, NPC = K::NPC, LDR = K::LDR, LDA = K::LDA, LDT = K::LDT;
+  constexpr uint32_t PB = K::PAIR * sizeof(Op);
+  static_assert(DVT == 1 || DVT == 2, "a wave's d tiles form one pair fragment");
   __shared__ __attribute__((aligned(16))) unsigned char smem[K::PREP_BYTES];
   Op* sQ = reinterpret_cast<Op*>(smem + K::PQ);
   Op* sK = reinterpret_cast<Op*>(smem + K::PK);
-  Op* sV = reinterpret_cast<Op*>(smem + K::PV);
-  float* sAT = reinterpret_cast<float*>(smem + K::PA);
-  Op* sP = reinterpret_cast<Op*>(smem + K::PP);
-  float* sG = reinterpret_cast<float*>(smem + K::PG);
+  float* sA = reinterpret_cast<float*>(smem + K::PA);
+  float* sG = reinterpret_cast<float*>(smem + K::PS);
   float* sB = sG + C;
-  float* sBE = sG + 2 * C;
+  float* sRQ = sG + 2 * C;
+  float* sRK = sG + 3 * C;
+  Op* sTW = reinterpret_cast<Op*>(smem + K::PTW);
+  Op* sTU = reinterpret_cast<Op*>(smem + K::PTU);
 
   const int gc = blockIdx.x / h_v;
   const int h = blockIdx.x % h_v;
@@ -214,18 +267,34 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   const int64_t c0 = seq_lo + (int64_t)(gc - cstart[n]) * C;
   const int nvalid = (int)min((int64_t)C, seq_hi - c0);
   unsigned char* unit = ws + ((int64_t)gc * h_v + h) * K::UNIT;
+  const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
+  const FragT zf = zero_frag<Op>();
+  FragT eye;  // B fragment of the 16x16 identity
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eye[i] = from_f32<Op>(4 * g4 + i == l16 ? 1.f : 0.f);
 
-  // ---- stage q^, k^ (normalised) and v row-major; gates
+  // ---- v blocks of this wave's d_v tiles, A layout, straight from memory
+  FragT Va[CT][DVT];
+  {
+    const T* vbase = qkv + (int64_t)(2 * h_k + h) * D + 16 * wave * DVT + 4 * g4;
+#pragma unroll
+    for (int kb = 0; kb < CT; ++kb)
+#pragma unroll
+      for (int j = 0; j < DVT; ++j) {
+        const int r = 16 * kb + l16;
+        Va[kb][j] = r < nvalid ? *reinterpret_cast<const FragT*>(vbase + (c0 + r) * c_ch + 16 * j) : zf;
+      }
+  }
+  // ---- raw q, k rows into LDS with their inverse norms; gates
   {
     const int e0 = (tid % LPR) * 8, r0 = tid / LPR;
-    const int64_t cols[3] = {(int64_t)hk * D, (int64_t)(h_k + hk) * D, (int64_t)(2 * h_k + h) * D};
-    Raw8<T> raw[3][RPT];
+    Raw8<T> raw[2][RPT];
 #pragma unroll
-    for (int kind = 0; kind < 3; ++kind)
+    for (int kind = 0; kind < 2; ++kind)
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
         const int r = r0 + j * RPP;
-        if (r < nvalid) raw[kind][j].load(qkv + (c0 + r) * c_ch + cols[kind] + e0);
+        if (r < nvalid) raw[kind][j].load(qkv + (c0 + r) * c_ch + (int64_t)(kind * h_k + hk) * D + e0);
         else raw[kind][j].zero();
       }
     float gv = 0.f, bv = 0.f;
@@ -234,25 +303,19 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       bv = beta_in[(c0 + lane) * h_v + h];
     }
 #pragma unroll
-    for (int kind = 0; kind < 3; ++kind)
+    for (int kind = 0; kind < 2; ++kind)
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
         const int r = r0 + j * RPP;
         float v[8];
         raw[kind][j].to_f32(v);
-        if (kind < 2) {
-          float ss = 0.f;
+        float ss = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-          ss = group_sum<LPR>(ss);
-          const float rn = fast_rsq(ss + 1e-6f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= rn;
-        }
+        for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+        ss = group_sum<LPR>(ss);
         if (r < C) {
-          Op* dst = (kind == 0 ? sQ : (kind == 1 ? sK : sV)) + r * LD_D + e0;
-          *reinterpret_cast<FragT*>(dst) = FragT{from_f32<Op>(v[0]), from_f32<Op>(v[1]), from_f32<Op>(v[2]), from_f32<Op>(v[3])};
-          *reinterpret_cast<FragT*>(dst + 4) = FragT{from_f32<Op>(v[4]), from_f32<Op>(v[5]), from_f32<Op>(v[6]), from_f32<Op>(v[7])};
+          raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&raw[kind][j]), (kind == 0 ? sQ : sK) + r * LDR + e0);
+          if (tid % LPR == 0) (kind == 0 ? sRQ : sRK)[r] = fast_rsq(ss + 1e-6f);
         }
       }
     if (wave == 0) {
@@ -264,90 +327,83 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       if (lane < C) {
         sG[lane] = gv;
         sB[lane] = bv;
-        sBE[lane] = bv * fast_exp(gv);
       }
-      if (lane == C - 1) reinterpret_cast<float*>(unit + K::F_OFF)[0] = fast_exp(gv);
+      if (lane == C - 1) *at<float>(unit, K::F_OFF) = fast_exp(gv);
     }
   }
   __syncthreads();
 
-  // ---- Gram tiles (lower triangle): K K^T -> A (fp32), Q K^T -> P
+  // ---- Gram work: P^T pairs -> P fragments, K K^T tiles -> A, Q' fragments
   {
-    constexpr int NLT = CT * (CT + 1) / 2;
-    constexpr int PER_WAVE = (2 * NLT + WAVES - 1) / WAVES;
+    // item lists: P pairs (ib, sp) with 2 sp <= ib; A tiles (ib, jb) with jb <= ib; Q' pairs (mt, sp)
+    constexpr int N_P = [] { int c = 0; for (int ib = 0; ib < CT; ++ib) c += ib / 2 + 1; return c; }();
+    constexpr int N_A = CT * (CT + 1) / 2;
+    constexpr int N_Q = CT * NPD;
+    for (int it = wave; it < N_P + N_A + N_Q; it += WAVES) {
+      if (it < N_P) {
+        int ib = 0, rest = it;
+        while (rest >= ib / 2 + 1) { rest -= ib / 2 + 1; ++ib; }
+        const int sp = rest;
+        const int i = 16 * ib + l16;
+        const float fi = scale * sRQ[i];
+        const float gi = sG[i];
+        FragT half[2];
 #pragma unroll
-    for (int k = 0; k < PER_WAVE; ++k) {
-      const int q = wave + k * WAVES;
-      if (q < 2 * NLT) {
-        const bool is_p = q >= NLT;
-        const int idx = is_p ? q - NLT : q;
-        int ti = 0;
-        while ((ti + 1) * (ti + 2) / 2 <= idx) ++ti;
-        const int tj = idx - ti * (ti + 1) / 2;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int jb = 2 * sp + hh;
+          if (jb > ib || jb >= CT) { half[hh] = zf; continue; }
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const Op* arow = sK + (16 * jb + l16) * LDR + 4 * g4;
+          const Op* brow = sQ + i * LDR + 4 * g4;
+#pragma unroll
+          for (int s2 = 0; s2 < NPD; ++s2) {
+            if (32 * s2 + 16 < D)
+              mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
+                      lds_frag<Op>(brow + 32 * s2 + 16));
+            else
+              mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
+          }
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int jj = 16 * jb + 4 * g4 + ii;
+            half[hh][ii] = from_f32<Op>(i >= jj ? fi * sRK[jj] * fast_exp(fminf(gi - sG[jj], 0.f)) * acc[ii] : 0.f);
+          }
+        }
+        store_pair<Op>(at<Op>(unit, K::P_OFF + (uint32_t)(ib * NPC + sp) * PB + lp), half[0], half[1]);
+      } else if (it < N_P + N_A) {
+        int ib = 0, rest = it - N_P;
+        while (rest >= ib + 1) { rest -= ib + 1; ++ib; }
+        const int jb = rest;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const Op* arow = (is_p ? sQ : sK) + (16 * ti + l16) * LD_D;
-        const Op* brow = sK + (16 * tj + l16) * LD_D;
-        int kb = 0;
+        const Op* arow = sK + (16 * ib + l16) * LDR + 4 * g4;
+        const Op* brow = sK + (16 * jb + l16) * LDR + 4 * g4;
 #pragma unroll
-        for (; kb + 1 < NT; kb += 2)
-          mma_k32(acc, lds_frag<Op>(arow + 16 * kb + 4 * g4), lds_frag<Op>(arow + 16 * kb + 16 + 4 * g4),
-                  lds_frag<Op>(brow + 16 * kb + 4 * g4), lds_frag<Op>(brow + 16 * kb + 16 + 4 * g4));
-        if (kb < NT) mma_k16(acc, lds_frag<Op>(arow + 16 * kb + 4 * g4), lds_frag<Op>(brow + 16 * kb + 4 * g4));
-        const int cc = 16 * tj + l16;
-        const float gc_ = sG[cc];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * ti + 4 * g4 + i;
-          const float dec = fast_exp(fminf(sG[r] - gc_, 0.f));
-          if (is_p) sP[r * LD_C + cc] = from_f32<Op>(r >= cc ? dec * acc[i] : 0.f);
-          else sAT[r * LD_F + cc] = r > cc ? sB[r] * dec * acc[i] : 0.f;
+        for (int s2 = 0; s2 < NPD; ++s2) {
+          if (32 * s2 + 16 < D)
+            mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
+                    lds_frag<Op>(brow + 32 * s2 + 16));
+          else
+            mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
         }
-      }
-    }
-    for (int e = tid; e < C * C; e += K::THREADS) {  // upper blocks
-      const int r = e / C, cc = e % C;
-      if ((r >> 4) < (cc >> 4)) {
-        sAT[r * LD_F + cc] = 0.f;
-        sP[r * LD_C + cc] = from_f32<Op>(0.f);
+        const int j = 16 * jb + l16;
+        const float rj = sRK[j], gj = sG[j];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * ib + 4 * g4 + ii;
+          sA[i * LDA + j] = i > j ? sB[i] * sRK[i] * rj * fast_exp(fminf(sG[i] - gj, 0.f)) * acc[ii] : 0.f;
+        }
+      } else {
+        const int q = it - N_P - N_A, mt = q / NPD, sp = q % NPD;
+        const int t = 16 * mt + l16;
+        const float f = scale * fast_exp(sG[t]) * sRQ[t];
+        const Op* src = sQ + t * LDR + 32 * sp + 4 * g4;
+        const FragT lo = frag_mul<Op>(lds_frag<Op>(src), f);
+        const FragT hi = 32 * sp + 16 < D ? frag_mul<Op>(lds_frag<Op>(src + 16), f) : zf;
+        store_pair<Op>(at<Op>(unit, K::Q_OFF + (uint32_t)(mt * NPD + sp) * PB + lp), lo, hi);
       }
     }
   }
   __syncthreads();
-
-  // ---- Q' = scale diag(e^G) Q^, K'^T = (diag(e^{G_n - G}) K^)^T and scale P as pair fragments.
-  // sQ, sK, sP and sG stay unchanged until the W phase, behind later barriers.
-  {
-    constexpr int NPD = K::NPD, NPC = K::NPC, NQ = CT * NPD, NK = NT * NPC, NP = CT * NPC;
-    const float g_n = sG[C - 1];
-    for (int q = wave; q < NQ + NK + NP; q += WAVES) {
-      FragT lo, hi;
-      Op* dst;
-      if (q < NQ) {
-        const int mt = q / NPD, sp = q % NPD, r = 16 * mt + l16;
-        const float f = scale * fast_exp(sG[r]);
-        const Op* src = sQ + r * LD_D + 32 * sp + 4 * g4;
-        lo = frag_mul<Op>(lds_frag<Op>(src), f);
-        hi = 32 * sp + 16 < D ? frag_mul<Op>(lds_frag<Op>(src + 16), f) : zero_frag<Op>();
-        dst = reinterpret_cast<Op*>(unit + K::Q_OFF) + (q * 64 + lane) * 8;
-      } else if (q < NQ + NK) {
-        const int idx = q - NQ, mt = idx / NPC, sp = idx % NPC;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
-          lo[i] = from_f32<Op>(t0 < C ? to_f32(sK[t0 * LD_D + 16 * mt + l16]) * fast_exp(g_n - sG[t0]) : 0.f);
-          hi[i] = from_f32<Op>(t1 < C ? to_f32(sK[t1 * LD_D + 16 * mt + l16]) * fast_exp(g_n - sG[t1]) : 0.f);
-        }
-        dst = reinterpret_cast<Op*>(unit + K::KT_OFF) + (idx * 64 + lane) * 8;
-      } else {
-        const int idx = q - NQ - NK, mt = idx / NPC, sp = idx % NPC;
-        const Op* src = sP + (16 * mt + l16) * LD_C + 32 * sp + 4 * g4;
-        lo = frag_mul<Op>(lds_frag<Op>(src), scale);
-        hi = 32 * sp + 16 < C ? frag_mul<Op>(lds_frag<Op>(src + 16), scale) : zero_frag<Op>();
-        dst = reinterpret_cast<Op*>(unit + K::P_OFF) + (idx * 64 + lane) * 8;
-      }
-      store_pair<Op>(dst, lo, hi);
-    }
-  }
 
   // ---- T = (I + A)^-1 in place.  (a) diagonal 16x16 blocks, one lane per column
   if (tid < CT * 16) {
@@ -355,7 +411,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float* arow = sAT + (16 * b + r) * LD_F + 16 * b;
+      const float* arow = sA + (16 * b + r) * LDA + 16 * b;
       float acc = r == c ? 1.f : 0.f;
 #pragma unroll
       for (int j = 0; j < r; ++j) acc = fmaf(-arow[j], x[j], acc);
@@ -363,7 +419,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     }
     // every read of this block above precedes these writes in the wave's program order
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sAT[(16 * b + r) * LD_F + 16 * b + c] = x[r];
+    for (int r = 0; r < 16; ++r) sA[(16 * b + r) * LDA + 16 * b + c] = x[r];
   }
   __syncthreads();
   // (b) block rows: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.  The A blocks of the
@@ -373,7 +429,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     f32x4 a_row[CT];
 #pragma unroll
     for (int bk = 0; bk < CT; ++bk)
-      if (bk < bi) a_row[bk] = lds_frag<float>(sAT + (16 * bi + l16) * LD_F + 16 * bk + 4 * g4);
+      if (bk < bi) a_row[bk] = lds_frag<float>(sA + (16 * bi + l16) * LDA + 16 * bk + 4 * g4);
     __syncthreads();
     for (int bj = wave; bj < bi; bj += WAVES) {
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
@@ -382,53 +438,89 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         if (bk >= bj && bk < bi) {
           f32x4 b;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) b[jj] = sAT[(16 * bk + 4 * g4 + jj) * LD_F + 16 * bj + l16];
+          for (int jj = 0; jj < 4; ++jj) b[jj] = sA[(16 * bk + 4 * g4 + jj) * LDA + 16 * bj + l16];
           mma_k16(X, a_row[bk], b);
         }
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      mma_k16(Y, lds_frag<float>(sAT + (16 * bi + l16) * LD_F + 16 * bi + 4 * g4), X);
+      mma_k16(Y, lds_frag<float>(sA + (16 * bi + l16) * LDA + 16 * bi + 4 * g4), X);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sAT[(16 * bi + 4 * g4 + jj) * LD_F + 16 * bj + l16] = -Y[jj];
+      for (int jj = 0; jj < 4; ++jj) sA[(16 * bi + 4 * g4 + jj) * LDA + 16 * bj + l16] = -Y[jj];
     }
     __syncthreads();
   }
 
-  // ---- W = T diag(b e^G) K -> LDS over q^ (dead), Ut = T diag(b) V -> workspace (fragment order)
-  {
-    Op* ut = reinterpret_cast<Op*>(unit + K::UT_OFF);
-    for (int q = wave; q < 2 * CT * NT; q += WAVES) {
-      const bool is_u = q >= CT * NT;
-      const int idx = is_u ? q - CT * NT : q;
-      const int mt = idx / NT, nt = idx % NT;
-      const float* scl = is_u ? sB : sBE;
-      const Op* src = is_u ? sV : sK;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const float* trow = sAT + (16 * mt + l16) * LD_F;
-      for (int kb = 0; kb <= mt; ++kb) {  // T is lower triangular
-        const FragT a = frag_scaled<Op>(trow + 16 * kb + 4 * g4, scl + 16 * kb + 4 * g4);
-        const FragT b = frag_col<Op>(src + (16 * kb + 4 * g4) * LD_D + 16 * nt + l16, LD_D);
-        mma_k16(acc, a, b);
-      }
-      if (is_u) {
-        // lane-fragment order: [mt][nt][lane][4], as the state kernel's accumulators
-        *reinterpret_cast<FragT*>(ut + ((mt * NT + nt) * 64 + lane) * 4) = frag_from<Op>(acc);
-      } else {
+  // ---- T_W = T diag(b e^G r_k), T_U = T diag(b) in the operand type, zero above
+  // the diagonal blocks (these may overwrite q, which is dead now)
+  for (int e = tid; e < C * C / 4; e += K::THREADS) {
+    const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
+    const bool keep = (c4 >> 4) <= (r >> 4);
+    const f32x4 t = keep ? *reinterpret_cast<const f32x4*>(sA + r * LDA + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    FragT tw, tu;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sQ[(16 * mt + 4 * g4 + i) * LD_D + 16 * nt + l16] = from_f32<Op>(acc[i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float b = sB[c4 + i];
+      tw[i] = from_f32<Op>(t[i] * b * fast_exp(sG[c4 + i]) * sRK[c4 + i]);
+      tu[i] = from_f32<Op>(t[i] * b);
     }
+    *reinterpret_cast<FragT*>(sTW + r * LDT + c4) = tw;
+    *reinterpret_cast<FragT*>(sTU + r * LDT + c4) = tu;
   }
   __syncthreads();
-  // ---- -W as pair fragments (the chain adds -W S^T to Ut)
+
+  // ---- this wave's d tiles: K and V column fragments, W^T, Ut and K'^T
   {
-    constexpr int NPD = K::NPD;
-    for (int q = wave; q < CT * NPD; q += WAVES) {
-      const int mt = q / NPD, sp = q % NPD;
-      const Op* src = sQ + (16 * mt + l16) * LD_D + 32 * sp + 4 * g4;
-      const FragT lo = frag_mul<Op>(lds_frag<Op>(src), -1.f);
-      const FragT hi = 32 * sp + 16 < D ? frag_mul<Op>(lds_frag<Op>(src + 16), -1.f) : zero_frag<Op>();
-      store_pair<Op>(reinterpret_cast<Op*>(unit + K::W_OFF) + (q * 64 + lane) * 8, lo, hi);
+    FragT Kc[CT][DVT], Vc[CT][DVT];
+#pragma unroll
+    for (int kb = 0; kb < CT; ++kb)
+#pragma unroll
+      for (int j = 0; j < DVT; ++j) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        mma_k16(a, lds_frag<Op>(sK + (16 * kb + l16) * LDR + 16 * (wave * DVT + j) + 4 * g4), eye);
+        Kc[kb][j] = frag_from<Op>(a);
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+        mma_k16(b, Va[kb][j], eye);
+        Vc[kb][j] = frag_from<Op>(b);
+      }
+    const int sp_w = wave;  // the pair of d tiles this wave owns (DVT == 2), or pair 0 (DVT == 1)
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt) {
+      f32x4 wacc[DVT];
+#pragma unroll
+      for (int j = 0; j < DVT; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
+        const Op* twrow = sTW + (16 * mt + l16) * LDT + 4 * g4;
+        const Op* turow = sTU + (16 * mt + l16) * LDT + 4 * g4;
+#pragma unroll
+        for (int s2 = 0; s2 < NPC; ++s2)
+          if (2 * s2 <= mt) {
+            const bool two = 2 * s2 + 1 < CT;
+            const FragT b0 = lds_frag<Op>(twrow + 32 * s2), b1 = two ? lds_frag<Op>(twrow + 32 * s2 + 16) : zf;
+            mma_k32(acc, Kc[2 * s2][j], two ? Kc[2 * s2 + 1][j] : zf, b0, b1);
+            const FragT a0 = lds_frag<Op>(turow + 32 * s2), a1 = two ? lds_frag<Op>(turow + 32 * s2 + 16) : zf;
+            mma_k32(uacc, a0, a1, Vc[2 * s2][j], two ? Vc[2 * s2 + 1][j] : zf);
+          }
+        wacc[j] = acc;
+        *at<FragT>(unit, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf) = frag_from<Op>(uacc);
+      }
+      store_pair<Op>(at<Op>(unit, K::W_OFF + (uint32_t)(mt * NPD + sp_w) * PB + lp), frag_from<Op>(wacc[0], -1.f),
+                     DVT == 2 ? frag_from<Op>(wacc[DVT - 1], -1.f) : zf);
     }
+    const float g_n = sG[C - 1];
+#pragma unroll
+    for (int j = 0; j < DVT; ++j)
+#pragma unroll
+      for (int sp = 0; sp < NPC; ++sp) {
+        FragT lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
+          lo[i] = from_f32<Op>(to_f32(Kc[2 * sp][j][i]) * fast_exp(g_n - sG[t0]) * sRK[t0]);
+          hi[i] = from_f32<Op>(2 * sp + 1 < CT ? to_f32(Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j][i]) *
+                                                     fast_exp(g_n - sG[t1 < C ? t1 : 0]) * sRK[t1 < C ? t1 : 0]
+                                               : 0.f);
+        }
+        store_pair<Op>(at<Op>(unit, K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), lo, hi);
+      }
   }
 }
 
@@ -436,29 +528,32 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 // One wave: the chain of one sequence's chunks for one V head and NTW 16-wide
 // tiles of d_v.  S^T[d_k][d_v-slice] lives in accumulators (lane: d_k rows
 // 4g..4g+3 of each 16-block, d_v column l16), which is also the B operand
-// layout for every product that contracts over d_k.  Operands of chunk c+1 are
-// loaded right after chunk c consumed the same registers.  Block order puts
-// all tiles of one (sequence, head) on one XCD, so its fragments are fetched
-// into that XCD's L2 once.
+// layout for every product that contracts over d_k.  Per chunk:
+//   h = bf16(S^T) -> workspace;  U = Ut - W S^T -> workspace (over Ut);
+//   S^T <- e^{G_n} S^T + K'^T U.
+// The next chunk's operands are loaded right after this chunk consumed the
+// same registers.  Block order puts all tiles of one (sequence, head) on one
+// XCD, so W and K'^T are fetched into that XCD's L2 once.
 template <typename Op, int D, int C, int NTW>
 __global__ __launch_bounds__(64) void chunk_state_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
-    const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws, float* __restrict__ state,
+    const int32_t* __restrict__ cstart, unsigned char* __restrict__ ws, float* __restrict__ state,
     int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v) {
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, NTILE = NT / NTW;
+  constexpr uint32_t PB = K::PAIR * sizeof(Op);  // bytes per pair tile
   const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3, tile = kq % NTILE;
   const int64_t grp = (int64_t)(kq / NTILE) * 8 + xcd;
   if (grp >= (int64_t)n_seq * h_v) return;
   const int n = (int)(grp / h_v), h = (int)(grp % h_v);
-  const int lane = threadIdx.x, g4 = lane >> 4, l16 = lane & 15;
-  const int col0 = h * D + 16 * NTW * tile;  // first output column of this wave
-  const int64_t o_ld = (int64_t)h_v * D;
+  const uint32_t lane = threadIdx.x, g4 = lane >> 4, l16 = lane & 15;
   const int64_t lo = min((int64_t)cu[n], t_total);
   const int64_t hi = min(max((int64_t)cu[n + 1], lo), t_total);
   const int32_t slot = slots[n];
-  if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs
+  if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs (the output pass skips it)
+    const int64_t o_ld = (int64_t)h_v * D;
+    const int col0 = h * D + 16 * NTW * tile;
     for (int64_t e = lane; e < (hi - lo) * 16 * NTW; e += 64)
       o[(lo + e / (16 * NTW)) * o_ld + col0 + e % (16 * NTW)] = from_f32<Op>(0.f);
     return;
@@ -480,52 +575,38 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
       }
     }
 
-  Pair<Op> wn[CT][NPD], qp[CT][NPD], kt[NT][NPC], pp[CT][NPC];
+  // lane-invariant byte offsets inside a unit
+  const uint32_t lp = lane * 8 * sizeof(Op);   // a lane's pair within a pair tile
+  const uint32_t lf = lane * 4 * sizeof(Op);   // a lane's fragment within a 16x16 tile
+  Pair<Op> wn[CT][NPD], kt[NT][NPC];
   FragT ut[CT][NTW];
   float egn = 0.f;
 #define GDN_LOAD_WU(u)                                                                              \
   {                                                                                                 \
-    const Op* w_ = reinterpret_cast<const Op*>((u) + K::W_OFF);                                     \
     _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp) wn[mt][sp].load(w_ + ((mt * NPD + sp) * 64 + lane) * 8); \
-    const Op* u_ = reinterpret_cast<const Op*>((u) + K::UT_OFF);                                    \
+    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                              \
+      wn[mt][sp].load(at<Op>((u), K::W_OFF + (mt * NPD + sp) * PB + lp));                           \
     _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
     _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
-      ut[mt][j] = *reinterpret_cast<const FragT*>(u_ + ((mt * NT + NTW * tile + j) * 64 + lane) * 4); \
-  }
-#define GDN_LOAD_Q(u)                                                                               \
-  {                                                                                                 \
-    const Op* q_ = reinterpret_cast<const Op*>((u) + K::Q_OFF);                                     \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp) qp[mt][sp].load(q_ + ((mt * NPD + sp) * 64 + lane) * 8); \
-  }
-#define GDN_LOAD_P(u)                                                                               \
-  {                                                                                                 \
-    const Op* p_ = reinterpret_cast<const Op*>((u) + K::P_OFF);                                     \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                              \
-      if (2 * sp <= mt) pp[mt][sp].load(p_ + ((mt * NPC + sp) * 64 + lane) * 8);                    \
+      ut[mt][j] = *at<FragT>((u), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf);  \
   }
 #define GDN_LOAD_KT(u)                                                                              \
   {                                                                                                 \
-    const Op* k_ = reinterpret_cast<const Op*>((u) + K::KT_OFF);                                    \
     _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp) kt[mt][sp].load(k_ + ((mt * NPC + sp) * 64 + lane) * 8); \
-    egn = *reinterpret_cast<const float*>((u) + K::F_OFF);                                          \
+    _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                              \
+      kt[mt][sp].load(at<Op>((u), K::KT_OFF + (mt * NPC + sp) * PB + lp));                          \
+    egn = *at<float>((u), K::F_OFF);                                                                \
   }
   int32_t gcx = cstart[n];
   if (lo < hi) {
     const unsigned char* u0 = ws + ((int64_t)gcx * h_v + h) * K::UNIT;
     GDN_LOAD_WU(u0);
-    GDN_LOAD_Q(u0);
-    GDN_LOAD_P(u0);
     GDN_LOAD_KT(u0);
   }
   const FragT zf = zero_frag<Op>();
-  const int32_t lane_off = (int32_t)(4 * g4 * o_ld) + l16;  // lane's row 4g and column within the tile
 
   for (int64_t c0 = lo; c0 < hi; c0 += C, ++gcx) {
-    const int nvalid = (int)min((int64_t)C, hi - c0);
+    unsigned char* uc = ws + ((int64_t)gcx * h_v + h) * K::UNIT;
     // The next chunk's operands are loaded unconditionally (the last chunk
     // re-reads its own unit), so the wait counts stay exact: a load under a
     // branch makes the compiler wait for every load issued after it as well.
@@ -533,11 +614,18 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
     // registers, a full iteration ahead of its use.
     const unsigned char* un = ws + ((int64_t)(c0 + C < hi ? gcx + 1 : gcx) * h_v + h) * K::UNIT;
 
+    // h = S^T at the chunk start, as B pairs [NPD][NT]
     FragT Sf[NT][NTW];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Sf[mt][j] = frag_from<Op>(Sacc[mt][j]);
+#pragma unroll
+    for (int sp = 0; sp < NPD; ++sp)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        store_pair<Op>(at<Op>(uc, K::H_OFF + (uint32_t)(sp * NT + NTW * tile + j) * PB + lp), Sf[2 * sp][j],
+                       2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
 
     // U = Ut - W S^T
     f32x4 Uacc[CT][NTW];
@@ -556,37 +644,15 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
     GDN_LOAD_WU(un);
     __builtin_amdgcn_sched_barrier(0);
 
-    // O = Q' S^T
-    f32x4 Oacc[CT][NTW];
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int sp = 0; sp < NPD; ++sp) qp[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
-        Oacc[mt][j] = acc;
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    GDN_LOAD_Q(un);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // O += P U
+    // U -> workspace over Ut (this wave's columns only)
     FragT Uf[CT][NTW];
 #pragma unroll
     for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) Uf[mt][j] = frag_from<Op>(Uacc[mt][j]);
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int sp = 0; sp < NPC; ++sp)
-          if (2 * sp <= mt) pp[mt][sp].mma(Oacc[mt][j], Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
-    __builtin_amdgcn_sched_barrier(0);
-    GDN_LOAD_P(un);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < NTW; ++j) {
+        Uf[mt][j] = frag_from<Op>(Uacc[mt][j]);
+        *at<FragT>(uc, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = Uf[mt][j];
+      }
 
     // S^T <- e^{G_n} S^T + K'^T U
 #pragma unroll
@@ -603,34 +669,8 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
     __builtin_amdgcn_sched_barrier(0);
     GDN_LOAD_KT(un);
     __builtin_amdgcn_sched_barrier(0);
-
-    // O out (the scale is in Q' and P).  Row bases are uniform, the lane part
-    // is loop-invariant; a full chunk stores without per-row guards.
-    if (nvalid == C) {
-#pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Op* orow = o + (c0 + 16 * mt + i) * o_ld + col0;
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) orow[lane_off + 16 * j] = from_f32<Op>(Oacc[mt][j][i]);
-        }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Op* orow = o + (c0 + 16 * mt + i) * o_ld + col0;
-          if (16 * mt + 4 * g4 + i < nvalid) {
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) orow[lane_off + 16 * j] = from_f32<Op>(Oacc[mt][j][i]);
-          }
-        }
-    }
   }
 #undef GDN_LOAD_WU
-#undef GDN_LOAD_Q
-#undef GDN_LOAD_P
 #undef GDN_LOAD_KT
 
 #pragma unroll
@@ -643,38 +683,110 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
     }
 }
 
-// ------------------------------------------------------------------ norm
-// out = o / sqrt(mean_dv(o^2) + eps) * w * silu(z) in place, o = scale * O as
-// the chain wrote it.  D / 8 lanes hold one (token, V head) row.  Tokens
-// outside [cu[0], cu[n_seq]) are left alone, as the chain leaves them.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void gated_norm_kernel(T* __restrict__ o, const T* __restrict__ z,
-                                                         const T* __restrict__ norm_w,
-                                                         const int32_t* __restrict__ cu, int32_t n_seq,
-                                                         int64_t t_total, int32_t h_v, float eps) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int e0 = (threadIdx.x % LPR) * 8;
-  const int64_t t = row / h_v;
-  const int64_t t_lo = max((int64_t)cu[0], (int64_t)0), t_hi = min((int64_t)cu[n_seq], t_total);
-  const bool live = t >= t_lo && t < t_hi;
-  float v[8], zz[8], w[8];
-  if (live) {
-    load8(o + row * D + e0, v);
-    load8(z + row * D + e0, zz);
-    load8(norm_w + e0, w);
-  } else {
+// ------------------------------------------------------------------ output
+// Per (chunk, V head): O = Q' h^T + P U (the scale is in Q' and P); with z,
+// out = O / sqrt(mean_dv(O^2) + eps) * w * silu(z).  Wave w computes d_v
+// tiles w*DVT .. w*DVT+DVT-1 for all C rows with every operand load issued up
+// front; the fp32 tile then goes through LDS so the norm and the z / out
+// traffic run row-wise, 8 consecutive elements (16 bytes of bf16) per lane.
+template <typename T, typename Op, int D, int C>
+__global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const int32_t* __restrict__ cstart,
+    const unsigned char* __restrict__ ws, int32_t n_slots, int32_t n_seq, int64_t t_total, int32_t h_v,
+    T* __restrict__ o, const T* __restrict__ z, const T* __restrict__ norm_w, float norm_eps) {
+  using K = Cfg<Op, D, C>;
+  using FragT = typename Frag<Op>::type;
+  constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, DVT = K::DVT, LD_O = K::LD_O;
+  constexpr int LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
+  constexpr uint32_t PB = K::PAIR * sizeof(Op);
+  __shared__ __attribute__((aligned(16))) float sO[K::OUT_BYTES / 4];
+  const int gc = blockIdx.x / h_v;
+  const int h = blockIdx.x % h_v;
+  if (gc >= cstart[n_seq]) return;
+  const int n = seq_of_chunk(cstart, n_seq, gc);
+  if (!slot_ok(slots[n], n_slots)) return;  // the chain zeroed this sequence's outputs
+  const uint32_t tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int64_t seq_lo = min((int64_t)cu[n], t_total);
+  const int64_t seq_hi = min(max((int64_t)cu[n + 1], seq_lo), t_total);
+  const int64_t c0 = seq_lo + (int64_t)(gc - cstart[n]) * C;
+  const int nvalid = (int)min((int64_t)C, seq_hi - c0);
+  const unsigned char* u = ws + ((int64_t)gc * h_v + h) * K::UNIT;
+  const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
+  const FragT zf = zero_frag<Op>();
+
+  // ---- all operand loads
+  Pair<Op> qa[CT][NPD], hp[NPD][DVT], pa[CT][NPC];
+  FragT Uf[CT][DVT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = zz[e] = w[e] = 0.f;
+  for (int sp = 0; sp < NPD; ++sp)
+#pragma unroll
+    for (int j = 0; j < DVT; ++j) hp[sp][j].load(at<Op>(u, K::H_OFF + (uint32_t)(sp * NT + wave * DVT + j) * PB + lp));
+#pragma unroll
+  for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+    for (int sp = 0; sp < NPD; ++sp) qa[mt][sp].load(at<Op>(u, K::Q_OFF + (uint32_t)(mt * NPD + sp) * PB + lp));
+#pragma unroll
+  for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+    for (int j = 0; j < DVT; ++j)
+      Uf[mt][j] = *at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf);
+#pragma unroll
+  for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+    for (int sp = 0; sp < NPC; ++sp)
+      if (2 * sp <= mt) pa[mt][sp].load(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
+
+  // ---- O = Q' h^T + P U
+#pragma unroll
+  for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+    for (int j = 0; j < DVT; ++j) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sp = 0; sp < NPD; ++sp) {
+        FragT b0, b1;
+        hp[sp][j].split(b0, b1);
+        qa[mt][sp].mma(acc, b0, b1);
+      }
+#pragma unroll
+      for (int sp = 0; sp < NPC; ++sp)
+        if (2 * sp <= mt) pa[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
+      // fp32 tile into LDS (row 16mt+4g+i, column of this lane)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sO[(16 * mt + 4 * g4 + i) * LD_O + 16 * (wave * DVT + j) + l16] = acc[i];
+    }
+  __syncthreads();
+
+  // ---- row-wise: gated RMSNorm and 16-byte stores
+  const int64_t o_ld = (int64_t)h_v * D;
+  const int e0 = (tid % LPR) * 8;
+  float w[8];
+  if (z) load8(norm_w + e0, w);
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int r = (int)(tid / LPR) + k * RPP;
+    if (r >= C) break;  // uniform over the LPR lanes of a row
+    float v[8];
+    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(sO + r * LD_O + e0);
+    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(sO + r * LD_O + e0 + 4);
+    const bool live = r < nvalid;
+    const int64_t off = (c0 + r) * o_ld + h * D + e0;
+    if (z) {
+      float zz[8];
+      if (live) load8(z + off, zz);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zz[e] = 0.f;
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+      ss = group_sum<LPR>(ss);
+      const float rstd = fast_rsq(ss * (1.0f / D) + norm_eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] * rstd * w[e] * fast_silu(zz[e]);
+    }
+    if (live) store8(o + off, v);
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-  ss = group_sum<LPR>(ss);  // LPR lanes of a row are an aligned group
-  const float rstd = fast_rsq(ss * (1.0f / D) + eps);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = v[e] * rstd * w[e] * fast_silu(zz[e]);
-  if (live) store8(o + row * D + e0, v);
 }
 
 // Tiles of d_v per wave: one for a single long sequence is the most
@@ -716,13 +828,10 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
                      a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state, a.n_slots, (Op*)a.o, a.t_total,
                      a.n_seq, a.s.h_v);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  if (a.z != nullptr && a.t_total > 0) {
-    constexpr int RPB = 256 / (D / 8);
-    const int64_t rows = a.t_total * a.s.h_v;
-    hipLaunchKernelGGL((gated_norm_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.cu_seqlens, a.n_seq, a.t_total, a.s.h_v,
-                       a.norm_eps);
-  }
+  if (max_chunks > 0)
+    hipLaunchKernelGGL((chunk_out_kernel<T, Op, D, C>), dim3((unsigned)(max_chunks * a.s.h_v)), dim3(K::THREADS), 0,
+                       st, a.cu_seqlens, a.slots, cstart, units, a.n_slots, a.n_seq, a.t_total, a.s.h_v, (T*)a.o,
+                       (const T*)a.z, (const T*)a.norm_w, a.norm_eps);
   return hipGetLastError();
 }
 
