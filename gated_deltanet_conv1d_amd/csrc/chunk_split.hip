@@ -14,12 +14,14 @@
 // sequence with 32 V heads already gives 256 independent waves, one per CU,
 // with no LDS and no barrier in the loop.  The chain keeps only what is
 // serial, U and the state update; it records S at every chunk start (h) and
-// U, and the output O = Q' h^T + P U with its gated RMSNorm is again chunk-
-// parallel.  The prep pass writes every operand as ready-made MFMA fragments:
-//   -W, Q' = scale diag(e^G) Q    (A operands, contraction over d_k)
+// U, and the output O = diag(f_q) Q h^T + P U with its gated RMSNorm is again
+// chunk-parallel.  The prep pass writes the operands as ready-made MFMA
+// fragments:
+//   -W                             (A operand, contraction over d_k)
 //   K'^T = (diag(e^{G_n-G}) K)^T   (A operand, contraction over the chunk)
 //   scale P                        (A operand, lower triangle)
 //   Ut                             (accumulator layout; the chain turns it into U)
+//   f_q = scale e^G r_q            (per token; the output pass reads raw q)
 // so every load is a 16- or 8-byte lane-contiguous vector.
 //
 //   chunk_index_kernel  first global chunk of every sequence (block scan)
@@ -53,29 +55,29 @@ struct Cfg {
   static constexpr int PAIR = 64 * 8;       // elements per pair tile
   // workspace unit per (chunk, V head), bytes
   static constexpr int W_OFF = 0;                                   // -W     [CT][NPD] pairs
-  static constexpr int Q_OFF = W_OFF + CT * NPD * PAIR * (int)sizeof(Op);   // Q'  [CT][NPD]
-  static constexpr int KT_OFF = Q_OFF + CT * NPD * PAIR * (int)sizeof(Op);  // K'^T [NT][NPC]
+  static constexpr int KT_OFF = W_OFF + CT * NPD * PAIR * (int)sizeof(Op);  // K'^T [NT][NPC]
   static constexpr int P_OFF = KT_OFF + NT * NPC * PAIR * (int)sizeof(Op);  // P   [CT][NPC]
   static constexpr int UT_OFF = P_OFF + CT * NPC * PAIR * (int)sizeof(Op);  // Ut  [CT][NT][64][4]
   static constexpr int H_OFF = UT_OFF + C * D * (int)sizeof(Op);            // S^T at chunk start, [NPD][NT] pairs
-  static constexpr int F_OFF = H_OFF + NPD * NT * PAIR * (int)sizeof(Op);   // e^{G_n}
-  static constexpr int UNIT = (F_OFF + 16 + 255) / 256 * 256;
-  // output kernel LDS: the fp32 O tile, row-major
+  static constexpr int F_OFF = H_OFF + NPD * NT * PAIR * (int)sizeof(Op);   // e^{G_n}, then f_q [C]
+  static constexpr int FQ_OFF = F_OFF + 16;                                 // scale e^{G_t} r_q[t]
+  static constexpr int UNIT = (FQ_OFF + C * 4 + 255) / 256 * 256;
+  // output kernel LDS: raw q rows, then (over them) the fp32 O tile, row-major
+  static constexpr int LD_Q = D + 16;
   static constexpr int LD_O = D + 4;
-  static constexpr int OUT_BYTES = C * LD_O * 4;
+  static constexpr int OUT_BYTES = C * LD_O * 4 > C * LD_Q * (int)sizeof(Op) ? C * LD_O * 4 : C * LD_Q * (int)sizeof(Op);
   // prep kernel LDS.  Row strides are padded so the 8-byte fragment reads of
   // a wave (16 rows x 4 column groups) hit distinct banks.
-  static constexpr int LDR = D + 16;   // raw q, k rows (elements)
+  static constexpr int LDR = D + 16;   // raw k rows (elements)
   static constexpr int LDA = C + 16;   // fp32 A, then T in place
   static constexpr int LDT = C + 8;    // T diag(b e^G r_k) and T diag(b), operand type
-  static constexpr int PQ = 0;
-  static constexpr int PK = PQ + C * LDR * (int)sizeof(Op);
+  static constexpr int PK = 0;
   static constexpr int PA = PK + C * LDR * (int)sizeof(Op);
-  static constexpr int PS = PA + C * LDA * 4;                      // G, b, r_q, r_k
-  static constexpr bool T_OVER_Q = 2 * LDT <= LDR;                 // the two T copies fit over q
-  static constexpr int PTW = T_OVER_Q ? PQ : PS + 4 * C * 4;
+  static constexpr int PS = PA + C * LDA * 4;                      // G, b, r_k
+  static constexpr bool T_OVER_A = 2 * LDT * (int)sizeof(Op) <= LDA * 4;  // the T copies fit over A
+  static constexpr int PTW = T_OVER_A ? PA : PS + 3 * C * 4;
   static constexpr int PTU = PTW + C * LDT * (int)sizeof(Op);
-  static constexpr int PREP_BYTES = T_OVER_Q ? PS + 4 * C * 4 : PTU + C * LDT * (int)sizeof(Op);
+  static constexpr int PREP_BYTES = T_OVER_A ? PS + 3 * C * 4 : PTU + C * LDT * (int)sizeof(Op);
 };
 
 __device__ __forceinline__ int32_t seq_of_chunk(const int32_t* __restrict__ cstart, int32_t n_seq, int32_t gc) {
@@ -223,13 +225,14 @@ __device__ __forceinline__ void raw_store<float>(const Raw8<float>& r, float* ds
 // L2 norms enter as per-token factors r = 1/sqrt(|x|^2 + 1e-6):
 //   A_ij  = b_i r_k[i] r_k[j] e^{G_i-G_j} (k_i.k_j), i > j;   T = (I + A)^{-1}
 //   P_ij  = scale r_q[i] r_k[j] e^{G_i-G_j} (q_i.k_j), i >= j
-//   W     = T diag(b e^G r_k) K,   Ut = T diag(b) V
-//   Q'    = diag(scale e^G r_q) Q, K' = diag(e^{G_n-G} r_k) K
+//   W     = T diag(b e^G r_k) K,   Ut = T diag(b) V,   K' = diag(e^{G_n-G} r_k) K
+// and f_q = scale e^G r_q, which the output pass applies to Q S^T.
 // No fragment is ever read down an LDS column.  P is formed as P^T = K Q^T,
 // whose accumulator layout is P's A-fragment layout; W is formed as
 // W^T = K^T (T diag(..))^T, whose accumulator layout is W's A-fragment layout;
 // K and V blocks reach the column (B operand) layout through one MFMA with an
-// identity operand, which is exact.
+// identity operand, which is exact.  Only k is staged in LDS: each wave loads
+// the q blocks and v tiles it uses as register fragments.
 template <typename T, typename Op, int D, int C>
 __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     const T* __restrict__ qkv, const float* __restrict__ g_in, const float* __restrict__ beta_in,
@@ -241,16 +244,15 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, DVT = K::DVT, LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
   constexpr int NPD = K::NPD, NPC = K::NPC, LDR = K::LDR, LDA = K::LDA, LDT = K::LDT;
+  constexpr int QB = (CT + WAVES - 1) / WAVES;  // q blocks per wave: blocks wave, wave + WAVES, ...
   constexpr uint32_t PB = K::PAIR * sizeof(Op);
   static_assert(DVT == 1 || DVT == 2, "a wave's d tiles form one pair fragment");
   __shared__ __attribute__((aligned(16))) unsigned char smem[K::PREP_BYTES];
-  Op* sQ = reinterpret_cast<Op*>(smem + K::PQ);
   Op* sK = reinterpret_cast<Op*>(smem + K::PK);
   float* sA = reinterpret_cast<float*>(smem + K::PA);
   float* sG = reinterpret_cast<float*>(smem + K::PS);
   float* sB = sG + C;
-  float* sRQ = sG + 2 * C;
-  float* sRK = sG + 3 * C;
+  float* sRK = sG + 2 * C;
   Op* sTW = reinterpret_cast<Op*>(smem + K::PTW);
   Op* sTU = reinterpret_cast<Op*>(smem + K::PTU);
 
@@ -273,9 +275,21 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) eye[i] = from_f32<Op>(4 * g4 + i == l16 ? 1.f : 0.f);
 
-  // ---- v blocks of this wave's d_v tiles, A layout, straight from memory
-  FragT Va[CT][DVT];
+  // ---- register fragments straight from memory: this wave's q blocks (B
+  // operand of P^T, row l16) and v tiles (A layout, row l16)
+  FragT Qb[QB][NPD][2], Va[CT][DVT];
   {
+    const T* qbase = qkv + (int64_t)hk * D + 4 * g4;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int r = 16 * (wave + b * WAVES) + l16;
+      const bool ok = wave + b * WAVES < CT && r < nvalid;
+#pragma unroll
+      for (int sp = 0; sp < NPD; ++sp) {
+        Qb[b][sp][0] = ok ? *reinterpret_cast<const FragT*>(qbase + (c0 + r) * c_ch + 32 * sp) : zf;
+        Qb[b][sp][1] = ok && 32 * sp + 16 < D ? *reinterpret_cast<const FragT*>(qbase + (c0 + r) * c_ch + 32 * sp + 16) : zf;
+      }
+    }
     const T* vbase = qkv + (int64_t)(2 * h_k + h) * D + 16 * wave * DVT + 4 * g4;
 #pragma unroll
     for (int kb = 0; kb < CT; ++kb)
@@ -285,39 +299,35 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         Va[kb][j] = r < nvalid ? *reinterpret_cast<const FragT*>(vbase + (c0 + r) * c_ch + 16 * j) : zf;
       }
   }
-  // ---- raw q, k rows into LDS with their inverse norms; gates
+  // ---- raw k rows into LDS with their inverse norms; gates
   {
     const int e0 = (tid % LPR) * 8, r0 = tid / LPR;
-    Raw8<T> raw[2][RPT];
+    Raw8<T> raw[RPT];
 #pragma unroll
-    for (int kind = 0; kind < 2; ++kind)
-#pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        const int r = r0 + j * RPP;
-        if (r < nvalid) raw[kind][j].load(qkv + (c0 + r) * c_ch + (int64_t)(kind * h_k + hk) * D + e0);
-        else raw[kind][j].zero();
-      }
+    for (int j = 0; j < RPT; ++j) {
+      const int r = r0 + j * RPP;
+      if (r < nvalid) raw[j].load(qkv + (c0 + r) * c_ch + (int64_t)(h_k + hk) * D + e0);
+      else raw[j].zero();
+    }
     float gv = 0.f, bv = 0.f;
     if (wave == 0 && lane < nvalid) {
       gv = g_in[(c0 + lane) * h_v + h];
       bv = beta_in[(c0 + lane) * h_v + h];
     }
 #pragma unroll
-    for (int kind = 0; kind < 2; ++kind)
+    for (int j = 0; j < RPT; ++j) {
+      const int r = r0 + j * RPP;
+      float v[8];
+      raw[j].to_f32(v);
+      float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        const int r = r0 + j * RPP;
-        float v[8];
-        raw[kind][j].to_f32(v);
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-        ss = group_sum<LPR>(ss);
-        if (r < C) {
-          raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&raw[kind][j]), (kind == 0 ? sQ : sK) + r * LDR + e0);
-          if (tid % LPR == 0) (kind == 0 ? sRQ : sRK)[r] = fast_rsq(ss + 1e-6f);
-        }
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+      ss = group_sum<LPR>(ss);
+      if (r < C) {
+        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&raw[j]), sK + r * LDR + e0);
+        if (tid % LPR == 0) sRK[r] = fast_rsq(ss + 1e-6f);
       }
+    }
     if (wave == 0) {
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -333,35 +343,47 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   }
   __syncthreads();
 
-  // ---- Gram work: P^T pairs -> P fragments, K K^T tiles -> A, Q' fragments
+  // ---- Gram work.  Wave w: the P^T tiles of its q blocks ib (pairs of
+  // column blocks -> P fragments) and f_q of those rows; then K K^T tiles -> A,
+  // taken in the order that evens out the per-wave tile count.
   {
-    // item lists: P pairs (ib, sp) with 2 sp <= ib; A tiles (ib, jb) with jb <= ib; Q' pairs (mt, sp)
-    constexpr int N_P = [] { int c = 0; for (int ib = 0; ib < CT; ++ib) c += ib / 2 + 1; return c; }();
-    constexpr int N_A = CT * (CT + 1) / 2;
-    constexpr int N_Q = CT * NPD;
-    for (int it = wave; it < N_P + N_A + N_Q; it += WAVES) {
-      if (it < N_P) {
-        int ib = 0, rest = it;
-        while (rest >= ib / 2 + 1) { rest -= ib / 2 + 1; ++ib; }
-        const int sp = rest;
-        const int i = 16 * ib + l16;
-        const float fi = scale * sRQ[i];
-        const float gi = sG[i];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int ib = wave + b * WAVES;
+      if (ib >= CT) break;
+      // r_q of row 16 ib + l16: the row's 32 pair values per lane, 4 lanes per row
+      float ss = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < NPD; ++sp)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = to_f32(Qb[b][sp][hh][e]);
+            ss = fmaf(x, x, ss);
+          }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const int i = 16 * ib + l16;
+      const float fi = scale * fast_rsq(ss + 1e-6f);  // scale r_q[i]
+      const float gi = sG[i];
+      if (g4 == 0) *at<float>(unit, K::FQ_OFF + 4 * i) = fi * fast_exp(gi);
+#pragma unroll
+      for (int sp = 0; sp < NPC; ++sp) {
+        if (2 * sp > ib) break;
         FragT half[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int jb = 2 * sp + hh;
-          if (jb > ib || jb >= CT) { half[hh] = zf; continue; }
+          if (jb > ib) { half[hh] = zf; continue; }
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           const Op* arow = sK + (16 * jb + l16) * LDR + 4 * g4;
-          const Op* brow = sQ + i * LDR + 4 * g4;
 #pragma unroll
           for (int s2 = 0; s2 < NPD; ++s2) {
             if (32 * s2 + 16 < D)
-              mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
-                      lds_frag<Op>(brow + 32 * s2 + 16));
+              mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), Qb[b][s2][0], Qb[b][s2][1]);
             else
-              mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
+              mma_k16(acc, lds_frag<Op>(arow + 32 * s2), Qb[b][s2][0]);
           }
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
@@ -370,36 +392,32 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
           }
         }
         store_pair<Op>(at<Op>(unit, K::P_OFF + (uint32_t)(ib * NPC + sp) * PB + lp), half[0], half[1]);
-      } else if (it < N_P + N_A) {
-        int ib = 0, rest = it - N_P;
-        while (rest >= ib + 1) { rest -= ib + 1; ++ib; }
-        const int jb = rest;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const Op* arow = sK + (16 * ib + l16) * LDR + 4 * g4;
-        const Op* brow = sK + (16 * jb + l16) * LDR + 4 * g4;
+      }
+    }
+    // A tiles (ib, jb), jb <= ib, enumerated from the last block row down so
+    // the waves with the fewest P tiles take the longest rows first
+    constexpr int N_A = CT * (CT + 1) / 2;
+    for (int it = WAVES - 1 - wave; it < N_A; it += WAVES) {
+      int ib = CT - 1, rest = it;
+      while (rest >= ib + 1) { rest -= ib + 1; --ib; }
+      const int jb = rest;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const Op* arow = sK + (16 * ib + l16) * LDR + 4 * g4;
+      const Op* brow = sK + (16 * jb + l16) * LDR + 4 * g4;
 #pragma unroll
-        for (int s2 = 0; s2 < NPD; ++s2) {
-          if (32 * s2 + 16 < D)
-            mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
-                    lds_frag<Op>(brow + 32 * s2 + 16));
-          else
-            mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
-        }
-        const int j = 16 * jb + l16;
-        const float rj = sRK[j], gj = sG[j];
+      for (int s2 = 0; s2 < NPD; ++s2) {
+        if (32 * s2 + 16 < D)
+          mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
+                  lds_frag<Op>(brow + 32 * s2 + 16));
+        else
+          mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
+      }
+      const int j = 16 * jb + l16;
+      const float rj = sRK[j], gj = sG[j];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * ib + 4 * g4 + ii;
-          sA[i * LDA + j] = i > j ? sB[i] * sRK[i] * rj * fast_exp(fminf(sG[i] - gj, 0.f)) * acc[ii] : 0.f;
-        }
-      } else {
-        const int q = it - N_P - N_A, mt = q / NPD, sp = q % NPD;
-        const int t = 16 * mt + l16;
-        const float f = scale * fast_exp(sG[t]) * sRQ[t];
-        const Op* src = sQ + t * LDR + 32 * sp + 4 * g4;
-        const FragT lo = frag_mul<Op>(lds_frag<Op>(src), f);
-        const FragT hi = 32 * sp + 16 < D ? frag_mul<Op>(lds_frag<Op>(src + 16), f) : zf;
-        store_pair<Op>(at<Op>(unit, K::Q_OFF + (uint32_t)(mt * NPD + sp) * PB + lp), lo, hi);
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * ib + 4 * g4 + ii;
+        sA[i * LDA + j] = i > j ? sB[i] * sRK[i] * rj * fast_exp(fminf(sG[i] - gj, 0.f)) * acc[ii] : 0.f;
       }
     }
   }
@@ -450,20 +468,35 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   }
 
   // ---- T_W = T diag(b e^G r_k), T_U = T diag(b) in the operand type, zero above
-  // the diagonal blocks (these may overwrite q, which is dead now)
-  for (int e = tid; e < C * C / 4; e += K::THREADS) {
-    const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
-    const bool keep = (c4 >> 4) <= (r >> 4);
-    const f32x4 t = keep ? *reinterpret_cast<const f32x4*>(sA + r * LDA + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    FragT tw, tu;
+  // the diagonal blocks.  They may overlay T itself: all of T is read first.
+  {
+    constexpr int PER = (C * C / 4 + K::THREADS - 1) / K::THREADS;
+    FragT tw[PER], tu[PER];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float b = sB[c4 + i];
-      tw[i] = from_f32<Op>(t[i] * b * fast_exp(sG[c4 + i]) * sRK[c4 + i]);
-      tu[i] = from_f32<Op>(t[i] * b);
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + k * K::THREADS;
+      if (e < C * C / 4) {
+        const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
+        const bool keep = (c4 >> 4) <= (r >> 4);
+        const f32x4 t = keep ? *reinterpret_cast<const f32x4*>(sA + r * LDA + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float b = sB[c4 + i];
+          tw[k][i] = from_f32<Op>(t[i] * b * fast_exp(sG[c4 + i]) * sRK[c4 + i]);
+          tu[k][i] = from_f32<Op>(t[i] * b);
+        }
+      }
     }
-    *reinterpret_cast<FragT*>(sTW + r * LDT + c4) = tw;
-    *reinterpret_cast<FragT*>(sTU + r * LDT + c4) = tu;
+    if (K::T_OVER_A) __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + k * K::THREADS;
+      if (e < C * C / 4) {
+        const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
+        *reinterpret_cast<FragT*>(sTW + r * LDT + c4) = tw[k];
+        *reinterpret_cast<FragT*>(sTU + r * LDT + c4) = tu[k];
+      }
+    }
   }
   __syncthreads();
 
@@ -684,16 +717,18 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
 }
 
 // ------------------------------------------------------------------ output
-// Per (chunk, V head): O = Q' h^T + P U (the scale is in Q' and P); with z,
+// Per (chunk, V head): O = diag(f_q) Q h^T + P U (the scale is in f_q and P); with z,
 // out = O / sqrt(mean_dv(O^2) + eps) * w * silu(z).  Wave w computes d_v
 // tiles w*DVT .. w*DVT+DVT-1 for all C rows with every operand load issued up
 // front; the fp32 tile then goes through LDS so the norm and the z / out
 // traffic run row-wise, 8 consecutive elements (16 bytes of bf16) per lane.
 template <typename T, typename Op, int D, int C>
 __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const int32_t* __restrict__ cstart,
-    const unsigned char* __restrict__ ws, int32_t n_slots, int32_t n_seq, int64_t t_total, int32_t h_v,
-    T* __restrict__ o, const T* __restrict__ z, const T* __restrict__ norm_w, float norm_eps) {
+    const T* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws, int32_t n_slots, int32_t n_seq,
+    int64_t t_total, int32_t h_k, int32_t h_v, T* __restrict__ o, const T* __restrict__ z,
+    const T* __restrict__ norm_w, float norm_eps) {
+  static_assert(sizeof(T) == sizeof(Op), "raw q rows are MFMA operands");
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, DVT = K::DVT, LD_O = K::LD_O;
@@ -715,16 +750,32 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
   const FragT zf = zero_frag<Op>();
 
   // ---- all operand loads
-  Pair<Op> qa[CT][NPD], hp[NPD][DVT], pa[CT][NPC];
+  // raw q rows of the chunk into LDS, 16-byte pieces
+  Op* sQ = reinterpret_cast<Op*>(sO);
+  {
+    const int hk = h / (h_v / h_k);
+    const int c_ch = 2 * h_k * D + h_v * D;
+    const int e0 = (tid % LPR) * 8;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int r = (int)(tid / LPR) + k * RPP;
+      if (r < C) {
+        Raw8<T> q;
+        if (r < nvalid) q.load(qkv + (c0 + r) * c_ch + (int64_t)hk * D + e0);
+        else q.zero();
+        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&q), sQ + r * K::LD_Q + e0);
+      }
+    }
+  }
+  Pair<Op> hp[NPD][DVT], pa[CT][NPC];
   FragT Uf[CT][DVT];
 #pragma unroll
   for (int sp = 0; sp < NPD; ++sp)
 #pragma unroll
     for (int j = 0; j < DVT; ++j) hp[sp][j].load(at<Op>(u, K::H_OFF + (uint32_t)(sp * NT + wave * DVT + j) * PB + lp));
+  f32x4 fq[CT];
 #pragma unroll
-  for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-    for (int sp = 0; sp < NPD; ++sp) qa[mt][sp].load(at<Op>(u, K::Q_OFF + (uint32_t)(mt * NPD + sp) * PB + lp));
+  for (int mt = 0; mt < CT; ++mt) fq[mt] = *at<f32x4>(u, K::FQ_OFF + 4 * (16 * mt + 4 * g4));
 #pragma unroll
   for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
@@ -736,25 +787,37 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
     for (int sp = 0; sp < NPC; ++sp)
       if (2 * sp <= mt) pa[mt][sp].load(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
 
-  // ---- O = Q' h^T + P U
+  __syncthreads();
+
+  // ---- O = diag(f_q) Q h^T + P U
+  f32x4 Oacc[CT][DVT];
 #pragma unroll
   for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
     for (int j = 0; j < DVT; ++j) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const Op* qrow = sQ + (16 * mt + l16) * K::LD_Q + 4 * g4;
 #pragma unroll
       for (int sp = 0; sp < NPD; ++sp) {
         FragT b0, b1;
         hp[sp][j].split(b0, b1);
-        qa[mt][sp].mma(acc, b0, b1);
+        if (32 * sp + 16 < D) mma_k32(acc, lds_frag<Op>(qrow + 32 * sp), lds_frag<Op>(qrow + 32 * sp + 16), b0, b1);
+        else mma_k16(acc, lds_frag<Op>(qrow + 32 * sp), b0);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= fq[mt][i];  // scale e^{G_t} r_q[t] on Q S^T only
 #pragma unroll
       for (int sp = 0; sp < NPC; ++sp)
         if (2 * sp <= mt) pa[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
-      // fp32 tile into LDS (row 16mt+4g+i, column of this lane)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sO[(16 * mt + 4 * g4 + i) * LD_O + 16 * (wave * DVT + j) + l16] = acc[i];
+      Oacc[mt][j] = acc;
     }
+  __syncthreads();  // q is read; the O tile goes over it
+#pragma unroll
+  for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+    for (int j = 0; j < DVT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sO[(16 * mt + 4 * g4 + i) * LD_O + 16 * (wave * DVT + j) + l16] = Oacc[mt][j][i];
   __syncthreads();
 
   // ---- row-wise: gated RMSNorm and 16-byte stores
@@ -830,8 +893,8 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (max_chunks > 0)
     hipLaunchKernelGGL((chunk_out_kernel<T, Op, D, C>), dim3((unsigned)(max_chunks * a.s.h_v)), dim3(K::THREADS), 0,
-                       st, a.cu_seqlens, a.slots, cstart, units, a.n_slots, a.n_seq, a.t_total, a.s.h_v, (T*)a.o,
-                       (const T*)a.z, (const T*)a.norm_w, a.norm_eps);
+                       st, (const T*)a.qkv, a.cu_seqlens, a.slots, cstart, units, a.n_slots, a.n_seq, a.t_total,
+                       a.s.h_k, a.s.h_v, (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.norm_eps);
   return hipGetLastError();
 }
 

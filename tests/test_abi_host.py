@@ -103,9 +103,9 @@ def test_chunk_prefill_workspace(L):
         assert ws == 0
         return
     # split path: a 256-byte-aligned chunk index, then one 256-byte-aligned unit
-    # per (chunk, V head) holding -W, Q', K'^T, Ut (bf16, C x D each),
-    # P (bf16, C x C), the chunk-start state (bf16, D x D) and e^{G_n}
-    unit = (4 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 255) // 256 * 256
+    # per (chunk, V head) holding -W, K'^T, Ut (bf16, C x D each), P (bf16, C x C),
+    # the chunk-start state (bf16, D x D), e^{G_n} (16 bytes) and f_q (fp32, C)
+    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 255) // 256 * 256
     assert ws == 256 + (4096 // 64 + 1) * 32 * unit
     # (same sizes as the query, so these calls stop at validation and never launch)
     assert chunk_call(L, t_total=4096) == WS
