@@ -611,100 +611,103 @@ __global__ __launch_bounds__(64) void chunk_state_kernel(
   // lane-invariant byte offsets inside a unit
   const uint32_t lp = lane * 8 * sizeof(Op);   // a lane's pair within a pair tile
   const uint32_t lf = lane * 4 * sizeof(Op);   // a lane's fragment within a 16x16 tile
-  Pair<Op> wn[CT][NPD], kt[NT][NPC];
-  FragT ut[CT][NTW];
-  float egn = 0.f;
-#define GDN_LOAD_WU(u)                                                                              \
+  // Two register stages (A: even chunks, B: odd chunks), so every chunk's
+  // operands are requested two chunks before they are used.
+  Pair<Op> wnA[CT][NPD], ktA[NT][NPC], wnB[CT][NPD], ktB[NT][NPC];
+  FragT utA[CT][NTW], utB[CT][NTW];
+  float egnA = 0.f, egnB = 0.f;
+#define GDN_LOAD_WU(X, u)                                                                           \
   {                                                                                                 \
     _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
     _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                              \
-      wn[mt][sp].load(at<Op>((u), K::W_OFF + (mt * NPD + sp) * PB + lp));                           \
+      wn##X[mt][sp].load(at<Op>((u), K::W_OFF + (mt * NPD + sp) * PB + lp));                        \
     _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
     _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
-      ut[mt][j] = *at<FragT>((u), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf);  \
+      ut##X[mt][j] = *at<FragT>((u), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf); \
   }
-#define GDN_LOAD_KT(u)                                                                              \
+#define GDN_LOAD_KT(X, u)                                                                           \
   {                                                                                                 \
     _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
     _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                              \
-      kt[mt][sp].load(at<Op>((u), K::KT_OFF + (mt * NPC + sp) * PB + lp));                          \
-    egn = *at<float>((u), K::F_OFF);                                                                \
+      kt##X[mt][sp].load(at<Op>((u), K::KT_OFF + (mt * NPC + sp) * PB + lp));                       \
+    egn##X = *at<float>((u), K::F_OFF);                                                             \
   }
-  int32_t gcx = cstart[n];
-  if (lo < hi) {
-    const unsigned char* u0 = ws + ((int64_t)gcx * h_v + h) * K::UNIT;
-    GDN_LOAD_WU(u0);
-    GDN_LOAD_KT(u0);
+  // h = S^T at the chunk start -> workspace;  U = Ut - W S^T
+#define GDN_PHASE_U(X, uc)                                                                          \
+  {                                                                                                 \
+    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
+    _Pragma("unroll") for (int j = 0; j < NTW; ++j) Sf[mt][j] = frag_from<Op>(Sacc[mt][j]);         \
+    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                              \
+    _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
+      store_pair<Op>(at<Op>((uc), K::H_OFF + (uint32_t)(sp * NT + NTW * tile + j) * PB + lp), Sf[2 * sp][j], \
+                     2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);                                     \
+    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
+    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
+      f32x4 acc;                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = to_f32(ut##X[mt][j][i]);               \
+      _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                            \
+        wn##X[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);            \
+      Uacc[mt][j] = acc;                                                                            \
+    }                                                                                               \
   }
+  // U -> workspace over Ut (this wave's columns);  S^T <- e^{G_n} S^T + K'^T U
+#define GDN_PHASE_S(X, uc)                                                                          \
+  {                                                                                                 \
+    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
+    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
+      Uf[mt][j] = frag_from<Op>(Uacc[mt][j]);                                                       \
+      *at<FragT>((uc), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = Uf[mt][j]; \
+    }                                                                                               \
+    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
+    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
+      f32x4 acc = Sacc[mt][j];                                                                      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] *= egn##X;                               \
+      _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                            \
+        kt##X[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);            \
+      Sacc[mt][j] = acc;                                                                            \
+    }                                                                                               \
+  }
+  const int32_t gc0 = cstart[n];
+  const int nch = (int)((hi - lo + C - 1) / C);
+  // unit of chunk k of this sequence, clamped to the last one: loads past the
+  // end re-read it, so every load is unconditional and the wait counts exact
+#define unit_of(k) (ws + ((int64_t)(gc0 + min((k), nch - 1)) * h_v + h) * K::UNIT)
   const FragT zf = zero_frag<Op>();
-
-  for (int64_t c0 = lo; c0 < hi; c0 += C, ++gcx) {
-    unsigned char* uc = ws + ((int64_t)gcx * h_v + h) * K::UNIT;
-    // The next chunk's operands are loaded unconditionally (the last chunk
-    // re-reads its own unit), so the wait counts stay exact: a load under a
-    // branch makes the compiler wait for every load issued after it as well.
-    // Scheduling fences keep each group right after the phase that frees its
-    // registers, a full iteration ahead of its use.
-    const unsigned char* un = ws + ((int64_t)(c0 + C < hi ? gcx + 1 : gcx) * h_v + h) * K::UNIT;
-
-    // h = S^T at the chunk start, as B pairs [NPD][NT]
-    FragT Sf[NT][NTW];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) Sf[mt][j] = frag_from<Op>(Sacc[mt][j]);
-#pragma unroll
-    for (int sp = 0; sp < NPD; ++sp)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        store_pair<Op>(at<Op>(uc, K::H_OFF + (uint32_t)(sp * NT + NTW * tile + j) * PB + lp), Sf[2 * sp][j],
-                       2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
-
-    // U = Ut - W S^T
-    f32x4 Uacc[CT][NTW];
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        f32x4 acc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = to_f32(ut[mt][j][i]);
-#pragma unroll
-        for (int sp = 0; sp < NPD; ++sp) wn[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);
-        Uacc[mt][j] = acc;
-      }
+  FragT Sf[NT][NTW], Uf[CT][NTW];
+  f32x4 Uacc[CT][NTW];
+  if (nch > 0) {
+    GDN_LOAD_WU(A, unit_of(0));
+    GDN_LOAD_KT(A, unit_of(0));
+    GDN_LOAD_WU(B, unit_of(1));
+    GDN_LOAD_KT(B, unit_of(1));
+  }
+  for (int k = 0; k < nch; k += 2) {
+    {
+      unsigned char* uc = unit_of(k);
+      GDN_PHASE_U(A, uc);
+      __builtin_amdgcn_sched_barrier(0);
+      GDN_LOAD_WU(A, unit_of(k + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      GDN_PHASE_S(A, uc);
+      __builtin_amdgcn_sched_barrier(0);
+      GDN_LOAD_KT(A, unit_of(k + 2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (k + 1 < nch) {
+      unsigned char* uc = unit_of(k + 1);
+      GDN_PHASE_U(B, uc);
+      GDN_PHASE_S(B, uc);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    GDN_LOAD_WU(un);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // U -> workspace over Ut (this wave's columns only)
-    FragT Uf[CT][NTW];
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        Uf[mt][j] = frag_from<Op>(Uacc[mt][j]);
-        *at<FragT>(uc, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = Uf[mt][j];
-      }
-
-    // S^T <- e^{G_n} S^T + K'^T U
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        f32x4 acc = Sacc[mt][j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= egn;
-#pragma unroll
-        for (int sp = 0; sp < NPC; ++sp) kt[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
-        Sacc[mt][j] = acc;
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    GDN_LOAD_KT(un);
+    GDN_LOAD_WU(B, unit_of(k + 3));
+    GDN_LOAD_KT(B, unit_of(k + 3));
     __builtin_amdgcn_sched_barrier(0);
   }
 #undef GDN_LOAD_WU
 #undef GDN_LOAD_KT
+#undef GDN_PHASE_U
+#undef GDN_PHASE_S
+#undef unit_of
 
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt)
