@@ -7,12 +7,15 @@ SiLU (gdn_conv1d_fwd), gating (gdn_gating), then the chunked gated delta rule
 with fused q/k L2 norm and gated-RMSNorm epilogue (gdn_chunk_prefill), on the
 single-sequence workload: batch 1, T=4096, 16 QK / 32 V heads, d=128, bf16
 activations, fp32 state, chunk 64, synthetic seeded inputs resident in HBM.
+The timed steps replay one captured HIP graph of that step (how a serving
+loop runs it; --eager times plain launches instead); per-kernel times come
+from an eager pass with HIP events on the launch stream.
 
 Prints ONE JSON line: tokens/s for that step (value), the roofline of the
-dominant kernel (its per-launch time measured with HIP events on the launch
-stream), the decode state-update bandwidth (256 requests x 1 token over a
-512-slot fp32 state pool, pools rotated so states come from HBM), and the
-fp64 CPU oracle timed on the host as a baseline.
+dominant call (gdn_chunk_prefill), the decode state-update bandwidth (256
+requests x 1 token over a 512-slot fp32 state pool, pools rotated so states
+come from HBM), the ~271k-token varlen prefill and the 128 x 4-token MTP step
+as extra rows, and the fp64 CPU oracle timed on the host as a baseline.
 """
 from __future__ import annotations
 
@@ -91,7 +94,23 @@ def counter_traffic(workload: str, kernels) -> float | None:
 
 # kernels one gdn_chunk_prefill call launches on the split path
 CHUNK_SPLIT_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64>",
-                       "void split::chunk_state_kernel<__bf16, __bf16, 128, 64>")
+                       "void split::chunk_state_kernel<__bf16, 128, 64, 1>",
+                       "void split::chunk_out_kernel<__bf16, __bf16, 128, 64>")
+
+
+def capture_graph(torch, fn):
+    """One HIP graph of fn's launches (a warm-up run off the capture first)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
 
 
 def device_info() -> dict:
@@ -139,6 +158,7 @@ def bench_prefill(args, torch, gdn, gi):
     g = torch.empty((T, d.h_v), dtype=torch.float32, device=dev)
     beta = torch.empty_like(g)
     o = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gdn.chunk_prefill_workspace_size(dims, 0, 1, T, case.chunk), dtype=torch.uint8, device=dev)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
@@ -148,9 +168,11 @@ def bench_prefill(args, torch, gdn, gi):
         if e: e[1].record()
         gdn.gating(a, b, A_log, dt_bias, g=g, beta=beta)
         if e: e[2].record()
-        gdn.chunk_prefill(dims, y, g, beta, cu, slots, ssm_pool, has_init, case.chunk, 1.0, z, norm_w, 1e-6, o=o)
+        gdn.chunk_prefill(dims, y, g, beta, cu, slots, ssm_pool, has_init, case.chunk, 1.0, z, norm_w, 1e-6, o=o,
+                          workspace=ws)
         if e: e[3].record()
 
+    # eager pass: per-kernel times with events on the launch stream
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -158,7 +180,19 @@ def bench_prefill(args, torch, gdn, gi):
     for k in range(args.steps):
         step(ev[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
+    # timed pass: graph replays of the same step
+    wall = wall_eager
+    if not args.eager:
+        graph = capture_graph(torch, step)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in ev]))
     t_conv, t_gate, t_chunk = ms(0, 1), ms(1, 2), ms(2, 3)
     t_step = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
@@ -166,12 +200,13 @@ def bench_prefill(args, torch, gdn, gi):
     achieved = nbytes / (t_chunk * 1e-3) / 1e9
     return dict(
         T=T, wall_s=wall, ms_per_step=wall / args.steps * 1e3, event_ms_per_step=t_step,
+        eager_ms_per_step=wall_eager / args.steps * 1e3,
         kernels_ms={"gdn_conv1d_fwd": t_conv, "gdn_gating": t_gate, "gdn_chunk_prefill": t_chunk},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)
                   if os.environ.get("GDN_PREFILL_PATH", "split") == "split" else None,
-                  "kernel": "gdn_chunk_prefill (split path: chunk_index + chunk_prep + chunk_state + gated_norm kernels)"
+                  "kernel": "gdn_chunk_prefill (split path: chunk_index + chunk_prep + chunk_state + chunk_out kernels)"
                   if os.environ.get("GDN_PREFILL_PATH", "split") == "split"
                   else "gdn_chunk_prefill (fused path: chunk_prefill_kernel)",
                   "algorithmic_bytes": nbytes,
@@ -230,6 +265,124 @@ def bench_decode(args, torch, gdn, gi):
             "tokens_per_s": round(case.n / ((t_rec + t_conv) * 1e-3), 1)}
 
 
+def bench_varlen(args, torch, gdn, gi):
+    """The ~271k-token varlen prefill: 64 sequences (lengths 128..8192, seed 0),
+    nonzero initial states from a 128-slot pool.  Inputs follow the recipe's
+    distributions but are drawn on the device (torch generator), since the
+    parity tests already cover the numpy-seeded values."""
+    case = gi.varlen_case()
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev).manual_seed(case.seed)
+    T, N = case.t_total, case.n_seq
+    rnd = lambda *shape: torch.randn(shape, device=dev, generator=gen).to(torch.bfloat16)
+    x, a, b, z = rnd(T, d.c_ch), rnd(T, d.h_v), rnd(T, d.h_v), rnd(T, d.h_v, d.d_v)
+    p = case.params
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log = torch.from_numpy(p.A_log).to(dev)
+    dt_bias = torch.from_numpy(p.dt_bias).to(dev)
+    cu = torch.from_numpy(case.cu_seqlens).to(dev)
+    slots = torch.from_numpy(case.slots).to(dev)
+    has_init = torch.ones(N, dtype=torch.uint8, device=dev)
+    conv_pool = rnd(case.n_slots, d.c_ch, d.conv_w - 1)
+    ssm_pool = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device=dev, generator=gen) * 0.02
+    y = torch.empty_like(x)
+    g = torch.empty((T, d.h_v), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(g)
+    o = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gdn.chunk_prefill_workspace_size(dims, 0, N, T, case.chunk), dtype=torch.uint8, device=dev)
+    steps = max(3, args.steps // 4)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        gdn.conv1d_fwd(dims, x, conv_w, cu, slots, conv_pool, has_init, y=y)
+        if e: e[1].record()
+        gdn.gating(a, b, A_log, dt_bias, g=g, beta=beta)
+        if e: e[2].record()
+        gdn.chunk_prefill(dims, y, g, beta, cu, slots, ssm_pool, has_init, case.chunk, 1.0, z, norm_w, 1e-6, o=o,
+                          workspace=ws)
+        if e: e[3].record()
+
+    step()
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in ev]))
+    t_step, t_chunk = ms(0, 3), ms(2, 3)
+    nbytes, flops = chunk_algorithmic(T, N, d.h_k, d.h_v, d.d_k, 2, True, case.chunk)
+    del x, y, z, o, ws
+    return {"workload": f"varlen_prefill_{N}seq_{T}tok", "tokens_per_s": round(T / (t_step * 1e-3), 1),
+            "ms_per_step": round(t_step, 4),
+            "kernels_ms": {"gdn_conv1d_fwd": round(ms(0, 1), 4), "gdn_gating": round(ms(1, 2), 4),
+                           "gdn_chunk_prefill": round(t_chunk, 4)},
+            "chunk_achieved_gbs": round(nbytes / (t_chunk * 1e-3) / 1e9, 1),
+            "chunk_hbm_frac": round(nbytes / (t_chunk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "chunk_mfma_frac": round(flops / (t_chunk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}
+
+
+def bench_mtp(args, torch, gdn, gi):
+    """128 requests x 4 MTP draft tokens: conv update and recurrent step with
+    per-position state writes, then the accepted states committed with
+    gdn_state_copy; pools rotated over 3 copies of 640 slots."""
+    case = gi.mtp_case()
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    dev = torch.device("cuda")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(case.seed)
+    pools = []
+    for _ in range(3):
+        ssm = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device=dev, generator=gen) * 0.02
+        conv = torch.randn((case.n_slots, d.c_ch, d.conv_w - 1), device=dev, generator=gen).to(torch.bfloat16)
+        pools.append((ssm, conv))
+    x, a, b, z = bf(case.x()), bf(case.a()), bf(case.b()), bf(case.z())
+    p = case.params
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log = torch.from_numpy(p.A_log).to(dev)
+    dt_bias = torch.from_numpy(p.dt_bias).to(dev)
+    slots = torch.from_numpy(case.slots).to(dev)
+    out_slots = torch.from_numpy(case.out_slots).to(dev)
+    sel = case.accept > 0
+    src = torch.from_numpy(case.out_slots[np.arange(case.n), np.maximum(case.accept - 1, 0)][sel]).to(dev)
+    dst = torch.from_numpy(case.slots[sel]).to(dev)
+    y = torch.empty_like(x)
+    o = torch.empty((case.n, case.t_step, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+    steps = max(args.steps, 30)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(k, e=None):
+        ssm, conv = pools[k % 3]
+        if e: e[0].record()
+        gdn.conv1d_update(dims, x, conv_w, conv, slots, out_slots, y=y)
+        if e: e[1].record()
+        gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, out_slots, 1.0, z, norm_w, 1e-6, o=o)
+        if e: e[2].record()
+        gdn.state_copy(dims, ssm, src, dst, conv)
+        if e: e[3].record()
+
+    for k in range(6):
+        step(k)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(k, ev[k])
+    torch.cuda.synchronize()
+    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in ev]))
+    t_conv, t_rec, t_copy = ms(0, 1), ms(1, 2), ms(2, 3)
+    nbytes = decode_algorithmic(case.n, case.t_step, d.h_k, d.h_v, d.d_k, 2, case.t_step)
+    copy_bytes = 2.0 * int(sel.sum()) * (d.h_v * d.d_v * d.d_k * 4 + d.c_ch * (d.conv_w - 1) * 2)
+    gbs = nbytes / (t_rec * 1e-3) / 1e9
+    return {"workload": f"mtp_{case.n}x{case.t_step}", "kernel": "recurrent_kernel<bf16,128>",
+            "launch_ms": round(t_rec, 4), "conv_update_ms": round(t_conv, 4), "state_copy_ms": round(t_copy, 4),
+            "algorithmic_bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "state_copy_gbs": round(copy_bytes / (t_copy * 1e-3) / 1e9, 1),
+            "draft_tokens_per_s": round(case.n * case.t_step / ((t_conv + t_rec + t_copy) * 1e-3), 1)}
+
+
 def cpu_baseline(inputs) -> dict:
     """The fp64 oracle on the host, one BLAS thread, on the whole 4096-token
     sequence (all 32 V heads): conv, gating, recurrence, gated RMSNorm."""
@@ -256,6 +409,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-mtp", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GDN layer's multi-GPU sharding "
@@ -273,6 +429,10 @@ def main() -> int:
     info = device_info()
     pre = bench_prefill(args, torch, gdn, gi)
     dec = None if args.no_decode else bench_decode(args, torch, gdn, gi)
+    mtp = None if args.no_mtp else bench_mtp(args, torch, gdn, gi)
+    torch.cuda.empty_cache()
+    var = None if args.no_varlen else bench_varlen(args, torch, gdn, gi)
+    torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth_gbs(torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre["inputs"])
     T = pre["T"]
@@ -294,7 +454,11 @@ def main() -> int:
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "kernels_ms": {k: round(v, 4) for k, v in pre["kernels_ms"].items()},
+        "timing": "graph replay" if not args.eager else "eager launches",
+        "eager_ms_per_step": round(pre["eager_ms_per_step"], 4),
         "decode": dec,
+        "mtp": mtp,
+        "varlen": var,
         "device": {**info, "copy_gbs": round(copy_gbs, 1)},
     }
     print(json.dumps(line), flush=True)

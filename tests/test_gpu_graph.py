@@ -1,0 +1,117 @@
+"""HIP-graph capture of the hot path.
+
+Every entry point launches kernels only (no allocation, no host sync, no
+memset), so a prefill step (conv1d + gating + chunked rule) and a decode step
+(conv update + recurrent step) can be captured once and replayed.  Each replay
+is checked bitwise against the eager result, with the program's own eager work
+and synchronisations between replays.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import gated_deltanet_conv1d_amd as gdn
+from tests.gpu_cases import DevPrefill, dev, i32
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def test_prefill_graph_replays_match_eager():
+    dims = gi.Dims(2, 4, 128, 128, 4)
+    case = gi.varlen_case(seed=21, dims=dims, lengths=np.array([77, 190, 64, 1]), n_slots=6)
+    dp = DevPrefill(case)
+    d = dp.dims
+    T = case.t_total
+    conv0, ssm0 = dp.conv_pool.clone(), dp.ssm_pool.clone()
+    y = torch.empty_like(dp.x)
+    g = torch.empty((T, d.h_v), dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(g)
+    o = torch.empty((T, d.h_v, d.d_v), dtype=dp.x.dtype, device="cuda")
+    ws = torch.empty(gdn.chunk_prefill_workspace_size(d, 0, case.n_seq, T, case.chunk), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        gdn.conv1d_fwd(d, dp.x, dp.conv_w, dp.cu, dp.slots, dp.conv_pool, dp.has_init, y=y)
+        gdn.gating(dp.a, dp.b, dp.A_log, dp.dt_bias, g=g, beta=beta)
+        gdn.chunk_prefill(d, y, g, beta, dp.cu, dp.slots, dp.ssm_pool, dp.has_init, case.chunk, 1.0, dp.z,
+                          dp.norm_w, 1e-6, o=o, workspace=ws)
+
+    def reset():
+        dp.conv_pool.copy_(conv0)
+        dp.ssm_pool.copy_(ssm0)
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = (o.clone(), dp.ssm_pool.clone(), dp.conv_pool.clone())
+
+    reset()
+    graph = _capture(step)
+    for k in range(3):
+        reset()
+        o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]), f"replay {k}: out"
+        assert torch.equal(dp.ssm_pool, ref[1]), f"replay {k}: state"
+        assert torch.equal(dp.conv_pool, ref[2]), f"replay {k}: conv state"
+        # eager work between replays, on other buffers
+        dp.run()
+        torch.cuda.synchronize()
+
+
+def test_decode_graph_replays_match_eager():
+    case = gi.decode_case(seed=22, n=8, n_slots=16, dims=gi.Dims(2, 4, 128, 128, 4))
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    bf = lambda v: dev(v, torch.bfloat16)
+    x, a, b, z = bf(case.x()), bf(case.a()), bf(case.b()), bf(case.z())
+    p = case.params
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log, dt_bias = dev(p.A_log, torch.float32), dev(p.dt_bias, torch.float32)
+    slots = i32(case.slots)
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    ssm0 = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device="cuda", generator=gen) * 0.02
+    conv0 = torch.randn((case.n_slots, d.c_ch, d.conv_w - 1), device="cuda", generator=gen).to(torch.bfloat16)
+    ssm, conv = ssm0.clone(), conv0.clone()
+    y = torch.empty_like(x)
+    o = torch.empty((case.n, 1, d.h_v, d.d_v), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        gdn.conv1d_update(dims, x, conv_w, conv, slots, y=y)
+        gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, None, 1.0, z, norm_w, 1e-6, o=o)
+
+    def reset():
+        ssm.copy_(ssm0)
+        conv.copy_(conv0)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (o.clone(), ssm.clone(), conv.clone())
+    reset()
+    graph = _capture(step)
+    for k in range(3):
+        reset()
+        o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(ssm, ref[1]) and torch.equal(conv, ref[2]), f"replay {k}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
