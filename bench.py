@@ -3,16 +3,18 @@
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
 One step = one pass of the prefill hot path over one batch: causal conv1d +
-SiLU (gdn_conv1d_fwd), gating (gdn_gating), then the chunked gated delta rule
-with fused q/k L2 norm and gated-RMSNorm epilogue (gdn_chunk_prefill), on the
-single-sequence workload: batch 1, T=4096, 16 QK / 32 V heads, d=128, bf16
-activations, fp32 state, chunk 64, synthetic seeded inputs resident in HBM.
-The timed steps replay one captured HIP graph of that step (how a serving
-loop runs it; --eager times plain launches instead); per-kernel times come
-from an eager pass with HIP events on the launch stream.
+SiLU, gating, the chunked gated delta rule with fused q/k L2 norm and the
+gated-RMSNorm epilogue, as the single gdn_prefill call (conv output and gates
+stay inside the chunk kernels), on the single-sequence workload: batch 1,
+T=4096, 16 QK / 32 V heads, d=128, bf16 activations, fp32 state, chunk 64,
+synthetic seeded inputs resident in HBM.  The same step as three calls
+(gdn_conv1d_fwd, gdn_gating, gdn_chunk_prefill) is reported beside it.  The
+timed steps replay one captured HIP graph of the step (how a serving loop
+runs it; --eager times plain launches instead); per-call times come from an
+eager pass with HIP events on the launch stream.
 
 Prints ONE JSON line: tokens/s for that step (value), the roofline of the
-dominant call (gdn_chunk_prefill), the decode state-update bandwidth (256
+dominant call (gdn_prefill), the decode state-update bandwidth (256
 requests x 1 token over a 512-slot fp32 state pool, pools rotated so states
 come from HBM), the ~271k-token varlen prefill and the 128 x 4-token MTP step
 as extra rows, and the fp64 CPU oracle timed on the host as a baseline.
@@ -55,6 +57,20 @@ def chunk_algorithmic(T: int, n_seq: int, h_k: int, h_v: int, d: int, act_bytes:
     return float(nbytes), float(flops)
 
 
+def prefill_algorithmic(T: int, n_seq: int, h_k: int, h_v: int, d: int, act_bytes: int, has_init: bool,
+                        chunk: int, conv_w: int) -> tuple[float, float]:
+    """Algorithmic bytes and flops of one gdn_prefill call: per token the conv
+    input row (2*h_k*d + h_v*d activations), a and b (2*h_v activations), z
+    read and out written; per sequence the fp32 state and the conv window
+    (written, and read when it has history).  Flops as chunk_algorithmic plus
+    the conv (2*conv_w per channel and token)."""
+    c_ch = 2 * h_k * d + h_v * d
+    per_tok = c_ch * act_bytes + 2 * h_v * act_bytes + 2 * h_v * d * act_bytes
+    per_seq = (h_v * d * d * 4 + c_ch * (conv_w - 1) * act_bytes) * (2 if has_init else 1)
+    _, flops = chunk_algorithmic(T, n_seq, h_k, h_v, d, act_bytes, has_init, chunk)
+    return float(T * per_tok + n_seq * per_seq), float(flops + 2 * conv_w * c_ch * T)
+
+
 def decode_algorithmic(n: int, t_step: int, h_k: int, h_v: int, d: int, act_bytes: int, n_pos_writes: int) -> float:
     """Bytes of one gdn_recurrent_decode launch: each state read once and written
     n_pos_writes times, plus per token q/k/v, a/b, z and out."""
@@ -93,9 +109,14 @@ def counter_traffic(workload: str, kernels) -> float | None:
 
 
 # kernels one gdn_chunk_prefill call launches on the split path
-CHUNK_SPLIT_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64>",
+CHUNK_SPLIT_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, false, 4>",
                        "void split::chunk_state_kernel<__bf16, 128, 64, 1>",
-                       "void split::chunk_out_kernel<__bf16, __bf16, 128, 64>")
+                       "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, false, 4>")
+# kernels one gdn_prefill call launches
+PREFILL_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, true, 4>",
+                   "void split::chunk_state_kernel<__bf16, 128, 64, 1>",
+                   "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, true, 4>",
+                   "void conv1d_store_state_kernel<__bf16, 4>")
 
 
 def capture_graph(torch, fn):
@@ -161,8 +182,9 @@ def bench_prefill(args, torch, gdn, gi):
     ws = torch.empty(gdn.chunk_prefill_workspace_size(dims, 0, 1, T, case.chunk), dtype=torch.uint8, device=dev)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
 
-    def step(e=None):
+    def step_sep(e=None):
         if e: e[0].record()
         gdn.conv1d_fwd(dims, x, conv_w, cu, slots, conv_pool, has_init, y=y)
         if e: e[1].record()
@@ -172,19 +194,25 @@ def bench_prefill(args, torch, gdn, gi):
                           workspace=ws)
         if e: e[3].record()
 
-    # eager pass: per-kernel times with events on the launch stream
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(ev[k])
-    torch.cuda.synchronize()
-    wall_eager = time.perf_counter() - t0
-    # timed pass: graph replays of the same step
-    wall = wall_eager
-    if not args.eager:
-        graph = capture_graph(torch, step)
+    def step(e=None):
+        if e: e[0].record()
+        gdn.prefill(dims, x, conv_w, a, b, A_log, dt_bias, cu, slots, conv_pool, ssm_pool, has_init, case.chunk,
+                    1.0, z, norm_w, 1e-6, o=o, workspace=ws)
+        if e: e[1].record()
+
+    def timed(fn, evs):
+        """eager pass with events, then (unless --eager) graph replays; wall seconds of the timed pass"""
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            fn(evs[k])
+        torch.cuda.synchronize()
+        wall_eager = time.perf_counter() - t0
+        if args.eager:
+            return wall_eager, wall_eager
+        graph = capture_graph(torch, fn)
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -192,28 +220,34 @@ def bench_prefill(args, torch, gdn, gi):
         for _ in range(args.steps):
             graph.replay()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in ev]))
-    t_conv, t_gate, t_chunk = ms(0, 1), ms(1, 2), ms(2, 3)
-    t_step = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
-    nbytes, flops = chunk_algorithmic(T, 1, d.h_k, d.h_v, d.d_k, 2, False, case.chunk)
-    achieved = nbytes / (t_chunk * 1e-3) / 1e9
+        return time.perf_counter() - t0, wall_eager
+
+    wall_sep, wall_sep_eager = timed(step_sep, ev)
+    wall, wall_eager = timed(step, evf)
+    ms = lambda evs, i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
+    t_conv, t_gate, t_chunk = ms(ev, 0, 1), ms(ev, 1, 2), ms(ev, 2, 3)
+    t_pre = ms(evf, 0, 1)
+    nbytes, flops = prefill_algorithmic(T, 1, d.h_k, d.h_v, d.d_k, 2, False, case.chunk, d.conv_w)
+    achieved = nbytes / (t_pre * 1e-3) / 1e9
     return dict(
-        T=T, wall_s=wall, ms_per_step=wall / args.steps * 1e3, event_ms_per_step=t_step,
-        eager_ms_per_step=wall_eager / args.steps * 1e3,
-        kernels_ms={"gdn_conv1d_fwd": t_conv, "gdn_gating": t_gate, "gdn_chunk_prefill": t_chunk},
+        T=T, wall_s=wall, ms_per_step=wall / args.steps * 1e3, eager_ms_per_step=wall_eager / args.steps * 1e3,
+        kernels_ms={"gdn_prefill": t_pre},
+        separate_calls={"ms_per_step": round(wall_sep / args.steps * 1e3, 4),
+                        "tokens_per_s": round(T * args.steps / wall_sep, 1),
+                        "eager_ms_per_step": round(wall_sep_eager / args.steps * 1e3, 4),
+                        "kernels_ms": {"gdn_conv1d_fwd": round(t_conv, 4), "gdn_gating": round(t_gate, 4),
+                                       "gdn_chunk_prefill": round(t_chunk, 4)},
+                        "chunk_traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)
+                        if os.environ.get("GDN_PREFILL_PATH", "split") == "split" else None},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
-                  "traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)
-                  if os.environ.get("GDN_PREFILL_PATH", "split") == "split" else None,
-                  "kernel": "gdn_chunk_prefill (split path: chunk_index + chunk_prep + chunk_state + chunk_out kernels)"
-                  if os.environ.get("GDN_PREFILL_PATH", "split") == "split"
-                  else "gdn_chunk_prefill (fused path: chunk_prefill_kernel)",
+                  "traffic": counter_traffic("prefill_4096", PREFILL_KERNELS),
+                  "kernel": "gdn_prefill (chunk_index + chunk_prep + chunk_state + chunk_out + conv1d_store_state)",
                   "algorithmic_bytes": nbytes,
-                  "launch_ms": round(t_chunk, 4),
-                  "mfma": {"algorithmic_flops": flops, "achieved_tflops": round(flops / (t_chunk * 1e-3) / 1e12, 2),
+                  "launch_ms": round(t_pre, 4),
+                  "mfma": {"algorithmic_flops": flops, "achieved_tflops": round(flops / (t_pre * 1e-3) / 1e12, 2),
                            "peak_tflops": BF16_PEAK_TFLOPS,
-                           "frac": round(flops / (t_chunk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}},
+                           "frac": round(flops / (t_pre * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}},
         inputs=dict(x=x, a=a, b=b, z=z, case=case))
 
 
@@ -306,22 +340,39 @@ def bench_varlen(args, torch, gdn, gi):
                           workspace=ws)
         if e: e[3].record()
 
-    step()
-    torch.cuda.synchronize()
-    for k in range(steps):
-        step(ev[k])
-    torch.cuda.synchronize()
-    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in ev]))
-    t_step, t_chunk = ms(0, 3), ms(2, 3)
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+
+    def step_fused(e=None):
+        if e: e[0].record()
+        gdn.prefill(dims, x, conv_w, a, b, A_log, dt_bias, cu, slots, conv_pool, ssm_pool, has_init, case.chunk,
+                    1.0, z, norm_w, 1e-6, o=o, workspace=ws)
+        if e: e[1].record()
+
+    for fn, evs in ((step, ev), (step_fused, evf)):
+        fn()
+        torch.cuda.synchronize()
+        for k in range(steps):
+            fn(evs[k])
+        torch.cuda.synchronize()
+    ms = lambda evs, i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
+    t_step, t_chunk, t_fused = ms(ev, 0, 3), ms(ev, 2, 3), ms(evf, 0, 1)
     nbytes, flops = chunk_algorithmic(T, N, d.h_k, d.h_v, d.d_k, 2, True, case.chunk)
+    pbytes, pflops = prefill_algorithmic(T, N, d.h_k, d.h_v, d.d_k, 2, True, case.chunk, d.conv_w)
     del x, y, z, o, ws
-    return {"workload": f"varlen_prefill_{N}seq_{T}tok", "tokens_per_s": round(T / (t_step * 1e-3), 1),
-            "ms_per_step": round(t_step, 4),
-            "kernels_ms": {"gdn_conv1d_fwd": round(ms(0, 1), 4), "gdn_gating": round(ms(1, 2), 4),
-                           "gdn_chunk_prefill": round(t_chunk, 4)},
-            "chunk_achieved_gbs": round(nbytes / (t_chunk * 1e-3) / 1e9, 1),
-            "chunk_hbm_frac": round(nbytes / (t_chunk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "chunk_mfma_frac": round(flops / (t_chunk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}
+    best = min(t_step, t_fused)
+    return {"workload": f"varlen_prefill_{N}seq_{T}tok", "tokens_per_s": round(T / (best * 1e-3), 1),
+            "path": "separate calls" if t_step <= t_fused else "gdn_prefill",
+            "separate_calls": {"ms_per_step": round(t_step, 4),
+                               "kernels_ms": {"gdn_conv1d_fwd": round(ms(ev, 0, 1), 4),
+                                              "gdn_gating": round(ms(ev, 1, 2), 4),
+                                              "gdn_chunk_prefill": round(t_chunk, 4)},
+                               "chunk_achieved_gbs": round(nbytes / (t_chunk * 1e-3) / 1e9, 1),
+                               "chunk_hbm_frac": round(nbytes / (t_chunk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "chunk_mfma_frac": round(flops / (t_chunk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
+            "gdn_prefill": {"ms_per_step": round(t_fused, 4),
+                            "achieved_gbs": round(pbytes / (t_fused * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(pbytes / (t_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "mfma_frac": round(pflops / (t_fused * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}}
 
 
 def bench_mtp(args, torch, gdn, gi):
@@ -456,6 +507,7 @@ def main() -> int:
         "kernels_ms": {k: round(v, 4) for k, v in pre["kernels_ms"].items()},
         "timing": "graph replay" if not args.eager else "eager launches",
         "eager_ms_per_step": round(pre["eager_ms_per_step"], 4),
+        "separate_calls": pre["separate_calls"],
         "decode": dec,
         "mtp": mtp,
         "varlen": var,

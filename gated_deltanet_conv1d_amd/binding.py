@@ -33,6 +33,9 @@ SIGNATURES = {
     "gdn_chunk_prefill_workspace_size": (_SZ, [_P, _I32, _I32, _I64, _I32]),
     "gdn_chunk_prefill": (ctypes.c_int, [_P, _I32, _I32, _I64, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
                                          _P, _F, _P, _SZ, _P]),
+    "gdn_prefill_workspace_size": (_SZ, [_P, _I32, _I32, _I64, _I32]),
+    "gdn_prefill": (ctypes.c_int, [_P, _I32, _I32, _I64, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _I32, _P, _P, _P, _F, _P, _SZ, _P]),
     "gdn_recurrent_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
                                             _P, _F, _P]),
     "gdn_state_copy": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
@@ -195,6 +198,41 @@ def chunk_prefill(dims: Dims, qkv, g, beta, cu_seqlens, slots, state, has_init=N
                                    _ptr(state, torch.float32, "state"), state.shape[0], _ptr(o, qkv.dtype, "o"),
                                    _ptr(z, qkv.dtype, "z"), _ptr(norm_w, qkv.dtype, "norm_w"), norm_eps,
                                    _ptr(workspace, None, "workspace"), ws_bytes, _stream()), "gdn_chunk_prefill")
+    return o
+
+
+def prefill_workspace_size(dims: Dims, act: int, n_seq: int, t_total: int, chunk: int) -> int:
+    return int(lib().gdn_prefill_workspace_size(ctypes.byref(_cdims(dims)), act, n_seq, t_total, chunk))
+
+
+def prefill(dims: Dims, x, conv_w, a, b, A_log, dt_bias, cu_seqlens, slots, conv_state, state, has_init=None,
+            chunk: int = 64, scale: float = 1.0, z=None, norm_w=None, norm_eps: float = 1e-6, conv_b=None, o=None,
+            workspace=None):
+    """The whole prefill path in one call (conv1d + SiLU, gating, chunked rule,
+    epilogue), with the conv output and gates kept inside the chunk kernels.
+    Updates conv_state and state in place; returns out."""
+    act = _act(x)
+    t_total, n_seq = x.shape[0], slots.shape[0]
+    _shape(x, (t_total, dims.c_ch), "x")
+    _shape(a, (t_total, dims.h_v), "a")
+    _shape(b, (t_total, dims.h_v), "b")
+    _shape(conv_state, (conv_state.shape[0], dims.c_ch, dims.conv_w - 1), "conv_state")
+    _shape(state, (state.shape[0], dims.h_v, dims.d_v, dims.d_k), "state")
+    if o is None:
+        o = torch.empty((t_total, dims.h_v, dims.d_v), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(prefill_workspace_size(dims, act, n_seq, t_total, chunk), 1), dtype=torch.uint8,
+                                device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().gdn_prefill(ctypes.byref(_cdims(dims)), act, n_seq, t_total, chunk, scale, _ptr(x, x.dtype, "x"),
+                             _ptr(conv_w, x.dtype, "conv_w"), _ptr(conv_b, x.dtype, "conv_b"), _ptr(a, x.dtype, "a"),
+                             _ptr(b, x.dtype, "b"), _ptr(A_log, torch.float32, "A_log"),
+                             _ptr(dt_bias, torch.float32, "dt_bias"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+                             _ptr(slots, torch.int32, "slots"), _ptr(has_init, torch.uint8, "has_init"),
+                             _ptr(conv_state, x.dtype, "conv_state"), _ptr(state, torch.float32, "state"),
+                             state.shape[0], _ptr(o, x.dtype, "o"), _ptr(z, x.dtype, "z"),
+                             _ptr(norm_w, x.dtype, "norm_w"), norm_eps, _ptr(workspace, None, "workspace"), ws_bytes,
+                             _stream()), "gdn_prefill")
     return o
 
 

@@ -1,905 +1,9 @@
-// Chunked gated delta rule, split into a chunk-parallel preparation pass and
-// a state pass that runs per (sequence, V head, 16-column d_v tile).  Same math
-// as chunk_prefill.hip (the chunked WY / UT form of the gated delta rule):
-//   A = strict-lower(b_i e^{G_i-G_j} k_i.k_j),  T = (I + A)^{-1},
-//   W = T diag(b e^G) K,  Ut = T diag(b) V,  P = M o Q K^T        (no state)
-//   U = Ut - W S0^T,  O = diag(e^G) Q S0^T + P U,
-//   S = e^{G_n} S0 + K^T diag(e^{G_n - G}) U                       (the chain)
-//
-// Why this shape on MI355X: the first line depends only on the chunk's own
-// tokens, so it runs as one workgroup per (chunk, V head) across the GPU.  In
-// the chain, the rows of S (the d_v index) never mix: every contraction runs
-// over d_k or over tokens.  So one wave owns a 16-wide slice of d_v for all of
-// d_k, holding its S^T slice in MFMA accumulators, and a single 4096-token
-// sequence with 32 V heads already gives 256 independent waves, one per CU,
-// with no LDS and no barrier in the loop.  The chain keeps only what is
-// serial, U and the state update; it records S at every chunk start (h) and
-// U, and the output O = diag(f_q) Q h^T + P U with its gated RMSNorm is again
-// chunk-parallel.  The prep pass writes the operands as ready-made MFMA
-// fragments:
-//   -W                             (A operand, contraction over d_k)
-//   K'^T = (diag(e^{G_n-G}) K)^T   (A operand, contraction over the chunk)
-//   scale P                        (A operand, lower triangle)
-//   Ut                             (accumulator layout; the chain turns it into U)
-//   f_q = scale e^G r_q            (per token; the output pass reads raw q)
-// so every load is a 16- or 8-byte lane-contiguous vector.
-//
-//   chunk_index_kernel  first global chunk of every sequence (block scan)
-//   chunk_prep_kernel   per (chunk, V head): q/k L2 norm, gates, Gram, T and
-//                       the operand fragments above
-//   chunk_state_kernel  per (sequence, V head, d_v tile): the chunk loop
-//   chunk_out_kernel    per (chunk, V head): O, gated RMSNorm over d_v, store
-#include "gdn_device.hpp"
-#include "gdn_launch.hpp"
+// Launchers of the split chunked prefill (kernels in chunk_split_kernels.hpp):
+// q, k, v from the conv1d output y and g, beta from the gating pass.
+#include "chunk_split_kernels.hpp"
 
 namespace gdn {
 namespace split {
-
-template <int D>
-constexpr int kThreads = (D >= 128 ? 4 : (D >= 64 ? 2 : 1)) * 64;
-
-template <typename Op, int D, int C>
-struct Cfg {
-  static constexpr int NT = D / 16;
-  static constexpr int CT = C / 16;
-  static constexpr int THREADS = kThreads<D>;
-  static constexpr int WAVES = THREADS / 64;
-  static constexpr int DVT = NT / WAVES;
-  static constexpr int LPR = D / 8;    // lanes per row piece of 8 elements
-  static constexpr int RPP = THREADS / LPR;
-  static constexpr int RPT = (C + RPP - 1) / RPP;
-  // Pair fragments: an A operand tile of 16 rows and a 32-wide step of the
-  // contraction, 8 values per lane (two 16-blocks, 4 each), zero past the end.
-  static constexpr int NPD = (NT + 1) / 2;  // 32-steps over d_k
-  static constexpr int NPC = (CT + 1) / 2;  // 32-steps over the chunk
-  static constexpr int PAIR = 64 * 8;       // elements per pair tile
-  // workspace unit per (chunk, V head), bytes
-  static constexpr int W_OFF = 0;                                   // -W     [CT][NPD] pairs
-  static constexpr int KT_OFF = W_OFF + CT * NPD * PAIR * (int)sizeof(Op);  // K'^T [NT][NPC]
-  static constexpr int P_OFF = KT_OFF + NT * NPC * PAIR * (int)sizeof(Op);  // P   [CT][NPC]
-  static constexpr int UT_OFF = P_OFF + CT * NPC * PAIR * (int)sizeof(Op);  // Ut  [CT][NT][64][4]
-  static constexpr int H_OFF = UT_OFF + C * D * (int)sizeof(Op);            // S^T at chunk start, [NPD][NT] pairs
-  static constexpr int F_OFF = H_OFF + NPD * NT * PAIR * (int)sizeof(Op);   // e^{G_n}, then f_q [C]
-  static constexpr int FQ_OFF = F_OFF + 16;                                 // scale e^{G_t} r_q[t]
-  static constexpr int UNIT = (FQ_OFF + C * 4 + 255) / 256 * 256;
-  // output kernel LDS: raw q rows, then (over them) the fp32 O tile, row-major
-  static constexpr int LD_Q = D + 16;
-  static constexpr int LD_O = D + 4;
-  static constexpr int OUT_BYTES = C * LD_O * 4 > C * LD_Q * (int)sizeof(Op) ? C * LD_O * 4 : C * LD_Q * (int)sizeof(Op);
-  // prep kernel LDS.  Row strides are padded so the 8-byte fragment reads of
-  // a wave (16 rows x 4 column groups) hit distinct banks.
-  static constexpr int LDR = D + 16;   // raw k rows (elements)
-  static constexpr int LDA = C + 16;   // fp32 A, then T in place
-  static constexpr int LDT = C + 8;    // T diag(b e^G r_k) and T diag(b), operand type
-  static constexpr int PK = 0;
-  static constexpr int PA = PK + C * LDR * (int)sizeof(Op);
-  static constexpr int PS = PA + C * LDA * 4;                      // G, b, r_k
-  static constexpr bool T_OVER_A = 2 * LDT * (int)sizeof(Op) <= LDA * 4;  // the T copies fit over A
-  static constexpr int PTW = T_OVER_A ? PA : PS + 3 * C * 4;
-  static constexpr int PTU = PTW + C * LDT * (int)sizeof(Op);
-  static constexpr int PREP_BYTES = T_OVER_A ? PS + 3 * C * 4 : PTU + C * LDT * (int)sizeof(Op);
-};
-
-__device__ __forceinline__ int32_t seq_of_chunk(const int32_t* __restrict__ cstart, int32_t n_seq, int32_t gc) {
-  int32_t lo = 0, hi = n_seq - 1;  // largest i with cstart[i] <= gc
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (cstart[mid] <= gc) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// cstart[i] = sum over j < i of ceil(len_j / C), for i = 0..n_seq.  One block.
-__global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t* __restrict__ cu, int32_t n_seq,
-                                                           int64_t t_total, int32_t chunk,
-                                                           int32_t* __restrict__ cstart) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  const int per = (n_seq + 1023) / 1024;
-  const int i0 = min(tid * per, n_seq), i1 = min(i0 + per, n_seq);
-  int32_t s = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int64_t lo = min((int64_t)cu[i], t_total);
-    const int64_t hi = min(max((int64_t)cu[i + 1], lo), t_total);
-    s += (int32_t)((hi - lo + chunk - 1) / chunk);
-  }
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    const int32_t v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = tid == 0 ? 0 : part[tid - 1];
-  for (int i = i0; i < i1; ++i) {
-    cstart[i] = run;
-    const int64_t lo = min((int64_t)cu[i], t_total);
-    const int64_t hi = min(max((int64_t)cu[i + 1], lo), t_total);
-    run += (int32_t)((hi - lo + chunk - 1) / chunk);
-  }
-  if (tid == 1023) cstart[n_seq] = part[1023];
-}
-
-template <typename Op>
-__device__ __forceinline__ typename Frag<Op>::type frag_scaled(const float* p, const float* s) {
-  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-  typename Frag<Op>::type r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = from_f32<Op>(v[i] * s[i]);
-  return r;
-}
-// 4 values down a column of a row-major tile (contraction index = row).
-template <typename Op>
-__device__ __forceinline__ typename Frag<Op>::type frag_col(const Op* p, int ld) {
-  typename Frag<Op>::type r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = p[i * ld];
-  return r;
-}
-
-template <typename Op>
-__device__ __forceinline__ typename Frag<Op>::type zero_frag() {
-  typename Frag<Op>::type r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = from_f32<Op>(0.f);
-  return r;
-}
-template <typename Op>
-__device__ __forceinline__ typename Frag<Op>::type frag_mul(const typename Frag<Op>::type& a, float f) {
-  typename Frag<Op>::type r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = from_f32<Op>(to_f32(a[i]) * f);
-  return r;
-}
-template <typename Op>
-__device__ __forceinline__ void store_pair(Op* dst, const typename Frag<Op>::type& lo,
-                                           const typename Frag<Op>::type& hi);
-template <>
-__device__ __forceinline__ void store_pair<bf16>(bf16* dst, const bf16x4& lo, const bf16x4& hi) {
-  *reinterpret_cast<bf16x8*>(dst) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-template <>
-__device__ __forceinline__ void store_pair<float>(float* dst, const f32x4& lo, const f32x4& hi) {
-  reinterpret_cast<f32x4*>(dst)[0] = lo;
-  reinterpret_cast<f32x4*>(dst)[1] = hi;
-}
-
-// A pair fragment in registers: one 16x16x32 bf16 MFMA, or two 16-blocks of
-// 16x16x4 fp32 MFMAs.  B is the two matching 16-blocks in accumulator layout.
-template <typename Op> struct Pair;
-template <> struct Pair<bf16> {
-  bf16x8 v;
-  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
-  __device__ __forceinline__ void split(bf16x4& a, bf16x4& b) const {
-    a = bf16x4{v[0], v[1], v[2], v[3]};
-    b = bf16x4{v[4], v[5], v[6], v[7]};
-  }
-  __device__ __forceinline__ void mma(f32x4& acc, const bf16x4& b0, const bf16x4& b1) const {
-    const bf16x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, b, acc, 0, 0, 0);
-  }
-};
-template <> struct Pair<float> {
-  f32x4 lo, hi;
-  __device__ __forceinline__ void load(const float* p) {
-    lo = reinterpret_cast<const f32x4*>(p)[0];
-    hi = reinterpret_cast<const f32x4*>(p)[1];
-  }
-  __device__ __forceinline__ void split(f32x4& a, f32x4& b) const {
-    a = lo;
-    b = hi;
-  }
-  __device__ __forceinline__ void mma(f32x4& acc, const f32x4& b0, const f32x4& b1) const {
-    mma_k32(acc, lo, hi, b0, b1);
-  }
-};
-
-// Address of a workspace vector: uniform base plus a 32-bit unsigned byte
-// offset, which lets the compiler use SGPR-base addressing with no 64-bit
-// VALU arithmetic per load.
-template <typename V>
-__device__ __forceinline__ const V* at(const unsigned char* base, uint32_t off) {
-  return reinterpret_cast<const V*>(base + off);
-}
-template <typename V>
-__device__ __forceinline__ V* at(unsigned char* base, uint32_t off) {
-  return reinterpret_cast<V*>(base + off);
-}
-
-// ------------------------------------------------------------------ prep
-// 8 raw activations into LDS unchanged (activation and operand types agree).
-template <typename T>
-__device__ __forceinline__ void raw_store(const Raw8<T>& r, T* dst);
-template <>
-__device__ __forceinline__ void raw_store<bf16>(const Raw8<bf16>& r, bf16* dst) {
-  *reinterpret_cast<uint4*>(dst) = r.u;
-}
-template <>
-__device__ __forceinline__ void raw_store<float>(const Raw8<float>& r, float* dst) {
-  reinterpret_cast<uint4*>(dst)[0] = r.u[0];
-  reinterpret_cast<uint4*>(dst)[1] = r.u[1];
-}
-
-// Per (chunk, V head).  Everything runs on the raw q, k, v of the chunk; the
-// L2 norms enter as per-token factors r = 1/sqrt(|x|^2 + 1e-6):
-//   A_ij  = b_i r_k[i] r_k[j] e^{G_i-G_j} (k_i.k_j), i > j;   T = (I + A)^{-1}
-//   P_ij  = scale r_q[i] r_k[j] e^{G_i-G_j} (q_i.k_j), i >= j
-//   W     = T diag(b e^G r_k) K,   Ut = T diag(b) V,   K' = diag(e^{G_n-G} r_k) K
-// and f_q = scale e^G r_q, which the output pass applies to Q S^T.
-// No fragment is ever read down an LDS column.  P is formed as P^T = K Q^T,
-// whose accumulator layout is P's A-fragment layout; W is formed as
-// W^T = K^T (T diag(..))^T, whose accumulator layout is W's A-fragment layout;
-// K and V blocks reach the column (B operand) layout through one MFMA with an
-// identity operand, which is exact.  Only k is staged in LDS: each wave loads
-// the q blocks and v tiles it uses as register fragments.
-template <typename T, typename Op, int D, int C>
-__global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
-    const T* __restrict__ qkv, const float* __restrict__ g_in, const float* __restrict__ beta_in,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const int32_t* __restrict__ cstart,
-    int32_t n_slots, int32_t n_seq, int64_t t_total, int32_t h_k, int32_t h_v, float scale,
-    unsigned char* __restrict__ ws) {
-  static_assert(sizeof(T) == sizeof(Op), "raw activations are MFMA operands");
-  using K = Cfg<Op, D, C>;
-  using FragT = typename Frag<Op>::type;
-  constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, DVT = K::DVT, LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
-  constexpr int NPD = K::NPD, NPC = K::NPC, LDR = K::LDR, LDA = K::LDA, LDT = K::LDT;
-  constexpr int QB = (CT + WAVES - 1) / WAVES;  // q blocks per wave: blocks wave, wave + WAVES, ...
-  constexpr uint32_t PB = K::PAIR * sizeof(Op);
-  static_assert(DVT == 1 || DVT == 2, "a wave's d tiles form one pair fragment");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[K::PREP_BYTES];
-  Op* sK = reinterpret_cast<Op*>(smem + K::PK);
-  float* sA = reinterpret_cast<float*>(smem + K::PA);
-  float* sG = reinterpret_cast<float*>(smem + K::PS);
-  float* sB = sG + C;
-  float* sRK = sG + 2 * C;
-  Op* sTW = reinterpret_cast<Op*>(smem + K::PTW);
-  Op* sTU = reinterpret_cast<Op*>(smem + K::PTU);
-
-  const int gc = blockIdx.x / h_v;
-  const int h = blockIdx.x % h_v;
-  if (gc >= cstart[n_seq]) return;
-  const int n = seq_of_chunk(cstart, n_seq, gc);
-  if (!slot_ok(slots[n], n_slots)) return;  // padding entry: nothing to prepare
-  const int hk = h / (h_v / h_k);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-  const int c_ch = 2 * h_k * D + h_v * D;
-  const int64_t seq_lo = min((int64_t)cu[n], t_total);
-  const int64_t seq_hi = min(max((int64_t)cu[n + 1], seq_lo), t_total);
-  const int64_t c0 = seq_lo + (int64_t)(gc - cstart[n]) * C;
-  const int nvalid = (int)min((int64_t)C, seq_hi - c0);
-  unsigned char* unit = ws + ((int64_t)gc * h_v + h) * K::UNIT;
-  const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
-  const FragT zf = zero_frag<Op>();
-  FragT eye;  // B fragment of the 16x16 identity
-#pragma unroll
-  for (int i = 0; i < 4; ++i) eye[i] = from_f32<Op>(4 * g4 + i == l16 ? 1.f : 0.f);
-
-  // ---- register fragments straight from memory: this wave's q blocks (B
-  // operand of P^T, row l16) and v tiles (A layout, row l16)
-  FragT Qb[QB][NPD][2], Va[CT][DVT];
-  {
-    const T* qbase = qkv + (int64_t)hk * D + 4 * g4;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const int r = 16 * (wave + b * WAVES) + l16;
-      const bool ok = wave + b * WAVES < CT && r < nvalid;
-#pragma unroll
-      for (int sp = 0; sp < NPD; ++sp) {
-        Qb[b][sp][0] = ok ? *reinterpret_cast<const FragT*>(qbase + (c0 + r) * c_ch + 32 * sp) : zf;
-        Qb[b][sp][1] = ok && 32 * sp + 16 < D ? *reinterpret_cast<const FragT*>(qbase + (c0 + r) * c_ch + 32 * sp + 16) : zf;
-      }
-    }
-    const T* vbase = qkv + (int64_t)(2 * h_k + h) * D + 16 * wave * DVT + 4 * g4;
-#pragma unroll
-    for (int kb = 0; kb < CT; ++kb)
-#pragma unroll
-      for (int j = 0; j < DVT; ++j) {
-        const int r = 16 * kb + l16;
-        Va[kb][j] = r < nvalid ? *reinterpret_cast<const FragT*>(vbase + (c0 + r) * c_ch + 16 * j) : zf;
-      }
-  }
-  // ---- raw k rows into LDS with their inverse norms; gates
-  {
-    const int e0 = (tid % LPR) * 8, r0 = tid / LPR;
-    Raw8<T> raw[RPT];
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int r = r0 + j * RPP;
-      if (r < nvalid) raw[j].load(qkv + (c0 + r) * c_ch + (int64_t)(h_k + hk) * D + e0);
-      else raw[j].zero();
-    }
-    float gv = 0.f, bv = 0.f;
-    if (wave == 0 && lane < nvalid) {
-      gv = g_in[(c0 + lane) * h_v + h];
-      bv = beta_in[(c0 + lane) * h_v + h];
-    }
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int r = r0 + j * RPP;
-      float v[8];
-      raw[j].to_f32(v);
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-      ss = group_sum<LPR>(ss);
-      if (r < C) {
-        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&raw[j]), sK + r * LDR + e0);
-        if (tid % LPR == 0) sRK[r] = fast_rsq(ss + 1e-6f);
-      }
-    }
-    if (wave == 0) {
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float up = __shfl_up(gv, off);
-        if (lane >= off) gv += up;
-      }
-      if (lane < C) {
-        sG[lane] = gv;
-        sB[lane] = bv;
-      }
-      if (lane == C - 1) *at<float>(unit, K::F_OFF) = fast_exp(gv);
-    }
-  }
-  __syncthreads();
-
-  // ---- Gram work.  Wave w: the P^T tiles of its q blocks ib (pairs of
-  // column blocks -> P fragments) and f_q of those rows; then K K^T tiles -> A,
-  // taken in the order that evens out the per-wave tile count.
-  {
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const int ib = wave + b * WAVES;
-      if (ib >= CT) break;
-      // r_q of row 16 ib + l16: the row's 32 pair values per lane, 4 lanes per row
-      float ss = 0.f;
-#pragma unroll
-      for (int sp = 0; sp < NPD; ++sp)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = to_f32(Qb[b][sp][hh][e]);
-            ss = fmaf(x, x, ss);
-          }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      const int i = 16 * ib + l16;
-      const float fi = scale * fast_rsq(ss + 1e-6f);  // scale r_q[i]
-      const float gi = sG[i];
-      if (g4 == 0) *at<float>(unit, K::FQ_OFF + 4 * i) = fi * fast_exp(gi);
-#pragma unroll
-      for (int sp = 0; sp < NPC; ++sp) {
-        if (2 * sp > ib) break;
-        FragT half[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int jb = 2 * sp + hh;
-          if (jb > ib) { half[hh] = zf; continue; }
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const Op* arow = sK + (16 * jb + l16) * LDR + 4 * g4;
-#pragma unroll
-          for (int s2 = 0; s2 < NPD; ++s2) {
-            if (32 * s2 + 16 < D)
-              mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), Qb[b][s2][0], Qb[b][s2][1]);
-            else
-              mma_k16(acc, lds_frag<Op>(arow + 32 * s2), Qb[b][s2][0]);
-          }
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int jj = 16 * jb + 4 * g4 + ii;
-            half[hh][ii] = from_f32<Op>(i >= jj ? fi * sRK[jj] * fast_exp(fminf(gi - sG[jj], 0.f)) * acc[ii] : 0.f);
-          }
-        }
-        store_pair<Op>(at<Op>(unit, K::P_OFF + (uint32_t)(ib * NPC + sp) * PB + lp), half[0], half[1]);
-      }
-    }
-    // A tiles (ib, jb), jb <= ib, enumerated from the last block row down so
-    // the waves with the fewest P tiles take the longest rows first
-    constexpr int N_A = CT * (CT + 1) / 2;
-    for (int it = WAVES - 1 - wave; it < N_A; it += WAVES) {
-      int ib = CT - 1, rest = it;
-      while (rest >= ib + 1) { rest -= ib + 1; --ib; }
-      const int jb = rest;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const Op* arow = sK + (16 * ib + l16) * LDR + 4 * g4;
-      const Op* brow = sK + (16 * jb + l16) * LDR + 4 * g4;
-#pragma unroll
-      for (int s2 = 0; s2 < NPD; ++s2) {
-        if (32 * s2 + 16 < D)
-          mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
-                  lds_frag<Op>(brow + 32 * s2 + 16));
-        else
-          mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
-      }
-      const int j = 16 * jb + l16;
-      const float rj = sRK[j], gj = sG[j];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * ib + 4 * g4 + ii;
-        sA[i * LDA + j] = i > j ? sB[i] * sRK[i] * rj * fast_exp(fminf(sG[i] - gj, 0.f)) * acc[ii] : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- T = (I + A)^-1 in place.  (a) diagonal 16x16 blocks, one lane per column
-  if (tid < CT * 16) {
-    const int b = tid >> 4, c = tid & 15;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float* arow = sA + (16 * b + r) * LDA + 16 * b;
-      float acc = r == c ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < r; ++j) acc = fmaf(-arow[j], x[j], acc);
-      x[r] = acc;
-    }
-    // every read of this block above precedes these writes in the wave's program order
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sA[(16 * b + r) * LDA + 16 * b + c] = x[r];
-  }
-  __syncthreads();
-  // (b) block rows: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.  The A blocks of the
-  // row are read into registers before any wave overwrites them with T.
-#pragma unroll
-  for (int bi = 1; bi < CT; ++bi) {
-    f32x4 a_row[CT];
-#pragma unroll
-    for (int bk = 0; bk < CT; ++bk)
-      if (bk < bi) a_row[bk] = lds_frag<float>(sA + (16 * bi + l16) * LDA + 16 * bk + 4 * g4);
-    __syncthreads();
-    for (int bj = wave; bj < bi; bj += WAVES) {
-      f32x4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int bk = 0; bk < CT; ++bk)
-        if (bk >= bj && bk < bi) {
-          f32x4 b;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) b[jj] = sA[(16 * bk + 4 * g4 + jj) * LDA + 16 * bj + l16];
-          mma_k16(X, a_row[bk], b);
-        }
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      mma_k16(Y, lds_frag<float>(sA + (16 * bi + l16) * LDA + 16 * bi + 4 * g4), X);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sA[(16 * bi + 4 * g4 + jj) * LDA + 16 * bj + l16] = -Y[jj];
-    }
-    __syncthreads();
-  }
-
-  // ---- T_W = T diag(b e^G r_k), T_U = T diag(b) in the operand type, zero above
-  // the diagonal blocks.  They may overlay T itself: all of T is read first.
-  {
-    constexpr int PER = (C * C / 4 + K::THREADS - 1) / K::THREADS;
-    FragT tw[PER], tu[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int e = tid + k * K::THREADS;
-      if (e < C * C / 4) {
-        const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
-        const bool keep = (c4 >> 4) <= (r >> 4);
-        const f32x4 t = keep ? *reinterpret_cast<const f32x4*>(sA + r * LDA + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float b = sB[c4 + i];
-          tw[k][i] = from_f32<Op>(t[i] * b * fast_exp(sG[c4 + i]) * sRK[c4 + i]);
-          tu[k][i] = from_f32<Op>(t[i] * b);
-        }
-      }
-    }
-    if (K::T_OVER_A) __syncthreads();
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int e = tid + k * K::THREADS;
-      if (e < C * C / 4) {
-        const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
-        *reinterpret_cast<FragT*>(sTW + r * LDT + c4) = tw[k];
-        *reinterpret_cast<FragT*>(sTU + r * LDT + c4) = tu[k];
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- this wave's d tiles: K and V column fragments, W^T, Ut and K'^T
-  {
-    FragT Kc[CT][DVT], Vc[CT][DVT];
-#pragma unroll
-    for (int kb = 0; kb < CT; ++kb)
-#pragma unroll
-      for (int j = 0; j < DVT; ++j) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        mma_k16(a, lds_frag<Op>(sK + (16 * kb + l16) * LDR + 16 * (wave * DVT + j) + 4 * g4), eye);
-        Kc[kb][j] = frag_from<Op>(a);
-        f32x4 b = {0.f, 0.f, 0.f, 0.f};
-        mma_k16(b, Va[kb][j], eye);
-        Vc[kb][j] = frag_from<Op>(b);
-      }
-    const int sp_w = wave;  // the pair of d tiles this wave owns (DVT == 2), or pair 0 (DVT == 1)
-#pragma unroll
-    for (int mt = 0; mt < CT; ++mt) {
-      f32x4 wacc[DVT];
-#pragma unroll
-      for (int j = 0; j < DVT; ++j) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
-        const Op* twrow = sTW + (16 * mt + l16) * LDT + 4 * g4;
-        const Op* turow = sTU + (16 * mt + l16) * LDT + 4 * g4;
-#pragma unroll
-        for (int s2 = 0; s2 < NPC; ++s2)
-          if (2 * s2 <= mt) {
-            const bool two = 2 * s2 + 1 < CT;
-            const FragT b0 = lds_frag<Op>(twrow + 32 * s2), b1 = two ? lds_frag<Op>(twrow + 32 * s2 + 16) : zf;
-            mma_k32(acc, Kc[2 * s2][j], two ? Kc[2 * s2 + 1][j] : zf, b0, b1);
-            const FragT a0 = lds_frag<Op>(turow + 32 * s2), a1 = two ? lds_frag<Op>(turow + 32 * s2 + 16) : zf;
-            mma_k32(uacc, a0, a1, Vc[2 * s2][j], two ? Vc[2 * s2 + 1][j] : zf);
-          }
-        wacc[j] = acc;
-        *at<FragT>(unit, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf) = frag_from<Op>(uacc);
-      }
-      store_pair<Op>(at<Op>(unit, K::W_OFF + (uint32_t)(mt * NPD + sp_w) * PB + lp), frag_from<Op>(wacc[0], -1.f),
-                     DVT == 2 ? frag_from<Op>(wacc[DVT - 1], -1.f) : zf);
-    }
-    const float g_n = sG[C - 1];
-#pragma unroll
-    for (int j = 0; j < DVT; ++j)
-#pragma unroll
-      for (int sp = 0; sp < NPC; ++sp) {
-        FragT lo, hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
-          lo[i] = from_f32<Op>(to_f32(Kc[2 * sp][j][i]) * fast_exp(g_n - sG[t0]) * sRK[t0]);
-          hi[i] = from_f32<Op>(2 * sp + 1 < CT ? to_f32(Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j][i]) *
-                                                     fast_exp(g_n - sG[t1 < C ? t1 : 0]) * sRK[t1 < C ? t1 : 0]
-                                               : 0.f);
-        }
-        store_pair<Op>(at<Op>(unit, K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), lo, hi);
-      }
-  }
-}
-
-// ----------------------------------------------------------------- state
-// One wave: the chain of one sequence's chunks for one V head and NTW 16-wide
-// tiles of d_v.  S^T[d_k][d_v-slice] lives in accumulators (lane: d_k rows
-// 4g..4g+3 of each 16-block, d_v column l16), which is also the B operand
-// layout for every product that contracts over d_k.  Per chunk:
-//   h = bf16(S^T) -> workspace;  U = Ut - W S^T -> workspace (over Ut);
-//   S^T <- e^{G_n} S^T + K'^T U.
-// The next chunk's operands are loaded right after this chunk consumed the
-// same registers.  Block order puts all tiles of one (sequence, head) on one
-// XCD, so W and K'^T are fetched into that XCD's L2 once.
-template <typename Op, int D, int C, int NTW>
-__global__ __launch_bounds__(64) void chunk_state_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
-    const int32_t* __restrict__ cstart, unsigned char* __restrict__ ws, float* __restrict__ state,
-    int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v) {
-  using K = Cfg<Op, D, C>;
-  using FragT = typename Frag<Op>::type;
-  constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, NTILE = NT / NTW;
-  constexpr uint32_t PB = K::PAIR * sizeof(Op);  // bytes per pair tile
-  const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3, tile = kq % NTILE;
-  const int64_t grp = (int64_t)(kq / NTILE) * 8 + xcd;
-  if (grp >= (int64_t)n_seq * h_v) return;
-  const int n = (int)(grp / h_v), h = (int)(grp % h_v);
-  const uint32_t lane = threadIdx.x, g4 = lane >> 4, l16 = lane & 15;
-  const int64_t lo = min((int64_t)cu[n], t_total);
-  const int64_t hi = min(max((int64_t)cu[n + 1], lo), t_total);
-  const int32_t slot = slots[n];
-  if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs (the output pass skips it)
-    const int64_t o_ld = (int64_t)h_v * D;
-    const int col0 = h * D + 16 * NTW * tile;
-    for (int64_t e = lane; e < (hi - lo) * 16 * NTW; e += 64)
-      o[(lo + e / (16 * NTW)) * o_ld + col0 + e % (16 * NTW)] = from_f32<Op>(0.f);
-    return;
-  }
-  const bool init = has_init == nullptr || has_init[n] != 0;
-  float* st_ptr = state + ((int64_t)slot * h_v + h) * D * D;
-
-  f32x4 Sacc[NT][NTW];
-#pragma unroll
-  for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int dv = 16 * (NTW * tile + j) + l16;
-      if (init) {
-        const float4 v = *reinterpret_cast<const float4*>(st_ptr + dv * D + 16 * mt + 4 * g4);
-        Sacc[mt][j] = f32x4{v.x, v.y, v.z, v.w};
-      } else {
-        Sacc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-
-  // lane-invariant byte offsets inside a unit
-  const uint32_t lp = lane * 8 * sizeof(Op);   // a lane's pair within a pair tile
-  const uint32_t lf = lane * 4 * sizeof(Op);   // a lane's fragment within a 16x16 tile
-  // Two register stages (A: even chunks, B: odd chunks), so every chunk's
-  // operands are requested two chunks before they are used.
-  Pair<Op> wnA[CT][NPD], ktA[NT][NPC], wnB[CT][NPD], ktB[NT][NPC];
-  FragT utA[CT][NTW], utB[CT][NTW];
-  float egnA = 0.f, egnB = 0.f;
-#define GDN_LOAD_WU(X, u)                                                                           \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                              \
-      wn##X[mt][sp].load(at<Op>((u), K::W_OFF + (mt * NPD + sp) * PB + lp));                        \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
-      ut##X[mt][j] = *at<FragT>((u), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf); \
-  }
-#define GDN_LOAD_KT(X, u)                                                                           \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                              \
-      kt##X[mt][sp].load(at<Op>((u), K::KT_OFF + (mt * NPC + sp) * PB + lp));                       \
-    egn##X = *at<float>((u), K::F_OFF);                                                             \
-  }
-  // h = S^T at the chunk start -> workspace;  U = Ut - W S^T
-#define GDN_PHASE_U(X, uc)                                                                          \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) Sf[mt][j] = frag_from<Op>(Sacc[mt][j]);         \
-    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                              \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
-      store_pair<Op>(at<Op>((uc), K::H_OFF + (uint32_t)(sp * NT + NTW * tile + j) * PB + lp), Sf[2 * sp][j], \
-                     2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);                                     \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
-      f32x4 acc;                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = to_f32(ut##X[mt][j][i]);               \
-      _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                            \
-        wn##X[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);            \
-      Uacc[mt][j] = acc;                                                                            \
-    }                                                                                               \
-  }
-  // U -> workspace over Ut (this wave's columns);  S^T <- e^{G_n} S^T + K'^T U
-#define GDN_PHASE_S(X, uc)                                                                          \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
-      Uf[mt][j] = frag_from<Op>(Uacc[mt][j]);                                                       \
-      *at<FragT>((uc), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = Uf[mt][j]; \
-    }                                                                                               \
-    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
-      f32x4 acc = Sacc[mt][j];                                                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] *= egn##X;                               \
-      _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                            \
-        kt##X[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);            \
-      Sacc[mt][j] = acc;                                                                            \
-    }                                                                                               \
-  }
-  const int32_t gc0 = cstart[n];
-  const int nch = (int)((hi - lo + C - 1) / C);
-  // unit of chunk k of this sequence, clamped to the last one: loads past the
-  // end re-read it, so every load is unconditional and the wait counts exact
-#define unit_of(k) (ws + ((int64_t)(gc0 + min((k), nch - 1)) * h_v + h) * K::UNIT)
-  const FragT zf = zero_frag<Op>();
-  FragT Sf[NT][NTW], Uf[CT][NTW];
-  f32x4 Uacc[CT][NTW];
-  if (nch > 0) {
-    GDN_LOAD_WU(A, unit_of(0));
-    GDN_LOAD_KT(A, unit_of(0));
-    GDN_LOAD_WU(B, unit_of(1));
-    GDN_LOAD_KT(B, unit_of(1));
-  }
-  for (int k = 0; k < nch; k += 2) {
-    {
-      unsigned char* uc = unit_of(k);
-      GDN_PHASE_U(A, uc);
-      __builtin_amdgcn_sched_barrier(0);
-      GDN_LOAD_WU(A, unit_of(k + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      GDN_PHASE_S(A, uc);
-      __builtin_amdgcn_sched_barrier(0);
-      GDN_LOAD_KT(A, unit_of(k + 2));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (k + 1 < nch) {
-      unsigned char* uc = unit_of(k + 1);
-      GDN_PHASE_U(B, uc);
-      GDN_PHASE_S(B, uc);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    GDN_LOAD_WU(B, unit_of(k + 3));
-    GDN_LOAD_KT(B, unit_of(k + 3));
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#undef GDN_LOAD_WU
-#undef GDN_LOAD_KT
-#undef GDN_PHASE_U
-#undef GDN_PHASE_S
-#undef unit_of
-
-#pragma unroll
-  for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int dv = 16 * (NTW * tile + j) + l16;
-      *reinterpret_cast<float4*>(st_ptr + dv * D + 16 * mt + 4 * g4) =
-          make_float4(Sacc[mt][j][0], Sacc[mt][j][1], Sacc[mt][j][2], Sacc[mt][j][3]);
-    }
-}
-
-// ------------------------------------------------------------------ output
-// Per (chunk, V head): O = diag(f_q) Q h^T + P U (the scale is in f_q and P); with z,
-// out = O / sqrt(mean_dv(O^2) + eps) * w * silu(z).  Wave w computes d_v
-// tiles w*DVT .. w*DVT+DVT-1 for all C rows with every operand load issued up
-// front; the fp32 tile then goes through LDS so the norm and the z / out
-// traffic run row-wise, 8 consecutive elements (16 bytes of bf16) per lane.
-template <typename T, typename Op, int D, int C>
-__global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
-    const T* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
-    const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws, int32_t n_slots, int32_t n_seq,
-    int64_t t_total, int32_t h_k, int32_t h_v, T* __restrict__ o, const T* __restrict__ z,
-    const T* __restrict__ norm_w, float norm_eps) {
-  static_assert(sizeof(T) == sizeof(Op), "raw q rows are MFMA operands");
-  using K = Cfg<Op, D, C>;
-  using FragT = typename Frag<Op>::type;
-  constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, DVT = K::DVT, LD_O = K::LD_O;
-  constexpr int LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
-  constexpr uint32_t PB = K::PAIR * sizeof(Op);
-  __shared__ __attribute__((aligned(16))) float sO[K::OUT_BYTES / 4];
-  const int gc = blockIdx.x / h_v;
-  const int h = blockIdx.x % h_v;
-  if (gc >= cstart[n_seq]) return;
-  const int n = seq_of_chunk(cstart, n_seq, gc);
-  if (!slot_ok(slots[n], n_slots)) return;  // the chain zeroed this sequence's outputs
-  const uint32_t tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-  const int64_t seq_lo = min((int64_t)cu[n], t_total);
-  const int64_t seq_hi = min(max((int64_t)cu[n + 1], seq_lo), t_total);
-  const int64_t c0 = seq_lo + (int64_t)(gc - cstart[n]) * C;
-  const int nvalid = (int)min((int64_t)C, seq_hi - c0);
-  const unsigned char* u = ws + ((int64_t)gc * h_v + h) * K::UNIT;
-  const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
-  const FragT zf = zero_frag<Op>();
-
-  // ---- all operand loads
-  // raw q rows of the chunk into LDS, 16-byte pieces
-  Op* sQ = reinterpret_cast<Op*>(sO);
-  {
-    const int hk = h / (h_v / h_k);
-    const int c_ch = 2 * h_k * D + h_v * D;
-    const int e0 = (tid % LPR) * 8;
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      const int r = (int)(tid / LPR) + k * RPP;
-      if (r < C) {
-        Raw8<T> q;
-        if (r < nvalid) q.load(qkv + (c0 + r) * c_ch + (int64_t)hk * D + e0);
-        else q.zero();
-        raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&q), sQ + r * K::LD_Q + e0);
-      }
-    }
-  }
-  Pair<Op> hp[NPD][DVT], pa[CT][NPC];
-  FragT Uf[CT][DVT];
-#pragma unroll
-  for (int sp = 0; sp < NPD; ++sp)
-#pragma unroll
-    for (int j = 0; j < DVT; ++j) hp[sp][j].load(at<Op>(u, K::H_OFF + (uint32_t)(sp * NT + wave * DVT + j) * PB + lp));
-  f32x4 fq[CT];
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt) fq[mt] = *at<f32x4>(u, K::FQ_OFF + 4 * (16 * mt + 4 * g4));
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-    for (int j = 0; j < DVT; ++j)
-      Uf[mt][j] = *at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf);
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-    for (int sp = 0; sp < NPC; ++sp)
-      if (2 * sp <= mt) pa[mt][sp].load(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
-
-  __syncthreads();
-
-  // ---- O = diag(f_q) Q h^T + P U
-  f32x4 Oacc[CT][DVT];
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-    for (int j = 0; j < DVT; ++j) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const Op* qrow = sQ + (16 * mt + l16) * K::LD_Q + 4 * g4;
-#pragma unroll
-      for (int sp = 0; sp < NPD; ++sp) {
-        FragT b0, b1;
-        hp[sp][j].split(b0, b1);
-        if (32 * sp + 16 < D) mma_k32(acc, lds_frag<Op>(qrow + 32 * sp), lds_frag<Op>(qrow + 32 * sp + 16), b0, b1);
-        else mma_k16(acc, lds_frag<Op>(qrow + 32 * sp), b0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= fq[mt][i];  // scale e^{G_t} r_q[t] on Q S^T only
-#pragma unroll
-      for (int sp = 0; sp < NPC; ++sp)
-        if (2 * sp <= mt) pa[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
-      Oacc[mt][j] = acc;
-    }
-  __syncthreads();  // q is read; the O tile goes over it
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-    for (int j = 0; j < DVT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sO[(16 * mt + 4 * g4 + i) * LD_O + 16 * (wave * DVT + j) + l16] = Oacc[mt][j][i];
-  __syncthreads();
-
-  // ---- row-wise: gated RMSNorm and 16-byte stores
-  const int64_t o_ld = (int64_t)h_v * D;
-  const int e0 = (tid % LPR) * 8;
-  float w[8];
-  if (z) load8(norm_w + e0, w);
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const int r = (int)(tid / LPR) + k * RPP;
-    if (r >= C) break;  // uniform over the LPR lanes of a row
-    float v[8];
-    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(sO + r * LD_O + e0);
-    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(sO + r * LD_O + e0 + 4);
-    const bool live = r < nvalid;
-    const int64_t off = (c0 + r) * o_ld + h * D + e0;
-    if (z) {
-      float zz[8];
-      if (live) load8(z + off, zz);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zz[e] = 0.f;
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-      ss = group_sum<LPR>(ss);
-      const float rstd = fast_rsq(ss * (1.0f / D) + norm_eps);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = v[e] * rstd * w[e] * fast_silu(zz[e]);
-    }
-    if (live) store8(o + off, v);
-  }
-}
-
-// Tiles of d_v per wave: one for a single long sequence is the most
-// parallel chain.
-template <typename Op, int D>
-constexpr int kTileW = 1;
-
-// workspace: [chunk index][units]
-inline size_t idx_bytes(int32_t n_seq) { return (((size_t)n_seq + 1) * 4 + 255) / 256 * 256; }
-
-template <typename T, typename Op, int D, int C>
-size_t ws_bytes(int32_t n_seq, int64_t t_total, int32_t h_v) {
-  using K = Cfg<Op, D, C>;
-  const int64_t max_chunks = t_total / C + n_seq;
-  return idx_bytes(n_seq) + (size_t)max_chunks * h_v * K::UNIT;
-}
-
-template <typename T, typename Op, int D, int C>
-hipError_t run(const ChunkArgs& a, hipStream_t st) {
-  using K = Cfg<Op, D, C>;
-  static_assert(sizeof(T) == sizeof(Op), "the chain writes O in the activation type");
-  static_assert(K::PREP_BYTES <= 160 * 1024, "LDS budget");
-  constexpr int NTW = kTileW<Op, D>, NTILE = K::NT / NTW;
-  if (a.n_seq == 0) return hipSuccess;
-  int32_t* cstart = reinterpret_cast<int32_t*>(a.workspace);
-  unsigned char* units = reinterpret_cast<unsigned char*>(a.workspace) + idx_bytes(a.n_seq);
-  hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seq, a.t_total, (int32_t)C,
-                     cstart);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  const int64_t max_chunks = a.t_total / C + a.n_seq;
-  if (max_chunks > 0) {
-    hipLaunchKernelGGL((chunk_prep_kernel<T, Op, D, C>), dim3((unsigned)(max_chunks * a.s.h_v)), dim3(K::THREADS), 0,
-                       st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, cstart, a.n_slots, a.n_seq, a.t_total,
-                       a.s.h_k, a.s.h_v, a.scale, units);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  }
-  const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
-  hipLaunchKernelGGL((chunk_state_kernel<Op, D, C, NTW>), dim3((unsigned)(groups * NTILE)), dim3(64), 0, st,
-                     a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state, a.n_slots, (Op*)a.o, a.t_total,
-                     a.n_seq, a.s.h_v);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  if (max_chunks > 0)
-    hipLaunchKernelGGL((chunk_out_kernel<T, Op, D, C>), dim3((unsigned)(max_chunks * a.s.h_v)), dim3(K::THREADS), 0,
-                       st, (const T*)a.qkv, a.cu_seqlens, a.slots, cstart, units, a.n_slots, a.n_seq, a.t_total,
-                       a.s.h_k, a.s.h_v, (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.norm_eps);
-  return hipGetLastError();
-}
 
 template <typename T, typename Op, int D>
 hipError_t by_chunk(const ChunkArgs& a, hipStream_t st) {

@@ -148,6 +148,45 @@ int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t 
   return from_hip(gdn::launch_chunk_prefill(a, (hipStream_t)stream));
 }
 
+size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk) {
+  Shape s;
+  if (check_dims(dims, &s) != GDN_OK || check_act(act) != GDN_OK || n_seq < 0 || t_total < 0) return 0;
+  return gdn::chunk_split_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
+}
+
+int gdn_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk, float scale,
+                const void* x, const void* conv_w, const void* conv_b, const void* a, const void* b,
+                const float* A_log, const float* dt_bias, const int32_t* cu_seqlens, const int32_t* slots,
+                const uint8_t* has_init, void* conv_state, float* state, int32_t n_slots, void* o, const void* z,
+                const void* norm_w, float norm_eps, void* workspace, size_t ws_bytes, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq == 0 && t_total > 0) return GDN_ERR_SHAPE;
+  if (!gdn::chunk_supported(s.d, chunk, act == GDN_BF16)) return GDN_ERR_UNSUPPORTED;
+  if (n_seq == 0) return GDN_OK;
+  GDN_TRY(need(cu_seqlens, slots, state, conv_state, conv_w));
+  if (t_total > 0) GDN_TRY(need(x, a, b, A_log, dt_bias, o));
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+  GDN_TRY(align_ok(x, conv_w, conv_b, conv_state, state, o, z, workspace));
+  const size_t need_ws = gdn::chunk_split_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
+  if (!workspace || ws_bytes < need_ws) return GDN_ERR_WORKSPACE;
+  gdn::ChunkArgs args{s,     act == GDN_BF16, n_seq,  t_total, chunk,  scale,    nullptr,  nullptr,   nullptr,
+                      cu_seqlens, slots, has_init, state,  n_slots, o,      z,        norm_w,   norm_eps,
+                      workspace, ws_bytes};
+  args.x = x;
+  args.conv_w = conv_w;
+  args.conv_b = conv_b;
+  args.conv_state = conv_state;
+  args.a_in = a;
+  args.b_in = b;
+  args.A_log = A_log;
+  args.dt_bias = dt_bias;
+  return from_hip(gdn::launch_prefill_fused(args, (hipStream_t)stream));
+}
+
 int gdn_recurrent_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step, float scale,
                          const void* qkv, const void* a, const void* b, const float* A_log, const float* dt_bias,
                          float* state, int32_t n_slots, const int32_t* slots, const int32_t* out_slots, void* o,

@@ -30,6 +30,9 @@ struct ConvFwdArgs {
   void* y;
 };
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t st);
+// Only the final-window write of launch_conv1d_fwd (y unused): the fused
+// prefill runs it after every kernel that reads the old conv state.
+hipError_t launch_conv1d_store_state(const ConvFwdArgs& a, hipStream_t st);
 
 struct ConvUpdateArgs {
   Shape s;
@@ -113,6 +116,16 @@ struct ChunkArgs {
   float norm_eps;
   void* workspace;
   size_t ws_bytes;
+  // Fused-input mode (x != nullptr): q, k, v are conv1d + SiLU of x, computed
+  // in the chunk kernels (qkv unused), and g, beta come from a, b (g, beta unused).
+  const void* x = nullptr;
+  const void* conv_w = nullptr;
+  const void* conv_b = nullptr;
+  const void* conv_state = nullptr;
+  const void* a_in = nullptr;
+  const void* b_in = nullptr;
+  const float* A_log = nullptr;
+  const float* dt_bias = nullptr;
 };
 // True when the chunk kernels have an instantiation for (d, chunk, dtype).
 bool chunk_supported(int d, int chunk, bool bf16);
@@ -124,5 +137,8 @@ hipError_t launch_chunk_prefill(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t st);
 size_t chunk_split_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk);
 hipError_t launch_chunk_split(const ChunkArgs& a, hipStream_t st);
+// The fused-input prefill on the split path (a.x != nullptr); the caller runs
+// launch_conv1d_store_state afterwards.
+hipError_t launch_prefill_fused(const ChunkArgs& a, hipStream_t st);
 
 }  // namespace gdn

@@ -152,6 +152,30 @@ int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t 
                       void* stream);
 
 /*
+ * gdn_prefill -- the whole prefill path in one call: conv1d + SiLU (as
+ * gdn_conv1d_fwd), gating (as gdn_gating) and the chunked rule with its
+ * epilogue (as gdn_chunk_prefill), with the conv output and the gates
+ * computed inside the chunk kernels instead of round-tripping through device
+ * memory (the fusion of the causal convolution into the chunked GDN operation
+ * that LightLLM #1097 lists among its specialized kernels).  Results equal
+ * those three calls in sequence; conv_state and state are updated in place
+ * the same way.
+ *   x        act [t_total][c_ch]   conv input;  conv_w act [c_ch][conv_w];  conv_b act [c_ch] or NULL
+ *   a, b     act [t_total][h_v];   A_log, dt_bias float [h_v]
+ *   conv_state act [n_slots][c_ch][conv_w-1];  state float [n_slots][h_v][d_v][d_k]
+ *   o, z, norm_w, norm_eps, scale, chunk: as in gdn_chunk_prefill
+ *   workspace  at least gdn_prefill_workspace_size() bytes (never NULL when t_total > 0)
+ * Supported as gdn_chunk_prefill (d, chunk, dtype) with conv_w in {2, 3, 4};
+ * always runs the chunk-parallel path.
+ */
+size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk);
+int gdn_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk, float scale,
+                const void* x, const void* conv_w, const void* conv_b, const void* a, const void* b,
+                const float* A_log, const float* dt_bias, const int32_t* cu_seqlens, const int32_t* slots,
+                const uint8_t* has_init, void* conv_state, float* state, int32_t n_slots, void* o, const void* z,
+                const void* norm_w, float norm_eps, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * gdn_recurrent_decode -- the fused recurrent step for decode (t_step = 1)
  * and MTP draft tokens (t_step > 1): gating, q/k L2 norm, the token-wise
  * recurrence and the gated-RMSNorm epilogue in one pass that reads each

@@ -147,6 +147,13 @@ class DevPrefill:
                                             chunk or c.chunk, scale, self.z if epilogue else None, self.norm_w)
         return out, y, g, beta
 
+    def run_fused(self, chunk=None, scale=1.0, epilogue=True):
+        """The same path through the single gdn_prefill call."""
+        c = self.case
+        return gdn.prefill(self.dims, self.x, self.conv_w, self.a, self.b, self.A_log, self.dt_bias, self.cu,
+                           self.slots, self.conv_pool, self.ssm_pool, self.has_init, chunk or c.chunk, scale,
+                           self.z if epilogue else None, self.norm_w)
+
 
 # The two activation-precision perturbations the tolerance rule measures.
 PERTURBATIONS = (dict(perturb=gi.round_bf16), dict(perturb=gi.round_bf16, perturb_qk=gi.round_bf16))

@@ -38,7 +38,7 @@ FAKE = 0x1000  # a 16-byte-aligned non-null address: every call below must fail 
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
         assert n in binding.SIGNATURES, n
@@ -111,6 +111,31 @@ def test_chunk_prefill_workspace(L):
     assert chunk_call(L, t_total=4096) == WS
     assert chunk_call(L, t_total=4096, ws=FAKE, ws_bytes=ws - 1) == WS
     assert L.gdn_chunk_prefill_workspace_size(None, 0, 1, 4096, 64) == 0
+
+
+def prefill_call(L, dims=None, act=0, n_seq=1, t_total=64, chunk=64, x=FAKE, a=FAKE, conv_state=FAKE, z=None,
+                 norm_w=None, eps=1e-6, ws=None, ws_bytes=0):
+    return L.gdn_prefill(dims or D(), act, n_seq, t_total, chunk, 1.0, x, FAKE, None, a, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, None, conv_state, FAKE, 4, FAKE + 16, z, norm_w, eps, ws, ws_bytes, None)
+
+
+def test_prefill_errors_and_workspace(L):
+    assert prefill_call(L, chunk=48) == UNSUP
+    assert prefill_call(L, act=1, chunk=64) == UNSUP          # fp32 at d=128 takes chunk <= 32
+    assert prefill_call(L, z=FAKE) == NULL                     # z without norm_w
+    assert prefill_call(L, eps=-1.0) == SHAPE
+    assert prefill_call(L, x=None) == NULL
+    assert prefill_call(L, a=None) == NULL
+    assert prefill_call(L, conv_state=None) == NULL
+    assert prefill_call(L, x=FAKE + 8) == ALIGN
+    assert prefill_call(L, n_seq=0, t_total=5) == SHAPE
+    assert prefill_call(L, n_seq=0, t_total=0) == OK
+    # the same workspace as the split chunked path, whatever path gdn_chunk_prefill takes
+    ws = L.gdn_prefill_workspace_size(D(), 0, 1, 4096, 64)
+    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 255) // 256 * 256
+    assert ws == 256 + (4096 // 64 + 1) * 32 * unit
+    assert prefill_call(L, t_total=4096) == WS                # (these stop at validation, never launch)
+    assert prefill_call(L, t_total=4096, ws=FAKE, ws_bytes=ws - 1) == WS
 
 
 def test_recurrent_and_copy_errors(L):
