@@ -571,45 +571,52 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         store_pair<Op>(at<Op>(unit, K::P_OFF + (uint32_t)(ib * NPC + sp) * PB + lp), half[0], half[1]);
       }
     }
-    // A tiles (ib, jb), jb <= ib, enumerated from the last block row down so
-    // the waves with the fewest P tiles take the longest rows first
-    constexpr int N_A = CT * (CT + 1) / 2;
-    for (int it = WAVES - 1 - wave; it < N_A; it += WAVES) {
-      int ib = CT - 1, rest = it;
-      while (rest >= ib + 1) { rest -= ib + 1; --ib; }
-      const int jb = rest;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const Op* arow = sK + (16 * ib + l16) * LDR + 4 * g4;
-      const Op* brow = sK + (16 * jb + l16) * LDR + 4 * g4;
+    // A tiles (ib, jb), jb <= ib: block row ib (ib + 1 tiles) goes to wave
+    // CT - 1 - ib (mod WAVES), so with CT == WAVES every wave has CT + 1 tiles
+    // in all (w + 1 P tiles and CT - w A tiles)
+    for (int ib = CT - 1 - (int)wave; ib >= 0; ib -= WAVES)
 #pragma unroll
-      for (int s2 = 0; s2 < NPD; ++s2) {
-        if (32 * s2 + 16 < D)
-          mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
-                  lds_frag<Op>(brow + 32 * s2 + 16));
-        else
-          mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
-      }
-      const int j = 16 * jb + l16;
-      const float rj = sRK[j], gj = sG[j];
+      for (int jb = 0; jb < CT; ++jb) {
+        if (jb > ib) break;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const Op* arow = sK + (16 * ib + l16) * LDR + 4 * g4;
+        const Op* brow = sK + (16 * jb + l16) * LDR + 4 * g4;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * ib + 4 * g4 + ii;
-        sA[i * LDA + j] = i > j ? sB[i] * sRK[i] * rj * fast_exp(fminf(sG[i] - gj, 0.f)) * acc[ii] : 0.f;
+        for (int s2 = 0; s2 < NPD; ++s2) {
+          if (32 * s2 + 16 < D)
+            mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), lds_frag<Op>(brow + 32 * s2),
+                    lds_frag<Op>(brow + 32 * s2 + 16));
+          else
+            mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
+        }
+        const int j = 16 * jb + l16;
+        const float rj = sRK[j], gj = sG[j];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * ib + 4 * g4 + ii;
+          sA[i * LDA + j] = i > j ? sB[i] * sRK[i] * rj * fast_exp(fminf(sG[i] - gj, 0.f)) * acc[ii] : 0.f;
+        }
       }
-    }
   }
   __syncthreads();
 
   // ---- T = (I + A)^-1 in place.  (a) diagonal 16x16 blocks, one lane per column
   if (tid < CT * 16) {
     const int b = tid >> 4, c = tid & 15;
+    // the block's rows into registers first, so the substitution chain runs
+    // on registers (16-byte reads; the upper triangle is read but unused)
+    float blk[16][16];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (4 * q < r) *reinterpret_cast<f32x4*>(&blk[r][4 * q]) = *reinterpret_cast<const f32x4*>(sA + (16 * b + r) * LDA + 16 * b + 4 * q);
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float* arow = sA + (16 * b + r) * LDA + 16 * b;
       float acc = r == c ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < r; ++j) acc = fmaf(-arow[j], x[j], acc);
+      for (int j = 0; j < r; ++j) acc = fmaf(-blk[r][j], x[j], acc);
       x[r] = acc;
     }
     // every read of this block above precedes these writes in the wave's program order
