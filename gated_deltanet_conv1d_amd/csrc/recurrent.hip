@@ -37,23 +37,46 @@ struct RowLayout {
   __device__ static int col(int j, int c) { return j * 16 * VW + VW * c; }
 };
 
-template <int VW>
+// In-place decode reads and writes each state once, so those accesses are
+// nontemporal: on gfx950 these streams reach the HBM rate that plain accesses
+// to scattered slots do not.  The MTP step (per-position states written token
+// after token) measures faster with plain accesses throughout.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <int VW, bool NT = true>
 __device__ __forceinline__ void ld_f32(const float* p, float* v) {
-  if constexpr (VW == 4) {
-    float4 a = *reinterpret_cast<const float4*>(p);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  if constexpr (!NT) {
+    if constexpr (VW == 4) {
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    } else if constexpr (VW == 2) {
+      const float2 a = *reinterpret_cast<const float2*>(p);
+      v[0] = a.x; v[1] = a.y;
+    } else {
+      v[0] = *p;
+    }
+  } else if constexpr (VW == 4) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
   } else if constexpr (VW == 2) {
-    float2 a = *reinterpret_cast<const float2*>(p);
-    v[0] = a.x; v[1] = a.y;
+    const f32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x2_t*>(p));
+    v[0] = a[0]; v[1] = a[1];
   } else {
-    v[0] = *p;
+    v[0] = __builtin_nontemporal_load(p);
   }
 }
-template <int VW>
+template <int VW, bool NT = true>
 __device__ __forceinline__ void st_f32(float* p, const float* v) {
-  if constexpr (VW == 4) *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  else if constexpr (VW == 2) *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
-  else *p = v[0];
+  if constexpr (!NT) {
+    if constexpr (VW == 4) *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    else if constexpr (VW == 2) *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    else *p = v[0];
+  } else if constexpr (VW == 4) {
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
+  } else if constexpr (VW == 2) {
+    __builtin_nontemporal_store(f32x2_t{v[0], v[1]}, reinterpret_cast<f32x2_t*>(p));
+  } else {
+    __builtin_nontemporal_store(v[0], p);
+  }
 }
 template <int VW, typename T>
 __device__ __forceinline__ void ld_act(const T* p, float* v) {
@@ -61,7 +84,7 @@ __device__ __forceinline__ void ld_act(const T* p, float* v) {
   for (int i = 0; i < VW; ++i) v[i] = to_f32(p[i]);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool MTP>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     const T* __restrict__ qkv, const T* __restrict__ a_in, const T* __restrict__ b_in,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, float* __restrict__ state, int32_t n_slots,
@@ -93,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 #pragma unroll
   for (int p = 0; p < PASSES; ++p)
 #pragma unroll
-    for (int j = 0; j < NG; ++j) ld_f32<VW>(src + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+    for (int j = 0; j < NG; ++j) ld_f32<VW, !MTP>(src + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
 
   const float neg_A = -expf(A_log[h]);
   const float dtb = dt_bias[h];
@@ -181,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 #pragma unroll
         for (int p = 0; p < PASSES; ++p)
 #pragma unroll
-          for (int j = 0; j < NG; ++j) st_f32<VW>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+          for (int j = 0; j < NG; ++j) st_f32<VW, false>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
       }
     }
   }
@@ -191,18 +214,23 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
 #pragma unroll
-      for (int j = 0; j < NG; ++j) st_f32<VW>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+      for (int j = 0; j < NG; ++j) st_f32<VW, !MTP>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
   }
 }
 
-template <typename T, int D>
-hipError_t impl(const RecurrentArgs& a, hipStream_t st) {
+template <typename T, int D, bool MTP>
+hipError_t impl_mode(const RecurrentArgs& a, hipStream_t st) {
   if (a.n_seq == 0 || a.t_step == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_kernel<T, D>), dim3((unsigned)((int64_t)a.n_seq * a.s.h_v)), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((recurrent_kernel<T, D, MTP>), dim3((unsigned)((int64_t)a.n_seq * a.s.h_v)), dim3(kThreads), 0, st,
                      (const T*)a.qkv, (const T*)a.a, (const T*)a.b, a.A_log, a.dt_bias, a.state, a.n_slots, a.slots,
                      a.out_slots, (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step,
                      a.s.h_k, a.s.h_v);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t impl(const RecurrentArgs& a, hipStream_t st) {
+  return a.out_slots ? impl_mode<T, D, true>(a, st) : impl_mode<T, D, false>(a, st);
 }
 
 }  // namespace

@@ -10,7 +10,8 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kIter = 8;                                     // 16-byte vectors per thread per piece
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kIter = 4;                                     // 16-byte vectors per thread per piece
 constexpr int64_t kPiece = (int64_t)kThreads * kIter * 16;  // bytes per block
 
 // grid: n pairs x (state pieces + conv pieces)
@@ -37,16 +38,18 @@ __global__ __launch_bounds__(kThreads) void state_copy_kernel(
     off = (int64_t)(piece - state_pieces) * kPiece;
     bytes = conv_bytes;
   }
-  uint4 v[kIter];
+  // nontemporal: every byte is read once and written once; on gfx950 this
+  // copy of scattered 2 MiB slots runs ~1.4x faster than with plain accesses
+  u32x4 v[kIter];
 #pragma unroll
   for (int k = 0; k < kIter; ++k) {
     const int64_t o = off + ((int64_t)k * kThreads + threadIdx.x) * 16;
-    if (o < bytes) v[k] = *reinterpret_cast<const uint4*>(from + o);
+    if (o < bytes) v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(from + o));
   }
 #pragma unroll
   for (int k = 0; k < kIter; ++k) {
     const int64_t o = off + ((int64_t)k * kThreads + threadIdx.x) * 16;
-    if (o < bytes) *reinterpret_cast<uint4*>(to + o) = v[k];
+    if (o < bytes) __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(to + o));
   }
 }
 
