@@ -164,6 +164,41 @@ __device__ __forceinline__ typename Frag<Op>::type frag_mul(const typename Frag<
   for (int i = 0; i < 4; ++i) r[i] = from_f32<Op>(to_f32(a[i]) * f);
   return r;
 }
+// Nontemporal vector access for the output pass's single-use streams (its
+// workspace reads, z, the output rows).  Workspace writes stay plain: the
+// next pass reads them back, and at single-sequence sizes the whole
+// workspace stays in the 256 MiB memory-side cache, which the latency-bound
+// chain depends on (nontemporal workspace writes slowed it by 15%).
+template <typename V>
+__device__ __forceinline__ V nt_ld(const V* p) { return __builtin_nontemporal_load(p); }
+template <typename V>
+__device__ __forceinline__ void nt_st(const V& v, V* p) { __builtin_nontemporal_store(v, p); }
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// 8 consecutive activations, nontemporal (as load8 / store8)
+__device__ __forceinline__ void load8_nt(const bf16* p, float* v) {
+  const u32x4_t u = nt_ld(reinterpret_cast<const u32x4_t*>(p));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8_nt(const float* p, float* v) {
+  const f32x4 a = nt_ld(reinterpret_cast<const f32x4*>(p)), b = nt_ld(reinterpret_cast<const f32x4*>(p) + 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+__device__ __forceinline__ void store8_nt(bf16* p, const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = from_f32<bf16>(v[i]);
+  nt_st(o, reinterpret_cast<bf16x8*>(p));
+}
+__device__ __forceinline__ void store8_nt(float* p, const float* v) {
+  nt_st(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
+  nt_st(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(p) + 1);
+}
+
 template <typename Op>
 __device__ __forceinline__ void store_pair(Op* dst, const typename Frag<Op>::type& lo,
                                            const typename Frag<Op>::type& hi);
@@ -183,6 +218,7 @@ template <typename Op> struct Pair;
 template <> struct Pair<bf16> {
   bf16x8 v;
   __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void load_nt(const bf16* p) { v = nt_ld(reinterpret_cast<const bf16x8*>(p)); }
   __device__ __forceinline__ void split(bf16x4& a, bf16x4& b) const {
     a = bf16x4{v[0], v[1], v[2], v[3]};
     b = bf16x4{v[4], v[5], v[6], v[7]};
@@ -197,6 +233,10 @@ template <> struct Pair<float> {
   __device__ __forceinline__ void load(const float* p) {
     lo = reinterpret_cast<const f32x4*>(p)[0];
     hi = reinterpret_cast<const f32x4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    lo = nt_ld(reinterpret_cast<const f32x4*>(p));
+    hi = nt_ld(reinterpret_cast<const f32x4*>(p) + 1);
   }
   __device__ __forceinline__ void split(f32x4& a, f32x4& b) const {
     a = lo;
@@ -968,7 +1008,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
 #pragma unroll
   for (int sp = 0; sp < NPD; ++sp)
 #pragma unroll
-    for (int j = 0; j < DVT; ++j) hp[sp][j].load(at<Op>(u, K::H_OFF + (uint32_t)(sp * NT + wave * DVT + j) * PB + lp));
+    for (int j = 0; j < DVT; ++j) hp[sp][j].load_nt(at<Op>(u, K::H_OFF + (uint32_t)(sp * NT + wave * DVT + j) * PB + lp));
   f32x4 fq[CT];
 #pragma unroll
   for (int mt = 0; mt < CT; ++mt) fq[mt] = *at<f32x4>(u, K::FQ_OFF + 4 * (16 * mt + 4 * g4));
@@ -976,12 +1016,12 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
   for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
     for (int j = 0; j < DVT; ++j)
-      Uf[mt][j] = *at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf);
+      Uf[mt][j] = nt_ld(at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf));
 #pragma unroll
   for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
     for (int sp = 0; sp < NPC; ++sp)
-      if (2 * sp <= mt) pa[mt][sp].load(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
+      if (2 * sp <= mt) pa[mt][sp].load_nt(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
 
   __syncthreads();
 
@@ -1032,7 +1072,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
     const int64_t off = (c0 + r) * o_ld + h * D + e0;
     if (z) {
       float zz[8];
-      if (live) load8(z + off, zz);
+      if (live) load8_nt(z + off, zz);
       else
 #pragma unroll
         for (int e = 0; e < 8; ++e) zz[e] = 0.f;
@@ -1044,7 +1084,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = v[e] * rstd * w[e] * fast_silu(zz[e]);
     }
-    if (live) store8(o + off, v);
+    if (live) store8_nt(o + off, v);
   }
 }
 
