@@ -169,36 +169,6 @@ __device__ __forceinline__ typename Frag<Op>::type frag_mul(const typename Frag<
 // next pass reads them back, and at single-sequence sizes the whole
 // workspace stays in the 256 MiB memory-side cache, which the latency-bound
 // chain depends on (nontemporal workspace writes slowed it by 15%).
-template <typename V>
-__device__ __forceinline__ V nt_ld(const V* p) { return __builtin_nontemporal_load(p); }
-template <typename V>
-__device__ __forceinline__ void nt_st(const V& v, V* p) { __builtin_nontemporal_store(v, p); }
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-// 8 consecutive activations, nontemporal (as load8 / store8)
-__device__ __forceinline__ void load8_nt(const bf16* p, float* v) {
-  const u32x4_t u = nt_ld(reinterpret_cast<const u32x4_t*>(p));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(u[i] << 16);
-    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void load8_nt(const float* p, float* v) {
-  const f32x4 a = nt_ld(reinterpret_cast<const f32x4*>(p)), b = nt_ld(reinterpret_cast<const f32x4*>(p) + 1);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
-}
-__device__ __forceinline__ void store8_nt(bf16* p, const float* v) {
-  bf16x8 o;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = from_f32<bf16>(v[i]);
-  nt_st(o, reinterpret_cast<bf16x8*>(p));
-}
-__device__ __forceinline__ void store8_nt(float* p, const float* v) {
-  nt_st(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
-  nt_st(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(p) + 1);
-}
-
 template <typename Op>
 __device__ __forceinline__ void store_pair(Op* dst, const typename Frag<Op>::type& lo,
                                            const typename Frag<Op>::type& hi);

@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVec = 8;  // channels per thread
+constexpr int kTile = 16;  // tokens per block on the fast path
 
 template <typename T, int W>
 struct Taps {
@@ -72,6 +73,31 @@ __global__ __launch_bounds__(kThreads) void conv1d_fwd_kernel(
   taps.load(wt, bias, c0);
 
   int32_t n = find_seq(cu, n_seq, t0);
+  // Fast path: a full tile inside one sequence, past its first W-1 tokens.
+  // All TILE + W - 1 row loads are issued before any use, so they overlap
+  // instead of costing one memory latency per token.
+  if (tile == kTile) {
+    const int64_t lo = min((int64_t)cu[n], t_total);
+    const int64_t hi = min(max((int64_t)cu[n + 1], lo), t_total);
+    if (t0 - (W - 1) >= lo && t0 + kTile <= hi && slot_ok(slots[n], n_slots)) {
+      float rows[kTile + W - 1][kVec];
+#pragma unroll
+      for (int k = 0; k < kTile + W - 1; ++k) load8(x + (t0 - (W - 1) + k) * c_ch + c0, rows[k]);
+#pragma unroll
+      for (int k = 0; k < kTile; ++k) {
+        float out[kVec];
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          float acc = taps.b[i];
+#pragma unroll
+          for (int j = 0; j < W; ++j) acc = fmaf(taps.w[j][i], rows[k + j][i], acc);
+          out[i] = fast_silu(acc);
+        }
+        store8(y + (t0 + k) * c_ch + c0, out);
+      }
+      return;
+    }
+  }
   int64_t t = t0;
   while (t < t1 && n < n_seq) {
     const int64_t lo = min((int64_t)cu[n], t_total);
@@ -215,8 +241,9 @@ hipError_t fwd_impl(const ConvFwdArgs& a, hipStream_t st) {
   const int n_cblk = (c_ch / kVec + kThreads - 1) / kThreads;
   if (a.t_total > 0 && a.n_seq > 0) {
     // aim for >= ~2048 blocks on 256 CUs; halo overhead is (W-1)/tile
-    int64_t tile = a.t_total * n_cblk / 2048;
-    tile = tile < 16 ? 16 : (tile > 64 ? 64 : tile);
+    // fixed 16-token tiles (the fast path's size): >= 1024 blocks from 4096
+    // tokens up, halo overhead (W-1)/16
+    const int64_t tile = kTile;
     const int64_t n_tiles = (a.t_total + tile - 1) / tile;
     hipLaunchKernelGGL((conv1d_fwd_kernel<T, W>), dim3((unsigned)(n_tiles * n_cblk)), dim3(kThreads), 0, st,
                        (const T*)a.x, (const T*)a.w, (const T*)a.bias, a.cu_seqlens, a.slots, a.has_init,
