@@ -473,7 +473,9 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       Op* const dst[3] = {sK, sQf, sVf};
       stage_conv<T, Op, D, C, W, 3, 16, K::THREADS>(ci, c_ch, cols, c0, nvalid, dst, LDR, tid);
     }
-    if (wave == 0) {  // gates: g, beta from a, b (as the gating kernel), then G = cumsum g
+    // gates: g, beta from a, b (as the gating kernel), then G = cumsum g; on
+    // the last wave, which has the fewest conv items
+    if (wave == WAVES - 1) {
       float gv = 0.f, bv = 0.f;
       if (lane < nvalid) {
         const int64_t i = (c0 + lane) * h_v + h;
