@@ -25,8 +25,9 @@
 // so every load is a 16- or 8-byte lane-contiguous vector.
 //
 //   chunk_index_kernel  first global chunk of every sequence (block scan)
-//   chunk_prep_kernel   per (chunk, V head): q/k L2 norm, gates, Gram, T and
-//                       the operand fragments above
+//   chunk_prep_kernel   per (chunk, V head, or both V heads of a QK head when
+//                       h_v = 2 h_k): q/k L2 norm, gates, Gram, T and the
+//                       operand fragments above
 //   chunk_state_kernel  per (sequence, V head, d_v tile): the chunk loop
 //   chunk_out_kernel    per (chunk, V head): O, gated RMSNorm over d_v, store
 #pragma once
@@ -72,24 +73,6 @@ struct Cfg {
   static constexpr int LDR = D + 16;   // raw k rows (elements)
   static constexpr int LDA = C + 16;   // fp32 A, then T in place
   static constexpr int LDT = C + 8;    // T diag(b e^G r_k) and T diag(b), operand type
-  static constexpr int PK = 0;
-  static constexpr int PA = PK + C * LDR * (int)sizeof(Op);
-  static constexpr int PS = PA + C * LDA * 4;                      // G, b, r_k
-  static constexpr bool T_OVER_A = 2 * LDT * (int)sizeof(Op) <= LDA * 4;  // the T copies fit over A
-  static constexpr int PTW = T_OVER_A ? PA : PS + 3 * C * 4;
-  static constexpr int PTU = PTW + C * LDT * (int)sizeof(Op);
-  static constexpr int PREP_BYTES = T_OVER_A ? PS + 3 * C * 4 : PTU + C * LDT * (int)sizeof(Op);
-  // fused-input prep: conv'd k, q, v rows; the A/T tile (and the T copies)
-  // later overlay the q and v rows, which are read into registers first
-  static constexpr int FK = 0;
-  static constexpr int FQ = FK + C * LDR * (int)sizeof(Op);
-  static constexpr int FV = FQ + C * LDR * (int)sizeof(Op);
-  static constexpr int FA = FQ;
-  static constexpr int FS_ = FV + C * LDR * (int)sizeof(Op);
-  static constexpr int FS = FS_ > FA + C * LDA * 4 ? FS_ : FA + C * LDA * 4;
-  static constexpr int FTW = T_OVER_A ? FA : FS + 3 * C * 4;
-  static constexpr int FTU = FTW + C * LDT * (int)sizeof(Op);
-  static constexpr int PREP_FUSED_BYTES = T_OVER_A ? FS + 3 * C * 4 : FTU + C * LDT * (int)sizeof(Op);
 };
 
 __device__ __forceinline__ int32_t seq_of_chunk(const int32_t* __restrict__ cstart, int32_t n_seq, int32_t gc) {
@@ -331,18 +314,6 @@ __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int
   }
 }
 
-// Per (chunk, V head).  Everything runs on the raw q, k, v of the chunk; the
-// L2 norms enter as per-token factors r = 1/sqrt(|x|^2 + 1e-6):
-//   A_ij  = b_i r_k[i] r_k[j] e^{G_i-G_j} (k_i.k_j), i > j;   T = (I + A)^{-1}
-//   P_ij  = scale r_q[i] r_k[j] e^{G_i-G_j} (q_i.k_j), i >= j
-//   W     = T diag(b e^G r_k) K,   Ut = T diag(b) V,   K' = diag(e^{G_n-G} r_k) K
-// and f_q = scale e^G r_q, which the output pass applies to Q S^T.
-// No fragment is ever read down an LDS column.  P is formed as P^T = K Q^T,
-// whose accumulator layout is P's A-fragment layout; W is formed as
-// W^T = K^T (T diag(..))^T, whose accumulator layout is W's A-fragment layout;
-// K and V blocks reach the column (B operand) layout through one MFMA with an
-// identity operand, which is exact.  Only k is staged in LDS: each wave loads
-// the q blocks and v tiles it uses as register fragments.
 // Gate inputs of the fused-input mode: g, beta from a, b exactly as the gating
 // kernel computes them.
 struct GateIn {
@@ -352,7 +323,48 @@ struct GateIn {
   const float* dt_bias;
 };
 
-template <typename T, typename Op, int D, int C, bool FUSE = false, int W = 4>
+// LDS layout of the prep kernel for G V heads per workgroup (one QK head when
+// G = h_v / h_k = 2).  Shared: the k rows (and, fused-input, the q rows); per
+// V head: its v rows (fused-input), its fp32 A/T tile, G and b.  The A tiles
+// overlay the q and v rows in the fused-input mode (those are read into
+// registers first); the scaled T copies overlay each A tile when they fit.
+template <typename Op, int D, int C, bool FUSE, int G>
+struct PrepLDS {
+  using K = Cfg<Op, D, C>;
+  static constexpr int S = (int)sizeof(Op);
+  static constexpr int ROWS = C * K::LDR * S;       // one [C][LDR] row tile
+  static constexpr int ATILE = C * K::LDA * 4;      // one fp32 A/T tile
+  static constexpr int TTILE = C * K::LDT * S;      // one scaled T copy
+  static constexpr int KR = 0;
+  static constexpr int QR = ROWS;                   // fused-input only
+  static constexpr int VR = 2 * ROWS;               // fused-input only, + s * ROWS
+  static constexpr int A0 = FUSE ? QR : ROWS;       // + s * ATILE
+  static constexpr int END_ROWS = FUSE ? (2 + G) * ROWS : ROWS;
+  static constexpr int END_A = A0 + G * ATILE;
+  static constexpr int SM = (END_ROWS > END_A ? END_ROWS : END_A);  // r_k [C], then per head G, b [C] each
+  static constexpr bool T_OVER_A = 2 * TTILE <= ATILE;
+  static constexpr int T0 = T_OVER_A ? A0 : SM + (1 + 2 * G) * C * 4;  // + s * (T_OVER_A ? ATILE : 2 * TTILE)
+  static constexpr int TSTEP = T_OVER_A ? ATILE : 2 * TTILE;
+  static constexpr int BYTES = T_OVER_A ? SM + (1 + 2 * G) * C * 4 : T0 + G * TSTEP;
+};
+
+// Per (chunk, QK head's group of G V heads).  Everything runs on the raw q, k,
+// v of the chunk; the L2 norms enter as per-token factors
+// r = 1/sqrt(|x|^2 + 1e-6), and per V head s (gates G_s, b_s):
+//   A_ij  = b_i r_k[i] r_k[j] e^{G_i-G_j} (k_i.k_j), i > j;   T = (I + A)^{-1}
+//   P_ij  = scale r_q[i] r_k[j] e^{G_i-G_j} (q_i.k_j), i >= j
+//   W     = T diag(b e^G r_k) K,   Ut = T diag(b) V,   K' = diag(e^{G_n-G} r_k) K
+// and f_q = scale e^G r_q, which the output pass applies to Q S^T.  The raw
+// products k_i.k_j and q_i.k_j and the loads (or convolutions) of q and k are
+// shared by the G V heads of the QK head.
+// No fragment is ever read down an LDS column.  P is formed as P^T = K Q^T,
+// whose accumulator layout is P's A-fragment layout; W is formed as
+// W^T = K^T (T diag(..))^T, whose accumulator layout is W's A-fragment layout;
+// K and V blocks reach the column (B operand) layout through one MFMA with an
+// identity operand, which is exact.  Only k (and, fused-input, q and v) is
+// staged in LDS; otherwise each wave loads its q blocks and v tiles as
+// register fragments.
+template <typename T, typename Op, int D, int C, bool FUSE = false, int W = 4, int G = 1>
 __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     const T* __restrict__ qkv, const float* __restrict__ g_in, const float* __restrict__ beta_in,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const int32_t* __restrict__ cstart,
@@ -360,44 +372,76 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     unsigned char* __restrict__ ws, ConvIn conv, GateIn gate, const uint8_t* __restrict__ has_init) {
   static_assert(sizeof(T) == sizeof(Op), "raw activations are MFMA operands");
   using K = Cfg<Op, D, C>;
+  using L = PrepLDS<Op, D, C, FUSE, G>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, WAVES = K::WAVES, DVT = K::DVT, LPR = K::LPR, RPP = K::RPP, RPT = K::RPT;
   constexpr int NPD = K::NPD, NPC = K::NPC, LDR = K::LDR, LDA = K::LDA, LDT = K::LDT;
   constexpr int QB = (CT + WAVES - 1) / WAVES;  // q blocks per wave: blocks wave, wave + WAVES, ...
   constexpr uint32_t PB = K::PAIR * sizeof(Op);
   static_assert(DVT == 1 || DVT == 2, "a wave's d tiles form one pair fragment");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[FUSE ? K::PREP_FUSED_BYTES : K::PREP_BYTES];
-  Op* sK = reinterpret_cast<Op*>(smem + (FUSE ? K::FK : K::PK));
-  float* sA = reinterpret_cast<float*>(smem + (FUSE ? K::FA : K::PA));
-  float* sG = reinterpret_cast<float*>(smem + (FUSE ? K::FS : K::PS));
-  float* sB = sG + C;
-  float* sRK = sG + 2 * C;
-  Op* sTW = reinterpret_cast<Op*>(smem + (FUSE ? K::FTW : K::PTW));
-  Op* sTU = reinterpret_cast<Op*>(smem + (FUSE ? K::FTU : K::PTU));
+  static_assert(G >= 1 && G <= 2, "V heads per workgroup");
+  static_assert(L::BYTES <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+  Op* sK = reinterpret_cast<Op*>(smem + L::KR);
+  float* sRK = reinterpret_cast<float*>(smem + L::SM);
+  // per V head s (s may be a runtime value: addresses, not pointer arrays)
+  auto sA = [&](int s) { return reinterpret_cast<float*>(smem + L::A0 + s * L::ATILE); };
+  auto sG = [&](int s) { return sRK + C + 2 * s * C; };
+  auto sB = [&](int s) { return sRK + 2 * C + 2 * s * C; };
+  auto sTW = [&](int s) { return reinterpret_cast<Op*>(smem + L::T0 + s * L::TSTEP); };
+  auto sTU = [&](int s) { return reinterpret_cast<Op*>(smem + L::T0 + s * L::TSTEP) + C * LDT; };
 
-  const int gc = blockIdx.x / h_v;
-  const int h = blockIdx.x % h_v;
+  const int hgroups = h_v / G;
+  const int gc = blockIdx.x / hgroups;
+  const int h0 = (blockIdx.x % hgroups) * G;  // first V head; G > 1 only when G == h_v / h_k
   if (gc >= cstart[n_seq]) return;
   const int n = seq_of_chunk(cstart, n_seq, gc);
   if (!slot_ok(slots[n], n_slots)) return;  // padding entry: nothing to prepare
-  const int hk = h / (h_v / h_k);
+  const int hk = h0 / (h_v / h_k);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int c_ch = 2 * h_k * D + h_v * D;
   const int64_t seq_lo = min((int64_t)cu[n], t_total);
   const int64_t seq_hi = min(max((int64_t)cu[n + 1], seq_lo), t_total);
   const int64_t c0 = seq_lo + (int64_t)(gc - cstart[n]) * C;
   const int nvalid = (int)min((int64_t)C, seq_hi - c0);
-  unsigned char* unit = ws + ((int64_t)gc * h_v + h) * K::UNIT;
+  auto unit = [&](int s) { return ws + ((int64_t)gc * h_v + h0 + s) * K::UNIT; };
   const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
   const FragT zf = zero_frag<Op>();
   FragT eye;  // B fragment of the 16x16 identity
 #pragma unroll
   for (int i = 0; i < 4; ++i) eye[i] = from_f32<Op>(4 * g4 + i == l16 ? 1.f : 0.f);
 
-  FragT Qb[QB][NPD][2], Va[CT][DVT];
+  // gates of V head h0 + s into LDS (and e^{G_n} to its unit), on one wave:
+  // from g, beta, or (fused-input) from a, b exactly as the gating kernel
+  auto gates = [&](int s) {
+    const int h = h0 + s;
+    float gv = 0.f, bv = 0.f;
+    if (lane < nvalid) {
+      const int64_t i = (c0 + lane) * h_v + h;
+      if constexpr (FUSE) {
+        gv = -expf(gate.A_log[h]) * softplusf_(to_f32(reinterpret_cast<const T*>(gate.a)[i]) + gate.dt_bias[h]);
+        bv = sigmoidf_(to_f32(reinterpret_cast<const T*>(gate.b)[i]));
+      } else {
+        gv = g_in[i];
+        bv = beta_in[i];
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float up = __shfl_up(gv, off);
+      if (lane >= off) gv += up;
+    }
+    if (lane < C) {
+      sG(s)[lane] = gv;
+      sB(s)[lane] = bv;
+    }
+    if (lane == C - 1) *at<float>(unit(s), K::F_OFF) = fast_exp(gv);
+  };
+
+  FragT Qb[QB][NPD][2], Va[G][CT][DVT];
   if constexpr (!FUSE) {
     // ---- register fragments straight from memory: this wave's q blocks (B
-    // operand of P^T, row l16) and v tiles (A layout, row l16)
+    // operand of P^T, row l16) and v tiles of each V head (A layout, row l16)
     {
       const T* qbase = qkv + (int64_t)hk * D + 4 * g4;
 #pragma unroll
@@ -410,14 +454,17 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
           Qb[b][sp][1] = ok && 32 * sp + 16 < D ? *reinterpret_cast<const FragT*>(qbase + (c0 + r) * c_ch + 32 * sp + 16) : zf;
         }
       }
-      const T* vbase = qkv + (int64_t)(2 * h_k + h) * D + 16 * wave * DVT + 4 * g4;
 #pragma unroll
-      for (int kb = 0; kb < CT; ++kb)
+      for (int s = 0; s < G; ++s) {
+        const T* vbase = qkv + (int64_t)(2 * h_k + h0 + s) * D + 16 * wave * DVT + 4 * g4;
 #pragma unroll
-        for (int j = 0; j < DVT; ++j) {
-          const int r = 16 * kb + l16;
-          Va[kb][j] = r < nvalid ? *reinterpret_cast<const FragT*>(vbase + (c0 + r) * c_ch + 16 * j) : zf;
-        }
+        for (int kb = 0; kb < CT; ++kb)
+#pragma unroll
+          for (int j = 0; j < DVT; ++j) {
+            const int r = 16 * kb + l16;
+            Va[s][kb][j] = r < nvalid ? *reinterpret_cast<const FragT*>(vbase + (c0 + r) * c_ch + 16 * j) : zf;
+          }
+      }
     }
     // ---- raw k rows into LDS with their inverse norms; gates
     {
@@ -428,11 +475,6 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         const int r = r0 + j * RPP;
         if (r < nvalid) raw[j].load(qkv + (c0 + r) * c_ch + (int64_t)(h_k + hk) * D + e0);
         else raw[j].zero();
-      }
-      float gv = 0.f, bv = 0.f;
-      if (wave == 0 && lane < nvalid) {
-        gv = g_in[(c0 + lane) * h_v + h];
-        bv = beta_in[(c0 + lane) * h_v + h];
       }
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
@@ -448,51 +490,34 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
           if (tid % LPR == 0) sRK[r] = fast_rsq(ss + 1e-6f);
         }
       }
-      if (wave == 0) {
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float up = __shfl_up(gv, off);
-          if (lane >= off) gv += up;
-        }
-        if (lane < C) {
-          sG[lane] = gv;
-          sB[lane] = bv;
-        }
-        if (lane == C - 1) *at<float>(unit, K::F_OFF) = fast_exp(gv);
-      }
+      for (int s = 0; s < G; ++s)
+        if (wave == s % WAVES) gates(s);
     }
     __syncthreads();
   } else {
-    // ---- conv1d + SiLU of x into LDS: k, q (this QK head) and v (this V head)
-    Op* sQf = reinterpret_cast<Op*>(smem + K::FQ);
-    Op* sVf = reinterpret_cast<Op*>(smem + K::FV);
+    // ---- conv1d + SiLU of x into LDS: k and q of this QK head, v of each V head
+    Op* sQf = reinterpret_cast<Op*>(smem + L::QR);
     {
       const int32_t slot = slots[n];
       const ConvIn ci{conv.x, conv.w, conv.bias, conv.state, slot, has_init == nullptr || has_init[n] != 0, seq_lo};
-      const int cols[3] = {(h_k + hk) * D, hk * D, (2 * h_k + h) * D};
-      Op* const dst[3] = {sK, sQf, sVf};
-      stage_conv<T, Op, D, C, W, 3, 16, K::THREADS>(ci, c_ch, cols, c0, nvalid, dst, LDR, tid);
-    }
-    // gates: g, beta from a, b (as the gating kernel), then G = cumsum g; on
-    // the last wave, which has the fewest conv items
-    if (wave == WAVES - 1) {
-      float gv = 0.f, bv = 0.f;
-      if (lane < nvalid) {
-        const int64_t i = (c0 + lane) * h_v + h;
-        gv = -expf(gate.A_log[h]) * softplusf_(to_f32(reinterpret_cast<const T*>(gate.a)[i]) + gate.dt_bias[h]);
-        bv = sigmoidf_(to_f32(reinterpret_cast<const T*>(gate.b)[i]));
-      }
+      int cols[2 + G];
+      Op* dst[2 + G];
+      cols[0] = (h_k + hk) * D;
+      dst[0] = sK;
+      cols[1] = hk * D;
+      dst[1] = sQf;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float up = __shfl_up(gv, off);
-        if (lane >= off) gv += up;
+      for (int s = 0; s < G; ++s) {
+        cols[2 + s] = (2 * h_k + h0 + s) * D;
+        dst[2 + s] = reinterpret_cast<Op*>(smem + L::VR + s * L::ROWS);
       }
-      if (lane < C) {
-        sG[lane] = gv;
-        sB[lane] = bv;
-      }
-      if (lane == C - 1) *at<float>(unit, K::F_OFF) = fast_exp(gv);
+      stage_conv<T, Op, D, C, W, 2 + G, 16, K::THREADS>(ci, c_ch, cols, c0, nvalid, dst, LDR, tid);
     }
+    // gates on the waves with the fewest conv items (the last ones)
+#pragma unroll
+    for (int s = 0; s < G; ++s)
+      if (wave == WAVES - 1 - s % WAVES) gates(s);
     __syncthreads();
     // the same fragments and norms as the unfused path, read from LDS
 #pragma unroll
@@ -506,12 +531,16 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       }
     }
 #pragma unroll
-    for (int kb = 0; kb < CT; ++kb)
+    for (int s = 0; s < G; ++s) {
+      const Op* sVf = reinterpret_cast<const Op*>(smem + L::VR + s * L::ROWS);
 #pragma unroll
-      for (int j = 0; j < DVT; ++j) {
-        const int r = 16 * kb + l16;
-        Va[kb][j] = r < nvalid ? lds_frag<Op>(sVf + r * LDR + 16 * (wave * DVT + j) + 4 * g4) : zf;
-      }
+      for (int kb = 0; kb < CT; ++kb)
+#pragma unroll
+        for (int j = 0; j < DVT; ++j) {
+          const int r = 16 * kb + l16;
+          Va[s][kb][j] = r < nvalid ? lds_frag<Op>(sVf + r * LDR + 16 * (wave * DVT + j) + 4 * g4) : zf;
+        }
+    }
     {
       const int e0 = (tid % LPR) * 8, r0 = tid / LPR;
 #pragma unroll
@@ -529,12 +558,13 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         if (r < C && tid % LPR == 0) sRK[r] = fast_rsq(ss + 1e-6f);
       }
     }
-    __syncthreads();  // r_k visible; q and v rows are read before the A tile overlays them
+    __syncthreads();  // r_k visible; q and v rows are read before the A tiles overlay them
   }
 
   // ---- Gram work.  Wave w: the P^T tiles of its q blocks ib (pairs of
-  // column blocks -> P fragments) and f_q of those rows; then K K^T tiles -> A,
-  // taken in the order that evens out the per-wave tile count.
+  // column blocks -> P fragments of each V head) and f_q of those rows; then
+  // K K^T tiles -> A of each V head, taken in the order that evens out the
+  // per-wave tile count.  Each raw product is formed once for the G V heads.
   {
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -555,32 +585,43 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       ss += __shfl_xor(ss, 32);
       const int i = 16 * ib + l16;
       const float fi = scale * fast_rsq(ss + 1e-6f);  // scale r_q[i]
-      const float gi = sG[i];
-      if (g4 == 0) *at<float>(unit, K::FQ_OFF + 4 * i) = fi * fast_exp(gi);
+      if (g4 == 0)
+#pragma unroll
+        for (int s = 0; s < G; ++s) *at<float>(unit(s), K::FQ_OFF + 4 * i) = fi * fast_exp(sG(s)[i]);
 #pragma unroll
       for (int sp = 0; sp < NPC; ++sp) {
         if (2 * sp > ib) break;
-        FragT half[2];
+        f32x4 raw[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int jb = 2 * sp + hh;
-          if (jb > ib) { half[hh] = zf; continue; }
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          raw[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (jb > ib) continue;
           const Op* arow = sK + (16 * jb + l16) * LDR + 4 * g4;
 #pragma unroll
           for (int s2 = 0; s2 < NPD; ++s2) {
             if (32 * s2 + 16 < D)
-              mma_k32(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), Qb[b][s2][0], Qb[b][s2][1]);
+              mma_k32(raw[hh], lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(arow + 32 * s2 + 16), Qb[b][s2][0],
+                      Qb[b][s2][1]);
             else
-              mma_k16(acc, lds_frag<Op>(arow + 32 * s2), Qb[b][s2][0]);
-          }
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int jj = 16 * jb + 4 * g4 + ii;
-            half[hh][ii] = from_f32<Op>(i >= jj ? fi * sRK[jj] * fast_exp(fminf(gi - sG[jj], 0.f)) * acc[ii] : 0.f);
+              mma_k16(raw[hh], lds_frag<Op>(arow + 32 * s2), Qb[b][s2][0]);
           }
         }
-        store_pair<Op>(at<Op>(unit, K::P_OFF + (uint32_t)(ib * NPC + sp) * PB + lp), half[0], half[1]);
+#pragma unroll
+        for (int s = 0; s < G; ++s) {
+          const float gi = sG(s)[i];
+          FragT half[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const int jj = 16 * (2 * sp + hh) + 4 * g4 + ii;
+              half[hh][ii] = from_f32<Op>(2 * sp + hh <= ib && i >= jj
+                                              ? fi * sRK[jj] * fast_exp(fminf(gi - sG(s)[jj], 0.f)) * raw[hh][ii]
+                                              : 0.f);
+            }
+          store_pair<Op>(at<Op>(unit(s), K::P_OFF + (uint32_t)(ib * NPC + sp) * PB + lp), half[0], half[1]);
+        }
       }
     }
     // A tiles (ib, jb), jb <= ib: block row ib (ib + 1 tiles) goes to wave
@@ -602,19 +643,24 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
             mma_k16(acc, lds_frag<Op>(arow + 32 * s2), lds_frag<Op>(brow + 32 * s2));
         }
         const int j = 16 * jb + l16;
-        const float rj = sRK[j], gj = sG[j];
+        const float rj = sRK[j];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * ib + 4 * g4 + ii;
-          sA[i * LDA + j] = i > j ? sB[i] * sRK[i] * rj * fast_exp(fminf(sG[i] - gj, 0.f)) * acc[ii] : 0.f;
+        for (int s = 0; s < G; ++s) {
+          const float gj = sG(s)[j];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int i = 16 * ib + 4 * g4 + ii;
+            sA(s)[i * LDA + j] = i > j ? sB(s)[i] * sRK[i] * rj * fast_exp(fminf(sG(s)[i] - gj, 0.f)) * acc[ii] : 0.f;
+          }
         }
       }
   }
   __syncthreads();
 
-  // ---- T = (I + A)^-1 in place.  (a) diagonal 16x16 blocks, one lane per column
-  if (tid < CT * 16) {
-    const int b = tid >> 4, c = tid & 15;
+  // ---- T = (I + A)^-1 in place, per V head.  (a) diagonal 16x16 blocks, one
+  // lane per column
+  if (tid < G * CT * 16) {
+    const int s = tid / (CT * 16), b = (tid / 16) % CT, c = tid & 15;
     // the block's rows into registers first, so the substitution chain runs
     // on registers (16-byte reads; the upper triangle is read but unused)
     float blk[16][16];
@@ -622,7 +668,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     for (int r = 1; r < 16; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (4 * q < r) *reinterpret_cast<f32x4*>(&blk[r][4 * q]) = *reinterpret_cast<const f32x4*>(sA + (16 * b + r) * LDA + 16 * b + 4 * q);
+        if (4 * q < r)
+          *reinterpret_cast<f32x4*>(&blk[r][4 * q]) = *reinterpret_cast<const f32x4*>(sA(s) + (16 * b + r) * LDA + 16 * b + 4 * q);
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -633,32 +680,39 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     }
     // every read of this block above precedes these writes in the wave's program order
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sA[(16 * b + r) * LDA + 16 * b + c] = x[r];
+    for (int r = 0; r < 16; ++r) sA(s)[(16 * b + r) * LDA + 16 * b + c] = x[r];
   }
   __syncthreads();
   // (b) block rows: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.  The A blocks of the
   // row are read into registers before any wave overwrites them with T.
 #pragma unroll
   for (int bi = 1; bi < CT; ++bi) {
-    f32x4 a_row[CT];
+    f32x4 a_row[G][CT];
 #pragma unroll
-    for (int bk = 0; bk < CT; ++bk)
-      if (bk < bi) a_row[bk] = lds_frag<float>(sA + (16 * bi + l16) * LDA + 16 * bk + 4 * g4);
+    for (int s = 0; s < G; ++s)
+#pragma unroll
+      for (int bk = 0; bk < CT; ++bk)
+        if (bk < bi) a_row[s][bk] = lds_frag<float>(sA(s) + (16 * bi + l16) * LDA + 16 * bk + 4 * g4);
     __syncthreads();
-    for (int bj = wave; bj < bi; bj += WAVES) {
+    for (int it = wave; it < G * bi; it += WAVES) {
+      const int s = it / bi, bj = it % bi;
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int bk = 0; bk < CT; ++bk)
         if (bk >= bj && bk < bi) {
           f32x4 b;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) b[jj] = sA[(16 * bk + 4 * g4 + jj) * LDA + 16 * bj + l16];
-          mma_k16(X, a_row[bk], b);
+          for (int jj = 0; jj < 4; ++jj) b[jj] = sA(s)[(16 * bk + 4 * g4 + jj) * LDA + 16 * bj + l16];
+          f32x4 av = a_row[0][bk];
+#pragma unroll
+          for (int s2 = 1; s2 < G; ++s2)
+            if (s == s2) av = a_row[s2][bk];
+          mma_k16(X, av, b);
         }
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      mma_k16(Y, lds_frag<float>(sA + (16 * bi + l16) * LDA + 16 * bi + 4 * g4), X);
+      mma_k16(Y, lds_frag<float>(sA(s) + (16 * bi + l16) * LDA + 16 * bi + 4 * g4), X);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sA[(16 * bi + 4 * g4 + jj) * LDA + 16 * bj + l16] = -Y[jj];
+      for (int jj = 0; jj < 4; ++jj) sA(s)[(16 * bi + 4 * g4 + jj) * LDA + 16 * bj + l16] = -Y[jj];
     }
     __syncthreads();
   }
@@ -666,39 +720,42 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   // ---- T_W = T diag(b e^G r_k), T_U = T diag(b) in the operand type, zero above
   // the diagonal blocks.  They may overlay T itself: all of T is read first.
   {
-    constexpr int PER = (C * C / 4 + K::THREADS - 1) / K::THREADS;
+    constexpr int PER = (G * C * C / 4 + K::THREADS - 1) / K::THREADS;
     FragT tw[PER], tu[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int e = tid + k * K::THREADS;
-      if (e < C * C / 4) {
-        const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
+      if (e < G * C * C / 4) {
+        const int s = e / (C * C / 4), er = e % (C * C / 4);
+        const int r = er / (C / 4), c4 = (er % (C / 4)) * 4;
         const bool keep = (c4 >> 4) <= (r >> 4);
-        const f32x4 t = keep ? *reinterpret_cast<const f32x4*>(sA + r * LDA + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 t = keep ? *reinterpret_cast<const f32x4*>(sA(s) + r * LDA + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float b = sB[c4 + i];
-          tw[k][i] = from_f32<Op>(t[i] * b * fast_exp(sG[c4 + i]) * sRK[c4 + i]);
+          const float b = sB(s)[c4 + i];
+          tw[k][i] = from_f32<Op>(t[i] * b * fast_exp(sG(s)[c4 + i]) * sRK[c4 + i]);
           tu[k][i] = from_f32<Op>(t[i] * b);
         }
       }
     }
-    if (K::T_OVER_A) __syncthreads();
+    if (L::T_OVER_A) __syncthreads();
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int e = tid + k * K::THREADS;
-      if (e < C * C / 4) {
-        const int r = e / (C / 4), c4 = (e % (C / 4)) * 4;
-        *reinterpret_cast<FragT*>(sTW + r * LDT + c4) = tw[k];
-        *reinterpret_cast<FragT*>(sTU + r * LDT + c4) = tu[k];
+      if (e < G * C * C / 4) {
+        const int s = e / (C * C / 4), er = e % (C * C / 4);
+        const int r = er / (C / 4), c4 = (er % (C / 4)) * 4;
+        *reinterpret_cast<FragT*>(sTW(s) + r * LDT + c4) = tw[k];
+        *reinterpret_cast<FragT*>(sTU(s) + r * LDT + c4) = tu[k];
       }
     }
   }
   __syncthreads();
 
-  // ---- this wave's d tiles: K and V column fragments, W^T, Ut and K'^T
+  // ---- this wave's d tiles: K and V column fragments, then per V head W^T,
+  // Ut and K'^T
   {
-    FragT Kc[CT][DVT], Vc[CT][DVT];
+    FragT Kc[CT][DVT];
 #pragma unroll
     for (int kb = 0; kb < CT; ++kb)
 #pragma unroll
@@ -706,50 +763,59 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         mma_k16(a, lds_frag<Op>(sK + (16 * kb + l16) * LDR + 16 * (wave * DVT + j) + 4 * g4), eye);
         Kc[kb][j] = frag_from<Op>(a);
-        f32x4 b = {0.f, 0.f, 0.f, 0.f};
-        mma_k16(b, Va[kb][j], eye);
-        Vc[kb][j] = frag_from<Op>(b);
       }
     const int sp_w = wave;  // the pair of d tiles this wave owns (DVT == 2), or pair 0 (DVT == 1)
 #pragma unroll
-    for (int mt = 0; mt < CT; ++mt) {
-      f32x4 wacc[DVT];
+    for (int s = 0; s < G; ++s) {
+      FragT Vc[CT][DVT];
 #pragma unroll
-      for (int j = 0; j < DVT; ++j) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
-        const Op* twrow = sTW + (16 * mt + l16) * LDT + 4 * g4;
-        const Op* turow = sTU + (16 * mt + l16) * LDT + 4 * g4;
+      for (int kb = 0; kb < CT; ++kb)
 #pragma unroll
-        for (int s2 = 0; s2 < NPC; ++s2)
-          if (2 * s2 <= mt) {
-            const bool two = 2 * s2 + 1 < CT;
-            const FragT b0 = lds_frag<Op>(twrow + 32 * s2), b1 = two ? lds_frag<Op>(twrow + 32 * s2 + 16) : zf;
-            mma_k32(acc, Kc[2 * s2][j], two ? Kc[2 * s2 + 1][j] : zf, b0, b1);
-            const FragT a0 = lds_frag<Op>(turow + 32 * s2), a1 = two ? lds_frag<Op>(turow + 32 * s2 + 16) : zf;
-            mma_k32(uacc, a0, a1, Vc[2 * s2][j], two ? Vc[2 * s2 + 1][j] : zf);
-          }
-        wacc[j] = acc;
-        *at<FragT>(unit, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf) = frag_from<Op>(uacc);
-      }
-      store_pair<Op>(at<Op>(unit, K::W_OFF + (uint32_t)(mt * NPD + sp_w) * PB + lp), frag_from<Op>(wacc[0], -1.f),
-                     DVT == 2 ? frag_from<Op>(wacc[DVT - 1], -1.f) : zf);
-    }
-    const float g_n = sG[C - 1];
-#pragma unroll
-    for (int j = 0; j < DVT; ++j)
-#pragma unroll
-      for (int sp = 0; sp < NPC; ++sp) {
-        FragT lo, hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
-          lo[i] = from_f32<Op>(to_f32(Kc[2 * sp][j][i]) * fast_exp(g_n - sG[t0]) * sRK[t0]);
-          hi[i] = from_f32<Op>(2 * sp + 1 < CT ? to_f32(Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j][i]) *
-                                                     fast_exp(g_n - sG[t1 < C ? t1 : 0]) * sRK[t1 < C ? t1 : 0]
-                                               : 0.f);
+        for (int j = 0; j < DVT; ++j) {
+          f32x4 b = {0.f, 0.f, 0.f, 0.f};
+          mma_k16(b, Va[s][kb][j], eye);
+          Vc[kb][j] = frag_from<Op>(b);
         }
-        store_pair<Op>(at<Op>(unit, K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), lo, hi);
+#pragma unroll
+      for (int mt = 0; mt < CT; ++mt) {
+        f32x4 wacc[DVT];
+#pragma unroll
+        for (int j = 0; j < DVT; ++j) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
+          const Op* twrow = sTW(s) + (16 * mt + l16) * LDT + 4 * g4;
+          const Op* turow = sTU(s) + (16 * mt + l16) * LDT + 4 * g4;
+#pragma unroll
+          for (int s2 = 0; s2 < NPC; ++s2)
+            if (2 * s2 <= mt) {
+              const bool two = 2 * s2 + 1 < CT;
+              const FragT b0 = lds_frag<Op>(twrow + 32 * s2), b1 = two ? lds_frag<Op>(twrow + 32 * s2 + 16) : zf;
+              mma_k32(acc, Kc[2 * s2][j], two ? Kc[2 * s2 + 1][j] : zf, b0, b1);
+              const FragT a0 = lds_frag<Op>(turow + 32 * s2), a1 = two ? lds_frag<Op>(turow + 32 * s2 + 16) : zf;
+              mma_k32(uacc, a0, a1, Vc[2 * s2][j], two ? Vc[2 * s2 + 1][j] : zf);
+            }
+          wacc[j] = acc;
+          *at<FragT>(unit(s), K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf) = frag_from<Op>(uacc);
+        }
+        store_pair<Op>(at<Op>(unit(s), K::W_OFF + (uint32_t)(mt * NPD + sp_w) * PB + lp), frag_from<Op>(wacc[0], -1.f),
+                       DVT == 2 ? frag_from<Op>(wacc[DVT - 1], -1.f) : zf);
       }
+      const float g_n = sG(s)[C - 1];
+#pragma unroll
+      for (int j = 0; j < DVT; ++j)
+#pragma unroll
+        for (int sp = 0; sp < NPC; ++sp) {
+          FragT lo, hi;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
+            lo[i] = from_f32<Op>(to_f32(Kc[2 * sp][j][i]) * fast_exp(g_n - sG(s)[t0]) * sRK[t0]);
+            hi[i] = from_f32<Op>(2 * sp + 1 < CT ? to_f32(Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j][i]) *
+                                                       fast_exp(g_n - sG(s)[t1 < C ? t1 : 0]) * sRK[t1 < C ? t1 : 0]
+                                                 : 0.f);
+          }
+          store_pair<Op>(at<Op>(unit(s), K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), lo, hi);
+        }
+    }
   }
 }
 
@@ -1082,7 +1148,6 @@ template <typename T, typename Op, int D, int C, bool FUSE = false, int W = 4>
 hipError_t run(const ChunkArgs& a, hipStream_t st) {
   using K = Cfg<Op, D, C>;
   static_assert(sizeof(T) == sizeof(Op), "the chain writes O in the activation type");
-  static_assert((FUSE ? K::PREP_FUSED_BYTES : K::PREP_BYTES) <= 160 * 1024, "LDS budget");
   constexpr int NTW = kTileW<Op, D>, NTILE = K::NT / NTW;
   if (a.n_seq == 0) return hipSuccess;
   int32_t* cstart = reinterpret_cast<int32_t*>(a.workspace);
@@ -1092,11 +1157,20 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int64_t max_chunks = a.t_total / C + a.n_seq;
   if (max_chunks > 0) {
-    hipLaunchKernelGGL((chunk_prep_kernel<T, Op, D, C, FUSE, W>), dim3((unsigned)(max_chunks * a.s.h_v)),
-                       dim3(K::THREADS), 0, st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, cstart,
-                       a.n_slots, a.n_seq, a.t_total, a.s.h_k, a.s.h_v, a.scale, units,
-                       ConvIn{a.x, a.conv_w, a.conv_b, a.conv_state, 0, false, 0},
-                       GateIn{a.a_in, a.b_in, a.A_log, a.dt_bias}, a.has_init);
+    // two V heads per QK head: one prep workgroup per QK head shares the q/k
+    // loads (or convolutions) and the raw Gram products between them
+    const ConvIn ci{a.x, a.conv_w, a.conv_b, a.conv_state, 0, false, 0};
+    const GateIn gi{a.a_in, a.b_in, a.A_log, a.dt_bias};
+    constexpr bool pair_fits = PrepLDS<Op, D, C, FUSE, 2>::BYTES <= 160 * 1024;
+    constexpr int G2 = pair_fits ? 2 : 1;  // (fp32 at d = 128 and C = 64, which no entry point takes)
+    if (pair_fits && a.s.h_v == 2 * a.s.h_k)
+      hipLaunchKernelGGL((chunk_prep_kernel<T, Op, D, C, FUSE, W, G2>), dim3((unsigned)(max_chunks * a.s.h_k)),
+                         dim3(K::THREADS), 0, st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, cstart,
+                         a.n_slots, a.n_seq, a.t_total, a.s.h_k, a.s.h_v, a.scale, units, ci, gi, a.has_init);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<T, Op, D, C, FUSE, W, 1>), dim3((unsigned)(max_chunks * a.s.h_v)),
+                         dim3(K::THREADS), 0, st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, cstart,
+                         a.n_slots, a.n_seq, a.t_total, a.s.h_k, a.s.h_v, a.scale, units, ci, gi, a.has_init);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
