@@ -200,6 +200,14 @@ template <> struct Pair<float> {
   }
 };
 
+// A wave-uniform 64-bit value kept in SGPRs (the compiler cannot always prove
+// the uniformity of a computed offset).
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Address of a workspace vector: uniform base plus a 32-bit unsigned byte
 // offset, which lets the compiler use SGPR-base addressing with no 64-bit
 // VALU arithmetic per load.
@@ -820,164 +828,217 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 }
 
 // ----------------------------------------------------------------- state
-// One wave: the chain of one sequence's chunks for one V head and NTW 16-wide
-// tiles of d_v.  S^T[d_k][d_v-slice] lives in accumulators (lane: d_k rows
-// 4g..4g+3 of each 16-block, d_v column l16), which is also the B operand
-// layout for every product that contracts over d_k.  Per chunk:
-//   h = bf16(S^T) -> workspace;  U = Ut - W S^T -> workspace (over Ut);
-//   S^T <- e^{G_n} S^T + K'^T U.
-// The next chunk's operands are loaded right after this chunk consumed the
-// same registers.  Block order puts all tiles of one (sequence, head) on one
-// XCD, so W and K'^T are fetched into that XCD's L2 once.
-template <typename Op, int D, int C, int NTW>
-__global__ __launch_bounds__(64) void chunk_state_kernel(
+// The chain of one sequence's chunks for one V head and NTW 16-wide tiles of
+// d_v, on one workgroup of NPD waves (NPD = d_k / 32, at least one).  The rows
+// of S^T[d_k][tiles] are split over the waves: wave w holds d_k tiles 2w and
+// 2w + 1 in accumulators (lane: d_k rows 4g..4g+3 of each 16-block, d_v
+// column l16), which is pair w of the B operand of every product over d_k.
+// Per chunk:
+//   h = bf16(S^T): each wave's pairs -> workspace and LDS;             barrier
+//   U = Ut - W S^T: wave w the chunk row tiles w, w + NPD, ... with all of h
+//       from LDS -> workspace (over Ut) and LDS;                         barrier
+//   S^T <- e^{G_n} S^T + K'^T U: each wave its d_k tiles, all of U from LDS.
+// A wave streams only the operand rows it uses (one row tile of -W and Ut,
+// two of K'^T), PD - 1 chunks ahead in registers, so a chunk's loads and its
+// MFMA work are spread over the CU's four SIMDs; NTW tiles share each -W and
+// K'^T load.  Block order puts all tiles of one (sequence, head) on one XCD,
+// so W and K'^T reach that XCD's L2 once.
+template <int D>
+constexpr int kChainThreads = 64 * ((D / 16 + 1) / 2);  // one wave per h pair
+
+template <typename Op, int D, int C, int NTW, int PD>
+__global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
     const int32_t* __restrict__ cstart, unsigned char* __restrict__ ws, float* __restrict__ state,
     int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v) {
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, NTILE = NT / NTW;
+  constexpr int MW = NPD;                   // waves
+  static_assert(64 * MW == kChainThreads<D>, "one wave per h pair");
+  static_assert(PD >= 2, "a chunk's loads go to a stage other than its own");
+  static_assert(NT % NTW == 0, "whole d_v tiles per workgroup");
+  constexpr int SM = NT >= 2 ? 2 : 1;       // d_k tiles of S^T per wave
+  constexpr int UPW = (CT + MW - 1) / MW;   // chunk row tiles of U per wave
   constexpr uint32_t PB = K::PAIR * sizeof(Op);  // bytes per pair tile
+  __shared__ __attribute__((aligned(16))) Op sH[NPD][NTW][64 * 8];  // h, pairs
+  __shared__ __attribute__((aligned(16))) Op sU[CT][NTW][64 * 4];   // U, accumulator layout
   const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3, tile = kq % NTILE;
   const int64_t grp = (int64_t)(kq / NTILE) * 8 + xcd;
   if (grp >= (int64_t)n_seq * h_v) return;
   const int n = (int)(grp / h_v), h = (int)(grp % h_v);
-  const uint32_t lane = threadIdx.x, g4 = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int64_t lo = min((int64_t)cu[n], t_total);
   const int64_t hi = min(max((int64_t)cu[n + 1], lo), t_total);
   const int32_t slot = slots[n];
   if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs (the output pass skips it)
     const int64_t o_ld = (int64_t)h_v * D;
     const int col0 = h * D + 16 * NTW * tile;
-    for (int64_t e = lane; e < (hi - lo) * 16 * NTW; e += 64)
+    for (int64_t e = tid; e < (hi - lo) * 16 * NTW; e += 64 * MW)
       o[(lo + e / (16 * NTW)) * o_ld + col0 + e % (16 * NTW)] = from_f32<Op>(0.f);
     return;
   }
   const bool init = has_init == nullptr || has_init[n] != 0;
   float* st_ptr = state + ((int64_t)slot * h_v + h) * D * D;
 
-  f32x4 Sacc[NT][NTW];
+  f32x4 Sacc[SM][NTW];
 #pragma unroll
-  for (int mt = 0; mt < NT; ++mt)
+  for (int m = 0; m < SM; ++m)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-      const int dv = 16 * (NTW * tile + j) + l16;
+      const int mt = SM * wave + m, dv = 16 * (NTW * tile + j) + l16;
       if (init) {
         const float4 v = *reinterpret_cast<const float4*>(st_ptr + dv * D + 16 * mt + 4 * g4);
-        Sacc[mt][j] = f32x4{v.x, v.y, v.z, v.w};
+        Sacc[m][j] = f32x4{v.x, v.y, v.z, v.w};
       } else {
-        Sacc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Sacc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 
-  // lane-invariant byte offsets inside a unit
-  const uint32_t lp = lane * 8 * sizeof(Op);   // a lane's pair within a pair tile
-  const uint32_t lf = lane * 4 * sizeof(Op);   // a lane's fragment within a 16x16 tile
-  // Two register stages (A: even chunks, B: odd chunks), so every chunk's
-  // operands are requested two chunks before they are used.
-  Pair<Op> wnA[CT][NPD], ktA[NT][NPC], wnB[CT][NPD], ktB[NT][NPC];
-  FragT utA[CT][NTW], utB[CT][NTW];
-  float egnA = 0.f, egnB = 0.f;
-#define GDN_LOAD_WU(X, u)                                                                           \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                              \
-      wn##X[mt][sp].load(at<Op>((u), K::W_OFF + (mt * NPD + sp) * PB + lp));                        \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
-      ut##X[mt][j] = *at<FragT>((u), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf); \
-  }
-#define GDN_LOAD_KT(X, u)                                                                           \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
-    _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                              \
-      kt##X[mt][sp].load(at<Op>((u), K::KT_OFF + (mt * NPC + sp) * PB + lp));                       \
-    egn##X = *at<float>((u), K::F_OFF);                                                             \
-  }
-  // h = S^T at the chunk start -> workspace;  U = Ut - W S^T
-#define GDN_PHASE_U(X, uc)                                                                          \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) Sf[mt][j] = frag_from<Op>(Sacc[mt][j]);         \
-    _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                              \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j)                                                 \
-      store_pair<Op>(at<Op>((uc), K::H_OFF + (uint32_t)(sp * NT + NTW * tile + j) * PB + lp), Sf[2 * sp][j], \
-                     2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);                                     \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
-      f32x4 acc;                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = to_f32(ut##X[mt][j][i]);               \
-      _Pragma("unroll") for (int sp = 0; sp < NPD; ++sp)                                            \
-        wn##X[mt][sp].mma(acc, Sf[2 * sp][j], 2 * sp + 1 < NT ? Sf[2 * sp + 1][j] : zf);            \
-      Uacc[mt][j] = acc;                                                                            \
-    }                                                                                               \
-  }
-  // U -> workspace over Ut (this wave's columns);  S^T <- e^{G_n} S^T + K'^T U
-#define GDN_PHASE_S(X, uc)                                                                          \
-  {                                                                                                 \
-    _Pragma("unroll") for (int mt = 0; mt < CT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
-      Uf[mt][j] = frag_from<Op>(Uacc[mt][j]);                                                       \
-      *at<FragT>((uc), K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = Uf[mt][j]; \
-    }                                                                                               \
-    _Pragma("unroll") for (int mt = 0; mt < NT; ++mt)                                               \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j) {                                               \
-      f32x4 acc = Sacc[mt][j];                                                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] *= egn##X;                               \
-      _Pragma("unroll") for (int sp = 0; sp < NPC; ++sp)                                            \
-        kt##X[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);            \
-      Sacc[mt][j] = acc;                                                                            \
-    }                                                                                               \
-  }
+  const uint32_t lp = lane * 8 * sizeof(Op);  // a lane's pair within a pair tile
+  const uint32_t lf = lane * 4 * sizeof(Op);  // a lane's fragment within a 16x16 tile
   const int32_t gc0 = cstart[n];
   const int nch = (int)((hi - lo + C - 1) / C);
   // unit of chunk k of this sequence, clamped to the last one: loads past the
   // end re-read it, so every load is unconditional and the wait counts exact
-#define unit_of(k) (ws + ((int64_t)(gc0 + min((k), nch - 1)) * h_v + h) * K::UNIT)
+  auto unit_of = [&](int k) { return ws + uniform_i64(((int64_t)(gc0 + min(k, nch - 1)) * h_v + h) * K::UNIT); };
+  Pair<Op> wn[PD][UPW][NPD], kt[PD][SM][NPC];
+  FragT ut[PD][UPW][NTW];
+  float egn[PD];
+  // A stage's operands as NPIECE single vector loads: the -W rows, Ut, the
+  // K'^T rows, e^{G_n}.
+  constexpr int NW = UPW * NPD, NU = UPW * NTW, NPIECE = NW + NU + SM * NPC + 1;
+  auto piece = [&](int s, const unsigned char* u, int j) {
+    if (j < NW) {
+      const int mt = min(wave + MW * (j / NPD), CT - 1);
+      wn[s][j / NPD][j % NPD].load(at<Op>(u, K::W_OFF + (uint32_t)(mt * NPD + j % NPD) * PB + lp));
+    } else if (j < NW + NU) {
+      const int i = (j - NW) / NTW, jt = (j - NW) % NTW;
+      const int mt = min(wave + MW * i, CT - 1);
+      ut[s][i][jt] = *at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + jt) * PB / 2 + lf);
+    } else if (j < NPIECE - 1) {
+      const int m = (j - NW - NU) / NPC, sp = (j - NW - NU) % NPC;
+      kt[s][m][sp].load(at<Op>(u, K::KT_OFF + (uint32_t)((SM * wave + m) * NPC + sp) * PB + lp));
+    } else {
+      egn[s] = *at<float>(u, K::F_OFF);
+    }
+  };
   const FragT zf = zero_frag<Op>();
-  FragT Sf[NT][NTW], Uf[CT][NTW];
-  f32x4 Uacc[CT][NTW];
-  if (nch > 0) {
-    GDN_LOAD_WU(A, unit_of(0));
-    GDN_LOAD_KT(A, unit_of(0));
-    GDN_LOAD_WU(B, unit_of(1));
-    GDN_LOAD_KT(B, unit_of(1));
-  }
-  for (int k = 0; k < nch; k += 2) {
-    {
-      unsigned char* uc = unit_of(k);
-      GDN_PHASE_U(A, uc);
-      __builtin_amdgcn_sched_barrier(0);
-      GDN_LOAD_WU(A, unit_of(k + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      GDN_PHASE_S(A, uc);
-      __builtin_amdgcn_sched_barrier(0);
-      GDN_LOAD_KT(A, unit_of(k + 2));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (k + 1 < nch) {
-      unsigned char* uc = unit_of(k + 1);
-      GDN_PHASE_U(B, uc);
-      GDN_PHASE_S(B, uc);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    GDN_LOAD_WU(B, unit_of(k + 3));
-    GDN_LOAD_KT(B, unit_of(k + 3));
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#undef GDN_LOAD_WU
-#undef GDN_LOAD_KT
-#undef GDN_PHASE_U
-#undef GDN_PHASE_S
-#undef unit_of
-
-#pragma unroll
-  for (int mt = 0; mt < NT; ++mt)
+  // One chunk from stage s (unit uc).  The NPIECE loads of stage ls (unit
+  // ul: the chunk PD - 1 ahead) are threaded one at a time between this
+  // chunk's MFMAs and LDS steps.  The CU's vector memory pipeline takes one
+  // 64-lane 16-byte load per ~16 clocks, and the waves run in step between
+  // barriers: issued in bursts the loads stall every wave together,
+  // interleaved they stream while the MFMA and LDS work runs.
+  auto step = [&](int s, unsigned char* uc, int ls, const unsigned char* ul) {
+    int pc = 0;
+    auto next_load = [&]() {
+      if (pc < NPIECE) {
+        __builtin_amdgcn_sched_barrier(0);
+        piece(ls, ul, pc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      ++pc;
+    };
+    // h = S^T at the chunk start: this wave's pairs
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-      const int dv = 16 * (NTW * tile + j) + l16;
+      const FragT h0 = frag_from<Op>(Sacc[0][j]), h1 = SM > 1 ? frag_from<Op>(Sacc[SM - 1][j]) : zf;
+      next_load();
+      store_pair<Op>(at<Op>(uc, K::H_OFF + (uint32_t)(wave * NT + NTW * tile + j) * PB + lp), h0, h1);
+      store_pair<Op>(&sH[wave][j][lane * 8], h0, h1);
+    }
+    next_load();
+    __syncthreads();
+    // U = Ut - W S^T for this wave's row tiles
+    {
+      Pair<Op> hp[NPD][NTW];
+#pragma unroll
+      for (int sp = 0; sp < NPD; ++sp)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) hp[sp][j].load(&sH[sp][j][lane * 8]);
+      __builtin_amdgcn_sched_barrier(0);  // all of h requested before the first product
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        const int mt = wave + MW * i;
+        if (CT % MW == 0 || mt < CT) {
+          f32x4 acc[NTW];
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] = to_f32(ut[s][i][j][e]);
+#pragma unroll
+          for (int sp = 0; sp < NPD; ++sp)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+              typename Frag<Op>::type b0, b1;
+              hp[sp][j].split(b0, b1);
+              wn[s][i][sp].mma(acc[j], b0, b1);
+              next_load();
+            }
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const FragT uf = frag_from<Op>(acc[j]);
+            *at<FragT>(uc, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = uf;
+            *reinterpret_cast<FragT*>(&sU[mt][j][lane * 4]) = uf;
+          }
+        }
+      }
+      // the decay of S^T does not wait for U
+#pragma unroll
+      for (int m = 0; m < SM; ++m)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Sacc[m][j][e] *= egn[s];
+    }
+    __syncthreads();
+    // S^T <- e^{G_n} S^T + K'^T U for this wave's d_k tiles
+    {
+      FragT uf[CT][NTW];
+#pragma unroll
+      for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) uf[t][j] = *reinterpret_cast<const FragT*>(&sU[t][j][lane * 4]);
+#pragma unroll
+      for (int sp = 0; sp < NPC; ++sp)
+#pragma unroll
+        for (int m = 0; m < SM; ++m)
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            kt[s][m][sp].mma(Sacc[m][j], uf[2 * sp][j], 2 * sp + 1 < CT ? uf[2 * sp + 1][j] : zf);
+            next_load();
+          }
+    }
+#pragma unroll
+    for (int j = 0; j < NPIECE; ++j) next_load();  // any left (small shapes)
+  };
+  // chunks 0 .. PD-2 into stages 0 .. PD-2 (in the loop's order, so the wait
+  // counts at the loop head need no slack); chunk c runs from stage c % PD
+  // and loads chunk c + PD - 1 into stage (c - 1) % PD
+  if (nch > 0) {
+#pragma unroll
+    for (int s = 0; s < PD - 1; ++s)
+#pragma unroll
+      for (int j = 0; j < NPIECE; ++j) piece(s, unit_of(s), j);
+  }
+  int k = 0;
+  for (; k + PD <= nch; k += PD) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) step(s, unit_of(k + s), (s + PD - 1) % PD, unit_of(k + s + PD - 1));
+  }
+#pragma unroll
+  for (int s = 0; s < PD - 1; ++s)  // the last nch % PD chunks (uniform over the workgroup)
+    if (k + s < nch) step(s, unit_of(k + s), (s + PD - 1) % PD, unit_of(k + s + PD - 1));
+
+#pragma unroll
+  for (int m = 0; m < SM; ++m)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int mt = SM * wave + m, dv = 16 * (NTW * tile + j) + l16;
       *reinterpret_cast<float4*>(st_ptr + dv * D + 16 * mt + 4 * g4) =
-          make_float4(Sacc[mt][j][0], Sacc[mt][j][1], Sacc[mt][j][2], Sacc[mt][j][3]);
+          make_float4(Sacc[m][j][0], Sacc[m][j][1], Sacc[m][j][2], Sacc[m][j][3]);
     }
 }
 
@@ -1126,10 +1187,23 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
   }
 }
 
-// Tiles of d_v per wave: one for a single long sequence is the most
-// parallel chain.
-template <typename Op, int D>
-constexpr int kTileW = 1;
+// Chain launch shape: d_v tiles per workgroup.  One tile per workgroup is
+// the most parallel and, with 4 register stages, the fastest chain; it is
+// used while the one-tile workgroups fit one per CU of an MI355X (256).
+// Beyond that the tiles per workgroup grow (2, then 4) so the launch stays
+// near one round of workgroups and the tiles share each -W and K'^T load,
+// which is what bounds many chains running at once (3 stages).
+constexpr int64_t kChainCUs = 256;
+
+template <typename Op, int D, int C, int NTW, int PD>
+hipError_t launch_chain(const ChunkArgs& a, int64_t groups, const int32_t* cstart, unsigned char* units,
+                        hipStream_t st) {
+  constexpr int TW = Cfg<Op, D, C>::NT >= NTW ? NTW : Cfg<Op, D, C>::NT;
+  hipLaunchKernelGGL((chunk_state_kernel<Op, D, C, TW, PD>), dim3((unsigned)(groups * (Cfg<Op, D, C>::NT / TW))),
+                     dim3(kChainThreads<D>), 0, st, a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state,
+                     a.n_slots, (Op*)a.o, a.t_total, a.n_seq, a.s.h_v);
+  return hipGetLastError();
+}
 
 // workspace: [chunk index][units]
 inline size_t idx_bytes(int32_t n_seq) { return (((size_t)n_seq + 1) * 4 + 255) / 256 * 256; }
@@ -1148,7 +1222,6 @@ template <typename T, typename Op, int D, int C, bool FUSE = false, int W = 4>
 hipError_t run(const ChunkArgs& a, hipStream_t st) {
   using K = Cfg<Op, D, C>;
   static_assert(sizeof(T) == sizeof(Op), "the chain writes O in the activation type");
-  constexpr int NTW = kTileW<Op, D>, NTILE = K::NT / NTW;
   if (a.n_seq == 0) return hipSuccess;
   int32_t* cstart = reinterpret_cast<int32_t*>(a.workspace);
   unsigned char* units = reinterpret_cast<unsigned char*>(a.workspace) + idx_bytes(a.n_seq);
@@ -1174,10 +1247,11 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
-  hipLaunchKernelGGL((chunk_state_kernel<Op, D, C, NTW>), dim3((unsigned)(groups * NTILE)), dim3(64), 0, st,
-                     a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state, a.n_slots, (Op*)a.o, a.t_total,
-                     a.n_seq, a.s.h_v);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int64_t chains = groups * K::NT;
+  const hipError_t ce = chains <= kChainCUs       ? launch_chain<Op, D, C, 1, 4>(a, groups, cstart, units, st)
+                        : chains <= 4 * kChainCUs ? launch_chain<Op, D, C, 2, 3>(a, groups, cstart, units, st)
+                                                  : launch_chain<Op, D, C, 4, 3>(a, groups, cstart, units, st);
+  if (ce != hipSuccess) return ce;
   if (max_chunks > 0)
     hipLaunchKernelGGL((chunk_out_kernel<T, Op, D, C, FUSE, W>), dim3((unsigned)(max_chunks * a.s.h_v)),
                        dim3(K::THREADS), 0, st, (const T*)a.qkv, a.cu_seqlens, a.slots, cstart, units, a.n_slots,

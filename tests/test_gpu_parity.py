@@ -297,6 +297,45 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, dp.ssm_pool) and torch.equal(c1, dp.conv_pool)
 
 
+def test_batch_composition_does_not_change_a_sequence():
+    """One sequence's outputs and final state are bitwise the same whether it
+    runs alone or packed with 3 or 8 more sequences.  With 32 V heads of
+    d=128 these batches give the chain pass 256, 1024 and 2304 (sequence,
+    head, d_v tile) chains, which it runs with 1, 2 and 4 tiles per
+    workgroup: every launch shape of the chain is covered, on both entry
+    points, and the packed runs also meet the oracle on the first sequence."""
+    lengths = np.array([300, 129, 64, 1, 700, 65, 0, 200, 333])
+    case = gi.varlen_case(seed=16, lengths=lengths, n_slots=12)
+    dp = DevPrefill(case)
+    conv0, ssm0 = dp.conv_pool.clone(), dp.ssm_pool.clone()
+    s0 = int(case.slots[0])
+    T0 = int(lengths[0])
+    res = {}
+    for n in (1, 4, 9):
+        T = int(case.cu_seqlens[n])
+        for fused in (False, True):
+            dp.conv_pool.copy_(conv0)
+            dp.ssm_pool.copy_(ssm0)
+            if fused:
+                o = gdn.prefill(dp.dims, dp.x[:T], dp.conv_w, dp.a[:T], dp.b[:T], dp.A_log, dp.dt_bias, dp.cu[:n + 1],
+                                dp.slots[:n], dp.conv_pool, dp.ssm_pool, dp.has_init[:n], 64, 1.0, dp.z[:T],
+                                dp.norm_w)
+            else:
+                o, *_ = gdn.prefill_layer(dp.dims, dp.x[:T], dp.conv_w, dp.A_log, dp.dt_bias, dp.a[:T], dp.b[:T],
+                                          dp.cu[:n + 1], dp.slots[:n], dp.conv_pool, dp.ssm_pool, dp.has_init[:n],
+                                          64, 1.0, dp.z[:T], dp.norm_w)
+            torch.cuda.synchronize()
+            res[(n, fused)] = (o[:T0].clone(), dp.ssm_pool[s0].clone(), dp.conv_pool[s0].clone())
+            if n == 9 and not fused:
+                w = compare_prefill(dp, o, seqs=[0], heads=[0, 5, 31])
+                log(f"packed 9: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
+                assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
+    ref = res[(1, False)]
+    for key, got in res.items():
+        for r, g in zip(ref, got):
+            assert torch.equal(r, g), f"sequence 0 differs with {key[0]} sequences (fused={key[1]})"
+
+
 def test_state_copy_bitwise_and_skips():
     dims = gdn.Dims(2, 4, 64, 64, 4)
     g = torch.Generator(device="cuda").manual_seed(0)
