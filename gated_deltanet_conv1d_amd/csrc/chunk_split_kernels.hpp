@@ -253,7 +253,7 @@ struct ConvIn {
 };
 template <typename T, typename Op, int D, int C, int W, int NP, int RB, int THREADS>
 __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int (&col)[NP], int64_t c0, int nvalid,
-                                           Op* const (&dst)[NP], int ldr, int tid) {
+                                           Op* base, const int (&dst)[NP], int ldr, int tid) {
   constexpr int NG = D / 8, NRB = C / RB, ITEMS = NP * NG * NRB;
   static_assert(C % RB == 0, "row blocks");
   const T* x = reinterpret_cast<const T*>(ci.x);
@@ -266,7 +266,7 @@ __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int
     if (rb * RB >= nvalid) {  // rows past the sequence's end: zeros, and no window to read
       const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < RB; ++k) store8(dst[p] + (rb * RB + k) * ldr + 8 * cg, zero);
+      for (int k = 0; k < RB; ++k) store8(base + dst[p] + (rb * RB + k) * ldr + 8 * cg, zero);
       continue;
     }
     // from here every window position lies in [seq_lo - (W-1), c0 + nvalid).
@@ -281,12 +281,28 @@ __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int
       const bool in_x = pos >= ci.seq_lo && pos < c0 + nvalid;
       raw[k].load(x + (in_x ? pos : c0) * c_ch + ch);
     }
+    // the 8 channels' taps are 8W consecutive weights: W vector loads
     float w[W][8], b[8];
+    {
+      float wf[W * 8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+      for (int j = 0; j < W; ++j) {
+        Raw8<T> r;
+        r.load(wt + (int64_t)ch * W + 8 * j);
+        r.to_f32(wf + 8 * j);
+      }
 #pragma unroll
-      for (int j = 0; j < W; ++j) w[j][i] = to_f32(wt[(int64_t)(ch + i) * W + j]);
-      b[i] = bias ? to_f32(bias[ch + i]) : 0.0f;
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < W; ++j) w[j][i] = wf[i * W + j];
+      if (bias) {
+        Raw8<T> r;
+        r.load(bias + ch);
+        r.to_f32(b);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = 0.0f;
+      }
     }
     float win[W][8];
 #pragma unroll
@@ -313,7 +329,7 @@ __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int
         for (int j = 0; j < W; ++j) acc = fmaf(w[j][i], win[j][i], acc);
         out[i] = r < nvalid ? fast_silu(acc) : 0.0f;
       }
-      store8(dst[p] + r * ldr + 8 * cg, out);
+      store8(base + dst[p] + r * ldr + 8 * cg, out);
 #pragma unroll
       for (int j = 0; j < W - 1; ++j)
 #pragma unroll
@@ -509,18 +525,20 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     {
       const int32_t slot = slots[n];
       const ConvIn ci{conv.x, conv.w, conv.bias, conv.state, slot, has_init == nullptr || has_init[n] != 0, seq_lo};
-      int cols[2 + G];
-      Op* dst[2 + G];
+      // (destinations as element offsets from the LDS base, so the stores
+      // stay LDS stores whichever part a thread's item falls in)
+      int cols[2 + G], dst[2 + G];
       cols[0] = (h_k + hk) * D;
-      dst[0] = sK;
+      dst[0] = L::KR / (int)sizeof(Op);
       cols[1] = hk * D;
-      dst[1] = sQf;
+      dst[1] = L::QR / (int)sizeof(Op);
 #pragma unroll
       for (int s = 0; s < G; ++s) {
         cols[2 + s] = (2 * h_k + h0 + s) * D;
-        dst[2 + s] = reinterpret_cast<Op*>(smem + L::VR + s * L::ROWS);
+        dst[2 + s] = (L::VR + s * L::ROWS) / (int)sizeof(Op);
       }
-      stage_conv<T, Op, D, C, W, 2 + G, 16, K::THREADS>(ci, c_ch, cols, c0, nvalid, dst, LDR, tid);
+      stage_conv<T, Op, D, C, W, 2 + G, 16, K::THREADS>(ci, c_ch, cols, c0, nvalid, reinterpret_cast<Op*>(smem), dst,
+                                                        LDR, tid);
     }
     // gates on the waves with the fewest conv items (the last ones)
 #pragma unroll
@@ -1084,9 +1102,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
     const int c_ch = 2 * h_k * D + h_v * D;
     const ConvIn ci{conv.x, conv.w, conv.bias, conv.state, slots[n], has_init == nullptr || has_init[n] != 0,
                     seq_lo};
-    const int cols[1] = {hk * D};
-    Op* const dst[1] = {sQ};
-    stage_conv<T, Op, D, C, W, 1, 4, K::THREADS>(ci, c_ch, cols, c0, nvalid, dst, K::LD_Q, (int)tid);
+    const int cols[1] = {hk * D}, dst[1] = {0};
+    stage_conv<T, Op, D, C, W, 1, 4, K::THREADS>(ci, c_ch, cols, c0, nvalid, sQ, dst, K::LD_Q, (int)tid);
   } else {
     const int hk = h / (h_v / h_k);
     const int c_ch = 2 * h_k * D + h_v * D;

@@ -336,6 +336,28 @@ def test_batch_composition_does_not_change_a_sequence():
             assert torch.equal(r, g), f"sequence 0 differs with {key[0]} sequences (fused={key[1]})"
 
 
+def test_many_short_sequences():
+    """300 sequences of 0..40 tokens (more than the kernels prefix-sum
+    themselves, so the chunk index table is built first): every output and
+    state against the oracle, on both entry points."""
+    rng = np.random.default_rng(17)
+    lengths = rng.integers(0, 41, size=300)
+    case = gi.varlen_case(seed=17, dims=gi.Dims(1, 2, 32, 32, 4), lengths=lengths, n_slots=320, chunk=16)
+    dp = DevPrefill(case)
+    conv0, ssm0 = dp.conv_pool.clone(), dp.ssm_pool.clone()
+    out, *_ = dp.run()
+    torch.cuda.synchronize()
+    w = compare_prefill(dp, out)
+    log(f"300 short sequences: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
+    assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
+    ref = (out.clone(), dp.ssm_pool.clone(), dp.conv_pool.clone())
+    dp.conv_pool.copy_(conv0)
+    dp.ssm_pool.copy_(ssm0)
+    out_f = dp.run_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, ref[0]) and torch.equal(dp.ssm_pool, ref[1]) and torch.equal(dp.conv_pool, ref[2])
+
+
 def test_state_copy_bitwise_and_skips():
     dims = gdn.Dims(2, 4, 64, 64, 4)
     g = torch.Generator(device="cuda").manual_seed(0)
