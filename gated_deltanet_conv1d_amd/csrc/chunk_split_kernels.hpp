@@ -979,22 +979,24 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
       __builtin_amdgcn_sched_barrier(0);  // all of h requested before the first product
 #pragma unroll
       for (int i = 0; i < UPW; ++i) {
+        // (a wave past the last row tile, CT < NPD, computes on the clamped
+        // tile it loaded and keeps nothing; its loads stay in step)
         const int mt = wave + MW * i;
+        f32x4 acc[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j][e] = to_f32(ut[s][i][j][e]);
+#pragma unroll
+        for (int sp = 0; sp < NPD; ++sp)
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            typename Frag<Op>::type b0, b1;
+            hp[sp][j].split(b0, b1);
+            wn[s][i][sp].mma(acc[j], b0, b1);
+            next_load();
+          }
         if (CT % MW == 0 || mt < CT) {
-          f32x4 acc[NTW];
-#pragma unroll
-          for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[j][e] = to_f32(ut[s][i][j][e]);
-#pragma unroll
-          for (int sp = 0; sp < NPD; ++sp)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-              typename Frag<Op>::type b0, b1;
-              hp[sp][j].split(b0, b1);
-              wn[s][i][sp].mma(acc[j], b0, b1);
-              next_load();
-            }
 #pragma unroll
           for (int j = 0; j < NTW; ++j) {
             const FragT uf = frag_from<Op>(acc[j]);

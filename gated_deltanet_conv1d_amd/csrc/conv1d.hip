@@ -25,12 +25,20 @@ template <typename T, int W>
 struct Taps {
   float w[W][kVec];
   float b[kVec];
+  // the kVec channels' taps are kVec * W consecutive weights: W vector loads
   __device__ void load(const T* __restrict__ wt, const T* __restrict__ bias, int c0) {
+    float f[W * kVec];
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) {
+    for (int j = 0; j < W; ++j) load8(wt + (int64_t)c0 * W + kVec * j, f + kVec * j);
 #pragma unroll
-      for (int j = 0; j < W; ++j) w[j][i] = to_f32(wt[(int64_t)(c0 + i) * W + j]);
-      b[i] = bias ? to_f32(bias[c0 + i]) : 0.0f;
+    for (int i = 0; i < kVec; ++i)
+#pragma unroll
+      for (int j = 0; j < W; ++j) w[j][i] = f[i * W + j];
+    if (bias) {
+      load8(bias + c0, b);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) b[i] = 0.0f;
     }
   }
   // out = silu(b + sum_j w[j] * win[j]) where win[W-1] is the current token.
@@ -44,6 +52,29 @@ struct Taps {
     }
   }
 };
+
+// A thread's kVec channels of one slot's conv state are kVec * (W-1)
+// consecutive values (channel-major, oldest first): W-1 vector accesses.
+template <typename T, int W>
+__device__ __forceinline__ void load_window(const T* __restrict__ st, float (&win)[W][kVec]) {
+  float f[(W - 1) * kVec];
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) load8(st + kVec * j, f + kVec * j);
+#pragma unroll
+  for (int i = 0; i < kVec; ++i)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) win[j][i] = f[i * (W - 1) + j];
+}
+template <typename T, int W>
+__device__ __forceinline__ void store_window(T* __restrict__ st, const float (&win)[W][kVec]) {
+  float f[(W - 1) * kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) f[i * (W - 1) + j] = win[j][i];
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) store8(st + kVec * j, f + kVec * j);
+}
 
 __device__ __forceinline__ int32_t find_seq(const int32_t* __restrict__ cu, int32_t n_seq, int64_t t) {
   // largest i in [0, n_seq) with cu[i] <= t
@@ -156,29 +187,32 @@ __global__ __launch_bounds__(kThreads) void conv1d_store_state_kernel(
   const int64_t lo = min((int64_t)cu[n], t_total);
   const int64_t len = min(max((int64_t)cu[n + 1], lo), t_total) - lo;
   T* st = conv_state + ((int64_t)slot * c_ch + c0) * (W - 1);
-  float old[kVec][W - 1];
+  // the old window matters only when the sequence is shorter than W - 1
+  float prev[W][kVec], nw[W][kVec];
+  if (init && len < W - 1) {
+    load_window<T, W>(st, prev);
+  } else {
 #pragma unroll
-  for (int i = 0; i < kVec; ++i)
+    for (int j = 0; j < W - 1; ++j)
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) old[i][j] = init ? to_f32(st[i * (W - 1) + j]) : 0.0f;
-  float nw[kVec][W - 1];
+      for (int i = 0; i < kVec; ++i) prev[j][i] = 0.0f;
+  }
 #pragma unroll
   for (int j = 0; j < W - 1; ++j) {
     const int64_t p = len - (W - 1) + j;  // position in the sequence; < 0 reaches into the old state
     if (p >= 0) {
-      float v[kVec];
-      load8(x + (lo + p) * c_ch + c0, v);
+      load8(x + (lo + p) * c_ch + c0, nw[j]);
+    } else {  // old window entry (W - 1) + p, selected without a runtime register index
 #pragma unroll
-      for (int i = 0; i < kVec; ++i) nw[i][j] = v[i];
-    } else {
+      for (int i = 0; i < kVec; ++i) {
+        float v = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kVec; ++i) nw[i][j] = old[i][(W - 1) + (int)p];
+        for (int t = 0; t < W - 1; ++t) v = t == (W - 1) + (int)p ? prev[t][i] : v;
+        nw[j][i] = v;
+      }
     }
   }
-#pragma unroll
-  for (int i = 0; i < kVec; ++i)
-#pragma unroll
-    for (int j = 0; j < W - 1; ++j) st[i * (W - 1) + j] = from_f32<T>(nw[i][j]);
+  store_window<T, W>(st, nw);
 }
 
 // Decode / MTP: one block per (request, channel block); the window lives in
@@ -201,11 +235,7 @@ __global__ __launch_bounds__(kThreads) void conv1d_update_kernel(
   Taps<T, W> taps;
   taps.load(wt, bias, c0);
   float win[W][kVec];
-  const T* st = conv_state + ((int64_t)slot * c_ch + c0) * (W - 1);
-#pragma unroll
-  for (int ii = 0; ii < kVec; ++ii)
-#pragma unroll
-    for (int j = 0; j < W - 1; ++j) win[j][ii] = to_f32(st[ii * (W - 1) + j]);
+  load_window<T, W>(conv_state + ((int64_t)slot * c_ch + c0) * (W - 1), win);
   for (int p = 0; p < t_step; ++p) {
     load8(x + (row0 + p) * c_ch + c0, win[W - 1]);
     float out[kVec];
@@ -217,22 +247,10 @@ __global__ __launch_bounds__(kThreads) void conv1d_update_kernel(
       for (int ii = 0; ii < kVec; ++ii) win[j][ii] = win[j + 1][ii];
     if (out_slots) {
       const int32_t d = out_slots[row0 + p];
-      if (slot_ok(d, n_slots)) {
-        T* dst = conv_state + ((int64_t)d * c_ch + c0) * (W - 1);
-#pragma unroll
-        for (int ii = 0; ii < kVec; ++ii)
-#pragma unroll
-          for (int j = 0; j < W - 1; ++j) dst[ii * (W - 1) + j] = from_f32<T>(win[j][ii]);
-      }
+      if (slot_ok(d, n_slots)) store_window<T, W>(conv_state + ((int64_t)d * c_ch + c0) * (W - 1), win);
     }
   }
-  if (!out_slots) {
-    T* dst = conv_state + ((int64_t)slot * c_ch + c0) * (W - 1);
-#pragma unroll
-    for (int ii = 0; ii < kVec; ++ii)
-#pragma unroll
-      for (int j = 0; j < W - 1; ++j) dst[ii * (W - 1) + j] = from_f32<T>(win[j][ii]);
-  }
+  if (!out_slots) store_window<T, W>(conv_state + ((int64_t)slot * c_ch + c0) * (W - 1), win);
 }
 
 template <typename T, int W>
