@@ -365,11 +365,13 @@ struct PrepLDS {
   static constexpr int A0 = FUSE ? QR : ROWS;       // + s * ATILE
   static constexpr int END_ROWS = FUSE ? (2 + G) * ROWS : ROWS;
   static constexpr int END_A = A0 + G * ATILE;
-  static constexpr int SM = (END_ROWS > END_A ? END_ROWS : END_A);  // r_k [C], then per head G, b [C] each
+  // r_k [C], then per head G, b, f_K, f_W [C] each
+  static constexpr int SM = (END_ROWS > END_A ? END_ROWS : END_A);
+  static constexpr int SMALL = (1 + 4 * G) * C * 4;
   static constexpr bool T_OVER_A = 2 * TTILE <= ATILE;
-  static constexpr int T0 = T_OVER_A ? A0 : SM + (1 + 2 * G) * C * 4;  // + s * (T_OVER_A ? ATILE : 2 * TTILE)
+  static constexpr int T0 = T_OVER_A ? A0 : SM + SMALL;  // + s * (T_OVER_A ? ATILE : 2 * TTILE)
   static constexpr int TSTEP = T_OVER_A ? ATILE : 2 * TTILE;
-  static constexpr int BYTES = T_OVER_A ? SM + (1 + 2 * G) * C * 4 : T0 + G * TSTEP;
+  static constexpr int BYTES = T_OVER_A ? SM + SMALL : T0 + G * TSTEP;
 };
 
 // Per (chunk, QK head's group of G V heads).  Everything runs on the raw q, k,
@@ -410,8 +412,10 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   float* sRK = reinterpret_cast<float*>(smem + L::SM);
   // per V head s (s may be a runtime value: addresses, not pointer arrays)
   auto sA = [&](int s) { return reinterpret_cast<float*>(smem + L::A0 + s * L::ATILE); };
-  auto sG = [&](int s) { return sRK + C + 2 * s * C; };
-  auto sB = [&](int s) { return sRK + 2 * C + 2 * s * C; };
+  auto sG = [&](int s) { return sRK + C + 4 * s * C; };
+  auto sB = [&](int s) { return sRK + 2 * C + 4 * s * C; };
+  auto sFK = [&](int s) { return sRK + 3 * C + 4 * s * C; };  // e^{G_n - G_t} r_k[t]
+  auto sFW = [&](int s) { return sRK + 4 * C + 4 * s * C; };  // b_t e^{G_t} r_k[t]
   auto sTW = [&](int s) { return reinterpret_cast<Op*>(smem + L::T0 + s * L::TSTEP); };
   auto sTU = [&](int s) { return reinterpret_cast<Op*>(smem + L::T0 + s * L::TSTEP) + C * LDT; };
 
@@ -683,6 +687,13 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   }
   __syncthreads();
 
+  // per-token column factors of W and K', once per (V head, token)
+  for (int e = tid; e < G * C; e += K::THREADS) {
+    const int s = e / C, t = e % C;
+    const float gt = sG(s)[t], rk = sRK[t];
+    sFK(s)[t] = fast_exp(sG(s)[C - 1] - gt) * rk;
+    sFW(s)[t] = sB(s)[t] * fast_exp(gt) * rk;
+  }
   // ---- T = (I + A)^-1 in place, per V head.  (a) diagonal 16x16 blocks, one
   // lane per column
   if (tid < G * CT * 16) {
@@ -759,7 +770,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float b = sB(s)[c4 + i];
-          tw[k][i] = from_f32<Op>(t[i] * b * fast_exp(sG(s)[c4 + i]) * sRK[c4 + i]);
+          tw[k][i] = from_f32<Op>(t[i] * sFW(s)[c4 + i]);
           tu[k][i] = from_f32<Op>(t[i] * b);
         }
       }
@@ -825,7 +836,6 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         store_pair<Op>(at<Op>(unit(s), K::W_OFF + (uint32_t)(mt * NPD + sp_w) * PB + lp), frag_from<Op>(wacc[0], -1.f),
                        DVT == 2 ? frag_from<Op>(wacc[DVT - 1], -1.f) : zf);
       }
-      const float g_n = sG(s)[C - 1];
 #pragma unroll
       for (int j = 0; j < DVT; ++j)
 #pragma unroll
@@ -834,9 +844,9 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
-            lo[i] = from_f32<Op>(to_f32(Kc[2 * sp][j][i]) * fast_exp(g_n - sG(s)[t0]) * sRK[t0]);
+            lo[i] = from_f32<Op>(to_f32(Kc[2 * sp][j][i]) * sFK(s)[t0]);
             hi[i] = from_f32<Op>(2 * sp + 1 < CT ? to_f32(Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j][i]) *
-                                                       fast_exp(g_n - sG(s)[t1 < C ? t1 : 0]) * sRK[t1 < C ? t1 : 0]
+                                                       sFK(s)[t1 < C ? t1 : 0]
                                                  : 0.f);
           }
           store_pair<Op>(at<Op>(unit(s), K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), lo, hi);
