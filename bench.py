@@ -110,11 +110,11 @@ def counter_traffic(workload: str, kernels) -> float | None:
 
 # kernels one gdn_chunk_prefill call launches on the split path
 CHUNK_SPLIT_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, false, 4, 2>",
-                       "void split::chunk_state_kernel<__bf16, 128, 64, 1>",
+                       "void split::chunk_state_kernel<__bf16, 128, 64, 1, 4>",
                        "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, false, 4>")
 # kernels one gdn_prefill call launches
 PREFILL_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, true, 4, 2>",
-                   "void split::chunk_state_kernel<__bf16, 128, 64, 1>",
+                   "void split::chunk_state_kernel<__bf16, 128, 64, 1, 4>",
                    "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, true, 4>",
                    "void conv1d_store_state_kernel<__bf16, 4>")
 
