@@ -24,7 +24,8 @@
 //   f_q = scale e^G r_q            (per token; the output pass reads raw q)
 // so every load is a 16- or 8-byte lane-contiguous vector.
 //
-//   chunk_index_kernel  first global chunk of every sequence (block scan)
+//   chunk_index_kernel  first global chunk of every sequence (block scan; only
+//                       with more than 8 sequences, else each wave scans)
 //   chunk_prep_kernel   per (chunk, V head, or both V heads of a QK head when
 //                       h_v = 2 h_k): q/k L2 norm, gates, Gram, T and the
 //                       operand fragments above
@@ -39,6 +40,7 @@ namespace split {
 
 template <int D>
 constexpr int kThreads = (D >= 128 ? 4 : (D >= 64 ? 2 : 1)) * 64;
+constexpr int kMaxConvW = 4;
 
 template <typename Op, int D, int C>
 struct Cfg {
@@ -63,7 +65,10 @@ struct Cfg {
   static constexpr int H_OFF = UT_OFF + C * D * (int)sizeof(Op);            // S^T at chunk start, [NPD][NT] pairs
   static constexpr int F_OFF = H_OFF + NPD * NT * PAIR * (int)sizeof(Op);   // e^{G_n}, then f_q [C]
   static constexpr int FQ_OFF = F_OFF + 16;                                 // scale e^{G_t} r_q[t]
-  static constexpr int UNIT = (FQ_OFF + C * 4 + 255) / 256 * 256;
+  // fused-input, a sequence's first chunk only: the old conv window of the q
+  // channels, [D][kMaxConvW - 1] like the conv state, for the output pass
+  static constexpr int HALO_OFF = FQ_OFF + C * 4;
+  static constexpr int UNIT = (HALO_OFF + D * (kMaxConvW - 1) * (int)sizeof(Op) + 255) / 256 * 256;
   // output kernel LDS: raw q rows, then (over them) the fp32 O tile, row-major
   static constexpr int LD_Q = D + 16;
   static constexpr int LD_O = D + 4;
@@ -82,6 +87,63 @@ __device__ __forceinline__ int32_t seq_of_chunk(const int32_t* __restrict__ csta
     if (cstart[mid] <= gc) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Chunk bookkeeping.  With more than kScanSeqs sequences, chunk_index_kernel
+// writes cstart (the first global chunk of every sequence) to the workspace.
+// Otherwise no index kernel runs (cstart == nullptr): every wave derives the
+// same numbers from cu_seqlens with a short scan in registers.  (Over 64
+// sequences of a varlen batch, 140k workgroups each scanning cost more than
+// the one-block index kernel they replace.)
+constexpr int kScanSeqs = 8;
+
+struct SeqScan {
+  int32_t excl, incl;  // this lane's sequence: first global chunk, one past its last
+};
+template <int C>
+__device__ __forceinline__ SeqScan seq_scan(const int32_t* __restrict__ cu, int32_t n_seq, int64_t t_total) {
+  const int lane = threadIdx.x & 63;
+  int32_t cnt = 0;
+  if (lane < n_seq) {
+    const int64_t lo = min((int64_t)cu[lane], t_total);
+    const int64_t hi = min(max((int64_t)cu[lane + 1], lo), t_total);
+    cnt = (int32_t)((hi - lo + C - 1) / C);
+  }
+  int32_t incl = cnt;
+  for (int off = 1; off < n_seq; off <<= 1) {  // (none for one sequence)
+    const int32_t up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  return {incl - cnt, incl};
+}
+
+// The sequence n holding global chunk gc and its first global chunk; n ==
+// n_seq when gc lies past the last chunk.  Wave-uniform; every lane calls it.
+template <int C>
+__device__ __forceinline__ void locate_chunk(const int32_t* __restrict__ cstart, const int32_t* __restrict__ cu,
+                                             int32_t n_seq, int64_t t_total, int32_t gc, int& n, int32_t& first) {
+  if (cstart) {
+    if (gc >= cstart[n_seq]) {
+      n = n_seq;
+      first = 0;
+      return;
+    }
+    n = seq_of_chunk(cstart, n_seq, gc);
+    first = cstart[n];
+    return;
+  }
+  const SeqScan sc = seq_scan<C>(cu, n_seq, t_total);
+  const int lane = threadIdx.x & 63;
+  n = __builtin_amdgcn_readfirstlane((int)__popcll(__ballot(lane < n_seq && sc.incl <= gc)));
+  first = __builtin_amdgcn_readfirstlane(__shfl(sc.excl, n < 64 ? n : 63));
+}
+
+// First global chunk of sequence n.  Every lane calls it.
+template <int C>
+__device__ __forceinline__ int32_t first_chunk(const int32_t* __restrict__ cstart, const int32_t* __restrict__ cu,
+                                               int32_t n_seq, int64_t t_total, int n) {
+  if (cstart) return cstart[n];
+  return __builtin_amdgcn_readfirstlane(__shfl(seq_scan<C>(cu, n_seq, t_total).excl, n));
 }
 
 // cstart[i] = sum over j < i of ceil(len_j / C), for i = 0..n_seq.  One block.
@@ -246,8 +308,8 @@ struct ConvIn {
   const void* x;
   const void* w;
   const void* bias;
-  const void* state;
-  int32_t slot;
+  const void* state;   // [rows][W-1] windows, channel c of this sequence at row state_row0 + c
+  int64_t state_row0;
   bool init;
   int64_t seq_lo;
 };
@@ -314,7 +376,7 @@ __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int
         const int64_t back = ci.seq_lo - pos;  // 1 .. W-1 steps before the sequence start
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          win[j][i] = ci.init ? to_f32(cst[((int64_t)ci.slot * c_ch + ch + i) * (W - 1) + (W - 1 - back)]) : 0.0f;
+          win[j][i] = ci.init ? to_f32(cst[(ci.state_row0 + ch + i) * (W - 1) + (W - 1 - back)]) : 0.0f;
       }
     }
 #pragma unroll
@@ -422,15 +484,17 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   const int hgroups = h_v / G;
   const int gc = blockIdx.x / hgroups;
   const int h0 = (blockIdx.x % hgroups) * G;  // first V head; G > 1 only when G == h_v / h_k
-  if (gc >= cstart[n_seq]) return;
-  const int n = seq_of_chunk(cstart, n_seq, gc);
+  int n;
+  int32_t first;
+  locate_chunk<C>(cstart, cu, n_seq, t_total, gc, n, first);
+  if (n >= n_seq) return;
   if (!slot_ok(slots[n], n_slots)) return;  // padding entry: nothing to prepare
   const int hk = h0 / (h_v / h_k);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int c_ch = 2 * h_k * D + h_v * D;
   const int64_t seq_lo = min((int64_t)cu[n], t_total);
   const int64_t seq_hi = min(max((int64_t)cu[n + 1], seq_lo), t_total);
-  const int64_t c0 = seq_lo + (int64_t)(gc - cstart[n]) * C;
+  const int64_t c0 = seq_lo + (int64_t)(gc - first) * C;
   const int nvalid = (int)min((int64_t)C, seq_hi - c0);
   auto unit = [&](int s) { return ws + ((int64_t)gc * h_v + h0 + s) * K::UNIT; };
   const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
@@ -528,7 +592,19 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     Op* sQf = reinterpret_cast<Op*>(smem + L::QR);
     {
       const int32_t slot = slots[n];
-      const ConvIn ci{conv.x, conv.w, conv.bias, conv.state, slot, has_init == nullptr || has_init[n] != 0, seq_lo};
+      const bool init = has_init == nullptr || has_init[n] != 0;
+      const ConvIn ci{conv.x, conv.w, conv.bias, conv.state, (int64_t)slot * c_ch, init, seq_lo};
+      // A sequence's first chunk keeps the old conv window of its q channels
+      // in its units: the chain pass stores the new windows before the output
+      // pass recomputes q.
+      if (gc == first && init) {
+        const T* cst = reinterpret_cast<const T*>(conv.state) + ((int64_t)slot * c_ch + hk * D) * (W - 1);
+        for (int e = tid; e < D * (W - 1); e += K::THREADS) {
+          const T v = cst[e];
+#pragma unroll
+          for (int s = 0; s < G; ++s) *at<T>(unit(s), K::HALO_OFF + e * (int)sizeof(T)) = v;
+        }
+      }
       // (destinations as element offsets from the LDS base, so the stores
       // stay LDS stores whichever part a thread's item falls in)
       int cols[2 + G], dst[2 + G];
@@ -878,7 +954,8 @@ template <typename Op, int D, int C, int NTW, int PD>
 __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
     const int32_t* __restrict__ cstart, unsigned char* __restrict__ ws, float* __restrict__ state,
-    int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v) {
+    int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v,
+    const Op* __restrict__ conv_x, Op* __restrict__ conv_state, int32_t c_ch, int32_t conv_w) {
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
   constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC, NTILE = NT / NTW;
@@ -909,6 +986,34 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
   }
   const bool init = has_init == nullptr || has_init[n] != 0;
   float* st_ptr = state + ((int64_t)slot * h_v + h) * D * D;
+  const int32_t gc0 = first_chunk<C>(cstart, cu, n_seq, t_total, n);
+
+  if (conv_x != nullptr) {
+    // Fused-input prefill: the sequence's final conv window, the last W-1
+    // rows of (old window ++ x), one channel per thread over the sequence's
+    // workgroups.  Every read of the old windows (the prep pass) is done, and
+    // the output pass takes its q halo from the units.
+    const int wm1 = conv_w - 1;
+    const int64_t len = hi - lo;
+    const int stride = 64 * MW * h_v * NTILE;
+    for (int c = (h * NTILE + tile) * 64 * MW + (int)tid; c < c_ch; c += stride) {
+      Op* cs = conv_state + ((int64_t)slot * c_ch + c) * wm1;
+      Op prev[kMaxConvW - 1], nw[kMaxConvW - 1];
+#pragma unroll
+      for (int j = 0; j < kMaxConvW - 1; ++j) prev[j] = j < wm1 && init && len < wm1 ? cs[j] : from_f32<Op>(0.f);
+#pragma unroll
+      for (int j = 0; j < kMaxConvW - 1; ++j) {
+        const int64_t p = len - wm1 + j;  // position in the sequence; < 0 reaches into the old window
+        Op v = from_f32<Op>(0.f);
+#pragma unroll
+        for (int t = 0; t < kMaxConvW - 1; ++t) v = t == wm1 + (int)p ? prev[t] : v;  // (no register index)
+        nw[j] = j < wm1 && p >= 0 ? conv_x[(lo + p) * c_ch + c] : v;
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxConvW - 1; ++j)
+        if (j < wm1) cs[j] = nw[j];
+    }
+  }
 
   f32x4 Sacc[SM][NTW];
 #pragma unroll
@@ -926,7 +1031,6 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
 
   const uint32_t lp = lane * 8 * sizeof(Op);  // a lane's pair within a pair tile
   const uint32_t lf = lane * 4 * sizeof(Op);  // a lane's fragment within a 16x16 tile
-  const int32_t gc0 = cstart[n];
   const int nch = (int)((hi - lo + C - 1) / C);
   // unit of chunk k of this sequence, clamped to the last one: loads past the
   // end re-read it, so every load is unconditional and the wait counts exact
@@ -1093,13 +1197,15 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
   __shared__ __attribute__((aligned(16))) float sO[K::OUT_BYTES / 4];
   const int gc = blockIdx.x / h_v;
   const int h = blockIdx.x % h_v;
-  if (gc >= cstart[n_seq]) return;
-  const int n = seq_of_chunk(cstart, n_seq, gc);
+  int n;
+  int32_t first;
+  locate_chunk<C>(cstart, cu, n_seq, t_total, gc, n, first);
+  if (n >= n_seq) return;
   if (!slot_ok(slots[n], n_slots)) return;  // the chain zeroed this sequence's outputs
   const uint32_t tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int64_t seq_lo = min((int64_t)cu[n], t_total);
   const int64_t seq_hi = min(max((int64_t)cu[n + 1], seq_lo), t_total);
-  const int64_t c0 = seq_lo + (int64_t)(gc - cstart[n]) * C;
+  const int64_t c0 = seq_lo + (int64_t)(gc - first) * C;
   const int nvalid = (int)min((int64_t)C, seq_hi - c0);
   const unsigned char* u = ws + ((int64_t)gc * h_v + h) * K::UNIT;
   const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
@@ -1112,8 +1218,10 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
   if constexpr (FUSE) {
     const int hk = h / (h_v / h_k);
     const int c_ch = 2 * h_k * D + h_v * D;
-    const ConvIn ci{conv.x, conv.w, conv.bias, conv.state, slots[n], has_init == nullptr || has_init[n] != 0,
-                    seq_lo};
+    // the window before the sequence start: the old q window the prep pass
+    // kept in this (first) chunk's unit, indexed like the conv state
+    const ConvIn ci{conv.x, conv.w, conv.bias, u + K::HALO_OFF, -(int64_t)hk * D,
+                    has_init == nullptr || has_init[n] != 0, seq_lo};
     const int cols[1] = {hk * D}, dst[1] = {0};
     stage_conv<T, Op, D, C, W, 1, 4, K::THREADS>(ci, c_ch, cols, c0, nvalid, sQ, dst, K::LD_Q, (int)tid);
   } else {
@@ -1224,13 +1332,16 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
 // which is what bounds many chains running at once (3 stages).
 constexpr int64_t kChainCUs = 256;
 
+// (conv_x non-null: the fused-input prefill, whose chain also stores the
+// final conv windows)
 template <typename Op, int D, int C, int NTW, int PD>
 hipError_t launch_chain(const ChunkArgs& a, int64_t groups, const int32_t* cstart, unsigned char* units,
-                        hipStream_t st) {
+                        const Op* conv_x, hipStream_t st) {
   constexpr int TW = Cfg<Op, D, C>::NT >= NTW ? NTW : Cfg<Op, D, C>::NT;
   hipLaunchKernelGGL((chunk_state_kernel<Op, D, C, TW, PD>), dim3((unsigned)(groups * (Cfg<Op, D, C>::NT / TW))),
                      dim3(kChainThreads<D>), 0, st, a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state,
-                     a.n_slots, (Op*)a.o, a.t_total, a.n_seq, a.s.h_v);
+                     a.n_slots, (Op*)a.o, a.t_total, a.n_seq, a.s.h_v, conv_x, (Op*)const_cast<void*>(a.conv_state),
+                     a.s.c_ch(), a.s.conv_w);
   return hipGetLastError();
 }
 
@@ -1244,19 +1355,23 @@ size_t ws_bytes(int32_t n_seq, int64_t t_total, int32_t h_v) {
   return idx_bytes(n_seq) + (size_t)max_chunks * h_v * K::UNIT;
 }
 
-// One split-path call: chunk index, prep, chain, output; FUSE computes q, k, v
-// (conv1d + SiLU of a.x, width W) and g, beta (from a.a_in, a.b_in) in the
-// prep and output kernels.
+// One split-path call: chunk index (more than kScanSeqs sequences), prep,
+// chain, output; FUSE computes q, k, v (conv1d + SiLU of a.x, width W) and
+// g, beta (from a.a_in, a.b_in) in the prep and output kernels, and stores
+// the final conv windows in the chain kernel.
 template <typename T, typename Op, int D, int C, bool FUSE = false, int W = 4>
 hipError_t run(const ChunkArgs& a, hipStream_t st) {
   using K = Cfg<Op, D, C>;
   static_assert(sizeof(T) == sizeof(Op), "the chain writes O in the activation type");
+  static_assert(W <= kMaxConvW, "conv window");
   if (a.n_seq == 0) return hipSuccess;
-  int32_t* cstart = reinterpret_cast<int32_t*>(a.workspace);
+  int32_t* cstart = a.n_seq > kScanSeqs ? reinterpret_cast<int32_t*>(a.workspace) : nullptr;
   unsigned char* units = reinterpret_cast<unsigned char*>(a.workspace) + idx_bytes(a.n_seq);
-  hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seq, a.t_total, (int32_t)C,
-                     cstart);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (cstart) {
+    hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seq, a.t_total, (int32_t)C,
+                       cstart);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
   const int64_t max_chunks = a.t_total / C + a.n_seq;
   if (max_chunks > 0) {
     // two V heads per QK head: one prep workgroup per QK head shares the q/k
@@ -1277,9 +1392,10 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   }
   const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
   const int64_t chains = groups * K::NT;
-  const hipError_t ce = chains <= kChainCUs       ? launch_chain<Op, D, C, 1, 4>(a, groups, cstart, units, st)
-                        : chains <= 4 * kChainCUs ? launch_chain<Op, D, C, 2, 3>(a, groups, cstart, units, st)
-                                                  : launch_chain<Op, D, C, 4, 3>(a, groups, cstart, units, st);
+  const Op* cx = FUSE ? reinterpret_cast<const Op*>(a.x) : nullptr;
+  const hipError_t ce = chains <= kChainCUs       ? launch_chain<Op, D, C, 1, 4>(a, groups, cstart, units, cx, st)
+                        : chains <= 4 * kChainCUs ? launch_chain<Op, D, C, 2, 3>(a, groups, cstart, units, cx, st)
+                                                  : launch_chain<Op, D, C, 4, 3>(a, groups, cstart, units, cx, st);
   if (ce != hipSuccess) return ce;
   if (max_chunks > 0)
     hipLaunchKernelGGL((chunk_out_kernel<T, Op, D, C, FUSE, W>), dim3((unsigned)(max_chunks * a.s.h_v)),

@@ -278,17 +278,6 @@ hipError_t fwd_impl(const ConvFwdArgs& a, hipStream_t st) {
 }
 
 template <typename T, int W>
-hipError_t store_state_impl(const ConvFwdArgs& a, hipStream_t st) {
-  const int c_ch = a.s.c_ch();
-  const int n_cblk = (c_ch / kVec + kThreads - 1) / kThreads;
-  if (a.n_seq == 0) return hipSuccess;
-  hipLaunchKernelGGL((conv1d_store_state_kernel<T, W>), dim3((unsigned)(a.n_seq * n_cblk)), dim3(kThreads), 0, st,
-                     (const T*)a.x, a.cu_seqlens, a.slots, a.has_init, (T*)a.conv_state, a.n_slots, a.t_total, c_ch,
-                     n_cblk);
-  return hipGetLastError();
-}
-
-template <typename T, int W>
 hipError_t update_impl(const ConvUpdateArgs& a, hipStream_t st) {
   const int c_ch = a.s.c_ch();
   const int n_cblk = (c_ch / kVec + kThreads - 1) / kThreads;
@@ -309,18 +298,6 @@ hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t st) {
     case 2 * 2: return fwd_impl<float, 2>(a, st);
     case 3 * 2: return fwd_impl<float, 3>(a, st);
     case 4 * 2: return fwd_impl<float, 4>(a, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_conv1d_store_state(const ConvFwdArgs& a, hipStream_t st) {
-  switch (a.s.conv_w * 2 + (a.bf16 ? 1 : 0)) {
-    case 2 * 2 + 1: return store_state_impl<bf16, 2>(a, st);
-    case 3 * 2 + 1: return store_state_impl<bf16, 3>(a, st);
-    case 4 * 2 + 1: return store_state_impl<bf16, 4>(a, st);
-    case 2 * 2: return store_state_impl<float, 2>(a, st);
-    case 3 * 2: return store_state_impl<float, 3>(a, st);
-    case 4 * 2: return store_state_impl<float, 4>(a, st);
   }
   return hipErrorInvalidValue;
 }

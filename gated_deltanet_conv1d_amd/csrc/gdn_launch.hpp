@@ -30,9 +30,6 @@ struct ConvFwdArgs {
   void* y;
 };
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t st);
-// Only the final-window write of launch_conv1d_fwd (y unused): the fused
-// prefill runs it after every kernel that reads the old conv state.
-hipError_t launch_conv1d_store_state(const ConvFwdArgs& a, hipStream_t st);
 
 struct ConvUpdateArgs {
   Shape s;
@@ -137,8 +134,8 @@ hipError_t launch_chunk_prefill(const ChunkArgs& a, hipStream_t st);
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t st);
 size_t chunk_split_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk);
 hipError_t launch_chunk_split(const ChunkArgs& a, hipStream_t st);
-// The fused-input prefill on the split path (a.x != nullptr); the caller runs
-// launch_conv1d_store_state afterwards.
+// The fused-input prefill on the split path (a.x != nullptr), final conv
+// windows included.
 hipError_t launch_prefill_fused(const ChunkArgs& a, hipStream_t st);
 
 }  // namespace gdn

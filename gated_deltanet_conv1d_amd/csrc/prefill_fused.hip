@@ -1,8 +1,10 @@
 // The fused-input prefill on the split path: the prep and output kernels
 // compute q, k, v as conv1d + SiLU of x in the chunk they work on (a W-1 row
 // halo, the slot's conv state before a sequence start), and g, beta from a, b,
-// so neither the conv output y nor g, beta ever reach HBM.  The final conv
-// windows are written afterwards, once every read of the old ones is done.
+// so neither the conv output y nor g, beta ever reach HBM.  The chain kernel
+// writes the final conv windows: the prep pass, which reads the old ones, is
+// done by then, and it keeps the old q window of every sequence's first
+// chunk in the workspace for the output pass.
 // The conv1d arithmetic, the gate formulas and everything downstream match
 // the separate gdn_conv1d_fwd + gdn_gating + gdn_chunk_prefill calls.
 #include "chunk_split_kernels.hpp"
@@ -40,10 +42,7 @@ hipError_t launch_prefill_fused(const ChunkArgs& a, hipStream_t st) {
     case 64: e = a.bf16 ? by_width<bf16, 64>(a, st) : by_width<float, 64>(a, st); break;
     case 128: e = a.bf16 ? by_width<bf16, 128>(a, st) : by_width<float, 128>(a, st); break;
   }
-  if (e != hipSuccess) return e;
-  const ConvFwdArgs c{a.s,         a.bf16,   a.n_seq, a.t_total,  a.x,       a.conv_w, a.conv_b,
-                      a.cu_seqlens, a.slots, a.has_init, const_cast<void*>(a.conv_state), a.n_slots, nullptr};
-  return launch_conv1d_store_state(c, st);
+  return e;
 }
 
 }  // namespace gdn

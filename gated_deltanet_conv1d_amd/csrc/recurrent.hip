@@ -78,22 +78,56 @@ __device__ __forceinline__ void st_f32(float* p, const float* v) {
     __builtin_nontemporal_store(v[0], p);
   }
 }
-template <int VW, typename T>
-__device__ __forceinline__ void ld_act(const T* p, float* v) {
-#pragma unroll
-  for (int i = 0; i < VW; ++i) v[i] = to_f32(p[i]);
-}
+// One token's inputs as loaded (raw activations, converted at use): q and k
+// of the QK head as vectors, this thread's v rows, its z rows (column lane 0
+// only) and the per-position state slot.
+template <typename T, int D>
+struct TokenIn {
+  using L = RowLayout<D>;
+  typedef T vec_t __attribute__((ext_vector_type(L::VW)));
+  vec_t k[L::NG], q[L::NG];
+  T v[L::PASSES], z[L::PASSES];
+  T a, b;
+  int32_t dst;
 
+  __device__ __forceinline__ void load(const T* __restrict__ qkv, const T* __restrict__ a_in,
+                                       const T* __restrict__ b_in, const int32_t* __restrict__ out_slots,
+                                       int64_t row, int c_ch, int hk, int h, int h_k, int h_v, int r16, int c) {
+    const T* q_ptr = qkv + row * c_ch + hk * D;
+    const T* k_ptr = qkv + row * c_ch + (h_k + hk) * D;
+    const T* v_ptr = qkv + row * c_ch + 2 * h_k * D + h * D;
+#pragma unroll
+    for (int j = 0; j < L::NG; ++j) {
+      k[j] = *reinterpret_cast<const vec_t*>(k_ptr + L::col(j, c));
+      q[j] = *reinterpret_cast<const vec_t*>(q_ptr + L::col(j, c));
+    }
+#pragma unroll
+    for (int p = 0; p < L::PASSES; ++p) v[p] = v_ptr[p * 16 + r16];
+    a = a_in[row * h_v + h];
+    b = b_in[row * h_v + h];
+    dst = out_slots ? out_slots[row] : -1;
+  }
+  __device__ __forceinline__ void load_z(const T* __restrict__ z_in, int64_t row, int h, int h_v, int r16, int c) {
+    const T* z_ptr = z_in + (row * h_v + h) * D;
+#pragma unroll
+    for (int p = 0; p < L::PASSES; ++p) z[p] = z_in && c == 0 ? z_ptr[p * 16 + r16] : from_f32<T>(0.0f);
+  }
+};
+
+// The step for one (request, V head).  In place (MTP false): the final state
+// goes back to slots[i].  MTP: the state after token t goes to out_slots[i][t],
+// and token t+1's inputs are requested before token t's output and 64 KiB
+// state stores: loads and stores share one counter that drains in issue order,
+// so inputs loaded after the stores would wait for every store to complete.
 template <typename T, int D, bool MTP>
-__global__ __launch_bounds__(kThreads) void recurrent_kernel(
+__device__ __forceinline__ void recurrent_step(
     const T* __restrict__ qkv, const T* __restrict__ a_in, const T* __restrict__ b_in,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, float* __restrict__ state, int32_t n_slots,
     const int32_t* __restrict__ slots, const int32_t* __restrict__ out_slots, T* __restrict__ o,
     const T* __restrict__ z, const T* __restrict__ norm_w, float norm_eps, float scale, int32_t t_step,
-    int32_t h_k, int32_t h_v) {
+    int32_t h_k, int32_t h_v, float* red) {
   using L = RowLayout<D>;
   constexpr int F = L::F, VW = L::VW, NG = L::NG, PASSES = L::PASSES;
-  __shared__ float red[kThreads / 64];
 
   const int i = blockIdx.x / h_v;
   const int h = blockIdx.x % h_v;
@@ -120,22 +154,23 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
 
   const float neg_A = -expf(A_log[h]);
   const float dtb = dt_bias[h];
+  TokenIn<T, D> in;
+  if (MTP) {
+    in.load(qkv, a_in, b_in, out_slots, (int64_t)i * t_step, c_ch, hk, h, h_k, h_v, r16, c);
+    in.load_z(z, (int64_t)i * t_step, h, h_v, r16, c);
+  }
 
   for (int t = 0; t < t_step; ++t) {
     const int64_t row = (int64_t)i * t_step + t;
-    const T* q_ptr = qkv + row * c_ch + hk * D;
-    const T* k_ptr = qkv + row * c_ch + (h_k + hk) * D;
-    const T* v_ptr = qkv + row * c_ch + 2 * h_k * D + h * D;
-
+    if (!MTP) in.load(qkv, a_in, b_in, out_slots, row, c_ch, hk, h, h_k, h_v, r16, c);
     float kv[F], qv[F];
 #pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      ld_act<VW>(k_ptr + L::col(j, c), &kv[j * VW]);
-      ld_act<VW>(q_ptr + L::col(j, c), &qv[j * VW]);
-    }
-    float vrow[PASSES];
+    for (int j = 0; j < NG; ++j)
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) vrow[p] = to_f32(v_ptr[p * 16 + r16]);
+      for (int e = 0; e < VW; ++e) {
+        kv[j * VW + e] = to_f32(in.k[j][e]);
+        qv[j * VW + e] = to_f32(in.q[j][e]);
+      }
 
     // q, k L2 norm over the head (eps 1e-6 inside the root) and k.q
     float sk = 0.f, sq = 0.f;
@@ -150,8 +185,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     kq = group_sum<16>(kq);
 
     // gating
-    const float g = neg_A * softplusf_(to_f32(a_in[row * h_v + h]) + dtb);
-    const float beta = sigmoidf_(to_f32(b_in[row * h_v + h]));
+    const float g = neg_A * softplusf_(to_f32(in.a) + dtb);
+    const float beta = sigmoidf_(to_f32(in.b));
     const float eg = expf(g);
 
     float orow[PASSES];
@@ -162,10 +197,20 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
       for (int e = 0; e < F; ++e) { dk = fmaf(s[p][e], kv[e], dk); dq = fmaf(s[p][e], qv[e], dq); }
       dk = group_sum<16>(dk);
       dq = group_sum<16>(dq);
-      const float u = beta * (vrow[p] - eg * dk);
+      const float u = beta * (to_f32(in.v[p]) - eg * dk);
       orow[p] = scale * (eg * dq + u * kq);
 #pragma unroll
       for (int e = 0; e < F; ++e) s[p][e] = fmaf(eg, s[p][e], u * kv[e]);
+    }
+    const int32_t pos_slot = in.dst;
+    float zrow[PASSES];
+    if (MTP) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) zrow[p] = to_f32(in.z[p]);
+      if (t + 1 < t_step) {
+        in.load(qkv, a_in, b_in, out_slots, row + 1, c_ch, hk, h, h_k, h_v, r16, c);
+        in.load_z(z, row + 1, h, h_v, r16, c);
+      }
     }
 
     T* o_ptr = o + (row * h_v + h) * D;
@@ -184,12 +229,16 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
       for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
       __syncthreads();
       const float rstd = fast_rsq(tot * (1.0f / D) + norm_eps);
-      const T* z_ptr = z + (row * h_v + h) * D;
+      if (!MTP) {
+        in.load_z(z, row, h, h_v, r16, c);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) zrow[p] = to_f32(in.z[p]);
+      }
       if (c == 0) {
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
           const int r = p * 16 + r16;
-          o_ptr[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * fast_silu(to_f32(z_ptr[r])));
+          o_ptr[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * fast_silu(zrow[p]));
         }
       }
     } else if (c == 0) {
@@ -197,40 +246,62 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
       for (int p = 0; p < PASSES; ++p) o_ptr[p * 16 + r16] = from_f32<T>(orow[p]);
     }
 
-    if (out_slots) {
-      const int32_t d = out_slots[row];
-      if (slot_ok(d, n_slots)) {
-        float* dst = state + ((int64_t)d * h_v + h) * D * D;
+    if (MTP && slot_ok(pos_slot, n_slots)) {
+      float* dp = state + ((int64_t)pos_slot * h_v + h) * D * D;
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p)
+      for (int p = 0; p < PASSES; ++p)
 #pragma unroll
-          for (int j = 0; j < NG; ++j) st_f32<VW, false>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
-      }
+        for (int j = 0; j < NG; ++j) st_f32<VW, false>(dp + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
     }
   }
 
-  if (!out_slots) {
-    float* dst = state + ((int64_t)slot * h_v + h) * D * D;
+  if (!MTP) {
+    float* dp = state + ((int64_t)slot * h_v + h) * D * D;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
 #pragma unroll
-      for (int j = 0; j < NG; ++j) st_f32<VW, !MTP>(dst + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+      for (int j = 0; j < NG; ++j) st_f32<VW, true>(dp + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
   }
 }
 
-template <typename T, int D, bool MTP>
-hipError_t impl_mode(const RecurrentArgs& a, hipStream_t st) {
-  if (a.n_seq == 0 || a.t_step == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_kernel<T, D, MTP>), dim3((unsigned)((int64_t)a.n_seq * a.s.h_v)), dim3(kThreads), 0, st,
-                     (const T*)a.qkv, (const T*)a.a, (const T*)a.b, a.A_log, a.dt_bias, a.state, a.n_slots, a.slots,
-                     a.out_slots, (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step,
-                     a.s.h_k, a.s.h_v);
-  return hipGetLastError();
+#define GDN_RECURRENT_ARGS                                                                                         \
+  const T *__restrict__ qkv, const T *__restrict__ a_in, const T *__restrict__ b_in,                               \
+      const float *__restrict__ A_log, const float *__restrict__ dt_bias, float *__restrict__ state,              \
+      int32_t n_slots, const int32_t *__restrict__ slots, const int32_t *__restrict__ out_slots,                    \
+      T *__restrict__ o, const T *__restrict__ z, const T *__restrict__ norm_w, float norm_eps, float scale,       \
+      int32_t t_step, int32_t h_k, int32_t h_v
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(GDN_RECURRENT_ARGS) {
+  __shared__ float red[kThreads / 64];
+  recurrent_step<T, D, false>(qkv, a_in, b_in, A_log, dt_bias, state, n_slots, slots, out_slots, o, z, norm_w,
+                              norm_eps, scale, t_step, h_k, h_v, red);
 }
+
+// (the prefetched inputs take it to two workgroups per CU; held to three,
+// as in place, it spills and runs 10 % slower)
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void recurrent_mtp_kernel(
+    GDN_RECURRENT_ARGS) {
+  __shared__ float red[kThreads / 64];
+  recurrent_step<T, D, true>(qkv, a_in, b_in, A_log, dt_bias, state, n_slots, slots, out_slots, o, z, norm_w,
+                             norm_eps, scale, t_step, h_k, h_v, red);
+}
+#undef GDN_RECURRENT_ARGS
 
 template <typename T, int D>
 hipError_t impl(const RecurrentArgs& a, hipStream_t st) {
-  return a.out_slots ? impl_mode<T, D, true>(a, st) : impl_mode<T, D, false>(a, st);
+  if (a.n_seq == 0 || a.t_step == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)a.n_seq * a.s.h_v));
+  if (a.out_slots)
+    hipLaunchKernelGGL((recurrent_mtp_kernel<T, D>), grid, dim3(kThreads), 0, st, (const T*)a.qkv, (const T*)a.a,
+                       (const T*)a.b, a.A_log, a.dt_bias, a.state, a.n_slots, a.slots, a.out_slots, (T*)a.o,
+                       (const T*)a.z, (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step, a.s.h_k, a.s.h_v);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<T, D>), grid, dim3(kThreads), 0, st, (const T*)a.qkv, (const T*)a.a,
+                       (const T*)a.b, a.A_log, a.dt_bias, a.state, a.n_slots, a.slots, a.out_slots, (T*)a.o,
+                       (const T*)a.z, (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step, a.s.h_k, a.s.h_v);
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -104,8 +104,9 @@ def test_chunk_prefill_workspace(L):
         return
     # split path: a 256-byte-aligned chunk index, then one 256-byte-aligned unit
     # per (chunk, V head) holding -W, K'^T, Ut (bf16, C x D each), P (bf16, C x C),
-    # the chunk-start state (bf16, D x D), e^{G_n} (16 bytes) and f_q (fp32, C)
-    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 255) // 256 * 256
+    # the chunk-start state (bf16, D x D), e^{G_n} (16 bytes), f_q (fp32, C) and
+    # the old conv window of the q channels (bf16, D x 3; single-call prefill)
+    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 128 * 3 * 2 + 255) // 256 * 256
     assert ws == 256 + (4096 // 64 + 1) * 32 * unit
     # (same sizes as the query, so these calls stop at validation and never launch)
     assert chunk_call(L, t_total=4096) == WS
@@ -132,7 +133,7 @@ def test_prefill_errors_and_workspace(L):
     assert prefill_call(L, n_seq=0, t_total=0) == OK
     # the same workspace as the split chunked path, whatever path gdn_chunk_prefill takes
     ws = L.gdn_prefill_workspace_size(D(), 0, 1, 4096, 64)
-    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 255) // 256 * 256
+    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 128 * 3 * 2 + 255) // 256 * 256
     assert ws == 256 + (4096 // 64 + 1) * 32 * unit
     assert prefill_call(L, t_total=4096) == WS                # (these stop at validation, never launch)
     assert prefill_call(L, t_total=4096, ws=FAKE, ws_bytes=ws - 1) == WS
