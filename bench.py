@@ -108,15 +108,15 @@ def counter_traffic(workload: str, kernels) -> float | None:
         return None
 
 
-# kernels one gdn_chunk_prefill call launches on the split path
-CHUNK_SPLIT_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, false, 4, 2>",
+# kernels one gdn_chunk_prefill call launches on the split path (one sequence:
+# no chunk index kernel)
+CHUNK_SPLIT_KERNELS = ("void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, false, 4, 2>",
                        "void split::chunk_state_kernel<__bf16, 128, 64, 1, 4>",
                        "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, false, 4>")
-# kernels one gdn_prefill call launches
-PREFILL_KERNELS = ("split::chunk_index_kernel", "void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, true, 4, 2>",
+# kernels one gdn_prefill call launches (the chain kernel also stores the conv windows)
+PREFILL_KERNELS = ("void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, true, 4, 2>",
                    "void split::chunk_state_kernel<__bf16, 128, 64, 1, 4>",
-                   "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, true, 4>",
-                   "void conv1d_store_state_kernel<__bf16, 4>")
+                   "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, true, 4>")
 
 
 def capture_graph(torch, fn):
@@ -242,7 +242,7 @@ def bench_prefill(args, torch, gdn, gi):
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": counter_traffic("prefill_4096", PREFILL_KERNELS),
-                  "kernel": "gdn_prefill (chunk_index + chunk_prep + chunk_state + chunk_out + conv1d_store_state)",
+                  "kernel": "gdn_prefill (chunk_prep + chunk_state + chunk_out)",
                   "algorithmic_bytes": nbytes,
                   "launch_ms": round(t_pre, 4),
                   "mfma": {"algorithmic_flops": flops, "achieved_tflops": round(flops / (t_pre * 1e-3) / 1e12, 2),
