@@ -1183,7 +1183,7 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
 // front; the fp32 tile then goes through LDS so the norm and the z / out
 // traffic run row-wise, 8 consecutive elements (16 bytes of bf16) per lane.
 template <typename T, typename Op, int D, int C, bool FUSE = false, int W = 4>
-__global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
+__global__ __launch_bounds__(kThreads<D>) __attribute__((amdgpu_waves_per_eu(3))) void chunk_out_kernel(
     const T* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
     const int32_t* __restrict__ cstart, const unsigned char* __restrict__ ws, int32_t n_slots, int32_t n_seq,
     int64_t t_total, int32_t h_k, int32_t h_v, T* __restrict__ o, const T* __restrict__ z,
@@ -1211,11 +1211,49 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
   const uint32_t lp = lane * 8 * sizeof(Op), lf = lane * 4 * sizeof(Op);
   const FragT zf = zero_frag<Op>();
 
-  // ---- all operand loads
+  // ---- all operand loads.  Fused-input: U, f_q and z are requested before
+  // the q conv staging so their latency overlaps it, h and P after it (the
+  // staging's taps and windows leave no registers for them).  Otherwise the
+  // q rows go first, then every operand.
+  Pair<Op> hp[NPD][DVT], pa[CT][NPC];
+  FragT Uf[CT][DVT];
+  f32x4 fq[CT];
+  Raw8<T> zr[RPT];  // this thread's z pieces of the epilogue rows
+  const int64_t o_ld = (int64_t)h_v * D;
+  const int e0 = (tid % LPR) * 8;
+  auto load_hp = [&]() {
+#pragma unroll
+    for (int sp = 0; sp < NPD; ++sp)
+#pragma unroll
+      for (int j = 0; j < DVT; ++j)
+        hp[sp][j].load_nt(at<Op>(u, K::H_OFF + (uint32_t)(sp * NT + wave * DVT + j) * PB + lp));
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int sp = 0; sp < NPC; ++sp)
+        if (2 * sp <= mt) pa[mt][sp].load_nt(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
+  };
+  auto load_uz = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt) fq[mt] = *at<f32x4>(u, K::FQ_OFF + 4 * (16 * mt + 4 * g4));
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt)
+#pragma unroll
+      for (int j = 0; j < DVT; ++j)
+        Uf[mt][j] = nt_ld(at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf));
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int r = (int)(tid / LPR) + k * RPP;
+      if (z && r < nvalid) zr[k].load_nt(z + (c0 + r) * o_ld + h * D + e0);
+      else zr[k].zero();
+    }
+  };
+
   // q rows of the chunk into LDS, 16-byte pieces: raw from qkv, or conv1d +
   // SiLU of x in the fused-input mode
   Op* sQ = reinterpret_cast<Op*>(sO);
   if constexpr (FUSE) {
+    load_uz();
     const int hk = h / (h_v / h_k);
     const int c_ch = 2 * h_k * D + h_v * D;
     // the window before the sequence start: the old q window the prep pass
@@ -1224,10 +1262,10 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
                     has_init == nullptr || has_init[n] != 0, seq_lo};
     const int cols[1] = {hk * D}, dst[1] = {0};
     stage_conv<T, Op, D, C, W, 1, 4, K::THREADS>(ci, c_ch, cols, c0, nvalid, sQ, dst, K::LD_Q, (int)tid);
+    load_hp();
   } else {
     const int hk = h / (h_v / h_k);
     const int c_ch = 2 * h_k * D + h_v * D;
-    const int e0 = (tid % LPR) * 8;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int r = (int)(tid / LPR) + k * RPP;
@@ -1238,27 +1276,9 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
         raw_store<Op>(*reinterpret_cast<const Raw8<Op>*>(&q), sQ + r * K::LD_Q + e0);
       }
     }
+    load_hp();
+    load_uz();
   }
-  Pair<Op> hp[NPD][DVT], pa[CT][NPC];
-  FragT Uf[CT][DVT];
-#pragma unroll
-  for (int sp = 0; sp < NPD; ++sp)
-#pragma unroll
-    for (int j = 0; j < DVT; ++j) hp[sp][j].load_nt(at<Op>(u, K::H_OFF + (uint32_t)(sp * NT + wave * DVT + j) * PB + lp));
-  f32x4 fq[CT];
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt) fq[mt] = *at<f32x4>(u, K::FQ_OFF + 4 * (16 * mt + 4 * g4));
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-    for (int j = 0; j < DVT; ++j)
-      Uf[mt][j] = nt_ld(at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf));
-#pragma unroll
-  for (int mt = 0; mt < CT; ++mt)
-#pragma unroll
-    for (int sp = 0; sp < NPC; ++sp)
-      if (2 * sp <= mt) pa[mt][sp].load_nt(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
-
   __syncthreads();
 
   // ---- O = diag(f_q) Q h^T + P U
@@ -1293,8 +1313,6 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
   __syncthreads();
 
   // ---- row-wise: gated RMSNorm and 16-byte stores
-  const int64_t o_ld = (int64_t)h_v * D;
-  const int e0 = (tid % LPR) * 8;
   float w[8];
   if (z) load8(norm_w + e0, w);
 #pragma unroll
@@ -1308,10 +1326,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_out_kernel(
     const int64_t off = (c0 + r) * o_ld + h * D + e0;
     if (z) {
       float zz[8];
-      if (live) load8_nt(z + off, zz);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zz[e] = 0.f;
+      zr[k].to_f32(zz);
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);

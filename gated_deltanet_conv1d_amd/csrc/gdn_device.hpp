@@ -105,6 +105,10 @@ template <typename T> struct Raw8;
 template <> struct Raw8<bf16> {
   uint4 u;
   __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_nt(const bf16* p) {
+    const u32x4_t v = nt_ld(reinterpret_cast<const u32x4_t*>(p));
+    u = make_uint4(v[0], v[1], v[2], v[3]);
+  }
   __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void to_f32(float* v) const {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -120,6 +124,11 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void load(const float* p) {
     u[0] = reinterpret_cast<const uint4*>(p)[0];
     u[1] = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    const u32x4_t a = nt_ld(reinterpret_cast<const u32x4_t*>(p)), b = nt_ld(reinterpret_cast<const u32x4_t*>(p) + 1);
+    u[0] = make_uint4(a[0], a[1], a[2], a[3]);
+    u[1] = make_uint4(b[0], b[1], b[2], b[3]);
   }
   __device__ __forceinline__ void zero() { u[0] = u[1] = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void to_f32(float* v) const {
