@@ -426,7 +426,7 @@ def bench_mtp(args, torch, gdn, gi):
     nbytes = decode_algorithmic(case.n, case.t_step, d.h_k, d.h_v, d.d_k, 2, case.t_step)
     copy_bytes = 2.0 * int(sel.sum()) * (d.h_v * d.d_v * d.d_k * 4 + d.c_ch * (d.conv_w - 1) * 2)
     gbs = nbytes / (t_rec * 1e-3) / 1e9
-    return {"workload": f"mtp_{case.n}x{case.t_step}", "kernel": "recurrent_kernel<bf16,128>",
+    return {"workload": f"mtp_{case.n}x{case.t_step}", "kernel": "recurrent_mtp_kernel<bf16,128>",
             "launch_ms": round(t_rec, 4), "conv_update_ms": round(t_conv, 4), "state_copy_ms": round(t_copy, 4),
             "algorithmic_bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
             "frac": round(gbs / HBM_PEAK_GBS, 4),
