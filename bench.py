@@ -17,7 +17,9 @@ Prints ONE JSON line: tokens/s for that step (value), the roofline of the
 dominant call (gdn_prefill), the decode state-update bandwidth (256
 requests x 1 token over a 512-slot fp32 state pool, pools rotated so states
 come from HBM), the ~271k-token varlen prefill and the 128 x 4-token MTP step
-as extra rows, and the fp64 CPU oracle timed on the host as a baseline.
+as extra rows, the decode step replayed as HIP graphs for a padded 256-request
+bucket, the prefill at one tensor-parallel rank's head counts (tp = 2, 4), and
+the fp64 CPU oracle timed on the host as a baseline.
 """
 from __future__ import annotations
 
@@ -251,6 +253,94 @@ def bench_prefill(args, torch, gdn, gi):
         inputs=dict(x=x, a=a, b=b, z=z, case=case))
 
 
+def bench_tp_shapes(args, torch, gdn, gi):
+    """The 4096-token single-sequence prefill (gdn_prefill) at one tensor-parallel
+    rank's head counts: h_k/h_v = 8/16 (tp = 2) and 4/8 (tp = 4), event-timed eager
+    launches.  A head-sharded layer runs these per rank with no exchange inside it."""
+    dev = torch.device("cuda")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    out = {}
+    for tp in (2, 4):
+        base = gi.QWEN3_NEXT
+        d = gi.Dims(base.h_k // tp, base.h_v // tp, base.d_k, base.d_v, base.conv_w)
+        case = gi.prefill_case(dims=d)
+        dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+        p = case.params
+        x, a, b, z = bf(case.seq_x(0)), bf(case.seq_a(0)), bf(case.seq_b(0)), bf(case.seq_z(0))
+        conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+        A_log, dt_bias = torch.from_numpy(p.A_log).to(dev), torch.from_numpy(p.dt_bias).to(dev)
+        cu = torch.tensor(case.cu_seqlens, dtype=torch.int32, device=dev)
+        slots = torch.zeros(1, dtype=torch.int32, device=dev)
+        has_init = torch.zeros(1, dtype=torch.uint8, device=dev)
+        conv_pool = torch.zeros((1, d.c_ch, d.conv_w - 1), dtype=torch.bfloat16, device=dev)
+        ssm_pool = torch.zeros((1, d.h_v, d.d_v, d.d_k), dtype=torch.float32, device=dev)
+        T = case.t_total
+        o = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(gdn.prefill_workspace_size(dims, 0, 1, T, case.chunk), dtype=torch.uint8, device=dev)
+        steps = max(min(args.steps, 50), 1)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+
+        def step(e=None):
+            if e: e[0].record()
+            gdn.prefill(dims, x, conv_w, a, b, A_log, dt_bias, cu, slots, conv_pool, ssm_pool, has_init, case.chunk,
+                        1.0, z, norm_w, 1e-6, o=o, workspace=ws)
+            if e: e[1].record()
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        for k in range(steps):
+            step(ev[k])
+        torch.cuda.synchronize()
+        t = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        out[f"tp{tp}_h{d.h_k}_{d.h_v}"] = {"gdn_prefill_ms": round(t, 4), "tokens_per_s_per_rank": round(T / (t * 1e-3), 1)}
+    return out
+
+
+def bench_decode_bucket(args, torch, gdn, gi):
+    """The decode step (gdn_conv1d_update + gdn_recurrent_decode) as a serving
+    loop runs it: captured once per state pool as a HIP graph for a fixed bucket
+    of 256 requests, of which 200 are live and 56 are pad entries (slot -1),
+    replayed over 3 pools so states come from HBM."""
+    case = gi.decode_case()
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    dev = torch.device("cuda")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(case.seed + 1)
+    live = 200
+    slots_np = case.slots.copy()
+    slots_np[live:] = -1
+    slots = torch.from_numpy(slots_np).to(dev)
+    x, a, b, z = bf(case.x()), bf(case.a()), bf(case.b()), bf(case.z())
+    p = case.params
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log, dt_bias = torch.from_numpy(p.A_log).to(dev), torch.from_numpy(p.dt_bias).to(dev)
+    y = torch.empty_like(x)
+    o = torch.empty((case.n, 1, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+    graphs = []
+    for _ in range(3):
+        ssm = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device=dev, generator=gen) * 0.02
+        conv = torch.randn((case.n_slots, d.c_ch, d.conv_w - 1), device=dev, generator=gen).to(torch.bfloat16)
+
+        def step(ssm=ssm, conv=conv):
+            gdn.conv1d_update(dims, x, conv_w, conv, slots, y=y)
+            gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, None, 1.0, z, norm_w, 1e-6, o=o)
+
+        graphs.append((capture_graph(torch, step), ssm, conv))
+    steps = max(args.steps, 30)
+    for k in range(6):
+        graphs[k % 3][0].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        graphs[k % 3][0].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    return {"workload": "decode_bucket256_live200", "bucket": case.n, "live": live, "graph_ms_per_step": round(ms, 4),
+            "tokens_per_s": round(live / (ms * 1e-3), 1)}
+
+
 def bench_decode(args, torch, gdn, gi):
     """256 requests x 1 token, in place, rotating over 3 state pools of 512 slots."""
     case = gi.decode_case()
@@ -462,6 +552,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-mtp", action="store_true")
+    ap.add_argument("--no-tp", action="store_true", help="skip the per-rank (tp = 2, 4) prefill rows")
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -480,6 +571,8 @@ def main() -> int:
     info = device_info()
     pre = bench_prefill(args, torch, gdn, gi)
     dec = None if args.no_decode else bench_decode(args, torch, gdn, gi)
+    bucket = None if args.no_decode else bench_decode_bucket(args, torch, gdn, gi)
+    tp = None if args.no_tp else bench_tp_shapes(args, torch, gdn, gi)
     mtp = None if args.no_mtp else bench_mtp(args, torch, gdn, gi)
     torch.cuda.empty_cache()
     var = None if args.no_varlen else bench_varlen(args, torch, gdn, gi)
@@ -509,8 +602,10 @@ def main() -> int:
         "eager_ms_per_step": round(pre["eager_ms_per_step"], 4),
         "separate_calls": pre["separate_calls"],
         "decode": dec,
+        "decode_bucket": bucket,
         "mtp": mtp,
         "varlen": var,
+        "tp_shapes": tp,
         "device": {**info, "copy_gbs": round(copy_gbs, 1)},
     }
     print(json.dumps(line), flush=True)
