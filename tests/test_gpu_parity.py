@@ -7,6 +7,8 @@ sampled sequences/heads otherwise (the ~271k-token varlen batch).
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -330,8 +332,12 @@ def test_batch_composition_does_not_change_a_sequence():
                 w = compare_prefill(dp, o, seqs=[0], heads=[0, 5, 31])
                 log(f"packed 9: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
                 assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
-    ref = res[(1, False)]
+    # gdn_prefill always runs the split evaluation; with GDN_PREFILL_PATH=fused
+    # the three-call path runs the one-workgroup-per-chain evaluation instead,
+    # whose rounding order differs, so each entry point is then its own reference
+    split_only = os.environ.get("GDN_PREFILL_PATH") == "fused"
     for key, got in res.items():
+        ref = res[(1, key[1] if split_only else False)]
         for r, g in zip(ref, got):
             assert torch.equal(r, g), f"sequence 0 differs with {key[0]} sequences (fused={key[1]})"
 
@@ -355,7 +361,11 @@ def test_many_short_sequences():
     dp.ssm_pool.copy_(ssm0)
     out_f = dp.run_fused()
     torch.cuda.synchronize()
-    assert torch.equal(out_f, ref[0]) and torch.equal(dp.ssm_pool, ref[1]) and torch.equal(dp.conv_pool, ref[2])
+    if os.environ.get("GDN_PREFILL_PATH") == "fused":  # different evaluations: each against the oracle
+        w = compare_prefill(dp, out_f)
+        assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
+    else:
+        assert torch.equal(out_f, ref[0]) and torch.equal(dp.ssm_pool, ref[1]) and torch.equal(dp.conv_pool, ref[2])
 
 
 def test_state_copy_bitwise_and_skips():
