@@ -181,7 +181,9 @@ def bench_prefill(args, torch, gdn, gi):
     g = torch.empty((T, d.h_v), dtype=torch.float32, device=dev)
     beta = torch.empty_like(g)
     o = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(gdn.chunk_prefill_workspace_size(dims, 0, 1, T, case.chunk), dtype=torch.uint8, device=dev)
+    # (one workspace serves both entry points: the larger of their sizes)
+    ws = torch.empty(max(gdn.chunk_prefill_workspace_size(dims, 0, 1, T, case.chunk),
+                         gdn.prefill_workspace_size(dims, 0, 1, T, case.chunk)), dtype=torch.uint8, device=dev)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -416,7 +418,8 @@ def bench_varlen(args, torch, gdn, gi):
     g = torch.empty((T, d.h_v), dtype=torch.float32, device=dev)
     beta = torch.empty_like(g)
     o = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(gdn.chunk_prefill_workspace_size(dims, 0, N, T, case.chunk), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(gdn.chunk_prefill_workspace_size(dims, 0, N, T, case.chunk),
+                         gdn.prefill_workspace_size(dims, 0, N, T, case.chunk)), dtype=torch.uint8, device=dev)
     steps = max(3, args.steps // 4)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
