@@ -556,6 +556,7 @@ def main() -> int:
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-mtp", action="store_true")
     ap.add_argument("--no-tp", action="store_true", help="skip the per-rank (tp = 2, 4) prefill rows")
+    ap.add_argument("--no-bucket", action="store_true", help="skip the padded decode-bucket graph row")
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -574,7 +575,7 @@ def main() -> int:
     info = device_info()
     pre = bench_prefill(args, torch, gdn, gi)
     dec = None if args.no_decode else bench_decode(args, torch, gdn, gi)
-    bucket = None if args.no_decode else bench_decode_bucket(args, torch, gdn, gi)
+    bucket = None if args.no_decode or args.no_bucket else bench_decode_bucket(args, torch, gdn, gi)
     tp = None if args.no_tp else bench_tp_shapes(args, torch, gdn, gi)
     mtp = None if args.no_mtp else bench_mtp(args, torch, gdn, gi)
     torch.cuda.empty_cache()

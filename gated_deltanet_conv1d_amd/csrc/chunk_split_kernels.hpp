@@ -29,7 +29,8 @@
 //   chunk_prep_kernel   per (chunk, V head, or both V heads of a QK head when
 //                       h_v = 2 h_k): q/k L2 norm, gates, Gram, T and the
 //                       operand fragments above
-//   chunk_state_kernel  per (sequence, V head, d_v tile): the chunk loop
+//   chunk_state_kernel  per (sequence, V head, d_v tile): the chunk loop; in
+//                       the single-call prefill also the final conv windows
 //   chunk_out_kernel    per (chunk, V head): O, gated RMSNorm over d_v, store
 #pragma once
 #include "gdn_device.hpp"

@@ -114,7 +114,9 @@ struct ChunkArgs {
   void* workspace;
   size_t ws_bytes;
   // Fused-input mode (x != nullptr): q, k, v are conv1d + SiLU of x, computed
-  // in the chunk kernels (qkv unused), and g, beta come from a, b (g, beta unused).
+  // in the chunk kernels (qkv unused), and g, beta come from a, b (g, beta
+  // unused).  conv_state is read for the window before each sequence and then
+  // updated in place with the final windows.
   const void* x = nullptr;
   const void* conv_w = nullptr;
   const void* conv_b = nullptr;

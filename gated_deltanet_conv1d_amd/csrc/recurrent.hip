@@ -18,7 +18,9 @@
 // consecutive-in-16-byte-groups columns, so every state load/store instruction
 // moves 256-byte contiguous row segments.  All D*D/256 values per thread are
 // loaded up front (D/16 rows x D/16 columns) so a workgroup has its whole
-// state in flight before the first reduction.
+// state in flight before the first reduction.  The MTP step is its own
+// kernel (recurrent_mtp_kernel): it writes one state per draft position and
+// requests each next token's inputs ahead of those stores.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
