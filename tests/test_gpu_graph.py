@@ -77,8 +77,14 @@ def test_prefill_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
-def test_decode_graph_replays_match_eager():
+@pytest.mark.parametrize("pad", [0, 3])
+def test_decode_graph_replays_match_eager(pad):
+    """The decode step captured once and replayed; with pad > 0 the last entries
+    of the bucket are pad slots (-1), as a serving loop fills a fixed-size
+    bucket: their output rows are zero and no pool slot they could name changes."""
     case = gi.decode_case(seed=22, n=8, n_slots=16, dims=gi.Dims(2, 4, 128, 128, 4))
+    if pad:
+        case.slots[case.n - pad:] = -1
     d = case.dims
     dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
     bf = lambda v: dev(v, torch.bfloat16)
@@ -113,5 +119,11 @@ def test_decode_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]) and torch.equal(ssm, ref[1]) and torch.equal(conv, ref[2]), f"replay {k}"
+        if pad:
+            assert torch.all(o[case.n - pad:] == 0), "pad rows must be zero"
+            live = set(int(v) for v in case.slots[:case.n - pad])
+            for sl in range(case.n_slots):
+                if sl not in live:
+                    assert torch.equal(ssm[sl], ssm0[sl]) and torch.equal(conv[sl], conv0[sl]), f"slot {sl} touched"
         step()  # eager work between replays
         torch.cuda.synchronize()
