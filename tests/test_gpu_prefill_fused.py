@@ -73,3 +73,19 @@ def test_fused_single_4096_vs_oracle():
     w = compare_prefill(dp, out)
     log(f"fused prefill 4096: out [{w['out']}] ssm [{w['ssm']}]")
     assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
+
+
+@pytest.mark.parametrize("h_k,h_v", [(8, 16), (4, 8)])
+def test_fused_at_tensor_parallel_rank_heads(h_k, h_v):
+    """gdn_prefill at one tensor-parallel rank's head counts (tp = 2 and 4 of
+    the 16/32-head layout), against the oracle: two sequences, one with
+    history, sampled V heads spanning both halves of each QK pairing."""
+    dims = gi.Dims(h_k, h_v, 128, 128, 4)
+    case = gi.varlen_case(seed=41 + h_k, dims=dims, lengths=np.array([300, 77]), n_slots=4)
+    case.has_init = np.array([0, 1], np.uint8)
+    dp = DevPrefill(case)
+    out = dp.run_fused()
+    torch.cuda.synchronize()
+    w = compare_prefill(dp, out, heads=[0, 1, h_v - 2, h_v - 1])
+    log(f"h_k={h_k} h_v={h_v}: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
+    assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
