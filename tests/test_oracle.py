@@ -7,6 +7,7 @@ plausible bugs in the oracle and checks that the pins fail on each.
 """
 from __future__ import annotations
 
+import inspect
 import math
 from fractions import Fraction
 
@@ -171,6 +172,105 @@ def pin_l2norm():
     return max(err, float(np.max(np.abs(cos - 1))))
 
 
+def _silu(x):
+    return x / (1.0 + math.exp(-x))
+
+
+def pin_layer_worked_example():
+    """The whole layer on a hand-worked case: T = 2 tokens, 1 QK head, 2 V heads,
+    d = 2, conv width 2, through layer_sequence, prefill_batch and the MTP
+    form of decode_batch.  Every expected value below is derived by hand from
+    the chosen inputs (worked in the comments), not by running the oracle's
+    code, so the pin checks the oracle's wiring: which of a, b feeds g and
+    beta, the [q | k | v] split and the V->QK head map, z's head slicing, the
+    per-position conv and state snapshots, and where the drivers store them.
+
+    Channels: q (0, 1), k (2, 3), v of V head 0 (4, 5), v of V head 1 (6, 7).
+    Taps (1, 2) on every channel: w[c, 1] multiplies the current token, so the
+    pre-activation is p[t] = x[t-1] + 2 x[t], with x[-1] the old conv window.
+    """
+    x_prev = np.array([2, 3, 0, -2, 1, 0, -1, 0.5])
+    x = np.array([[-1, -1, 1, 1, 1, -1, 0.5, 0.25],
+                  [1, 0.5, -0.5, 0.5, -1, 2, 1, -1]])
+    # p[0] = x_prev + 2 x[0] = [0, 1, 2, 0, 3, -2, 0, 1]
+    # p[1] = x[0] + 2 x[1]   = [1, 0, 0, 2, -1, 3, 5/2, -7/4]
+    p = np.array([[0, 1, 2, 0, 3, -2, 0, 1], [1, 0, 0, 2, -1, 3, 2.5, -1.75]])
+    y = np.vectorize(_silu)(p)
+    # q0 = (0, silu 1), q1 = (silu 1, 0); k0 = (silu 2, 0), k1 = (0, silu 2):
+    # normalised with eps = 1e-6 they are c1 e2, c1 e1, c2 e1, c2 e2
+    c1 = _silu(1.0) / math.sqrt(_silu(1.0) ** 2 + 1e-6)
+    c2 = _silu(2.0) / math.sqrt(_silu(2.0) ** 2 + 1e-6)
+    v = [[(y[0, 4], y[0, 5]), (y[0, 6], y[0, 7])], [(y[1, 4], y[1, 5]), (y[1, 6], y[1, 7])]]   # v[t][h]
+    # gates: A_log = (0, ln 2), dt_bias = (0, 1/2); softplus(ln m) = ln(1 + m)
+    #   head 0: a + dt_bias = 0, ln 3       -> e^g = 1/2, 1/4     (A = 1)
+    #   head 1: a + dt_bias = ln 3, 0       -> e^g = 1/16, 1/4    (A = 2)
+    #   beta = sigmoid(b): b = (ln 3, 0), (-ln 3, ln 7) -> 3/4, 1/2 and 1/4, 7/8
+    a = np.array([[0.0, math.log(3) - 0.5], [math.log(3), -0.5]])
+    b = np.array([[math.log(3), 0.0], [-math.log(3), math.log(7)]])
+    A_log, dt_bias = np.array([0.0, math.log(2)]), np.array([0.0, 0.5])
+    eg = np.array([[0.5, 1 / 16], [0.25, 0.25]])
+    beta = np.array([[0.75, 0.5], [0.25, 0.875]])
+    S0 = np.array([[[1, -1], [2, 0.5]], [[-0.5, 1], [1, -2]]])
+    scale = 0.5
+    # With k0 = c2 e1 the first token only rewrites column 1 of S, with
+    # k1 = c2 e2 the second only column 2 (u = beta (v - e^g S k), S <- e^g S + u k^T):
+    #   S1[:, 0] = e0 (1 - b0 c2^2) S0[:, 0] + b0 c2 v0,   S1[:, 1] = e0 S0[:, 1]
+    #   S2[:, 0] = e1 S1[:, 0],   S2[:, 1] = e1 (1 - b1 c2^2) S1[:, 1] + b1 c2 v1
+    # and q0 = c1 e2, q1 = c1 e1 read o0 = scale c1 S1[:, 1], o1 = scale c1 S2[:, 0].
+    S1, S2, o = np.zeros((2, 2, 2)), np.zeros((2, 2, 2)), np.zeros((2, 2, 2))
+    for h in range(2):
+        e0, e1, b0, b1 = eg[0, h], eg[1, h], beta[0, h], beta[1, h]
+        S1[h][:, 0] = e0 * (1 - b0 * c2 * c2) * S0[h][:, 0] + b0 * c2 * np.array(v[0][h])
+        S1[h][:, 1] = e0 * S0[h][:, 1]
+        S2[h][:, 0] = e1 * S1[h][:, 0]
+        S2[h][:, 1] = e1 * (1 - b1 * c2 * c2) * S1[h][:, 1] + b1 * c2 * np.array(v[1][h])
+        o[0, h] = scale * c1 * S1[h][:, 1]
+        o[1, h] = scale * c1 * S2[h][:, 0]
+    # epilogue per (token, V head): o / sqrt(mean o^2 + 1e-6) * w * silu(z)
+    z = np.array([[[1, -1], [2, 0]], [[0, 3], [-1, 1]]], dtype=np.float64)
+    norm_w = np.array([1.0, 0.5])
+    out = np.zeros((2, 2, 2))
+    for t in range(2):
+        for h in range(2):
+            r = math.sqrt((o[t, h, 0] ** 2 + o[t, h, 1] ** 2) / 2 + 1e-6)
+            out[t, h] = [o[t, h, e] / r * norm_w[e] * _silu(z[t, h, e]) for e in range(2)]
+
+    dims = (1, 2, 2, 2)
+    taps = np.tile([1.0, 2.0], (8, 1))
+    prm = dict(conv_w=taps, conv_b=None, A_log=A_log, dt_bias=dt_bias, norm_w=norm_w)
+    err = 0.0
+
+    def d(got, ref):
+        return float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))))
+
+    r = O.layer_sequence(x, a, b, z, taps, None, A_log, dt_bias, norm_w, x_prev[:, None], S0, dims, scale,
+                         1e-6, keep_states=True)
+    err = max(err, d(r["y"], y), d(np.exp(r["g"]), eg), d(r["beta"], beta), d(r["o"], o), d(r["out"], out),
+              d(r["ssm"], S2), d(r["ssm_states"][0], S1), d(r["ssm_states"][1], S2))
+    # conv windows (width 2 keeps one input): after token 0 it holds x[0], after token 1 x[1]
+    err = max(err, d(r["conv"], x[1][:, None]), d(r["conv_states"][0], x[0][:, None]),
+              d(r["conv_states"][1], x[1][:, None]))
+    # one V head alone reads its own z, gates and v
+    r1 = O.layer_sequence(x, a, b, z, taps, None, A_log, dt_bias, norm_w, x_prev[:, None], S0, dims, scale,
+                          1e-6, heads=[1])
+    err = max(err, d(r1["out"][:, 0], out[:, 1]), d(r1["ssm"][0], S2[1]))
+    # prefill driver: the sequence in slot 2, then a padding entry; slots 0, 1 untouched
+    conv_pool = np.stack([np.full((8, 1), 7.0), np.full((8, 1), 8.0), x_prev[:, None]])
+    ssm_pool = np.stack([np.full((2, 2, 2), 7.0), np.full((2, 2, 2), 8.0), S0])
+    xs, as_, bs, zs = (np.concatenate([u, u[:1]]) for u in (x, a, b, z))
+    got, cp, sp = O.prefill_batch(xs, as_, bs, zs, [0, 2, 3], [2, -1], [1, 1], conv_pool, ssm_pool, prm, dims,
+                                  scale)
+    err = max(err, d(got[:2], out), d(got[2], 0.0), d(cp[2], x[1][:, None]), d(sp[2], S2),
+              d(cp[:2], conv_pool[:2]), d(sp[:2], ssm_pool[:2]))
+    # MTP draft step from home slot 0: the state after token p goes to out_slots[0][p]
+    got, cp, sp = O.decode_batch(x[None], a[None], b[None], z[None], [0], [[3, 1]],
+                                 np.stack([x_prev[:, None], conv_pool[0], conv_pool[1], conv_pool[1]]),
+                                 np.stack([S0, ssm_pool[0], ssm_pool[1], ssm_pool[1]]), prm, dims, scale)
+    err = max(err, d(got[0], out), d(cp[3], x[0][:, None]), d(sp[3], S1), d(cp[1], x[1][:, None]),
+              d(sp[1], S2), d(cp[0], x_prev[:, None]), d(sp[0], S0), d(cp[2], conv_pool[1]))
+    return err
+
+
 PINS = {
     "exact_product_form": (pin_exact_product_form, 1e-12),
     "chunked_equals_recurrent": (pin_chunked_equals_recurrent, 1e-11),
@@ -181,6 +281,7 @@ PINS = {
     "gating_vs_torch": (pin_gating_vs_torch, 1e-13),
     "rmsnorm_vs_torch": (pin_rmsnorm_vs_torch, 1e-13),
     "l2norm": (pin_l2norm, 1e-13),
+    "layer_worked_example": (pin_layer_worked_example, 1e-12),
 }
 
 
@@ -378,6 +479,16 @@ _orig_conv = O.causal_conv1d_silu
 _orig_qk_head = O.qk_head
 _orig_rms = O.gated_rmsnorm
 
+def _mutated(fn_name, old, new):
+    """A copy of oracle function fn_name with one source fragment replaced
+    (a wiring mistake planted in the oracle; it runs on the CPU only)."""
+    src = inspect.getsource(getattr(O, fn_name))
+    assert old in src, (fn_name, old)
+    ns = dict(vars(O))
+    exec(compile(src.replace(old, new), O.__file__, "exec"), ns)
+    return ns[fn_name]
+
+
 MUTATIONS = {
     "no_decay": ("delta_step", _mut_no_decay),
     "update_sign": ("delta_step", _mut_sign),
@@ -393,6 +504,13 @@ MUTATIONS = {
                             np.asarray(x) / (np.sum(np.asarray(x) ** 2, -1, keepdims=True) + eps)),
     "rmsnorm_sum_not_mean": ("gated_rmsnorm", lambda o, z, w, eps:
                              _orig_rms(o, z, w, eps) / math.sqrt(np.asarray(o).shape[-1])),
+    "gates_a_b_swapped": ("layer_sequence", _mutated("layer_sequence", "gating(a, b,", "gating(b, a,")),
+    "z_heads_reversed": ("layer_sequence", _mutated("layer_sequence", "_f64(z)[:, hs]", "_f64(z)[:, hs[::-1]]")),
+    "z_first_heads": ("layer_sequence", _mutated("layer_sequence", "_f64(z)[:, hs]", "_f64(z)[:, :len(hs)]")),
+    "conv_snapshot_off_by_one": ("layer_sequence", _mutated("layer_sequence", "x[: p + 1]", "x[: p + 2]")),
+    "qkv_split_k_before_q": ("split_qkv", _mutated("split_qkv", "q = y[:, : h_k * d_k]", "q = y[:, h_k * d_k: 2 * h_k * d_k]")),
+    "mtp_snapshot_of_next_token": ("decode_batch", _mutated("decode_batch", 'r["ssm_states"][p]', 'r["ssm_states"][-1]')),
+    "prefill_state_to_wrong_slot": ("prefill_batch", _mutated("prefill_batch", "ssm_pool[s] = r[\"ssm\"]", "ssm_pool[s - 1] = r[\"ssm\"]")),
 }
 
 
