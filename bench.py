@@ -241,8 +241,7 @@ def bench_prefill(args, torch, gdn, gi):
                         "eager_ms_per_step": round(wall_sep_eager / args.steps * 1e3, 4),
                         "kernels_ms": {"gdn_conv1d_fwd": round(t_conv, 4), "gdn_gating": round(t_gate, 4),
                                        "gdn_chunk_prefill": round(t_chunk, 4)},
-                        "chunk_traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)
-                        if os.environ.get("GDN_PREFILL_PATH", "split") == "split" else None},
+                        "chunk_traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": counter_traffic("prefill_4096", PREFILL_KERNELS),

@@ -27,6 +27,10 @@ size_t ws_by_chunk(int chunk, int32_t n_seq, int64_t t_total, int32_t h_v) {
 
 }  // namespace split
 
+bool chunk_supported(int d, int chunk, bool) {
+  return (d == 16 || d == 32 || d == 64 || d == 128) && (chunk == 16 || chunk == 32 || chunk == 64);
+}
+
 size_t chunk_split_workspace_size(const Shape& s, bool is_bf16, int32_t n_seq, int64_t t_total, int32_t chunk) {
   switch (s.d) {
     case 16: return is_bf16 ? split::ws_by_chunk<bf16, bf16, 16>(chunk, n_seq, t_total, s.h_v)

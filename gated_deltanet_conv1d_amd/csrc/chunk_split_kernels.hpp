@@ -1,6 +1,9 @@
 // Chunked gated delta rule, split into a chunk-parallel preparation pass and
-// a state pass that runs per (sequence, V head, 16-column d_v tile).  Same math
-// as chunk_prefill.hip (the chunked WY / UT form of the gated delta rule):
+// a state pass that runs per (sequence, V head, 16-column d_v tile).  The
+// math is the chunked WY / UT form of the gated delta rule, from unrolling
+// S_t = e^{g_t} S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T (row form, S in
+// R^{d_v x d_k}) over a chunk with incoming state S0 and inclusive cumulative
+// log-decay G_i = g_1 + ... + g_i:
 //   A = strict-lower(b_i e^{G_i-G_j} k_i.k_j),  T = (I + A)^{-1},
 //   W = T diag(b e^G) K,  Ut = T diag(b) V,  P = M o Q K^T        (no state)
 //   U = Ut - W S0^T,  O = diag(e^G) Q S0^T + P U,

@@ -121,7 +121,7 @@ size_t gdn_chunk_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32
                                         int32_t chunk) {
   Shape s;
   if (check_dims(dims, &s) != GDN_OK || check_act(act) != GDN_OK || n_seq < 0 || t_total < 0) return 0;
-  return gdn::chunk_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
+  return gdn::chunk_split_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
 }
 
 int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk, float scale,
@@ -141,11 +141,11 @@ int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t 
   if (z && !norm_w) return GDN_ERR_NULL;
   if (!(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
   GDN_TRY(align_ok(qkv, state, o, z, workspace));
-  const size_t need_ws = gdn::chunk_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
-  if (need_ws > 0 && (!workspace || ws_bytes < need_ws)) return GDN_ERR_WORKSPACE;
+  const size_t need_ws = gdn::chunk_split_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
+  if (!workspace || ws_bytes < need_ws) return GDN_ERR_WORKSPACE;
   gdn::ChunkArgs a{s,     act == GDN_BF16, n_seq,  t_total, chunk,  scale,    qkv,      g,         beta,    cu_seqlens,
                    slots, has_init,        state,  n_slots, o,      z,        norm_w,   norm_eps,  workspace, ws_bytes};
-  return from_hip(gdn::launch_chunk_prefill(a, (hipStream_t)stream));
+  return from_hip(gdn::launch_chunk_split(a, (hipStream_t)stream));
 }
 
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk) {

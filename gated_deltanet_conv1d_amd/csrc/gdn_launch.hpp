@@ -128,12 +128,9 @@ struct ChunkArgs {
 };
 // True when the chunk kernels have an instantiation for (d, chunk, dtype).
 bool chunk_supported(int d, int chunk, bool bf16);
-size_t chunk_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk);
-hipError_t launch_chunk_prefill(const ChunkArgs& a, hipStream_t st);
-// The two evaluations of the chunked form (selected by launch_chunk_prefill):
-// one fused workgroup per (sequence, V head), or a chunk-parallel preparation
-// pass followed by a per-(sequence, V head) state pass through a workspace.
-hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t st);
+// The chunked form runs as a chunk-parallel preparation pass, a per-(sequence,
+// V head, d_v tile) state pass and a chunk-parallel output pass, which talk
+// through a caller-owned workspace of this many bytes.
 size_t chunk_split_workspace_size(const Shape& s, bool bf16, int32_t n_seq, int64_t t_total, int32_t chunk);
 hipError_t launch_chunk_split(const ChunkArgs& a, hipStream_t st);
 // The fused-input prefill on the split path (a.x != nullptr), final conv

@@ -42,7 +42,7 @@
  *  - Returns GDN_OK or a negative gdn_status.  Argument errors are reported
  *    before anything is enqueued; GDN_ERR_HIP means a launch failed.
  *  - Supported sizes: d_k == d_v in {16, 32, 64, 128}; h_v a multiple of h_k;
- *    conv_w in {2, 3, 4}; chunk in {16, 32, 64} (fp32 with d = 128: chunk <= 32).
+ *    conv_w in {2, 3, 4}; chunk in {16, 32, 64}.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -142,7 +142,7 @@ size_t gdn_chunk_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32
  *   o          act [t_total][h_v][d_v]     output
  *   z          act [t_total][h_v][d_v] or NULL;  norm_w act [d_v] (needed with z)
  *   workspace  device scratch of at least gdn_chunk_prefill_workspace_size() bytes
- *              (may be NULL when that size is 0)
+ *              (a pure function of the sizes; never NULL when n_seq > 0)
  * The result does not depend on `chunk` in exact arithmetic.
  */
 int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk,

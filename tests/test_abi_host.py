@@ -88,7 +88,7 @@ def chunk_call(L, dims=None, act=0, n_seq=1, t_total=64, chunk=64, z=None, norm_
 def test_chunk_prefill_errors(L):
     assert chunk_call(L, chunk=48) == UNSUP
     assert chunk_call(L, chunk=128) == UNSUP
-    assert chunk_call(L, act=1, chunk=64) == UNSUP          # fp32 at d=128 takes chunk <= 32
+    assert chunk_call(L, act=1, chunk=64) == WS             # fp32 at d=128, C=64 is supported
     assert chunk_call(L, z=FAKE) == NULL                     # z without norm_w
     assert chunk_call(L, eps=-1.0) == SHAPE
     assert chunk_call(L, qkv=None) == NULL
@@ -99,10 +99,7 @@ def test_chunk_prefill_errors(L):
 
 def test_chunk_prefill_workspace(L):
     ws = L.gdn_chunk_prefill_workspace_size(D(), 0, 1, 4096, 64)
-    if os.environ.get("GDN_PREFILL_PATH") == "fused":
-        assert ws == 0
-        return
-    # split path: a 256-byte-aligned chunk index, then one 256-byte-aligned unit
+    # a 256-byte-aligned chunk index, then one 256-byte-aligned unit
     # per (chunk, V head) holding -W, K'^T, Ut (bf16, C x D each), P (bf16, C x C),
     # the chunk-start state (bf16, D x D), e^{G_n} (16 bytes), f_q (fp32, C) and
     # the old conv window of the q channels (bf16, D x 3; single-call prefill)
@@ -122,7 +119,7 @@ def prefill_call(L, dims=None, act=0, n_seq=1, t_total=64, chunk=64, x=FAKE, a=F
 
 def test_prefill_errors_and_workspace(L):
     assert prefill_call(L, chunk=48) == UNSUP
-    assert prefill_call(L, act=1, chunk=64) == UNSUP          # fp32 at d=128 takes chunk <= 32
+    assert prefill_call(L, act=1, chunk=64) == WS             # fp32 at d=128, C=64 is supported
     assert prefill_call(L, z=FAKE) == NULL                     # z without norm_w
     assert prefill_call(L, eps=-1.0) == SHAPE
     assert prefill_call(L, x=None) == NULL
@@ -131,7 +128,7 @@ def test_prefill_errors_and_workspace(L):
     assert prefill_call(L, x=FAKE + 8) == ALIGN
     assert prefill_call(L, n_seq=0, t_total=5) == SHAPE
     assert prefill_call(L, n_seq=0, t_total=0) == OK
-    # the same workspace as the split chunked path, whatever path gdn_chunk_prefill takes
+    # the same workspace as gdn_chunk_prefill
     ws = L.gdn_prefill_workspace_size(D(), 0, 1, 4096, 64)
     unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 128 * 3 * 2 + 255) // 256 * 256
     assert ws == 256 + (4096 // 64 + 1) * 32 * unit

@@ -7,7 +7,6 @@ sampled sequences/heads otherwise (the ~271k-token varlen batch).
 """
 from __future__ import annotations
 
-import os
 
 import numpy as np
 import pytest
@@ -59,8 +58,8 @@ def test_tiny_case_recurrent_and_chunked():
 SMALL_LENGTHS = [1, 3, 17, 64, 65, 200, 0, 130]
 
 
-@pytest.mark.parametrize("act,d,chunk", [("bf16", 128, 64), ("f32", 128, 32), ("bf16", 64, 32), ("f32", 16, 16),
-                                         ("bf16", 32, 16), ("f32", 64, 64)])
+@pytest.mark.parametrize("act,d,chunk", [("bf16", 128, 64), ("f32", 128, 64), ("f32", 128, 32), ("bf16", 64, 32),
+                                         ("f32", 16, 16), ("bf16", 32, 16), ("f32", 64, 64)])
 def test_prefill_small_varlen(act, d, chunk):
     """Several sequences (ragged tails, len 0 and 1, mixed has_init, permuted
     slots, one padding entry) through conv -> gating -> chunked rule ->
@@ -332,12 +331,8 @@ def test_batch_composition_does_not_change_a_sequence():
                 w = compare_prefill(dp, o, seqs=[0], heads=[0, 5, 31])
                 log(f"packed 9: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
                 assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
-    # gdn_prefill always runs the split evaluation; with GDN_PREFILL_PATH=fused
-    # the three-call path runs the one-workgroup-per-chain evaluation instead,
-    # whose rounding order differs, so each entry point is then its own reference
-    split_only = os.environ.get("GDN_PREFILL_PATH") == "fused"
     for key, got in res.items():
-        ref = res[(1, key[1] if split_only else False)]
+        ref = res[(1, False)]
         for r, g in zip(ref, got):
             assert torch.equal(r, g), f"sequence 0 differs with {key[0]} sequences (fused={key[1]})"
 
@@ -361,11 +356,7 @@ def test_many_short_sequences():
     dp.ssm_pool.copy_(ssm0)
     out_f = dp.run_fused()
     torch.cuda.synchronize()
-    if os.environ.get("GDN_PREFILL_PATH") == "fused":  # different evaluations: each against the oracle
-        w = compare_prefill(dp, out_f)
-        assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
-    else:
-        assert torch.equal(out_f, ref[0]) and torch.equal(dp.ssm_pool, ref[1]) and torch.equal(dp.conv_pool, ref[2])
+    assert torch.equal(out_f, ref[0]) and torch.equal(dp.ssm_pool, ref[1]) and torch.equal(dp.conv_pool, ref[2])
 
 
 def test_state_copy_bitwise_and_skips():

@@ -5,7 +5,6 @@ since it runs the same arithmetic in the same order, and it is checked
 against the oracle on its own as well."""
 from __future__ import annotations
 
-import os
 
 import numpy as np
 import pytest
@@ -26,9 +25,7 @@ def _small_case(act, d, chunk, conv_w, seed=31):
     return case
 
 
-@pytest.mark.skipif(os.environ.get("GDN_PREFILL_PATH") == "fused",
-                    reason="bit equality holds against the split chunked path")
-@pytest.mark.parametrize("act,d,chunk,conv_w", [("bf16", 128, 64, 4), ("f32", 128, 32, 4), ("bf16", 64, 32, 3),
+@pytest.mark.parametrize("act,d,chunk,conv_w", [("bf16", 128, 64, 4), ("f32", 128, 64, 4), ("f32", 128, 32, 4), ("bf16", 64, 32, 3),
                                                 ("f32", 16, 16, 2), ("bf16", 32, 16, 4), ("bf16", 128, 16, 2)])
 def test_fused_equals_separate_calls(act, d, chunk, conv_w):
     case = _small_case(act, d, chunk, conv_w)
