@@ -38,6 +38,8 @@ SIGNATURES = {
                                    _I32, _P, _P, _P, _F, _P, _SZ, _P]),
     "gdn_recurrent_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
                                             _P, _F, _P]),
+    "gdn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
+                                  _P, _P, _F, _P]),
     "gdn_state_copy": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
 }
 
@@ -255,6 +257,32 @@ def recurrent_decode(dims: Dims, qkv, a, b, A_log, dt_bias, state, slots, out_sl
                                       _ptr(o, qkv.dtype, "o"), _ptr(z, qkv.dtype, "z"),
                                       _ptr(norm_w, qkv.dtype, "norm_w"), norm_eps, _stream()),
            "gdn_recurrent_decode")
+    return o
+
+
+def decode(dims: Dims, x, conv_w, a, b, A_log, dt_bias, slots, conv_state, state, out_slots=None,
+           scale: float = 1.0, z=None, norm_w=None, norm_eps: float = 1e-6, conv_b=None, o=None):
+    """The whole decode / MTP step in one call (gdn_decode): conv window update,
+    gating, the recurrent step and the epilogue over request-major rows
+    [n_seq, t_step, ...].  Returns out [n_seq, t_step, h_v, d_v]."""
+    act = _act(x)
+    n_seq, t_step = x.shape[0], x.shape[1]
+    _shape(x, (n_seq, t_step, dims.c_ch), "x")
+    _shape(conv_w, (dims.c_ch, dims.conv_w), "conv_w")
+    _shape(a, (n_seq, t_step, dims.h_v), "a")
+    _shape(b, (n_seq, t_step, dims.h_v), "b")
+    _shape(slots, (n_seq,), "slots")
+    if out_slots is not None:
+        _shape(out_slots, (n_seq, t_step), "out_slots")
+    if o is None:
+        o = torch.empty((n_seq, t_step, dims.h_v, dims.d_v), dtype=x.dtype, device=x.device)
+    _check(lib().gdn_decode(ctypes.byref(_cdims(dims)), act, n_seq, t_step, scale, _ptr(x, x.dtype, "x"),
+                            _ptr(conv_w, x.dtype, "conv_w"), _ptr(conv_b, x.dtype, "conv_b"), _ptr(a, x.dtype, "a"),
+                            _ptr(b, x.dtype, "b"), _ptr(A_log, torch.float32, "A_log"),
+                            _ptr(dt_bias, torch.float32, "dt_bias"), _ptr(conv_state, x.dtype, "conv_state"),
+                            _ptr(state, torch.float32, "state"), state.shape[0], _ptr(slots, torch.int32, "slots"),
+                            _ptr(out_slots, torch.int32, "out_slots"), _ptr(o, x.dtype, "o"), _ptr(z, x.dtype, "z"),
+                            _ptr(norm_w, x.dtype, "norm_w"), norm_eps, _stream()), "gdn_decode")
     return o
 
 

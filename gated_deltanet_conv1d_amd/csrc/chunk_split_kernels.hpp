@@ -21,11 +21,14 @@
 // chunk-parallel.  The prep pass writes the operands as ready-made MFMA
 // fragments:
 //   -W                             (A operand, contraction over d_k)
-//   K'^T = (diag(e^{G_n-G}) K)^T   (A operand, contraction over the chunk)
-//   scale P                        (A operand, lower triangle)
+//   K^T                            (A operand, contraction over the chunk; raw k)
+//   scale P                        (A operand, lower triangle; bf16 as hi + lo)
 //   Ut                             (accumulator layout; the chain turns it into U)
 //   f_q = scale e^G r_q            (per token; the output pass reads raw q)
-// so every load is a 16- or 8-byte lane-contiguous vector.
+//   f_k = e^{G_n-G} r_k            (per token; the chain scales U's rows by it)
+// so every load is a 16- or 8-byte lane-contiguous vector.  The state update
+// K'^T U with K' = diag(f_k) K runs as K^T (diag(f_k) U): k enters exactly as
+// the bf16 conv output, and the one rounding is that of the scaled U.
 //
 //   chunk_index_kernel  first global chunk of every sequence (block scan; only
 //                       with more than 8 sequences, else each wave scans)
@@ -63,15 +66,18 @@ struct Cfg {
   static constexpr int PAIR = 64 * 8;       // elements per pair tile
   // workspace unit per (chunk, V head), bytes
   static constexpr int W_OFF = 0;                                   // -W     [CT][NPD] pairs
-  static constexpr int KT_OFF = W_OFF + CT * NPD * PAIR * (int)sizeof(Op);  // K'^T [NT][NPC]
+  static constexpr int KT_OFF = W_OFF + CT * NPD * PAIR * (int)sizeof(Op);  // K^T  [NT][NPC]
   static constexpr int P_OFF = KT_OFF + NT * NPC * PAIR * (int)sizeof(Op);  // P   [CT][NPC]
-  static constexpr int UT_OFF = P_OFF + CT * NPC * PAIR * (int)sizeof(Op);  // Ut  [CT][NT][64][4]
+  // bf16 operands: P as a hi + lo pair (the low part, P - bf16(P), next)
+  static constexpr int P_PARTS = sizeof(Op) == 2 ? 2 : 1;
+  static constexpr int UT_OFF = P_OFF + P_PARTS * CT * NPC * PAIR * (int)sizeof(Op);  // Ut  [CT][NT][64][4]
   static constexpr int H_OFF = UT_OFF + C * D * (int)sizeof(Op);            // S^T at chunk start, [NPD][NT] pairs
   static constexpr int F_OFF = H_OFF + NPD * NT * PAIR * (int)sizeof(Op);   // e^{G_n}, then f_q [C]
   static constexpr int FQ_OFF = F_OFF + 16;                                 // scale e^{G_t} r_q[t]
   // fused-input, a sequence's first chunk only: the old conv window of the q
   // channels, [D][kMaxConvW - 1] like the conv state, for the output pass
-  static constexpr int HALO_OFF = FQ_OFF + C * 4;
+  static constexpr int FK_OFF = FQ_OFF + C * 4;                             // e^{G_n-G_t} r_k[t]
+  static constexpr int HALO_OFF = FK_OFF + C * 4;
   static constexpr int UNIT = (HALO_OFF + D * (kMaxConvW - 1) * (int)sizeof(Op) + 255) / 256 * 256;
   // output kernel LDS: raw q rows, then (over them) the fp32 O tile, row-major
   static constexpr int LD_Q = D + 16;
@@ -424,7 +430,7 @@ struct PrepLDS {
   static constexpr int S = (int)sizeof(Op);
   static constexpr int ROWS = C * K::LDR * S;       // one [C][LDR] row tile
   static constexpr int ATILE = C * K::LDA * 4;      // one fp32 A/T tile
-  static constexpr int TTILE = C * K::LDT * S;      // one scaled T copy
+  static constexpr int TTILE = C * K::LDT * S;      // the scaled T copy of W
   static constexpr int KR = 0;
   static constexpr int QR = ROWS;                   // fused-input only
   static constexpr int VR = 2 * ROWS;               // fused-input only, + s * ROWS
@@ -434,9 +440,9 @@ struct PrepLDS {
   // r_k [C], then per head G, b, f_K, f_W [C] each
   static constexpr int SM = (END_ROWS > END_A ? END_ROWS : END_A);
   static constexpr int SMALL = (1 + 4 * G) * C * 4;
-  static constexpr bool T_OVER_A = 2 * TTILE <= ATILE;
-  static constexpr int T0 = T_OVER_A ? A0 : SM + SMALL;  // + s * (T_OVER_A ? ATILE : 2 * TTILE)
-  static constexpr int TSTEP = T_OVER_A ? ATILE : 2 * TTILE;
+  static constexpr bool T_OVER_A = TTILE <= ATILE;
+  static constexpr int T0 = T_OVER_A ? A0 : SM + SMALL;  // + s * (T_OVER_A ? ATILE : TTILE)
+  static constexpr int TSTEP = T_OVER_A ? ATILE : TTILE;
   static constexpr int BYTES = T_OVER_A ? SM + SMALL : T0 + G * TSTEP;
 };
 
@@ -480,10 +486,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   auto sA = [&](int s) { return reinterpret_cast<float*>(smem + L::A0 + s * L::ATILE); };
   auto sG = [&](int s) { return sRK + C + 4 * s * C; };
   auto sB = [&](int s) { return sRK + 2 * C + 4 * s * C; };
-  auto sFK = [&](int s) { return sRK + 3 * C + 4 * s * C; };  // e^{G_n - G_t} r_k[t]
   auto sFW = [&](int s) { return sRK + 4 * C + 4 * s * C; };  // b_t e^{G_t} r_k[t]
   auto sTW = [&](int s) { return reinterpret_cast<Op*>(smem + L::T0 + s * L::TSTEP); };
-  auto sTU = [&](int s) { return reinterpret_cast<Op*>(smem + L::T0 + s * L::TSTEP) + C * LDT; };
 
   const int hgroups = h_v / G;
   const int gc = blockIdx.x / hgroups;
@@ -720,17 +724,21 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 #pragma unroll
         for (int s = 0; s < G; ++s) {
           const float gi = sG(s)[i];
-          FragT half[2];
+          FragT half[2], low[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
               const int jj = 16 * (2 * sp + hh) + 4 * g4 + ii;
-              half[hh][ii] = from_f32<Op>(2 * sp + hh <= ib && i >= jj
-                                              ? fi * sRK[jj] * fast_exp(fminf(gi - sG(s)[jj], 0.f)) * raw[hh][ii]
-                                              : 0.f);
+              const float pv = 2 * sp + hh <= ib && i >= jj
+                                   ? fi * sRK[jj] * fast_exp(fminf(gi - sG(s)[jj], 0.f)) * raw[hh][ii]
+                                   : 0.f;
+              half[hh][ii] = from_f32<Op>(pv);
+              low[hh][ii] = from_f32<Op>(pv - to_f32(half[hh][ii]));
             }
           store_pair<Op>(at<Op>(unit(s), K::P_OFF + (uint32_t)(ib * NPC + sp) * PB + lp), half[0], half[1]);
+          if constexpr (K::P_PARTS == 2)
+            store_pair<Op>(at<Op>(unit(s), K::P_OFF + (uint32_t)((CT + ib) * NPC + sp) * PB + lp), low[0], low[1]);
         }
       }
     }
@@ -767,11 +775,11 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
   }
   __syncthreads();
 
-  // per-token column factors of W and K', once per (V head, token)
+  // per-token column factors of W (LDS) and K' (f_k, to the unit), once per (V head, token)
   for (int e = tid; e < G * C; e += K::THREADS) {
     const int s = e / C, t = e % C;
     const float gt = sG(s)[t], rk = sRK[t];
-    sFK(s)[t] = fast_exp(sG(s)[C - 1] - gt) * rk;
+    *at<float>(unit(s), K::FK_OFF + 4 * t) = fast_exp(sG(s)[C - 1] - gt) * rk;
     sFW(s)[t] = sB(s)[t] * fast_exp(gt) * rk;
   }
   // ---- T = (I + A)^-1 in place, per V head.  (a) diagonal 16x16 blocks, one
@@ -834,11 +842,67 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     __syncthreads();
   }
 
-  // ---- T_W = T diag(b e^G r_k), T_U = T diag(b) in the operand type, zero above
-  // the diagonal blocks.  They may overlay T itself: all of T is read first.
+  // ---- Ut = T diag(b) V (this wave's d tiles) straight from the fp32 T tile.  T can have large
+  // entries of both signs (it inverts I + A), and Ut cancels them, so the
+  // operand keeps T diag(b) to fp32 accuracy: in bf16 as a hi + lo pair, two
+  // MFMAs per block.  (W's T diag(b e^G r_k) enters a product whose result the
+  // chain and output passes combine with the state; one bf16 copy suffices.)
+#pragma unroll
+  for (int s = 0; s < G; ++s) {
+    FragT Vc[CT][DVT];
+#pragma unroll
+    for (int kb = 0; kb < CT; ++kb)
+#pragma unroll
+      for (int j = 0; j < DVT; ++j) {
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+        mma_k16(b, Va[s][kb][j], eye);
+        Vc[kb][j] = frag_from<Op>(b);
+      }
+#pragma unroll
+    for (int mt = 0; mt < CT; ++mt) {
+      f32x4 uacc[DVT];
+#pragma unroll
+      for (int j = 0; j < DVT; ++j) uacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* trow = sA(s) + (16 * mt + l16) * LDA + 4 * g4;
+#pragma unroll
+      for (int s2 = 0; s2 < NPC; ++s2)
+        if (2 * s2 <= mt) {
+          const bool two = 2 * s2 + 1 <= mt;  // (block 2 s2 + 1 above the diagonal is zero)
+          f32x4 t0 = lds_frag<float>(trow + 32 * s2), t1 = two ? lds_frag<float>(trow + 32 * s2 + 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            t0[i] *= sB(s)[32 * s2 + 4 * g4 + i];
+            t1[i] *= two ? sB(s)[32 * s2 + 16 + 4 * g4 + i] : 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < DVT; ++j) {
+            const FragT v0 = Vc[2 * s2][j], v1 = two ? Vc[2 * s2 + 1][j] : zf;
+            if constexpr (sizeof(Op) == 2) {
+              const FragT h0 = frag_from<Op>(t0), h1 = frag_from<Op>(t1);
+              f32x4 r0, r1;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                r0[i] = t0[i] - to_f32(h0[i]);
+                r1[i] = t1[i] - to_f32(h1[i]);
+              }
+              mma_k32(uacc[j], h0, h1, v0, v1);
+              mma_k32(uacc[j], frag_from<Op>(r0), frag_from<Op>(r1), v0, v1);
+            } else {
+              mma_k32(uacc[j], frag_from<Op>(t0), frag_from<Op>(t1), v0, v1);
+            }
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < DVT; ++j)
+        *at<FragT>(unit(s), K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf) = frag_from<Op>(uacc[j]);
+    }
+  }
+
+  // ---- T_W = T diag(b e^G r_k) in the operand type, zero above the diagonal
+  // blocks.  It may overlay T itself: all of T is read first.
   {
     constexpr int PER = (G * C * C / 4 + K::THREADS - 1) / K::THREADS;
-    FragT tw[PER], tu[PER];
+    FragT tw[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int e = tid + k * K::THREADS;
@@ -848,11 +912,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         const bool keep = (c4 >> 4) <= (r >> 4);
         const f32x4 t = keep ? *reinterpret_cast<const f32x4*>(sA(s) + r * LDA + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float b = sB(s)[c4 + i];
-          tw[k][i] = from_f32<Op>(t[i] * sFW(s)[c4 + i]);
-          tu[k][i] = from_f32<Op>(t[i] * b);
-        }
+        for (int i = 0; i < 4; ++i) tw[k][i] = from_f32<Op>(t[i] * sFW(s)[c4 + i]);
       }
     }
     if (L::T_OVER_A) __syncthreads();
@@ -863,55 +923,41 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         const int s = e / (C * C / 4), er = e % (C * C / 4);
         const int r = er / (C / 4), c4 = (er % (C / 4)) * 4;
         *reinterpret_cast<FragT*>(sTW(s) + r * LDT + c4) = tw[k];
-        *reinterpret_cast<FragT*>(sTU(s) + r * LDT + c4) = tu[k];
       }
     }
   }
   __syncthreads();
 
-  // ---- this wave's d tiles: K and V column fragments, then per V head W^T,
-  // Ut and K'^T
+  // ---- this wave's d tiles of K as column (B operand) fragments; per V head
+  // W^T and K^T
+  FragT Kc[CT][DVT];
+#pragma unroll
+  for (int kb = 0; kb < CT; ++kb)
+#pragma unroll
+    for (int j = 0; j < DVT; ++j) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      mma_k16(a, lds_frag<Op>(sK + (16 * kb + l16) * LDR + 16 * (wave * DVT + j) + 4 * g4), eye);
+      Kc[kb][j] = frag_from<Op>(a);
+    }
   {
-    FragT Kc[CT][DVT];
-#pragma unroll
-    for (int kb = 0; kb < CT; ++kb)
-#pragma unroll
-      for (int j = 0; j < DVT; ++j) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        mma_k16(a, lds_frag<Op>(sK + (16 * kb + l16) * LDR + 16 * (wave * DVT + j) + 4 * g4), eye);
-        Kc[kb][j] = frag_from<Op>(a);
-      }
     const int sp_w = wave;  // the pair of d tiles this wave owns (DVT == 2), or pair 0 (DVT == 1)
 #pragma unroll
     for (int s = 0; s < G; ++s) {
-      FragT Vc[CT][DVT];
-#pragma unroll
-      for (int kb = 0; kb < CT; ++kb)
-#pragma unroll
-        for (int j = 0; j < DVT; ++j) {
-          f32x4 b = {0.f, 0.f, 0.f, 0.f};
-          mma_k16(b, Va[s][kb][j], eye);
-          Vc[kb][j] = frag_from<Op>(b);
-        }
 #pragma unroll
       for (int mt = 0; mt < CT; ++mt) {
         f32x4 wacc[DVT];
 #pragma unroll
         for (int j = 0; j < DVT; ++j) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           const Op* twrow = sTW(s) + (16 * mt + l16) * LDT + 4 * g4;
-          const Op* turow = sTU(s) + (16 * mt + l16) * LDT + 4 * g4;
 #pragma unroll
           for (int s2 = 0; s2 < NPC; ++s2)
             if (2 * s2 <= mt) {
               const bool two = 2 * s2 + 1 < CT;
               const FragT b0 = lds_frag<Op>(twrow + 32 * s2), b1 = two ? lds_frag<Op>(twrow + 32 * s2 + 16) : zf;
               mma_k32(acc, Kc[2 * s2][j], two ? Kc[2 * s2 + 1][j] : zf, b0, b1);
-              const FragT a0 = lds_frag<Op>(turow + 32 * s2), a1 = two ? lds_frag<Op>(turow + 32 * s2 + 16) : zf;
-              mma_k32(uacc, a0, a1, Vc[2 * s2][j], two ? Vc[2 * s2 + 1][j] : zf);
             }
           wacc[j] = acc;
-          *at<FragT>(unit(s), K::UT_OFF + (uint32_t)(mt * NT + wave * DVT + j) * PB / 2 + lf) = frag_from<Op>(uacc);
         }
         store_pair<Op>(at<Op>(unit(s), K::W_OFF + (uint32_t)(mt * NPD + sp_w) * PB + lp), frag_from<Op>(wacc[0], -1.f),
                        DVT == 2 ? frag_from<Op>(wacc[DVT - 1], -1.f) : zf);
@@ -920,16 +966,8 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       for (int j = 0; j < DVT; ++j)
 #pragma unroll
         for (int sp = 0; sp < NPC; ++sp) {
-          FragT lo, hi;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t0 = 32 * sp + 4 * g4 + i, t1 = t0 + 16;
-            lo[i] = from_f32<Op>(to_f32(Kc[2 * sp][j][i]) * sFK(s)[t0]);
-            hi[i] = from_f32<Op>(2 * sp + 1 < CT ? to_f32(Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j][i]) *
-                                                       sFK(s)[t1 < C ? t1 : 0]
-                                                 : 0.f);
-          }
-          store_pair<Op>(at<Op>(unit(s), K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), lo, hi);
+          store_pair<Op>(at<Op>(unit(s), K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), Kc[2 * sp][j],
+                         2 * sp + 1 < CT ? Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j] : zf);
         }
     }
   }
@@ -945,12 +983,13 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
 //   h = bf16(S^T): each wave's pairs -> workspace and LDS;             barrier
 //   U = Ut - W S^T: wave w the chunk row tiles w, w + NPD, ... with all of h
 //       from LDS -> workspace (over Ut) and LDS;                         barrier
-//   S^T <- e^{G_n} S^T + K'^T U: each wave its d_k tiles, all of U from LDS.
+//   S^T <- e^{G_n} S^T + K^T (diag(f_k) U): each wave its d_k tiles, all of the
+//       scaled U from LDS.
 // A wave streams only the operand rows it uses (one row tile of -W and Ut,
-// two of K'^T), PD - 1 chunks ahead in registers, so a chunk's loads and its
+// two of K^T), PD - 1 chunks ahead in registers, so a chunk's loads and its
 // MFMA work are spread over the CU's four SIMDs; NTW tiles share each -W and
-// K'^T load.  Block order puts all tiles of one (sequence, head) on one XCD,
-// so W and K'^T reach that XCD's L2 once.
+// K^T load.  Block order puts all tiles of one (sequence, head) on one XCD,
+// so W and K^T reach that XCD's L2 once.
 template <int D>
 constexpr int kChainThreads = 64 * ((D / 16 + 1) / 2);  // one wave per h pair
 
@@ -1041,10 +1080,11 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
   auto unit_of = [&](int k) { return ws + uniform_i64(((int64_t)(gc0 + min(k, nch - 1)) * h_v + h) * K::UNIT); };
   Pair<Op> wn[PD][UPW][NPD], kt[PD][SM][NPC];
   FragT ut[PD][UPW][NTW];
+  f32x4 fk[PD][UPW];
   float egn[PD];
   // A stage's operands as NPIECE single vector loads: the -W rows, Ut, the
-  // K'^T rows, e^{G_n}.
-  constexpr int NW = UPW * NPD, NU = UPW * NTW, NPIECE = NW + NU + SM * NPC + 1;
+  // K^T rows, f_k of the U rows, e^{G_n}.
+  constexpr int NW = UPW * NPD, NU = UPW * NTW, NK = SM * NPC, NPIECE = NW + NU + NK + UPW + 1;
   auto piece = [&](int s, const unsigned char* u, int j) {
     if (j < NW) {
       const int mt = min(wave + MW * (j / NPD), CT - 1);
@@ -1053,9 +1093,13 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
       const int i = (j - NW) / NTW, jt = (j - NW) % NTW;
       const int mt = min(wave + MW * i, CT - 1);
       ut[s][i][jt] = *at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + jt) * PB / 2 + lf);
-    } else if (j < NPIECE - 1) {
+    } else if (j < NW + NU + NK) {
       const int m = (j - NW - NU) / NPC, sp = (j - NW - NU) % NPC;
       kt[s][m][sp].load(at<Op>(u, K::KT_OFF + (uint32_t)((SM * wave + m) * NPC + sp) * PB + lp));
+    } else if (j < NPIECE - 1) {
+      const int i = j - NW - NU - NK;
+      const int mt = min(wave + MW * i, CT - 1);
+      fk[s][i] = *at<f32x4>(u, K::FK_OFF + 4 * (16 * mt + 4 * g4));
     } else {
       egn[s] = *at<float>(u, K::F_OFF);
     }
@@ -1117,9 +1161,11 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
         if (CT % MW == 0 || mt < CT) {
 #pragma unroll
           for (int j = 0; j < NTW; ++j) {
-            const FragT uf = frag_from<Op>(acc[j]);
-            *at<FragT>(uc, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = uf;
-            *reinterpret_cast<FragT*>(&sU[mt][j][lane * 4]) = uf;
+            *at<FragT>(uc, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + j) * PB / 2 + lf) = frag_from<Op>(acc[j]);
+            f32x4 su;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) su[e] = acc[j][e] * fk[s][i][e];
+            *reinterpret_cast<FragT*>(&sU[mt][j][lane * 4]) = frag_from<Op>(su);
           }
         }
       }
@@ -1132,7 +1178,7 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
           for (int e = 0; e < 4; ++e) Sacc[m][j][e] *= egn[s];
     }
     __syncthreads();
-    // S^T <- e^{G_n} S^T + K'^T U for this wave's d_k tiles
+    // S^T <- e^{G_n} S^T + K^T diag(f_k) U for this wave's d_k tiles
     {
       FragT uf[CT][NTW];
 #pragma unroll
@@ -1219,7 +1265,7 @@ __global__ __launch_bounds__(kThreads<D>) __attribute__((amdgpu_waves_per_eu(3))
   // the q conv staging so their latency overlaps it, h and P after it (the
   // staging's taps and windows leave no registers for them).  Otherwise the
   // q rows go first, then every operand.
-  Pair<Op> hp[NPD][DVT], pa[CT][NPC];
+  Pair<Op> hp[NPD][DVT], pa[CT][NPC], pl[CT][NPC];  // (pl: P's low part, bf16 operands only)
   FragT Uf[CT][DVT];
   f32x4 fq[CT];
   Raw8<T> zr[RPT];  // this thread's z pieces of the epilogue rows
@@ -1235,7 +1281,11 @@ __global__ __launch_bounds__(kThreads<D>) __attribute__((amdgpu_waves_per_eu(3))
     for (int mt = 0; mt < CT; ++mt)
 #pragma unroll
       for (int sp = 0; sp < NPC; ++sp)
-        if (2 * sp <= mt) pa[mt][sp].load_nt(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
+        if (2 * sp <= mt) {
+          pa[mt][sp].load_nt(at<Op>(u, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
+          if constexpr (K::P_PARTS == 2)
+            pl[mt][sp].load_nt(at<Op>(u, K::P_OFF + (uint32_t)((CT + mt) * NPC + sp) * PB + lp));
+        }
   };
   auto load_uz = [&]() {
 #pragma unroll
@@ -1304,7 +1354,10 @@ __global__ __launch_bounds__(kThreads<D>) __attribute__((amdgpu_waves_per_eu(3))
       for (int i = 0; i < 4; ++i) acc[i] *= fq[mt][i];  // scale e^{G_t} r_q[t] on Q S^T only
 #pragma unroll
       for (int sp = 0; sp < NPC; ++sp)
-        if (2 * sp <= mt) pa[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
+        if (2 * sp <= mt) {
+          pa[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
+          if constexpr (K::P_PARTS == 2) pl[mt][sp].mma(acc, Uf[2 * sp][j], 2 * sp + 1 < CT ? Uf[2 * sp + 1][j] : zf);
+        }
       Oacc[mt][j] = acc;
     }
   __syncthreads();  // q is read; the O tile goes over it
@@ -1347,7 +1400,7 @@ __global__ __launch_bounds__(kThreads<D>) __attribute__((amdgpu_waves_per_eu(3))
 // the most parallel and, with 4 register stages, the fastest chain; it is
 // used while the one-tile workgroups fit one per CU of an MI355X (256).
 // Beyond that the tiles per workgroup grow (2, then 4) so the launch stays
-// near one round of workgroups and the tiles share each -W and K'^T load,
+// near one round of workgroups and the tiles share each -W and K^T load,
 // which is what bounds many chains running at once (3 stages).
 constexpr int64_t kChainCUs = 256;
 

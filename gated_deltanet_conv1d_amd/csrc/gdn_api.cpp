@@ -205,6 +205,25 @@ int gdn_recurrent_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32
   return from_hip(gdn::launch_recurrent(args, (hipStream_t)stream));
 }
 
+int gdn_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step, float scale, const void* x,
+               const void* conv_w, const void* conv_b, const void* a, const void* b, const float* A_log,
+               const float* dt_bias, void* conv_state, float* state, int32_t n_slots, const int32_t* slots,
+               const int32_t* out_slots, void* o, const void* z, const void* norm_w, float norm_eps, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (n_seq < 0 || t_step < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (!gdn::decode_supported(s)) return GDN_ERR_UNSUPPORTED;
+  if (n_seq == 0 || t_step == 0) return GDN_OK;
+  GDN_TRY(need(x, conv_w, a, b, A_log, dt_bias, conv_state, state, slots, o));
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+  GDN_TRY(align_ok(x, conv_w, conv_b, conv_state, state, o, z));
+  gdn::DecodeArgs args{s,       act == GDN_BF16, n_seq, t_step, scale, x,         conv_w, conv_b, conv_state, a, b,
+                       A_log,   dt_bias,         state, n_slots, slots, out_slots, o,      z,      norm_w,     norm_eps};
+  return from_hip(gdn::launch_decode(args, (hipStream_t)stream));
+}
+
 int gdn_state_copy(const gdn_dims* dims, int32_t act, float* state, void* conv_state, int32_t n_slots,
                    const int32_t* src, const int32_t* dst, int32_t n, void* stream) {
   Shape s;

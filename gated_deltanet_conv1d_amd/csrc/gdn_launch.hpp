@@ -92,6 +92,33 @@ struct RecurrentArgs {
 };
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t st);
 
+// The whole decode / MTP step in one launch: conv window update + SiLU and
+// the fused recurrent step, for h_v / h_k in {1, 2}.
+struct DecodeArgs {
+  Shape s;
+  bool bf16;
+  int32_t n_seq, t_step;
+  float scale;
+  const void* x;
+  const void* conv_w;
+  const void* conv_b;
+  void* conv_state;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  float* state;
+  int32_t n_slots;
+  const int32_t* slots;
+  const int32_t* out_slots;
+  void* o;
+  const void* z;
+  const void* norm_w;
+  float norm_eps;
+};
+bool decode_supported(const Shape& s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
 struct ChunkArgs {
   Shape s;
   bool bf16;

@@ -80,6 +80,20 @@ __device__ __forceinline__ void st_f32(float* p, const float* v) {
     __builtin_nontemporal_store(v[0], p);
   }
 }
+// VW consecutive floats from LDS.
+template <int VW>
+__device__ __forceinline__ void ld_lds_f32(const float* p, float* v) {
+  if constexpr (VW == 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  } else if constexpr (VW == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(p);
+    v[0] = a.x; v[1] = a.y;
+  } else {
+    v[0] = *p;
+  }
+}
+
 // One token's inputs as loaded (raw activations, converted at use): q and k
 // of the QK head as vectors, this thread's v rows, its z rows (column lane 0
 // only) and the per-position state slot.
@@ -266,6 +280,255 @@ __device__ __forceinline__ void recurrent_step(
   }
 }
 
+// ---------------------------------------------------------------- decode
+// The whole decode / MTP step in one kernel (gdn_decode): conv window update
+// + SiLU, gating, q/k L2 norm, the recurrence and the gated-RMSNorm epilogue.
+// One workgroup per (request, QK head) with 256 threads per V head of that QK
+// head (G = h_v / h_k of them).  Every conv channel the workgroup reads -- q
+// and k of the QK head, v of its G V heads -- is owned by one thread, which
+// reads its slot window, computes the conv outputs of its channel for a block
+// of tokens into LDS (in fp32: the conv output never reaches memory and is
+// never rounded to the activation type), and writes the channel's new window
+// itself; no other thread of any workgroup touches that channel, so the
+// in-place window update needs no ordering between workgroups.  Each group of
+// 256 threads then runs the token steps of its V head exactly as
+// recurrent_step does, taking q, k, v from LDS.
+template <int D, int G>
+struct FusedLayout {
+  static constexpr int THREADS = 256 * G;
+  static constexpr int NCH = (2 + G) * D;          // conv channels per workgroup
+  static constexpr int TB = 4;                     // tokens per LDS block
+  static constexpr int CPT = (NCH + THREADS - 1) / THREADS;  // channels per thread
+};
+
+template <typename T, int D, int G, int W, bool MTP>
+__global__ __launch_bounds__(256 * G) void decode_fused_kernel(
+    const T* __restrict__ x, const T* __restrict__ conv_w, const T* __restrict__ conv_b, T* __restrict__ conv_state,
+    const T* __restrict__ a_in, const T* __restrict__ b_in, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, float* __restrict__ state, int32_t n_slots, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ out_slots, T* __restrict__ o, const T* __restrict__ z, const T* __restrict__ norm_w,
+    float norm_eps, float scale, int32_t t_step, int32_t h_k, int32_t h_v) {
+  using L = RowLayout<D>;
+  using FL = FusedLayout<D, G>;
+  constexpr int F = L::F, VW = L::VW, NG = L::NG, PASSES = L::PASSES, TB = FL::TB, NCH = FL::NCH;
+  __shared__ __attribute__((aligned(16))) float ys[TB][NCH];   // conv outputs: q | k | v of the G heads
+  __shared__ float red[G * 4];
+
+  const int i = blockIdx.x / h_k;
+  const int hk = blockIdx.x % h_k;
+  const int tid = threadIdx.x;
+  const int half = tid >> 8;             // which V head of the QK head
+  const int htid = tid & 255;
+  const int h = hk * G + half;
+  const int r16 = htid >> 4, c = htid & 15;
+  const int c_ch = 2 * h_k * D + h_v * D;
+  const int32_t slot = slots[i];
+
+  if (!slot_ok(slot, n_slots)) {  // padding request: zero outputs, no pool entry touched
+    for (int t = 0; t < t_step; ++t)
+      for (int r = htid; r < D; r += 256) o[(((int64_t)i * t_step + t) * h_v + h) * D + r] = from_f32<T>(0.0f);
+    return;
+  }
+
+  // ---- the state of V head h into registers first, so its loads are in
+  // flight while the conv runs
+  float s[PASSES][F];
+  const float* src = state + ((int64_t)slot * h_v + h) * D * D;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+    for (int j = 0; j < NG; ++j) ld_f32<VW, !MTP>(src + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+
+  // ---- this thread's conv channels: global channel, taps, bias, window
+  int ch[FL::CPT];
+  float wt[FL::CPT][W], bias[FL::CPT], win[FL::CPT][W - 1];
+#pragma unroll
+  for (int k = 0; k < FL::CPT; ++k) {
+    const int lc = tid + k * FL::THREADS;  // local channel: q (D), k (D), v of the G heads (G D)
+    ch[k] = lc < D ? hk * D + lc : lc < 2 * D ? h_k * D + hk * D + (lc - D) : 2 * h_k * D + hk * G * D + (lc - 2 * D);
+    if (lc < NCH) {
+#pragma unroll
+      for (int j = 0; j < W; ++j) wt[k][j] = to_f32(conv_w[(int64_t)ch[k] * W + j]);
+      bias[k] = conv_b ? to_f32(conv_b[ch[k]]) : 0.0f;
+      const T* cs = conv_state + ((int64_t)slot * c_ch + ch[k]) * (W - 1);
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j) win[k][j] = to_f32(cs[j]);
+    }
+  }
+
+  const float neg_A = -expf(A_log[h]);
+  const float dtb = dt_bias[h];
+  T* o_base = o + ((int64_t)i * t_step * h_v + h) * D;
+
+  for (int t0 = 0; t0 < t_step; t0 += TB) {
+    const int nt = min(TB, t_step - t0);
+    // conv + SiLU of this block's tokens, channel by channel (bias, then the
+    // window oldest first, fp32 FMA: the order of the conv kernels)
+#pragma unroll
+    for (int k = 0; k < FL::CPT; ++k) {
+      const int lc = tid + k * FL::THREADS;
+      if (lc < NCH) {
+        for (int tt = 0; tt < nt; ++tt) {
+          const int64_t row = (int64_t)i * t_step + t0 + tt;
+          const T xv = x[row * c_ch + ch[k]];
+          float acc = bias[k];
+#pragma unroll
+          for (int j = 0; j < W - 1; ++j) acc = fmaf(wt[k][j], win[k][j], acc);
+          acc = fmaf(wt[k][W - 1], to_f32(xv), acc);
+          ys[tt][lc] = fast_silu(acc);
+#pragma unroll
+          for (int j = 0; j < W - 2; ++j) win[k][j] = win[k][j + 1];
+          win[k][W - 2] = to_f32(xv);
+          if (MTP) {  // the window after this draft token, to its position slot
+            const int32_t d = out_slots[row];
+            if (slot_ok(d, n_slots)) {
+              T* cd = conv_state + ((int64_t)d * c_ch + ch[k]) * (W - 1);
+#pragma unroll
+              for (int j = 0; j < W - 1; ++j) cd[j] = from_f32<T>(win[k][j]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    for (int tt = 0; tt < nt; ++tt) {
+      const int t = t0 + tt;
+      const int64_t row = (int64_t)i * t_step + t;
+      float kv[F], qv[F];
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        ld_lds_f32<VW>(&ys[tt][L::col(j, c)], &qv[j * VW]);
+        ld_lds_f32<VW>(&ys[tt][D + L::col(j, c)], &kv[j * VW]);
+      }
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < F; ++e) { sk = fmaf(kv[e], kv[e], sk); sq = fmaf(qv[e], qv[e], sq); }
+      sk = group_sum<16>(sk);
+      sq = group_sum<16>(sq);
+      const float rk = fast_rsq(sk + 1e-6f), rq = fast_rsq(sq + 1e-6f);
+      float kq = 0.f;
+#pragma unroll
+      for (int e = 0; e < F; ++e) { kv[e] *= rk; qv[e] *= rq; kq = fmaf(kv[e], qv[e], kq); }
+      kq = group_sum<16>(kq);
+      const float g = neg_A * softplusf_(to_f32(a_in[row * h_v + h]) + dtb);
+      const float beta = sigmoidf_(to_f32(b_in[row * h_v + h]));
+      const float eg = expf(g);
+      const float* vs = &ys[tt][2 * D + half * D];
+
+      float orow[PASSES];
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        float dk = 0.f, dq = 0.f;
+#pragma unroll
+        for (int e = 0; e < F; ++e) { dk = fmaf(s[p][e], kv[e], dk); dq = fmaf(s[p][e], qv[e], dq); }
+        dk = group_sum<16>(dk);
+        dq = group_sum<16>(dq);
+        const float u = beta * (vs[p * 16 + r16] - eg * dk);
+        orow[p] = scale * (eg * dq + u * kq);
+#pragma unroll
+        for (int e = 0; e < F; ++e) s[p][e] = fmaf(eg, s[p][e], u * kv[e]);
+      }
+
+      T* o_ptr = o_base + (int64_t)t * h_v * D;
+      if (z) {
+        float zrow[PASSES];
+        const T* z_ptr = z + (row * h_v + h) * D;
+        if (c == 0)
+#pragma unroll
+          for (int p = 0; p < PASSES; ++p) zrow[p] = to_f32(z_ptr[p * 16 + r16]);
+        float ss = 0.f;
+        if (c == 0) {
+#pragma unroll
+          for (int p = 0; p < PASSES; ++p) ss = fmaf(orow[p], orow[p], ss);
+        }
+        ss = wave_sum(ss);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) tot += red[half * 4 + w];
+        __syncthreads();
+        const float rstd = fast_rsq(tot * (1.0f / D) + norm_eps);
+        if (c == 0) {
+#pragma unroll
+          for (int p = 0; p < PASSES; ++p) {
+            const int r = p * 16 + r16;
+            o_ptr[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * fast_silu(zrow[p]));
+          }
+        }
+      } else if (c == 0) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) o_ptr[p * 16 + r16] = from_f32<T>(orow[p]);
+      }
+
+      if (MTP) {
+        const int32_t d = out_slots[row];
+        if (slot_ok(d, n_slots)) {
+          float* dp = state + ((int64_t)d * h_v + h) * D * D;
+#pragma unroll
+          for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+            for (int j = 0; j < NG; ++j) st_f32<VW, false>(dp + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+        }
+      }
+    }
+    __syncthreads();  // the block's conv outputs are read before the next block overwrites them
+  }
+
+  if (!MTP) {
+    float* dp = state + ((int64_t)slot * h_v + h) * D * D;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int j = 0; j < NG; ++j) st_f32<VW, true>(dp + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+#pragma unroll
+    for (int k = 0; k < FL::CPT; ++k) {
+      const int lc = tid + k * FL::THREADS;
+      if (lc < NCH) {
+        T* cs = conv_state + ((int64_t)slot * c_ch + ch[k]) * (W - 1);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) cs[j] = from_f32<T>(win[k][j]);
+      }
+    }
+  }
+}
+
+template <typename T, int D, int G, int W>
+hipError_t decode_launch(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.n_seq * a.s.h_k));
+  if (a.out_slots)
+    hipLaunchKernelGGL((decode_fused_kernel<T, D, G, W, true>), grid, dim3(256 * G), 0, st, (const T*)a.x,
+                       (const T*)a.conv_w, (const T*)a.conv_b, (T*)a.conv_state, (const T*)a.a, (const T*)a.b,
+                       a.A_log, a.dt_bias, a.state, a.n_slots, a.slots, a.out_slots, (T*)a.o, (const T*)a.z,
+                       (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step, a.s.h_k, a.s.h_v);
+  else
+    hipLaunchKernelGGL((decode_fused_kernel<T, D, G, W, false>), grid, dim3(256 * G), 0, st, (const T*)a.x,
+                       (const T*)a.conv_w, (const T*)a.conv_b, (T*)a.conv_state, (const T*)a.a, (const T*)a.b,
+                       a.A_log, a.dt_bias, a.state, a.n_slots, a.slots, a.out_slots, (T*)a.o, (const T*)a.z,
+                       (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step, a.s.h_k, a.s.h_v);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t decode_by_width(const DecodeArgs& a, hipStream_t st) {
+  switch (a.s.conv_w) {
+    case 2: return decode_launch<T, D, G, 2>(a, st);
+    case 3: return decode_launch<T, D, G, 3>(a, st);
+    case 4: return decode_launch<T, D, G, 4>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+hipError_t decode_by_group(const DecodeArgs& a, hipStream_t st) {
+  switch (a.s.h_v / a.s.h_k) {
+    case 1: return decode_by_width<T, D, 1>(a, st);
+    case 2: return decode_by_width<T, D, 2>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 #define GDN_RECURRENT_ARGS                                                                                         \
   const T *__restrict__ qkv, const T *__restrict__ a_in, const T *__restrict__ b_in,                               \
       const float *__restrict__ A_log, const float *__restrict__ dt_bias, float *__restrict__ state,              \
@@ -307,6 +570,22 @@ hipError_t impl(const RecurrentArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+bool decode_supported(const Shape& s) {
+  const int g = s.h_v / s.h_k;
+  return g == 1 || g == 2;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.n_seq == 0 || a.t_step == 0) return hipSuccess;
+  switch (a.s.d) {
+    case 16: return a.bf16 ? decode_by_group<bf16, 16>(a, st) : decode_by_group<float, 16>(a, st);
+    case 32: return a.bf16 ? decode_by_group<bf16, 32>(a, st) : decode_by_group<float, 32>(a, st);
+    case 64: return a.bf16 ? decode_by_group<bf16, 64>(a, st) : decode_by_group<float, 64>(a, st);
+    case 128: return a.bf16 ? decode_by_group<bf16, 128>(a, st) : decode_by_group<float, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t st) {
   switch (a.s.d) {

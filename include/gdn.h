@@ -194,6 +194,29 @@ int gdn_recurrent_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32
                          const void* z, const void* norm_w, float norm_eps, void* stream);
 
 /*
+ * gdn_decode -- the whole decode / MTP draft step in one call: the conv window
+ * update + SiLU (as gdn_conv1d_update) and the fused recurrent step with its
+ * epilogue (as gdn_recurrent_decode), with the conv output kept in fp32 inside
+ * the kernel instead of round-tripping through device memory in the
+ * activation type (the fusion of the causal convolution and the fused
+ * recurrent GDN step that LightLLM PR #1184 lists under Highlights, "Advanced
+ * Triton Kernel Optimizations").  Because the conv output is not rounded, the
+ * results are not bit-equal to the two separate calls; both follow the same
+ * definitions.  conv_state and state are updated as those calls update them:
+ * in place (out_slots NULL), or per draft position into out_slots with the
+ * home slots only read.
+ *   x      act [n_seq][t_step][c_ch]   conv input;  conv_w act [c_ch][conv_w];  conv_b act [c_ch] or NULL
+ *   a, b   act [n_seq][t_step][h_v];   A_log, dt_bias float [h_v]
+ *   conv_state act [n_slots][c_ch][conv_w-1];  state float [n_slots][h_v][d_v][d_k]
+ *   slots, out_slots, o, z, norm_w, norm_eps, scale: as in gdn_recurrent_decode
+ * Supported for h_v / h_k in {1, 2} (GDN_ERR_UNSUPPORTED otherwise).
+ */
+int gdn_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step, float scale, const void* x,
+               const void* conv_w, const void* conv_b, const void* a, const void* b, const float* A_log,
+               const float* dt_bias, void* conv_state, float* state, int32_t n_slots, const int32_t* slots,
+               const int32_t* out_slots, void* o, const void* z, const void* norm_w, float norm_eps, void* stream);
+
+/*
  * gdn_state_copy -- bitwise pool[dst[i]] <- pool[src[i]] for i < n, for the
  * recurrent state pool and (when conv_state is non-NULL) the conv state pool.
  * This is the MTP commit copy of LightLLM PR #1184 (copy buffers from source

@@ -11,6 +11,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+    # The GPU parity tests run the oracle on CPU worker processes.  Their fork
+    # server starts here, before anything in this process touches the GPU, so
+    # no worker is ever forked from (or execs out of) a process holding it.
+    if "not gpu" not in (config.getoption("markexpr", "") or ""):
+        from tests.oracle_pool import start_server
+        start_server()
 
 
 def pytest_collection_modifyitems(config, items):

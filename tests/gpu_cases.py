@@ -1,23 +1,32 @@
 """Helpers for the GPU parity tests: upload seeded cases, run the HIP path
 through the binding, evaluate the oracle on the same inputs, compare.
 
-Tolerance rule (the reading of "max relative error 2e-2 for bf16 inputs
-with fp32 accumulation, 1e-4 in the all-fp32 mode"): for every compared
-slice -- one (sequence, V head) of an output, one (slot, V head) of a
-recurrent state -- with x the HIP result and r the exact fp64 oracle,
+Tolerance rule -- the reading of "max relative error 2e-2 for bf16 inputs with
+fp32 accumulation, 1e-4 in the all-fp32 mode".  A row is one (token, V head)
+of an output over d_v, or one (slot, V head) recurrent state.  With x the HIP
+result, r the exact fp64 oracle and r~1, r~2 the oracle evaluated with its
+conv output held at the activation precision (the tensor the pages' conv
+kernel hands to the GDN kernels; bf16, or fp32 in the all-fp32 mode) in two
+realisations, rounded, and rounded after a seeded half-ulp nudge:
 
-    ||x - r||_inf  <=  tol * ||r||_inf  +  SENS * ||r~ - r||_inf,
+    err = ||x - r||_inf,  mag = ||r||_inf,  sens = max_k ||r~k - r||_inf   (per row)
 
-where ||r~ - r||_inf is the larger change of the oracle's result under two
-activation-precision (bf16) perturbations: its conv output rounded, and its
-conv output plus its normalised q/k rounded; SENS = 4.  The second term is
-the oracle's own measure of how far one activation rounding moves the exact
-answer.  It is zero in the all-fp32 mode and negligible for
-well-conditioned slices; it matters where the layer is ill-conditioned (a
-token whose q and k are nearly orthogonal under strong decay leaves o tiny,
-and the gated RMSNorm's epsilon regime then turns any rounding into an O(1)
-relative change).  The plain max relative error is reported next to it.
-Index work (slots, copies, conv states holding raw inputs) is bit-exact.
+  (i)   every row:                      err <= tol * mag + SENS * sens, SENS = 2
+  (ii)  rows with sens <= tol * mag / 10: err <= tol * mag        (plain)
+  (iii) the rows over plain tol number at most the ill-conditioned rows
+        (sens > tol * mag / 2), and those are at most ILL_MAX = 10% of the
+        rows of a workload (checked from 200 rows up).
+
+sens is the oracle's own measure of the row's conditioning: how far an
+activation-precision rounding of its input moves the exact answer (two
+realisations, since one alone understates it on the worst rows).  It is
+large only where the layer is ill-conditioned: a token whose q and k are nearly
+orthogonal under strong decay leaves o tiny, and the gated RMSNorm's epsilon
+regime then turns any rounding into an O(1) relative change of that row.  SENS
+= 2 comes from the measured ratio err / sens on the rows that activation
+rounding dominates (median 1.00, maximum 1.75 over the 4096-token prefill, the
+256-request decode and the 128 x 4 MTP step).  Index work (slots, copies, conv
+states holding raw inputs) is bit-exact.
 """
 from __future__ import annotations
 
@@ -30,9 +39,14 @@ import torch
 import gdn_inputs as gi
 import gated_deltanet_conv1d_amd as gdn
 from oracle import gdn_oracle as O
+from tests.oracle_pool import (decode_req_check, from_raw, oracle_prefill_seq, perturbations,  # noqa: F401
+                               prefill_seq_check, round_act, row_stats, run_map)
 
 TOL = {"bf16": 2e-2, "f32": 1e-4}
-SENS = 4.0
+SENS = 2.0          # bound widening, in units of the oracle's own sensitivity
+WELL = 0.1          # sens <= WELL * tol * mag: the plain tolerance applies
+ILL = 0.5           # sens > ILL * tol * mag: an ill-conditioned row
+ILL_MAX = 0.10      # at most this fraction of rows may be ill-conditioned
 DEV = torch.device("cuda:0")
 
 
@@ -61,6 +75,13 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def host_raw(t: torch.Tensor) -> np.ndarray:
+    """A device tensor as raw host values: bf16 as its uint16 bit patterns, else fp32."""
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.float().cpu().numpy()
+
+
 def rel(x: np.ndarray, r: np.ndarray) -> float:
     """Plain max-norm relative error ||x - r||_inf / ||r||_inf."""
     if r.size == 0:
@@ -71,32 +92,71 @@ def rel(x: np.ndarray, r: np.ndarray) -> float:
 
 
 class Score:
-    """Worst plain relative error and worst error/bound ratio over slices."""
+    """Accumulates rows under the tolerance rule above."""
 
     def __init__(self, tol: float):
         self.tol = tol
-        self.plain = 0.0
-        self.ratio = 0.0
-        self.sens_slices = 0
+        self.rows = self.well = self.ill = self.over = self.fails = 0
+        self.plain = 0.0        # worst plain relative error over all rows
+        self.well_plain = 0.0   # worst plain relative error over well-conditioned rows
+        self.ratio = 0.0        # worst err / bound
+        self.ill_sens = 0.0     # worst err / sens over ill-conditioned rows
+        self.first_fail = ""
+        self.worst = []         # the rows with the largest err / bound: (ratio, label, row, err, mag, sens)
 
-    def add(self, x: np.ndarray, r: np.ndarray, rts) -> None:
-        """rts: None, or a list of perturbed oracle results for this slice."""
-        if r.size == 0:
+    def add_stats(self, err, mag, sens, label: str = "") -> None:
+        err, mag, sens = (np.atleast_1d(np.asarray(v, np.float64)) for v in (err, mag, sens))
+        if err.size == 0:
             return
-        err = float(np.max(np.abs(x - r)))
-        mag = float(np.max(np.abs(r)))
-        sens = 0.0 if rts is None else max(float(np.max(np.abs(rt - r))) for rt in rts)
-        bound = self.tol * mag + SENS * sens
-        self.plain = max(self.plain, err / mag if mag > 0 else err)
-        if err > self.tol * mag:
-            self.sens_slices += 1
-        self.ratio = max(self.ratio, err / bound if bound > 0 else (0.0 if err == 0 else float("inf")))
+        tolm = self.tol * mag
+        bound = tolm + SENS * sens
+        well = sens <= WELL * tolm
+        over = err > tolm
+        bad = (err > bound) | (well & over)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            rel_ = np.where(mag > 0, err / np.where(mag > 0, mag, 1.0), np.where(err > 0, np.inf, 0.0))
+            ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+        self.rows += err.size
+        self.well += int(well.sum())
+        ill = sens > ILL * tolm
+        self.ill += int(ill.sum())
+        if ill.any():
+            self.ill_sens = max(self.ill_sens, float((err[ill] / sens[ill]).max()))
+        self.over += int(over.sum())
+        self.plain = max(self.plain, float(rel_.max()))
+        if well.any():
+            self.well_plain = max(self.well_plain, float(rel_[well].max()))
+        self.ratio = max(self.ratio, float(ratio.max()))
+        for j in np.argsort(-ratio)[:4]:
+            self.worst.append((float(ratio[j]), label, int(j), float(err[j]), float(mag[j]), float(sens[j])))
+        self.worst = sorted(self.worst, key=lambda w: -w[0])[:6]
+        if bad.any():
+            if not self.fails:
+                j = int(np.argmax(bad))
+                self.first_fail = (f"{label} row {j}: err {err[j]:.3e} mag {mag[j]:.3e} sens {sens[j]:.3e} "
+                                   f"(well-conditioned: {bool(well[j])})")
+            self.fails += int(bad.sum())
+
+    def add(self, x, r, rts=None, label: str = "") -> None:
+        """Rows along the last axis of x, r (rts: the perturbed oracle results)."""
+        self.add_stats(*row_stats(x, r, rts), label=label)
+
+    def add_slice(self, x, r, rts=None, label: str = "") -> None:
+        """The whole of x, r as one row (a recurrent state slice)."""
+        r = np.asarray(r)
+        self.add_stats(*row_stats(x, r, rts, n=r.size), label=label)
 
     def ok(self) -> bool:
-        return self.ratio <= 1.0
+        # (the fraction of ill-conditioned rows is a property of a workload:
+        # it is checked once a score holds enough rows to estimate it)
+        frac_ok = self.rows < 200 or self.ill <= ILL_MAX * self.rows
+        return self.fails == 0 and self.over <= self.ill and frac_ok
 
     def __str__(self) -> str:
-        return f"plain {self.plain:.2e} err/bound {self.ratio:.3f} (slices over plain tol: {self.sens_slices})"
+        s = (f"rows {self.rows}: plain worst {self.plain:.2e}, well-conditioned {self.well} worst "
+             f"{self.well_plain:.2e}; ill-conditioned {self.ill} (err/sens worst {self.ill_sens:.2f}), over plain tol "
+             f"{self.over}; err/bound worst {self.ratio:.3f}")
+        return s + (f"; FAILS {self.fails} ({self.first_fail})" if self.fails else "")
 
 
 def params_dict(p: gi.LayerParams) -> dict:
@@ -155,53 +215,45 @@ class DevPrefill:
                            self.z if epilogue else None, self.norm_w)
 
 
-# The two activation-precision perturbations the tolerance rule measures.
-PERTURBATIONS = (dict(perturb=gi.round_bf16), dict(perturb=gi.round_bf16, perturb_qk=gi.round_bf16))
-
-
-def oracle_prefill_seq(case: gi.PrefillCase, i: int, heads=None, scale=1.0, epilogue=True, **pert):
-    """Oracle for sequence i of a prefill case (optionally a subset of V heads)."""
-    d = case.dims
-    s = int(case.slots[i])
-    init = bool(case.has_init[i])
-    return O.layer_sequence(case.seq_x(i), case.seq_a(i), case.seq_b(i), case.seq_z(i) if epilogue else None,
-                            case.params.conv_w, case.params.conv_b, case.params.A_log, case.params.dt_bias,
-                            case.params.norm_w, case.slot_conv(s) if init else None,
-                            case.slot_ssm(s) if init else None, (d.h_k, d.h_v, d.d_k, d.d_v), scale, 1e-6,
-                            heads=heads, **pert)
-
-
 def oracle_with_perturbed(fn, act: str):
-    """(exact result, list of perturbed results or None) for an oracle call fn(**pert)."""
-    r = fn()
-    return r, ([fn(**pe) for pe in PERTURBATIONS] if act == "bf16" else None)
+    """(exact result, results with the conv output at activation precision) for
+    an oracle call fn(**pert)."""
+    return fn(), [fn(perturb=pe) for pe in perturbations(act)]
 
 
 def compare_prefill(dp: DevPrefill, out: torch.Tensor, seqs=None, heads=None, scale=1.0, epilogue=True,
                     check_states=True) -> dict:
-    """Element-wise comparison for the chosen sequences (and heads).
-    Returns Scores for outputs and states and the worst conv-state difference."""
+    """Row-wise comparison for the chosen sequences (and heads), the oracle
+    running on the worker pool.  Returns Scores for outputs and states and the
+    worst conv-state difference (conv states hold raw inputs: exact)."""
     case = dp.case
     tol = TOL[case.act]
-    seqs = range(case.n_seq) if seqs is None else seqs
+    seqs = list(range(case.n_seq)) if seqs is None else list(seqs)
     hs = list(range(case.dims.h_v)) if heads is None else list(heads)
     so, ss = Score(tol), Score(tol)
-    worst_conv = 0.0
-    conv_pool = dp.conv_pool.float().cpu().numpy() if check_states else None
+    t0 = time.time()
+    tasks = []
     for i in seqs:
         s = int(case.slots[i])
         lo, hi = int(case.cu_seqlens[i]), int(case.cu_seqlens[i + 1])
-        t0 = time.time()
-        r, rts = oracle_with_perturbed(
-            lambda **pe: oracle_prefill_seq(case, i, heads=hs, scale=scale, epilogue=epilogue, **pe), case.act)
-        got = host(out[lo:hi][:, hs])
-        for j in range(len(hs)):
-            so.add(got[:, j], r["out"][:, j], None if rts is None else [rt["out"][:, j] for rt in rts])
-        if check_states and 0 <= s < case.n_slots:
-            gs = dp.ssm_pool[s, hs].cpu().numpy().astype(np.float64)
-            for j in range(len(hs)):
-                ss.add(gs[j], r["ssm"][j], None if rts is None else [rt["ssm"][j] for rt in rts])
-            if r["conv"].size:   # conv states hold raw inputs: exact
-                worst_conv = max(worst_conv, float(np.max(np.abs(conv_pool[s] - r["conv"]))))
-        log(f"  seq {i} len {hi - lo} slot {s}: out [{so}] ssm [{ss}] (oracle {time.time() - t0:.1f}s)")
+        live = check_states and 0 <= s < case.n_slots
+        tasks.append((case, i, hs, scale, epilogue, host_raw(out[lo:hi][:, hs]),
+                      dp.ssm_pool[s, hs].cpu().numpy() if live else None,
+                      host_raw(dp.conv_pool[s]) if live else None))
+    worst_conv = 0.0
+
+    def progress(k, n):
+        if n >= 16 and (k % 8 == 0 or k == n):
+            log(f"  oracle: {k}/{n} sequences ({time.time() - t0:.0f}s)")
+
+    for i, (o_st, s_st, conv_d) in zip(seqs, run_map(prefill_seq_check, tasks, progress)):
+        so.add_stats(*o_st, label=f"seq {i} out")
+        for j, st in enumerate(s_st or []):
+            ss.add_stats(*st, label=f"seq {i} head {hs[j]} state")
+        worst_conv = max(worst_conv, conv_d)
+    log(f"  {len(seqs)} sequences x {len(hs)} heads: out [{so}] ssm [{ss}] conv {worst_conv:.1e} "
+        f"(oracle {time.time() - t0:.1f}s)")
+    for ratio, label, j, err, mag, sens in so.worst:
+        log(f"    worst: {label} token {j // len(hs)} head {hs[j % len(hs)]}: err/bound {ratio:.3f} err {err:.3e} "
+            f"mag {mag:.3e} sens {sens:.3e}")
     return dict(out=so, ssm=ss, conv=worst_conv)

@@ -38,7 +38,7 @@ FAKE = 0x1000  # a 16-byte-aligned non-null address: every call below must fail 
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
         assert n in binding.SIGNATURES, n
@@ -100,10 +100,10 @@ def test_chunk_prefill_errors(L):
 def test_chunk_prefill_workspace(L):
     ws = L.gdn_chunk_prefill_workspace_size(D(), 0, 1, 4096, 64)
     # a 256-byte-aligned chunk index, then one 256-byte-aligned unit
-    # per (chunk, V head) holding -W, K'^T, Ut (bf16, C x D each), P (bf16, C x C),
-    # the chunk-start state (bf16, D x D), e^{G_n} (16 bytes), f_q (fp32, C) and
-    # the old conv window of the q channels (bf16, D x 3; single-call prefill)
-    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 128 * 3 * 2 + 255) // 256 * 256
+    # per (chunk, V head) holding -W, K^T, Ut (bf16, C x D each), P (bf16 hi and lo, C x C each),
+    # the chunk-start state (bf16, D x D), e^{G_n} (16 bytes), f_q and f_k (fp32,
+    # C each) and the old conv window of the q channels (bf16, D x 3; single-call prefill)
+    unit = (3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 128 * 2 + 16 + 2 * 64 * 4 + 128 * 3 * 2 + 255) // 256 * 256
     assert ws == 256 + (4096 // 64 + 1) * 32 * unit
     # (same sizes as the query, so these calls stop at validation and never launch)
     assert chunk_call(L, t_total=4096) == WS
@@ -130,7 +130,7 @@ def test_prefill_errors_and_workspace(L):
     assert prefill_call(L, n_seq=0, t_total=0) == OK
     # the same workspace as gdn_chunk_prefill
     ws = L.gdn_prefill_workspace_size(D(), 0, 1, 4096, 64)
-    unit = (3 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 128 * 2 + 16 + 64 * 4 + 128 * 3 * 2 + 255) // 256 * 256
+    unit = (3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 128 * 2 + 16 + 2 * 64 * 4 + 128 * 3 * 2 + 255) // 256 * 256
     assert ws == 256 + (4096 // 64 + 1) * 32 * unit
     assert prefill_call(L, t_total=4096) == WS                # (these stop at validation, never launch)
     assert prefill_call(L, t_total=4096, ws=FAKE, ws_bytes=ws - 1) == WS
@@ -148,6 +148,27 @@ def test_recurrent_and_copy_errors(L):
     assert L.gdn_state_copy(D(), 0, None, None, 8, FAKE, FAKE, 3, None) == NULL
     assert L.gdn_state_copy(D(), 0, FAKE, FAKE + 4, 8, FAKE, FAKE, 3, None) == ALIGN
     assert L.gdn_state_copy(D(), 0, None, None, 8, None, None, 0, None) == OK
+
+
+def decode_call(L, dims=None, act=0, n_seq=2, t_step=1, x=FAKE, conv_state=FAKE, state=FAKE, z=None, norm_w=None,
+                eps=1e-6, out_slots=None):
+    return L.gdn_decode(dims or D(), act, n_seq, t_step, 1.0, x, FAKE, None, FAKE, FAKE, FAKE, FAKE, conv_state, state,
+                        8, FAKE, out_slots, FAKE + 16, z, norm_w, eps, None)
+
+
+def test_decode_errors(L):
+    assert decode_call(L, n_seq=-1) == SHAPE
+    assert decode_call(L, t_step=-1) == SHAPE
+    assert decode_call(L, n_seq=0) == OK
+    assert decode_call(L, t_step=0) == OK
+    assert decode_call(L, x=None) == NULL
+    assert decode_call(L, conv_state=None) == NULL
+    assert decode_call(L, state=None) == NULL
+    assert decode_call(L, z=FAKE) == NULL                     # z without norm_w
+    assert decode_call(L, eps=-1.0) == SHAPE
+    assert decode_call(L, x=FAKE + 8) == ALIGN
+    assert decode_call(L, act=5) == DTYPE
+    assert decode_call(L, dims=D(h_k=4, h_v=16)) == UNSUP     # 4 V heads per QK head
 
 
 def test_binding_rejects_host_tensors():

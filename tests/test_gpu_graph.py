@@ -77,9 +77,11 @@ def test_prefill_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("single_call", [False, True])
 @pytest.mark.parametrize("pad", [0, 3])
-def test_decode_graph_replays_match_eager(pad):
-    """The decode step captured once and replayed; with pad > 0 the last entries
+def test_decode_graph_replays_match_eager(pad, single_call):
+    """The decode step (gdn_conv1d_update + gdn_recurrent_decode, or the single
+    gdn_decode call) captured once and replayed; with pad > 0 the last entries
     of the bucket are pad slots (-1), as a serving loop fills a fixed-size
     bucket: their output rows are zero and no pool slot they could name changes."""
     case = gi.decode_case(seed=22, n=8, n_slots=16, dims=gi.Dims(2, 4, 128, 128, 4))
@@ -101,6 +103,9 @@ def test_decode_graph_replays_match_eager(pad):
     o = torch.empty((case.n, 1, d.h_v, d.d_v), dtype=torch.bfloat16, device="cuda")
 
     def step():
+        if single_call:
+            gdn.decode(dims, x, conv_w, a, b, A_log, dt_bias, slots, conv, ssm, None, 1.0, z, norm_w, 1e-6, o=o)
+            return
         gdn.conv1d_update(dims, x, conv_w, conv, slots, y=y)
         gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, None, 1.0, z, norm_w, 1e-6, o=o)
 
@@ -127,3 +132,82 @@ def test_decode_graph_replays_match_eager(pad):
                     assert torch.equal(ssm[sl], ssm0[sl]) and torch.equal(conv[sl], conv0[sl]), f"slot {sl} touched"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("single_call", [False, True])
+def test_mtp_bucket_graph(single_call):
+    """The MTP draft step as a serving loop runs it: a fixed bucket of requests,
+    each with mtp_step + 1 rows (so the bucket's row count is a multiple of
+    mtp_step + 1), the draft step and the commit copy captured as one graph.
+    Pad requests (slot -1, out slots -1) leave zero rows and no pool slot
+    changed.  The accept lengths live in device index buffers the graph reads
+    at replay: two different accept patterns replay bitwise equal to eager."""
+    mtp_step = 3
+    t_step = mtp_step + 1
+    bucket, live = 8, 5
+    case = gi.mtp_case(seed=23, n=bucket, t_step=t_step, dims=gi.Dims(2, 4, 128, 128, 4))
+    slots_np, out_np = case.slots.copy(), case.out_slots.copy()
+    slots_np[live:] = -1
+    out_np[live:] = -1
+    assert (bucket * t_step) % (mtp_step + 1) == 0
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    bf = lambda v: dev(v, torch.bfloat16)
+    x, a, b, z = bf(case.x()), bf(case.a()), bf(case.b()), bf(case.z())
+    p = case.params
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log, dt_bias = dev(p.A_log, torch.float32), dev(p.dt_bias, torch.float32)
+    slots, out_slots = i32(slots_np), i32(out_np)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    ssm0 = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device="cuda", generator=gen) * 0.02
+    conv0 = torch.randn((case.n_slots, d.c_ch, d.conv_w - 1), device="cuda", generator=gen).to(torch.bfloat16)
+    ssm, conv = ssm0.clone(), conv0.clone()
+    y = torch.empty_like(x)
+    o = torch.empty((bucket, t_step, d.h_v, d.d_v), dtype=torch.bfloat16, device="cuda")
+    src = torch.full((bucket,), -1, dtype=torch.int32, device="cuda")
+    dst = torch.full((bucket,), -1, dtype=torch.int32, device="cuda")
+
+    def set_accept(acc):
+        s_np = np.full(bucket, -1, np.int32)
+        d_np = np.full(bucket, -1, np.int32)
+        for i in range(live):
+            if acc[i] > 0:
+                s_np[i], d_np[i] = out_np[i, acc[i] - 1], slots_np[i]
+        src.copy_(torch.from_numpy(s_np))
+        dst.copy_(torch.from_numpy(d_np))
+
+    def step():
+        if single_call:
+            gdn.decode(dims, x, conv_w, a, b, A_log, dt_bias, slots, conv, ssm, out_slots, 1.0, z, norm_w, 1e-6, o=o)
+        else:
+            gdn.conv1d_update(dims, x, conv_w, conv, slots, out_slots, y=y)
+            gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, out_slots, 1.0, z, norm_w, 1e-6, o=o)
+        gdn.state_copy(dims, ssm, src, dst, conv)
+
+    def reset():
+        ssm.copy_(ssm0)
+        conv.copy_(conv0)
+
+    graph = None
+    for acc in (case.accept, (case.accept + 2) % (t_step + 1)):
+        set_accept(acc)
+        reset()
+        step()
+        torch.cuda.synchronize()
+        ref = (o.clone(), ssm.clone(), conv.clone())
+        if graph is None:
+            reset()
+            graph = _capture(step)
+        for k in range(2):
+            reset()
+            o.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, ref[0]) and torch.equal(ssm, ref[1]) and torch.equal(conv, ref[2]), f"replay {k}"
+            assert torch.all(o[live:] == 0), "pad rows must be zero"
+            named = set(int(v) for v in slots_np[:live]) | set(int(v) for v in out_np[:live].reshape(-1))
+            for sl in range(case.n_slots):
+                if sl not in named:
+                    assert torch.equal(ssm[sl], ssm0[sl]) and torch.equal(conv[sl], conv0[sl]), f"slot {sl} touched"
+            step()  # eager work between replays
+            torch.cuda.synchronize()
