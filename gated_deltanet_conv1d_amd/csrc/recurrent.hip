@@ -301,8 +301,83 @@ struct FusedLayout {
   static constexpr int CPT = (NCH + THREADS - 1) / THREADS;  // channels per thread
 };
 
-template <typename T, int D, int G, int W, bool MTP>
-__global__ __launch_bounds__(256 * G) void decode_fused_kernel(
+// One token step of V head h (256 threads: 16 row groups x 16 column lanes)
+// with q, k, v of the token read from LDS: gating, q/k L2 norm, the state
+// rows' update and the output, with the gated RMSNorm over d_v when z is given.
+template <typename T, int D>
+__device__ __forceinline__ void fused_token(float (&s)[D / 16][D / 16], const float* __restrict__ yq,
+                                            const float* __restrict__ yk, const float* __restrict__ yv, float a_t, float b_t,
+                                            float neg_A, float dtb, float scale, const T* __restrict__ z_row,
+                                            const T* __restrict__ norm_w, float norm_eps, T* __restrict__ o_row,
+                                            float* red, int red_base, int tid, int r16, int c) {
+  using L = RowLayout<D>;
+  constexpr int F = L::F, VW = L::VW, NG = L::NG, PASSES = L::PASSES;
+  float kv[F], qv[F];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    ld_lds_f32<VW>(yq + L::col(j, c), &qv[j * VW]);
+    ld_lds_f32<VW>(yk + L::col(j, c), &kv[j * VW]);
+  }
+  float sk = 0.f, sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < F; ++e) { sk = fmaf(kv[e], kv[e], sk); sq = fmaf(qv[e], qv[e], sq); }
+  sk = group_sum<16>(sk);
+  sq = group_sum<16>(sq);
+  const float rk = fast_rsq(sk + 1e-6f), rq = fast_rsq(sq + 1e-6f);
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < F; ++e) { kv[e] *= rk; qv[e] *= rq; kq = fmaf(kv[e], qv[e], kq); }
+  kq = group_sum<16>(kq);
+  const float g = neg_A * softplusf_(a_t + dtb);
+  const float beta = sigmoidf_(b_t);
+  const float eg = expf(g);
+
+  float orow[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    float dk = 0.f, dq = 0.f;
+#pragma unroll
+    for (int e = 0; e < F; ++e) { dk = fmaf(s[p][e], kv[e], dk); dq = fmaf(s[p][e], qv[e], dq); }
+    dk = group_sum<16>(dk);
+    dq = group_sum<16>(dq);
+    const float u = beta * (yv[p * 16 + r16] - eg * dk);
+    orow[p] = scale * (eg * dq + u * kq);
+#pragma unroll
+    for (int e = 0; e < F; ++e) s[p][e] = fmaf(eg, s[p][e], u * kv[e]);
+  }
+
+  if (z_row) {
+    float ss = 0.f;
+    if (c == 0) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) ss = fmaf(orow[p], orow[p], ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) tot += red[red_base + w];
+    __syncthreads();
+    const float rstd = fast_rsq(tot * (1.0f / D) + norm_eps);
+    if (c == 0) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int r = p * 16 + r16;
+        o_row[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * fast_silu(to_f32(z_row[r])));
+      }
+    }
+  } else if (c == 0) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) o_row[p * 16 + r16] = from_f32<T>(orow[p]);
+  }
+}
+
+// ONE: all t_step tokens fit one LDS block (t_step <= TB), so the block loop,
+// and the conv registers' lifetime across it, disappear; TOK1: exactly one
+// token (decode), with no token loop at all.
+template <typename T, int D, int G, int W, bool MTP, bool ONE, bool TOK1 = false>
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(ONE && (MTP || TOK1) ? 4 : 1))) void decode_fused_kernel(
     const T* __restrict__ x, const T* __restrict__ conv_w, const T* __restrict__ conv_b, T* __restrict__ conv_state,
     const T* __restrict__ a_in, const T* __restrict__ b_in, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, float* __restrict__ state, int32_t n_slots, const int32_t* __restrict__ slots,
@@ -310,8 +385,10 @@ __global__ __launch_bounds__(256 * G) void decode_fused_kernel(
     float norm_eps, float scale, int32_t t_step, int32_t h_k, int32_t h_v) {
   using L = RowLayout<D>;
   using FL = FusedLayout<D, G>;
-  constexpr int F = L::F, VW = L::VW, NG = L::NG, PASSES = L::PASSES, TB = FL::TB, NCH = FL::NCH;
+  constexpr int VW = L::VW, NG = L::NG, PASSES = L::PASSES, TB = FL::TB, NCH = FL::NCH;
   __shared__ __attribute__((aligned(16))) float ys[TB][NCH];   // conv outputs: q | k | v of the G heads
+  __shared__ __attribute__((aligned(16))) T zs[TB][G][D];       // z rows of the block's tokens
+  __shared__ float gab[TB][G][2];                               // a, b of the block's tokens
   __shared__ float red[G * 4];
 
   const int i = blockIdx.x / h_k;
@@ -332,38 +409,34 @@ __global__ __launch_bounds__(256 * G) void decode_fused_kernel(
 
   // ---- the state of V head h into registers first, so its loads are in
   // flight while the conv runs
-  float s[PASSES][F];
+  float s[PASSES][L::F];
   const float* src = state + ((int64_t)slot * h_v + h) * D * D;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p)
 #pragma unroll
     for (int j = 0; j < NG; ++j) ld_f32<VW, !MTP>(src + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
 
-  // ---- this thread's conv channels: global channel, taps, bias, window
-  int ch[FL::CPT];
-  float wt[FL::CPT][W], bias[FL::CPT], win[FL::CPT][W - 1];
-#pragma unroll
-  for (int k = 0; k < FL::CPT; ++k) {
-    const int lc = tid + k * FL::THREADS;  // local channel: q (D), k (D), v of the G heads (G D)
-    ch[k] = lc < D ? hk * D + lc : lc < 2 * D ? h_k * D + hk * D + (lc - D) : 2 * h_k * D + hk * G * D + (lc - 2 * D);
-    if (lc < NCH) {
-#pragma unroll
-      for (int j = 0; j < W; ++j) wt[k][j] = to_f32(conv_w[(int64_t)ch[k] * W + j]);
-      bias[k] = conv_b ? to_f32(conv_b[ch[k]]) : 0.0f;
-      const T* cs = conv_state + ((int64_t)slot * c_ch + ch[k]) * (W - 1);
-#pragma unroll
-      for (int j = 0; j < W - 1; ++j) win[k][j] = to_f32(cs[j]);
-    }
-  }
-
   const float neg_A = -expf(A_log[h]);
   const float dtb = dt_bias[h];
-  T* o_base = o + ((int64_t)i * t_step * h_v + h) * D;
 
-  for (int t0 = 0; t0 < t_step; t0 += TB) {
-    const int nt = min(TB, t_step - t0);
-    // conv + SiLU of this block's tokens, channel by channel (bias, then the
-    // window oldest first, fp32 FMA: the order of the conv kernels)
+  // conv + SiLU of tokens [t0, t0 + nt) into LDS, channel by channel (bias,
+  // then the window oldest first, fp32 FMA: the order of the conv kernels);
+  // per-position windows (MTP) and the final in-place window are stored as
+  // soon as they are known
+  auto conv_block = [&](float (&win)[FL::CPT][W - 1], const float (&wt)[FL::CPT][W], const float (&bias)[FL::CPT],
+                        const int (&ch)[FL::CPT], int t0, int nt) {
+    // the block's a, b and z rows into LDS too, so no token step loads from
+    // memory after a state store (loads and stores drain in issue order)
+    for (int e = tid; e < nt * G; e += FL::THREADS) {
+      const int64_t ab = ((int64_t)i * t_step + t0 + e / G) * h_v + hk * G + e % G;
+      gab[e / G][e % G][0] = to_f32(a_in[ab]);
+      gab[e / G][e % G][1] = to_f32(b_in[ab]);
+    }
+    if (z)
+      for (int e = tid; e < nt * G * D; e += FL::THREADS) {
+        const int tt = e / (G * D), g = (e / D) % G, r = e % D;
+        zs[tt][g][r] = z[(((int64_t)i * t_step + t0 + tt) * h_v + hk * G + g) * D + r];
+      }
 #pragma unroll
     for (int k = 0; k < FL::CPT; ++k) {
       const int lc = tid + k * FL::THREADS;
@@ -379,7 +452,7 @@ __global__ __launch_bounds__(256 * G) void decode_fused_kernel(
 #pragma unroll
           for (int j = 0; j < W - 2; ++j) win[k][j] = win[k][j + 1];
           win[k][W - 2] = to_f32(xv);
-          if (MTP) {  // the window after this draft token, to its position slot
+          if (MTP) {
             const int32_t d = out_slots[row];
             if (slot_ok(d, n_slots)) {
               T* cd = conv_state + ((int64_t)d * c_ch + ch[k]) * (W - 1);
@@ -388,80 +461,21 @@ __global__ __launch_bounds__(256 * G) void decode_fused_kernel(
             }
           }
         }
+        if (!MTP && t0 + nt == t_step) {
+          T* cs = conv_state + ((int64_t)slot * c_ch + ch[k]) * (W - 1);
+#pragma unroll
+          for (int j = 0; j < W - 1; ++j) cs[j] = from_f32<T>(win[k][j]);
+        }
       }
     }
-    __syncthreads();
-
+  };
+  // the token steps of a block, reading the block's conv outputs from LDS
+  auto token_block = [&](int t0, int nt) {
     for (int tt = 0; tt < nt; ++tt) {
-      const int t = t0 + tt;
-      const int64_t row = (int64_t)i * t_step + t;
-      float kv[F], qv[F];
-#pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        ld_lds_f32<VW>(&ys[tt][L::col(j, c)], &qv[j * VW]);
-        ld_lds_f32<VW>(&ys[tt][D + L::col(j, c)], &kv[j * VW]);
-      }
-      float sk = 0.f, sq = 0.f;
-#pragma unroll
-      for (int e = 0; e < F; ++e) { sk = fmaf(kv[e], kv[e], sk); sq = fmaf(qv[e], qv[e], sq); }
-      sk = group_sum<16>(sk);
-      sq = group_sum<16>(sq);
-      const float rk = fast_rsq(sk + 1e-6f), rq = fast_rsq(sq + 1e-6f);
-      float kq = 0.f;
-#pragma unroll
-      for (int e = 0; e < F; ++e) { kv[e] *= rk; qv[e] *= rq; kq = fmaf(kv[e], qv[e], kq); }
-      kq = group_sum<16>(kq);
-      const float g = neg_A * softplusf_(to_f32(a_in[row * h_v + h]) + dtb);
-      const float beta = sigmoidf_(to_f32(b_in[row * h_v + h]));
-      const float eg = expf(g);
-      const float* vs = &ys[tt][2 * D + half * D];
-
-      float orow[PASSES];
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        float dk = 0.f, dq = 0.f;
-#pragma unroll
-        for (int e = 0; e < F; ++e) { dk = fmaf(s[p][e], kv[e], dk); dq = fmaf(s[p][e], qv[e], dq); }
-        dk = group_sum<16>(dk);
-        dq = group_sum<16>(dq);
-        const float u = beta * (vs[p * 16 + r16] - eg * dk);
-        orow[p] = scale * (eg * dq + u * kq);
-#pragma unroll
-        for (int e = 0; e < F; ++e) s[p][e] = fmaf(eg, s[p][e], u * kv[e]);
-      }
-
-      T* o_ptr = o_base + (int64_t)t * h_v * D;
-      if (z) {
-        float zrow[PASSES];
-        const T* z_ptr = z + (row * h_v + h) * D;
-        if (c == 0)
-#pragma unroll
-          for (int p = 0; p < PASSES; ++p) zrow[p] = to_f32(z_ptr[p * 16 + r16]);
-        float ss = 0.f;
-        if (c == 0) {
-#pragma unroll
-          for (int p = 0; p < PASSES; ++p) ss = fmaf(orow[p], orow[p], ss);
-        }
-        ss = wave_sum(ss);
-        if ((tid & 63) == 0) red[tid >> 6] = ss;
-        __syncthreads();
-        float tot = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) tot += red[half * 4 + w];
-        __syncthreads();
-        const float rstd = fast_rsq(tot * (1.0f / D) + norm_eps);
-        if (c == 0) {
-#pragma unroll
-          for (int p = 0; p < PASSES; ++p) {
-            const int r = p * 16 + r16;
-            o_ptr[r] = from_f32<T>(orow[p] * rstd * to_f32(norm_w[r]) * fast_silu(zrow[p]));
-          }
-        }
-      } else if (c == 0) {
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) o_ptr[p * 16 + r16] = from_f32<T>(orow[p]);
-      }
-
+      const int64_t row = (int64_t)i * t_step + t0 + tt;
+      fused_token<T, D>(s, &ys[tt][0], &ys[tt][D], &ys[tt][2 * D + half * D], gab[tt][half][0], gab[tt][half][1],
+                        neg_A, dtb, scale, z ? &zs[tt][half][0] : nullptr, norm_w, norm_eps,
+                        o + (row * h_v + h) * D, red, half * 4, tid, r16, c);
       if (MTP) {
         const int32_t d = out_slots[row];
         if (slot_ok(d, n_slots)) {
@@ -471,43 +485,65 @@ __global__ __launch_bounds__(256 * G) void decode_fused_kernel(
 #pragma unroll
             for (int j = 0; j < NG; ++j) st_f32<VW, false>(dp + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
         }
+      } else if (t0 + tt == t_step - 1) {  // in place: the final state back to the home slot
+        float* dp = state + ((int64_t)slot * h_v + h) * D * D;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+          for (int j = 0; j < NG; ++j) st_f32<VW, true>(dp + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
       }
     }
-    __syncthreads();  // the block's conv outputs are read before the next block overwrites them
-  }
+  };
 
-  if (!MTP) {
-    float* dp = state + ((int64_t)slot * h_v + h) * D * D;
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-#pragma unroll
-      for (int j = 0; j < NG; ++j) st_f32<VW, true>(dp + (p * 16 + r16) * D + L::col(j, c), &s[p][j * VW]);
+  {
+    // this thread's conv channels: global channel, taps, bias, window
+    int ch[FL::CPT];
+    float wt[FL::CPT][W], bias[FL::CPT], win[FL::CPT][W - 1];
 #pragma unroll
     for (int k = 0; k < FL::CPT; ++k) {
-      const int lc = tid + k * FL::THREADS;
+      const int lc = tid + k * FL::THREADS;  // local channel: q (D), k (D), v of the G heads (G D)
+      ch[k] = lc < D ? hk * D + lc : lc < 2 * D ? h_k * D + hk * D + (lc - D) : 2 * h_k * D + hk * G * D + (lc - 2 * D);
       if (lc < NCH) {
-        T* cs = conv_state + ((int64_t)slot * c_ch + ch[k]) * (W - 1);
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) cs[j] = from_f32<T>(win[k][j]);
+        for (int j = 0; j < W; ++j) wt[k][j] = to_f32(conv_w[(int64_t)ch[k] * W + j]);
+        bias[k] = conv_b ? to_f32(conv_b[ch[k]]) : 0.0f;
+        const T* cs = conv_state + ((int64_t)slot * c_ch + ch[k]) * (W - 1);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) win[k][j] = to_f32(cs[j]);
+      }
+    }
+    if constexpr (ONE) {
+      conv_block(win, wt, bias, ch, 0, TOK1 ? 1 : t_step);
+      __syncthreads();
+    } else {
+      for (int t0 = 0; t0 < t_step; t0 += TB) {
+        const int nt = min(TB, t_step - t0);
+        conv_block(win, wt, bias, ch, t0, nt);
+        __syncthreads();
+        token_block(t0, nt);
+        __syncthreads();  // the block's conv outputs are read before the next block overwrites them
       }
     }
   }
+  if constexpr (ONE) token_block(0, TOK1 ? 1 : t_step);
+}
+
+template <typename T, int D, int G, int W, bool MTP, bool ONE, bool TOK1 = false>
+hipError_t decode_launch1(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_fused_kernel<T, D, G, W, MTP, ONE, TOK1>), dim3((unsigned)((int64_t)a.n_seq * a.s.h_k)),
+                     dim3(256 * G), 0, st, (const T*)a.x, (const T*)a.conv_w, (const T*)a.conv_b, (T*)a.conv_state,
+                     (const T*)a.a, (const T*)a.b, a.A_log, a.dt_bias, a.state, a.n_slots, a.slots, a.out_slots,
+                     (T*)a.o, (const T*)a.z, (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step, a.s.h_k, a.s.h_v);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int G, int W>
 hipError_t decode_launch(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)a.n_seq * a.s.h_k));
+  const bool one = a.t_step <= FusedLayout<D, G>::TB;
   if (a.out_slots)
-    hipLaunchKernelGGL((decode_fused_kernel<T, D, G, W, true>), grid, dim3(256 * G), 0, st, (const T*)a.x,
-                       (const T*)a.conv_w, (const T*)a.conv_b, (T*)a.conv_state, (const T*)a.a, (const T*)a.b,
-                       a.A_log, a.dt_bias, a.state, a.n_slots, a.slots, a.out_slots, (T*)a.o, (const T*)a.z,
-                       (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step, a.s.h_k, a.s.h_v);
-  else
-    hipLaunchKernelGGL((decode_fused_kernel<T, D, G, W, false>), grid, dim3(256 * G), 0, st, (const T*)a.x,
-                       (const T*)a.conv_w, (const T*)a.conv_b, (T*)a.conv_state, (const T*)a.a, (const T*)a.b,
-                       a.A_log, a.dt_bias, a.state, a.n_slots, a.slots, a.out_slots, (T*)a.o, (const T*)a.z,
-                       (const T*)a.norm_w, a.norm_eps, a.scale, a.t_step, a.s.h_k, a.s.h_v);
-  return hipGetLastError();
+    return one ? decode_launch1<T, D, G, W, true, true>(a, st) : decode_launch1<T, D, G, W, true, false>(a, st);
+  if (a.t_step == 1) return decode_launch1<T, D, G, W, false, true, true>(a, st);
+  return one ? decode_launch1<T, D, G, W, false, true>(a, st) : decode_launch1<T, D, G, W, false, false>(a, st);
 }
 
 template <typename T, int D, int G>
