@@ -7,19 +7,23 @@ SiLU, gating, the chunked gated delta rule with fused q/k L2 norm and the
 gated-RMSNorm epilogue, as the single gdn_prefill call (conv output and gates
 stay inside the chunk kernels), on the single-sequence workload: batch 1,
 T=4096, 16 QK / 32 V heads, d=128, bf16 activations, fp32 state, chunk 64,
-synthetic seeded inputs resident in HBM.  The same step as three calls
-(gdn_conv1d_fwd, gdn_gating, gdn_chunk_prefill) is reported beside it.  The
-timed steps replay one captured HIP graph of the step (how a serving loop
-runs it; --eager times plain launches instead); per-call times come from an
-eager pass with HIP events on the launch stream.
+synthetic seeded inputs resident in HBM.  Steps alternate between two copies
+of every input, output, pool and workspace (about 0.6 GB together, more than
+the 256 MiB memory-side cache).  The timed steps replay one captured HIP
+graph per copy (how a serving loop runs it; --eager times plain launches);
+per-call times (median, p10, p90 and mean) come from an eager pass with HIP
+events on the launch stream.  The same step as three calls (gdn_conv1d_fwd,
+gdn_gating, gdn_chunk_prefill) is reported beside it.
 
 Prints ONE JSON line: tokens/s for that step (value), the roofline of the
-dominant call (gdn_prefill), the decode state-update bandwidth (256
-requests x 1 token over a 512-slot fp32 state pool, pools rotated so states
-come from HBM), the ~271k-token varlen prefill and the 128 x 4-token MTP step
-as extra rows, the decode step replayed as HIP graphs for a padded 256-request
-bucket, the prefill at one tensor-parallel rank's head counts (tp = 2, 4), and
-the fp64 CPU oracle timed on the host as a baseline.
+dominant call (gdn_prefill), then the other workloads as extra rows: the
+decode step (256 requests x 1 token over 512-slot pools, gdn_decode and the two
+separate calls, pools rotated so states come from HBM) and its padded-bucket
+graph, the 128 x 4-token MTP step (gdn_decode, the two separate calls, the
+commit copy) and its bucket graph, the ~271k-token varlen prefill on the
+seeded inputs of the parity tests, the prefill at one tensor-parallel rank's
+head counts (tp = 2, 4), and the fp64 CPU oracle timed on the host's cores on
+a sample of every workload.
 """
 from __future__ import annotations
 
@@ -81,6 +85,24 @@ def decode_algorithmic(n: int, t_step: int, h_k: int, h_v: int, d: int, act_byte
     return float(n * (state * (1 + n_pos_writes) + t_step * per_tok))
 
 
+def decode_fused_algorithmic(n: int, t_step: int, h_k: int, h_v: int, d: int, act_bytes: int, conv_w: int,
+                             n_pos_writes: int) -> float:
+    """Bytes of one gdn_decode launch: per request the state and the conv window
+    read once and written n_pos_writes times; per token the conv input row, a
+    and b, z read and out written."""
+    c_ch = 2 * h_k * d + h_v * d
+    state = h_v * d * d * 4 + c_ch * (conv_w - 1) * act_bytes
+    per_tok = c_ch * act_bytes + 2 * h_v * act_bytes + 2 * h_v * d * act_bytes
+    return float(n * (state * (1 + n_pos_writes) + t_step * per_tok))
+
+
+def pct(ms) -> dict:
+    """Median, p10, p90 and mean of a list of times (ms)."""
+    a = np.asarray(ms, np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4)}
+
+
 def kernel_src_sha() -> str:
     """Hash of the HIP sources; counter figures apply only to the sources they were taken on."""
     import glob
@@ -119,6 +141,26 @@ CHUNK_SPLIT_KERNELS = ("void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, f
 PREFILL_KERNELS = ("void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, true, 4, 2>",
                    "void split::chunk_state_kernel<__bf16, 128, 64, 1, 4>",
                    "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, true, 4>")
+
+
+def counter_mfma(workload: str, kernels) -> dict | None:
+    """MFMA utilisation from the committed rocprofv3 counter pass
+    (profiles/<workload>_mfma.json): MFMA-busy cycles over CU-busy cycles of
+    the kernels' dispatches, summed; None when the sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("src_sha") != kernel_src_sha():
+        return None
+    per = rec["per_dispatch"]
+    try:
+        busy = sum(per[k]["mfma_busy_cycles"] for k in kernels)
+        total = sum(per[k]["cu_busy_cycles"] for k in kernels)
+    except KeyError:
+        return None
+    return {"mfma_busy_frac": round(busy / total, 4) if total else None, "counters": rec.get("counters")}
 
 
 def capture_graph(torch, fn):
@@ -165,8 +207,7 @@ def bench_prefill(args, torch, gdn, gi):
     dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
     dev = torch.device("cuda")
     bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
-    x = bf(case.seq_x(0))
-    a, b, z = bf(case.seq_a(0)), bf(case.seq_b(0)), bf(case.seq_z(0))
+    T = case.t_total
     p = case.params
     conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
     A_log = torch.from_numpy(p.A_log).to(dev)
@@ -174,84 +215,91 @@ def bench_prefill(args, torch, gdn, gi):
     cu = torch.tensor(case.cu_seqlens, dtype=torch.int32, device=dev)
     slots = torch.zeros(1, dtype=torch.int32, device=dev)
     has_init = torch.zeros(1, dtype=torch.uint8, device=dev)
-    conv_pool = torch.zeros((1, d.c_ch, d.conv_w - 1), dtype=torch.bfloat16, device=dev)
-    ssm_pool = torch.zeros((1, d.h_v, d.d_v, d.d_k), dtype=torch.float32, device=dev)
-    T = case.t_total
-    y = torch.empty_like(x)
-    g = torch.empty((T, d.h_v), dtype=torch.float32, device=dev)
-    beta = torch.empty_like(g)
-    o = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
     # (one workspace serves both entry points: the larger of their sizes)
-    ws = torch.empty(max(gdn.chunk_prefill_workspace_size(dims, 0, 1, T, case.chunk),
-                         gdn.prefill_workspace_size(dims, 0, 1, T, case.chunk)), dtype=torch.uint8, device=dev)
+    ws_bytes = max(gdn.chunk_prefill_workspace_size(dims, 0, 1, T, case.chunk),
+                   gdn.prefill_workspace_size(dims, 0, 1, T, case.chunk))
+    x0, a0, b0, z0 = case.seq_x(0), case.seq_a(0), case.seq_b(0), case.seq_z(0)
+    copies = []
+    for _ in range(2):  # every buffer twice: the steps alternate, the footprint exceeds the memory-side cache
+        copies.append(dict(
+            x=bf(x0), a=bf(a0), b=bf(b0), z=bf(z0),
+            conv_pool=torch.zeros((1, d.c_ch, d.conv_w - 1), dtype=torch.bfloat16, device=dev),
+            ssm_pool=torch.zeros((1, d.h_v, d.d_v, d.d_k), dtype=torch.float32, device=dev),
+            y=torch.empty((T, d.c_ch), dtype=torch.bfloat16, device=dev),
+            g=torch.empty((T, d.h_v), dtype=torch.float32, device=dev),
+            beta=torch.empty((T, d.h_v), dtype=torch.float32, device=dev),
+            o=torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev),
+            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
+    footprint = sum(t.numel() * t.element_size() for c in copies for t in c.values())
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-
-    def step_sep(e=None):
+    def step_sep(k, e=None):
+        c = copies[k % 2]
         if e: e[0].record()
-        gdn.conv1d_fwd(dims, x, conv_w, cu, slots, conv_pool, has_init, y=y)
+        gdn.conv1d_fwd(dims, c["x"], conv_w, cu, slots, c["conv_pool"], has_init, y=c["y"])
         if e: e[1].record()
-        gdn.gating(a, b, A_log, dt_bias, g=g, beta=beta)
+        gdn.gating(c["a"], c["b"], A_log, dt_bias, g=c["g"], beta=c["beta"])
         if e: e[2].record()
-        gdn.chunk_prefill(dims, y, g, beta, cu, slots, ssm_pool, has_init, case.chunk, 1.0, z, norm_w, 1e-6, o=o,
-                          workspace=ws)
+        gdn.chunk_prefill(dims, c["y"], c["g"], c["beta"], cu, slots, c["ssm_pool"], has_init, case.chunk, 1.0,
+                          c["z"], norm_w, 1e-6, o=c["o"], workspace=c["ws"])
         if e: e[3].record()
 
-    def step(e=None):
+    def step(k, e=None):
+        c = copies[k % 2]
         if e: e[0].record()
-        gdn.prefill(dims, x, conv_w, a, b, A_log, dt_bias, cu, slots, conv_pool, ssm_pool, has_init, case.chunk,
-                    1.0, z, norm_w, 1e-6, o=o, workspace=ws)
+        gdn.prefill(dims, c["x"], conv_w, c["a"], c["b"], A_log, dt_bias, cu, slots, c["conv_pool"], c["ssm_pool"],
+                    has_init, case.chunk, 1.0, c["z"], norm_w, 1e-6, o=c["o"], workspace=c["ws"])
         if e: e[1].record()
 
-    def timed(fn, evs):
-        """eager pass with events, then (unless --eager) graph replays; wall seconds of the timed pass"""
-        for _ in range(args.warmup):
-            fn()
+    def timed(fn, n_ev):
+        """eager pass with events, then (unless --eager) graph replays, one graph
+        per copy; returns (wall seconds of the timed pass, eager wall, events)"""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+        for k in range(args.warmup):
+            fn(k)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
-            fn(evs[k])
+            fn(k, evs[k])
         torch.cuda.synchronize()
         wall_eager = time.perf_counter() - t0
         if args.eager:
-            return wall_eager, wall_eager
-        graph = capture_graph(torch, fn)
-        for _ in range(args.warmup):
-            graph.replay()
+            return wall_eager, wall_eager, evs
+        graphs = [capture_graph(torch, lambda k=k: fn(k)) for k in range(2)]
+        for k in range(args.warmup):
+            graphs[k % 2].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
+        for k in range(args.steps):
+            graphs[k % 2].replay()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, wall_eager
+        return time.perf_counter() - t0, wall_eager, evs
 
-    wall_sep, wall_sep_eager = timed(step_sep, ev)
-    wall, wall_eager = timed(step, evf)
-    ms = lambda evs, i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
-    t_conv, t_gate, t_chunk = ms(ev, 0, 1), ms(ev, 1, 2), ms(ev, 2, 3)
-    t_pre = ms(evf, 0, 1)
+    wall_sep, wall_sep_eager, ev = timed(step_sep, 4)
+    wall, wall_eager, evf = timed(step, 2)
+    ms = lambda evs, i, j: [e[i].elapsed_time(e[j]) for e in evs]
+    t_pre = pct(ms(evf, 0, 1))
     nbytes, flops = prefill_algorithmic(T, 1, d.h_k, d.h_v, d.d_k, 2, False, case.chunk, d.conv_w)
-    achieved = nbytes / (t_pre * 1e-3) / 1e9
+    achieved = nbytes / (t_pre["mean"] * 1e-3) / 1e9
+    mfma_tflops = flops / (t_pre["mean"] * 1e-3) / 1e12
     return dict(
         T=T, wall_s=wall, ms_per_step=wall / args.steps * 1e3, eager_ms_per_step=wall_eager / args.steps * 1e3,
-        kernels_ms={"gdn_prefill": t_pre},
+        kernels_ms={"gdn_prefill": t_pre}, footprint_bytes=footprint,
         separate_calls={"ms_per_step": round(wall_sep / args.steps * 1e3, 4),
                         "tokens_per_s": round(T * args.steps / wall_sep, 1),
                         "eager_ms_per_step": round(wall_sep_eager / args.steps * 1e3, 4),
-                        "kernels_ms": {"gdn_conv1d_fwd": round(t_conv, 4), "gdn_gating": round(t_gate, 4),
-                                       "gdn_chunk_prefill": round(t_chunk, 4)},
+                        "kernels_ms": {"gdn_conv1d_fwd": pct(ms(ev, 0, 1)), "gdn_gating": pct(ms(ev, 1, 2)),
+                                       "gdn_chunk_prefill": pct(ms(ev, 2, 3))},
                         "chunk_traffic": counter_traffic("prefill_4096", CHUNK_SPLIT_KERNELS)},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": counter_traffic("prefill_4096", PREFILL_KERNELS),
                   "kernel": "gdn_prefill (chunk_prep + chunk_state + chunk_out)",
                   "algorithmic_bytes": nbytes,
-                  "launch_ms": round(t_pre, 4),
-                  "mfma": {"algorithmic_flops": flops, "achieved_tflops": round(flops / (t_pre * 1e-3) / 1e12, 2),
-                           "peak_tflops": BF16_PEAK_TFLOPS,
-                           "frac": round(flops / (t_pre * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}},
-        inputs=dict(x=x, a=a, b=b, z=z, case=case))
+                  "launch_ms": t_pre["mean"],
+                  "mfma": {"algorithmic_flops": flops, "achieved_tflops": round(mfma_tflops, 2),
+                           "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(mfma_tflops / BF16_PEAK_TFLOPS, 5),
+                           "counters": counter_mfma("prefill_4096", PREFILL_KERNELS)}},
+        inputs=dict(case=case))
 
 
 def bench_tp_shapes(args, torch, gdn, gi):
@@ -293,16 +341,16 @@ def bench_tp_shapes(args, torch, gdn, gi):
         for k in range(steps):
             step(ev[k])
         torch.cuda.synchronize()
-        t = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        out[f"tp{tp}_h{d.h_k}_{d.h_v}"] = {"gdn_prefill_ms": round(t, 4), "tokens_per_s_per_rank": round(T / (t * 1e-3), 1)}
+        t = pct([e[0].elapsed_time(e[1]) for e in ev])
+        out[f"tp{tp}_h{d.h_k}_{d.h_v}"] = {"gdn_prefill_ms": t, "tokens_per_s_per_rank": round(T / (t["mean"] * 1e-3), 1)}
     return out
 
 
 def bench_decode_bucket(args, torch, gdn, gi):
-    """The decode step (gdn_conv1d_update + gdn_recurrent_decode) as a serving
-    loop runs it: captured once per state pool as a HIP graph for a fixed bucket
-    of 256 requests, of which 200 are live and 56 are pad entries (slot -1),
-    replayed over 3 pools so states come from HBM."""
+    """The decode step as a serving loop runs it: gdn_decode captured once per
+    state pool as a HIP graph for a fixed bucket of 256 requests, of which 200
+    are live and 56 are pad entries (slot -1), replayed over 3 pools so states
+    come from HBM."""
     case = gi.decode_case()
     d = case.dims
     dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
@@ -317,7 +365,6 @@ def bench_decode_bucket(args, torch, gdn, gi):
     p = case.params
     conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
     A_log, dt_bias = torch.from_numpy(p.A_log).to(dev), torch.from_numpy(p.dt_bias).to(dev)
-    y = torch.empty_like(x)
     o = torch.empty((case.n, 1, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
     graphs = []
     for _ in range(3):
@@ -325,8 +372,7 @@ def bench_decode_bucket(args, torch, gdn, gi):
         conv = torch.randn((case.n_slots, d.c_ch, d.conv_w - 1), device=dev, generator=gen).to(torch.bfloat16)
 
         def step(ssm=ssm, conv=conv):
-            gdn.conv1d_update(dims, x, conv_w, conv, slots, y=y)
-            gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, None, 1.0, z, norm_w, 1e-6, o=o)
+            gdn.decode(dims, x, conv_w, a, b, A_log, dt_bias, slots, conv, ssm, None, 1.0, z, norm_w, 1e-6, o=o)
 
         graphs.append((capture_graph(torch, step), ssm, conv))
     steps = max(args.steps, 30)
@@ -338,12 +384,14 @@ def bench_decode_bucket(args, torch, gdn, gi):
         graphs[k % 3][0].replay()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
-    return {"workload": "decode_bucket256_live200", "bucket": case.n, "live": live, "graph_ms_per_step": round(ms, 4),
-            "tokens_per_s": round(live / (ms * 1e-3), 1)}
+    return {"workload": "decode_bucket256_live200", "call": "gdn_decode", "bucket": case.n, "live": live,
+            "graph_ms_per_step": round(ms, 4), "tokens_per_s": round(live / (ms * 1e-3), 1)}
 
 
 def bench_decode(args, torch, gdn, gi):
-    """256 requests x 1 token, in place, rotating over 3 state pools of 512 slots."""
+    """256 requests x 1 token, in place, rotating over 3 state pools of 512
+    slots: the single gdn_decode call, and the two calls gdn_conv1d_update +
+    gdn_recurrent_decode."""
     case = gi.decode_case()
     d = case.dims
     dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
@@ -364,7 +412,7 @@ def bench_decode(args, torch, gdn, gi):
     y = torch.empty_like(x)
     o = torch.empty((case.n, 1, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
     steps = max(args.steps, 30)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(k, e=None):
         ssm, conv = pools[k % 3]
@@ -373,6 +421,9 @@ def bench_decode(args, torch, gdn, gi):
         if e: e[1].record()
         gdn.recurrent_decode(dims, y, a, b, A_log, dt_bias, ssm, slots, None, 1.0, z, norm_w, 1e-6, o=o)
         if e: e[2].record()
+        ssm, conv = pools[(k + 1) % 3]
+        gdn.decode(dims, x, conv_w, a, b, A_log, dt_bias, slots, conv, ssm, None, 1.0, z, norm_w, 1e-6, o=o)
+        if e: e[3].record()
 
     for k in range(6):
         step(k)
@@ -380,39 +431,55 @@ def bench_decode(args, torch, gdn, gi):
     for k in range(steps):
         step(k, ev[k])
     torch.cuda.synchronize()
-    t_conv = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    t_rec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    nbytes = decode_algorithmic(case.n, 1, d.h_k, d.h_v, d.d_k, 2, 1)
-    gbs = nbytes / (t_rec * 1e-3) / 1e9
-    return {"workload": "decode_256x1", "kernel": "recurrent_kernel<bf16,128>", "launch_ms": round(t_rec, 4),
-            "conv_update_ms": round(t_conv, 4), "algorithmic_bytes": nbytes, "value": round(gbs, 1),
-            "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "tokens_per_s": round(case.n / ((t_rec + t_conv) * 1e-3), 1)}
+    ms = lambda i, j: pct([e[i].elapsed_time(e[j]) for e in ev])
+    t_conv, t_rec, t_dec = ms(0, 1), ms(1, 2), ms(2, 3)
+    nb_dec = decode_fused_algorithmic(case.n, 1, d.h_k, d.h_v, d.d_k, 2, d.conv_w, 1)
+    nb_rec = decode_algorithmic(case.n, 1, d.h_k, d.h_v, d.d_k, 2, 1)
+    gbs = nb_dec / (t_dec["mean"] * 1e-3) / 1e9
+    gbs_rec = nb_rec / (t_rec["mean"] * 1e-3) / 1e9
+    return {"workload": "decode_256x1", "call": "gdn_decode", "kernel": "decode_fused_kernel<bf16,128,2,4,false>",
+            "launch_ms": t_dec, "algorithmic_bytes": nb_dec, "value": round(gbs, 1), "unit": "GB/s",
+            "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(case.n / (t_dec["mean"] * 1e-3), 1),
+            "separate_calls": {"conv_update_ms": t_conv, "recurrent_ms": t_rec, "recurrent_algorithmic_bytes": nb_rec,
+                               "recurrent_gbs": round(gbs_rec, 1), "recurrent_frac": round(gbs_rec / HBM_PEAK_GBS, 4),
+                               "tokens_per_s": round(case.n / ((t_conv["mean"] + t_rec["mean"]) * 1e-3), 1)}}
 
 
 def bench_varlen(args, torch, gdn, gi):
     """The ~271k-token varlen prefill: 64 sequences (lengths 128..8192, seed 0),
-    nonzero initial states from a 128-slot pool.  Inputs follow the recipe's
-    distributions but are drawn on the device (torch generator), since the
-    parity tests already cover the numpy-seeded values."""
+    nonzero initial states from a 128-slot pool, on the seeded inputs of the
+    parity tests (generated on host threads, sequence by sequence)."""
+    from concurrent.futures import ThreadPoolExecutor
     case = gi.varlen_case()
     d = case.dims
     dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
     dev = torch.device("cuda")
-    gen = torch.Generator(device=dev).manual_seed(case.seed)
     T, N = case.t_total, case.n_seq
-    rnd = lambda *shape: torch.randn(shape, device=dev, generator=gen).to(torch.bfloat16)
-    x, a, b, z = rnd(T, d.c_ch), rnd(T, d.h_v), rnd(T, d.h_v), rnd(T, d.h_v, d.d_v)
-    p = case.params
+    x = torch.empty((T, d.c_ch), dtype=torch.bfloat16, device=dev)
+    a = torch.empty((T, d.h_v), dtype=torch.bfloat16, device=dev)
+    b = torch.empty((T, d.h_v), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((T, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
     bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+
+    def gen(i):
+        return i, case.seq_x(i), case.seq_a(i), case.seq_b(i), case.seq_z(i)
+
+    t_gen = time.perf_counter()
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        for i, xs, as_, bs, zs in ex.map(gen, range(N)):
+            lo, hi = int(case.cu_seqlens[i]), int(case.cu_seqlens[i + 1])
+            x[lo:hi], a[lo:hi], b[lo:hi], z[lo:hi] = bf(xs), bf(as_), bf(bs), bf(zs)
+    t_gen = time.perf_counter() - t_gen
+    p = case.params
     conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
     A_log = torch.from_numpy(p.A_log).to(dev)
     dt_bias = torch.from_numpy(p.dt_bias).to(dev)
     cu = torch.from_numpy(case.cu_seqlens).to(dev)
     slots = torch.from_numpy(case.slots).to(dev)
     has_init = torch.ones(N, dtype=torch.uint8, device=dev)
-    conv_pool = rnd(case.n_slots, d.c_ch, d.conv_w - 1)
-    ssm_pool = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device=dev, generator=gen) * 0.02
+    conv_pool = bf(np.stack([case.slot_conv(s) for s in range(case.n_slots)]))
+    ssm_pool = torch.from_numpy(np.stack([case.slot_ssm(s) for s in range(case.n_slots)])).to(dev)
     y = torch.empty_like(x)
     g = torch.empty((T, d.h_v), dtype=torch.float32, device=dev)
     beta = torch.empty_like(g)
@@ -446,30 +513,31 @@ def bench_varlen(args, torch, gdn, gi):
         for k in range(steps):
             fn(evs[k])
         torch.cuda.synchronize()
-    ms = lambda evs, i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
+    ms = lambda evs, i, j: pct([e[i].elapsed_time(e[j]) for e in evs])
     t_step, t_chunk, t_fused = ms(ev, 0, 3), ms(ev, 2, 3), ms(evf, 0, 1)
     nbytes, flops = chunk_algorithmic(T, N, d.h_k, d.h_v, d.d_k, 2, True, case.chunk)
     pbytes, pflops = prefill_algorithmic(T, N, d.h_k, d.h_v, d.d_k, 2, True, case.chunk, d.conv_w)
     del x, y, z, o, ws
-    best = min(t_step, t_fused)
+    best = min(t_step["mean"], t_fused["mean"])
+    rate = lambda nb, t: round(nb / (t["mean"] * 1e-3) / 1e9, 1)
     return {"workload": f"varlen_prefill_{N}seq_{T}tok", "tokens_per_s": round(T / (best * 1e-3), 1),
-            "path": "separate calls" if t_step <= t_fused else "gdn_prefill",
-            "separate_calls": {"ms_per_step": round(t_step, 4),
-                               "kernels_ms": {"gdn_conv1d_fwd": round(ms(ev, 0, 1), 4),
-                                              "gdn_gating": round(ms(ev, 1, 2), 4),
-                                              "gdn_chunk_prefill": round(t_chunk, 4)},
-                               "chunk_achieved_gbs": round(nbytes / (t_chunk * 1e-3) / 1e9, 1),
-                               "chunk_hbm_frac": round(nbytes / (t_chunk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                               "chunk_mfma_frac": round(flops / (t_chunk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
-            "gdn_prefill": {"ms_per_step": round(t_fused, 4),
-                            "achieved_gbs": round(pbytes / (t_fused * 1e-3) / 1e9, 1),
-                            "hbm_frac": round(pbytes / (t_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "mfma_frac": round(pflops / (t_fused * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}}
+            "path": "separate calls" if t_step["mean"] <= t_fused["mean"] else "gdn_prefill",
+            "inputs": f"seeded (the parity tests' recipe), generated in {t_gen:.1f} s",
+            "separate_calls": {"ms_per_step": t_step,
+                               "kernels_ms": {"gdn_conv1d_fwd": ms(ev, 0, 1), "gdn_gating": ms(ev, 1, 2),
+                                              "gdn_chunk_prefill": t_chunk},
+                               "chunk_achieved_gbs": rate(nbytes, t_chunk),
+                               "chunk_hbm_frac": round(rate(nbytes, t_chunk) / HBM_PEAK_GBS, 4),
+                               "chunk_mfma_frac": round(flops / (t_chunk["mean"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
+            "gdn_prefill": {"ms_per_step": t_fused, "achieved_gbs": rate(pbytes, t_fused),
+                            "hbm_frac": round(rate(pbytes, t_fused) / HBM_PEAK_GBS, 4),
+                            "mfma_frac": round(pflops / (t_fused["mean"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}}
 
 
 def bench_mtp(args, torch, gdn, gi):
-    """128 requests x 4 MTP draft tokens: conv update and recurrent step with
-    per-position state writes, then the accepted states committed with
+    """128 requests x 4 MTP draft tokens: the draft step with per-position state
+    and conv-window writes (gdn_decode, and the two calls gdn_conv1d_update +
+    gdn_recurrent_decode), then the accepted states committed with
     gdn_state_copy; pools rotated over 3 copies of 640 slots."""
     case = gi.mtp_case()
     d = case.dims
@@ -495,7 +563,7 @@ def bench_mtp(args, torch, gdn, gi):
     y = torch.empty_like(x)
     o = torch.empty((case.n, case.t_step, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
     steps = max(args.steps, 30)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
 
     def step(k, e=None):
         ssm, conv = pools[k % 3]
@@ -506,6 +574,11 @@ def bench_mtp(args, torch, gdn, gi):
         if e: e[2].record()
         gdn.state_copy(dims, ssm, src, dst, conv)
         if e: e[3].record()
+        ssm, conv = pools[(k + 1) % 3]
+        gdn.decode(dims, x, conv_w, a, b, A_log, dt_bias, slots, conv, ssm, out_slots, 1.0, z, norm_w, 1e-6, o=o)
+        if e: e[4].record()
+        gdn.state_copy(dims, ssm, src, dst, conv)
+        if e: e[5].record()
 
     for k in range(6):
         step(k)
@@ -513,36 +586,134 @@ def bench_mtp(args, torch, gdn, gi):
     for k in range(steps):
         step(k, ev[k])
     torch.cuda.synchronize()
-    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in ev]))
-    t_conv, t_rec, t_copy = ms(0, 1), ms(1, 2), ms(2, 3)
-    nbytes = decode_algorithmic(case.n, case.t_step, d.h_k, d.h_v, d.d_k, 2, case.t_step)
+    ms = lambda i, j: pct([e[i].elapsed_time(e[j]) for e in ev])
+    t_conv, t_rec, t_copy, t_dec, t_copy2 = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4), ms(4, 5)
+    nb_dec = decode_fused_algorithmic(case.n, case.t_step, d.h_k, d.h_v, d.d_k, 2, d.conv_w, case.t_step)
+    nb_rec = decode_algorithmic(case.n, case.t_step, d.h_k, d.h_v, d.d_k, 2, case.t_step)
     copy_bytes = 2.0 * int(sel.sum()) * (d.h_v * d.d_v * d.d_k * 4 + d.c_ch * (d.conv_w - 1) * 2)
-    gbs = nbytes / (t_rec * 1e-3) / 1e9
-    return {"workload": f"mtp_{case.n}x{case.t_step}", "kernel": "recurrent_mtp_kernel<bf16,128>",
-            "launch_ms": round(t_rec, 4), "conv_update_ms": round(t_conv, 4), "state_copy_ms": round(t_copy, 4),
-            "algorithmic_bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "state_copy_gbs": round(copy_bytes / (t_copy * 1e-3) / 1e9, 1),
-            "draft_tokens_per_s": round(case.n * case.t_step / ((t_conv + t_rec + t_copy) * 1e-3), 1)}
+    gbs = nb_dec / (t_dec["mean"] * 1e-3) / 1e9
+    gbs_rec = nb_rec / (t_rec["mean"] * 1e-3) / 1e9
+    return {"workload": f"mtp_{case.n}x{case.t_step}", "call": "gdn_decode",
+            "kernel": "decode_fused_kernel<bf16,128,2,4,true>", "launch_ms": t_dec, "algorithmic_bytes": nb_dec,
+            "value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "state_copy_ms": t_copy2, "state_copy_gbs": round(copy_bytes / (t_copy2["mean"] * 1e-3) / 1e9, 1),
+            "draft_tokens_per_s": round(case.n * case.t_step / ((t_dec["mean"] + t_copy2["mean"]) * 1e-3), 1),
+            "separate_calls": {"conv_update_ms": t_conv, "recurrent_ms": t_rec, "state_copy_ms": t_copy,
+                               "recurrent_algorithmic_bytes": nb_rec, "recurrent_gbs": round(gbs_rec, 1),
+                               "recurrent_frac": round(gbs_rec / HBM_PEAK_GBS, 4),
+                               "draft_tokens_per_s": round(case.n * case.t_step /
+                                                           ((t_conv["mean"] + t_rec["mean"] + t_copy["mean"]) * 1e-3),
+                                                           1)}}
 
 
-def cpu_baseline(inputs) -> dict:
-    """The fp64 oracle on the host, one BLAS thread, on the whole 4096-token
-    sequence (all 32 V heads): conv, gating, recurrence, gated RMSNorm."""
-    from threadpoolctl import threadpool_limits
-    from oracle import gdn_oracle as O
-    case = inputs["case"]
+def bench_mtp_bucket(args, torch, gdn, gi):
+    """The MTP step as a serving loop runs it: a bucket of 128 requests x
+    (mtp_step + 1) = 4 rows, 100 live and 28 pad requests, the draft step
+    (gdn_decode) and the commit copy captured as one HIP graph per state pool,
+    replayed over 3 pools."""
+    case = gi.mtp_case()
     d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    dev = torch.device("cuda")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(case.seed + 1)
+    live = 100
+    slots_np, out_np = case.slots.copy(), case.out_slots.copy()
+    slots_np[live:] = -1
+    out_np[live:] = -1
+    acc = case.accept.copy()
+    acc[live:] = 0
+    sel = acc > 0
+    src_np = np.where(sel, out_np[np.arange(case.n), np.maximum(acc - 1, 0)], -1).astype(np.int32)
+    dst_np = np.where(sel, slots_np, -1).astype(np.int32)
+    slots, out_slots = torch.from_numpy(slots_np).to(dev), torch.from_numpy(out_np).to(dev)
+    src, dst = torch.from_numpy(src_np).to(dev), torch.from_numpy(dst_np).to(dev)
+    x, a, b, z = bf(case.x()), bf(case.a()), bf(case.b()), bf(case.z())
     p = case.params
-    T = int(os.environ.get("GDN_CPU_BASELINE_TOKENS", case.t_total))
-    x, a, b, z = (case.seq_x(0)[:T], case.seq_a(0)[:T], case.seq_b(0)[:T], case.seq_z(0)[:T])
-    with threadpool_limits(limits=1):
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log, dt_bias = torch.from_numpy(p.A_log).to(dev), torch.from_numpy(p.dt_bias).to(dev)
+    o = torch.empty((case.n, case.t_step, d.h_v, d.d_v), dtype=torch.bfloat16, device=dev)
+    graphs = []
+    for _ in range(3):
+        ssm = torch.randn((case.n_slots, d.h_v, d.d_v, d.d_k), device=dev, generator=gen) * 0.02
+        conv = torch.randn((case.n_slots, d.c_ch, d.conv_w - 1), device=dev, generator=gen).to(torch.bfloat16)
+
+        def step(ssm=ssm, conv=conv):
+            gdn.decode(dims, x, conv_w, a, b, A_log, dt_bias, slots, conv, ssm, out_slots, 1.0, z, norm_w, 1e-6, o=o)
+            gdn.state_copy(dims, ssm, src, dst, conv)
+
+        graphs.append((capture_graph(torch, step), ssm, conv))
+    steps = max(args.steps, 30)
+    for k in range(6):
+        graphs[k % 3][0].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        graphs[k % 3][0].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    return {"workload": f"mtp_bucket{case.n}x{case.t_step}_live{live}", "call": "gdn_decode + gdn_state_copy",
+            "bucket_requests": case.n, "rows_per_request": case.t_step, "live": live,
+            "graph_ms_per_step": round(ms, 4), "draft_tokens_per_s": round(live * case.t_step / (ms * 1e-3), 1)}
+
+
+def cpu_baseline(case2) -> dict:
+    """The fp64 oracle, as it stands, on the host's cores: a pool of
+    single-threaded worker processes (started before this process touched the
+    GPU), one task per V-head pair (prefill) or per group of requests
+    (decode, MTP), on every workload or a stated sample of it."""
+    from tests import oracle_pool as P
+    import gdn_inputs as gi
+
+    cores = P.n_workers()
+    res = {}
+
+    def timed(name, fn, tasks, tokens, sample):
         t0 = time.perf_counter()
-        O.layer_sequence(x, a, b, z, p.conv_w, None, p.A_log, p.dt_bias, p.norm_w, None, None,
-                         (d.h_k, d.h_v, d.d_k, d.d_v), 1.0, 1e-6)
+        P.run_map(fn, tasks)
         dt = time.perf_counter() - t0
-    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {T} tokens of the 4096-token sequence, all 32 V heads, {dt:.1f} s"}
+        res[name] = {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                     "sample": f"{sample}; {dt:.1f} s wall"}
+
+    T = case2.t_total
+    timed("prefill_single_4096", P.prefill_oracle_heads, [(case2, [2 * j, 2 * j + 1]) for j in range(16)], T,
+          f"the whole {T}-token sequence, all 32 V heads, one task per V-head pair")
+    dec = gi.decode_case()
+    timed("decode_256x1", P.decode_oracle_requests, [(dec, list(range(r, r + 16))) for r in range(0, dec.n, 16)],
+          dec.n, "all 256 requests, 16 per task")
+    mtp = gi.mtp_case()
+    timed("mtp_128x4", P.decode_oracle_requests, [(mtp, list(range(r, r + 8))) for r in range(0, mtp.n, 8)],
+          mtp.n * mtp.t_step, "all 128 requests x 4 draft tokens, 8 requests per task")
+    var = gi.varlen_case()
+    seqs = [int(i) for i in np.argsort(var.lengths)[:16]]
+    timed("varlen_prefill", P.prefill_oracle_heads, [(var, None, i) for i in seqs],
+          int(sum(var.lengths[i] for i in seqs)), "the 16 shortest of the 64 sequences, all heads, one per task")
+    out = dict(res["prefill_single_4096"])
+    out["per_workload"] = res
+    return out
+
+
+def rocminfo_gpu() -> dict | None:
+    """CU count and peak engine clock of the first GPU agent, from rocminfo
+    (run before this process touches the GPU)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    for agent in out.split("*******")[1:]:
+        if "Device Type:" in agent and "GPU" in agent.split("Device Type:")[1].split("\n")[0]:
+            info = {}
+            for line in agent.splitlines():
+                key, _, val = line.strip().partition(":")
+                if key == "Compute Unit":
+                    info["compute_units"] = int(val.split()[0])
+                elif key == "Max Clock Freq. (MHz)":
+                    info["max_clock_mhz"] = int(val.split()[0])
+                elif key == "Name" and "name" not in info:
+                    info["name"] = val.strip()
+            return info
+    return None
 
 
 def main() -> int:
@@ -555,13 +726,20 @@ def main() -> int:
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-mtp", action="store_true")
     ap.add_argument("--no-tp", action="store_true", help="skip the per-rank (tp = 2, 4) prefill rows")
-    ap.add_argument("--no-bucket", action="store_true", help="skip the padded decode-bucket graph row")
+    ap.add_argument("--no-bucket", action="store_true", help="skip the padded decode and MTP bucket graph rows")
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GDN layer's multi-GPU sharding "
               "is a design, not a measured path", file=sys.stderr)
         return 2
+
+    # before anything touches the GPU: the device's CU count and clock, and the
+    # CPU worker pool of the oracle baseline (forked from a clean server process)
+    rinfo = rocminfo_gpu()
+    if not args.no_cpu_baseline:
+        from tests.oracle_pool import start_server
+        start_server()
 
     import torch
     import gdn_inputs as gi
@@ -572,16 +750,27 @@ def main() -> int:
         return 1
     gdn.lib()
     info = device_info()
-    pre = bench_prefill(args, torch, gdn, gi)
-    dec = None if args.no_decode else bench_decode(args, torch, gdn, gi)
-    bucket = None if args.no_decode or args.no_bucket else bench_decode_bucket(args, torch, gdn, gi)
-    tp = None if args.no_tp else bench_tp_shapes(args, torch, gdn, gi)
-    mtp = None if args.no_mtp else bench_mtp(args, torch, gdn, gi)
+    t_start = time.perf_counter()
+
+    def run(name, skip, fn, *a):
+        # one progress line per row on stderr; the JSON line is the only stdout
+        if skip:
+            return None
+        r = fn(*a)
+        print(f"bench: {name} done ({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
+        return r
+
+    pre = run("prefill 4096", False, bench_prefill, args, torch, gdn, gi)
+    dec = run("decode 256x1", args.no_decode, bench_decode, args, torch, gdn, gi)
+    bucket = run("decode bucket", args.no_decode or args.no_bucket, bench_decode_bucket, args, torch, gdn, gi)
+    tp = run("tp shapes", args.no_tp, bench_tp_shapes, args, torch, gdn, gi)
+    mtp = run("mtp 128x4", args.no_mtp, bench_mtp, args, torch, gdn, gi)
+    mtp_bucket = run("mtp bucket", args.no_mtp or args.no_bucket, bench_mtp_bucket, args, torch, gdn, gi)
     torch.cuda.empty_cache()
-    var = None if args.no_varlen else bench_varlen(args, torch, gdn, gi)
+    var = run("varlen", args.no_varlen, bench_varlen, args, torch, gdn, gi)
     torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth_gbs(torch)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(pre["inputs"])
+    cpu = run("cpu baseline", args.no_cpu_baseline, cpu_baseline, pre["inputs"]["case"])
     T = pre["T"]
     line = {
         "metric": METRIC,
@@ -597,19 +786,21 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "prefill_single_4096", "batch": 1, "seq_len": T, "h_k": 16, "h_v": 32,
-                   "head_dim": 128, "conv_w": 4, "chunk": 64, "state": "fp32"},
+                   "head_dim": 128, "conv_w": 4, "chunk": 64, "state": "fp32",
+                   "input_copies": 2, "footprint_bytes": pre["footprint_bytes"]},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
-        "kernels_ms": {k: round(v, 4) for k, v in pre["kernels_ms"].items()},
+        "kernels_ms": pre["kernels_ms"],
         "timing": "graph replay" if not args.eager else "eager launches",
         "eager_ms_per_step": round(pre["eager_ms_per_step"], 4),
         "separate_calls": pre["separate_calls"],
         "decode": dec,
         "decode_bucket": bucket,
         "mtp": mtp,
+        "mtp_bucket": mtp_bucket,
         "varlen": var,
         "tp_shapes": tp,
-        "device": {**info, "copy_gbs": round(copy_gbs, 1)},
+        "device": {**info, "rocminfo": rinfo, "copy_gbs": round(copy_gbs, 1)},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -82,3 +82,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_single_call_decode_bytes():
+    # gdn_decode reads the conv input row instead of the conv output, and moves the
+    # conv window (bf16, c_ch x (W-1)) with each state read or write
+    per_tok = C_CH * 2 + 2 * H_V * 2 + 2 * H_V * D * 2
+    window = C_CH * (W - 1) * 2
+    assert bench.decode_fused_algorithmic(256, 1, H_K, H_V, D, 2, W, 1) == 256 * (2 * (STATE + window) + per_tok)
+    assert bench.decode_fused_algorithmic(128, 4, H_K, H_V, D, 2, W, 4) == 128 * (5 * (STATE + window) + 4 * per_tok)
+
+
+def test_percentiles():
+    p = bench.pct([1.0, 2.0, 3.0, 4.0, 100.0])
+    assert p["median"] == 3.0 and p["mean"] == 22.0
+    assert p["p10"] == pytest.approx(1.4) and p["p90"] == pytest.approx(61.6)
