@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_BF16, GDN_F32 = 0, 1
 _STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE", -4: "GDN_ERR_UNSUPPORTED",
-           -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIGN"}
+           -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_HIP", -7: "GDN_ERR_ALIGN", -8: "GDN_ERR_TOO_LARGE"}
 
 # Names and signatures of every exported entry point (mirrors include/gdn.h).
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -38,6 +38,9 @@ SIGNATURES = {
                                    _I32, _P, _P, _P, _F, _P, _SZ, _P]),
     "gdn_recurrent_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
                                             _P, _F, _P]),
+    "gdn_prefill_noalloc_limit": (_SZ, []),
+    "gdn_prefill_noalloc": (ctypes.c_int, [_P, _I32, _I32, _I64, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _I32, _P, _P, _P, _F, _P]),
     "gdn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
                                   _P, _P, _F, _P]),
     "gdn_state_copy": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),

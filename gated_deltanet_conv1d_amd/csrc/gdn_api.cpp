@@ -68,6 +68,7 @@ const char* gdn_status_string(int status) {
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: a kernel launch failed";
     case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer not 16-byte aligned";
+    case GDN_ERR_TOO_LARGE: return "GDN_ERR_TOO_LARGE: sizes exceed the static scratch of gdn_prefill_noalloc";
   }
   return "unknown gdn_status";
 }

@@ -62,7 +62,8 @@ typedef enum {
   GDN_ERR_UNSUPPORTED = -4, /* a valid but unsupported size (head dim, chunk, conv width) */
   GDN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
   GDN_ERR_HIP = -6,         /* a kernel launch failed                           */
-  GDN_ERR_ALIGN = -7        /* a pointer is not 16-byte aligned                 */
+  GDN_ERR_ALIGN = -7,       /* a pointer is not 16-byte aligned                 */
+  GDN_ERR_TOO_LARGE = -8    /* the sizes need more than gdn_prefill_noalloc's static scratch */
 } gdn_status;
 
 typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
@@ -174,6 +175,27 @@ int gdn_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_tota
                 const float* A_log, const float* dt_bias, const int32_t* cu_seqlens, const int32_t* slots,
                 const uint8_t* has_init, void* conv_state, float* state, int32_t n_slots, void* o, const void* z,
                 const void* norm_w, float norm_eps, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gdn_prefill_noalloc -- gdn_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as gdn_prefill without the
+ * workspace: the library keeps one static scratch array of
+ * gdn_prefill_noalloc_limit() bytes (256 MiB) per device, held from the
+ * library's first use on that device until the process ends, and allocates
+ * nothing.  Sizes whose gdn_prefill_workspace_size() exceeds the limit return
+ * GDN_ERR_TOO_LARGE before anything is enqueued (a 4096-token prefill at 32 V
+ * heads, d = 128, chunk 64 fits with up to 20 sequences).  The call runs on
+ * the current device, which must be the stream's.  Every call on a device
+ * shares that device's scratch: calls that overlap on one device (different
+ * streams, no ordering between them) race.
+ */
+size_t gdn_prefill_noalloc_limit(void);
+int gdn_prefill_noalloc(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk,
+                        float scale, const void* x, const void* conv_w, const void* conv_b, const void* a,
+                        const void* b, const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                        const int32_t* slots, const uint8_t* has_init, void* conv_state, float* state,
+                        int32_t n_slots, void* o, const void* z, const void* norm_w, float norm_eps, void* stream);
 
 /*
  * gdn_recurrent_decode -- the fused recurrent step for decode (t_step = 1)
