@@ -220,7 +220,7 @@ def bench_prefill(args, torch, gdn, gi):
                    gdn.prefill_workspace_size(dims, 0, 1, T, case.chunk))
     x0, a0, b0, z0 = case.seq_x(0), case.seq_a(0), case.seq_b(0), case.seq_z(0)
     copies = []
-    for _ in range(2):  # every buffer twice: the steps alternate, the footprint exceeds the memory-side cache
+    for _ in range(args.prefill_copies):  # (default 2: the steps alternate, the footprint exceeds the memory-side cache)
         copies.append(dict(
             x=bf(x0), a=bf(a0), b=bf(b0), z=bf(z0),
             conv_pool=torch.zeros((1, d.c_ch, d.conv_w - 1), dtype=torch.bfloat16, device=dev),
@@ -232,8 +232,10 @@ def bench_prefill(args, torch, gdn, gi):
             ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
     footprint = sum(t.numel() * t.element_size() for c in copies for t in c.values())
 
+    nc = len(copies)
+
     def step_sep(k, e=None):
-        c = copies[k % 2]
+        c = copies[k % nc]
         if e: e[0].record()
         gdn.conv1d_fwd(dims, c["x"], conv_w, cu, slots, c["conv_pool"], has_init, y=c["y"])
         if e: e[1].record()
@@ -244,7 +246,7 @@ def bench_prefill(args, torch, gdn, gi):
         if e: e[3].record()
 
     def step(k, e=None):
-        c = copies[k % 2]
+        c = copies[k % nc]
         if e: e[0].record()
         gdn.prefill(dims, c["x"], conv_w, c["a"], c["b"], A_log, dt_bias, cu, slots, c["conv_pool"], c["ssm_pool"],
                     has_init, case.chunk, 1.0, c["z"], norm_w, 1e-6, o=c["o"], workspace=c["ws"])
@@ -264,13 +266,13 @@ def bench_prefill(args, torch, gdn, gi):
         wall_eager = time.perf_counter() - t0
         if args.eager:
             return wall_eager, wall_eager, evs
-        graphs = [capture_graph(torch, lambda k=k: fn(k)) for k in range(2)]
+        graphs = [capture_graph(torch, lambda k=k: fn(k)) for k in range(nc)]
         for k in range(args.warmup):
-            graphs[k % 2].replay()
+            graphs[k % nc].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
-            graphs[k % 2].replay()
+            graphs[k % nc].replay()
         torch.cuda.synchronize()
         return time.perf_counter() - t0, wall_eager, evs
 
@@ -728,6 +730,8 @@ def main() -> int:
     ap.add_argument("--no-tp", action="store_true", help="skip the per-rank (tp = 2, 4) prefill rows")
     ap.add_argument("--no-bucket", action="store_true", help="skip the padded decode and MTP bucket graph rows")
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
+    ap.add_argument("--prefill-copies", type=int, default=2,
+                    help="copies of the prefill buffers the steps rotate over (2: more than the memory-side cache)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GDN layer's multi-GPU sharding "
@@ -787,7 +791,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "prefill_single_4096", "batch": 1, "seq_len": T, "h_k": 16, "h_v": 32,
                    "head_dim": 128, "conv_w": 4, "chunk": 64, "state": "fp32",
-                   "input_copies": 2, "footprint_bytes": pre["footprint_bytes"]},
+                   "input_copies": args.prefill_copies, "footprint_bytes": pre["footprint_bytes"]},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "kernels_ms": pre["kernels_ms"],

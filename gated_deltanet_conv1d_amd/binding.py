@@ -71,13 +71,16 @@ class _CDims(ctypes.Structure):
 _lib: Optional[ctypes.CDLL] = None
 
 
-def lib() -> ctypes.CDLL:
-    """Load libgdn.so (once) and attach the ABI signatures."""
+def lib(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libgdn.so (once per process) and attach the ABI signatures.  path:
+    another build of the library to load instead (the launch-shape tuner
+    times variant builds this way); only before the first load."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise GdnError(f"{LIB_PATH} is not built: run gated_deltanet_conv1d_amd.build.build() first")
-        handle = ctypes.CDLL(LIB_PATH)
+        path = path or LIB_PATH
+        if not os.path.exists(path):
+            raise GdnError(f"{path} is not built: run gated_deltanet_conv1d_amd.build.build() first")
+        handle = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype, fn.argtypes = res, args

@@ -45,22 +45,25 @@ def _compile(src: str, obj: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
+def build(verbose: bool = True, csrc: str = CSRC, lib: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source under csrc and link them into lib (defaults: the
+    package's sources and libgdn.so; the launch-shape tuner builds variants
+    of a copied source tree elsewhere)."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.cpp")))
+    objs = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in srcs]
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(_compile, srcs, objs))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources", file=sys.stderr)
+    return lib
 
 
 if __name__ == "__main__":

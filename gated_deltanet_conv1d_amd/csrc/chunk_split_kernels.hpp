@@ -41,6 +41,7 @@
 #pragma once
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
+#include "launch_table.hpp"
 
 namespace gdn {
 namespace split {
@@ -1396,14 +1397,6 @@ __global__ __launch_bounds__(kThreads<D>) __attribute__((amdgpu_waves_per_eu(3))
   }
 }
 
-// Chain launch shape: d_v tiles per workgroup.  One tile per workgroup is
-// the most parallel and, with 4 register stages, the fastest chain; it is
-// used while the one-tile workgroups fit one per CU of an MI355X (256).
-// Beyond that the tiles per workgroup grow (2, then 4) so the launch stays
-// near one round of workgroups and the tiles share each -W and K^T load,
-// which is what bounds many chains running at once (3 stages).
-constexpr int64_t kChainCUs = 256;
-
 // (conv_x non-null: the fused-input prefill, whose chain also stores the
 // final conv windows)
 template <typename Op, int D, int C, int NTW, int PD>
@@ -1463,11 +1456,16 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
-  const int64_t chains = groups * K::NT;
   const Op* cx = FUSE ? reinterpret_cast<const Op*>(a.x) : nullptr;
-  const hipError_t ce = chains <= kChainCUs       ? launch_chain<Op, D, C, 1, 4>(a, groups, cstart, units, cx, st)
-                        : chains <= 4 * kChainCUs ? launch_chain<Op, D, C, 2, 3>(a, groups, cstart, units, cx, st)
-                                                  : launch_chain<Op, D, C, 4, 3>(a, groups, cstart, units, cx, st);
+  // the chain's launch shape from the measured table (launch_table.hpp): one
+  // d_v tile per workgroup is the most parallel chain, more tiles per
+  // workgroup share each -W and K^T load, which bounds many chains at once
+  const ChainShape shape = chain_shape((int64_t)a.n_seq * a.s.h_v, a.t_total / a.n_seq);
+  hipError_t ce = hipErrorInvalidValue;
+#define GDN_CHAIN_CASE(NTW_, PD_) \
+  if (shape.ntw == NTW_ && shape.pd == PD_) ce = launch_chain<Op, D, C, NTW_, PD_>(a, groups, cstart, units, cx, st);
+  GDN_CHAIN_SHAPES(GDN_CHAIN_CASE)
+#undef GDN_CHAIN_CASE
   if (ce != hipSuccess) return ce;
   if (max_chunks > 0)
     hipLaunchKernelGGL((chunk_out_kernel<T, Op, D, C, FUSE, W>), dim3((unsigned)(max_chunks * a.s.h_v)),
