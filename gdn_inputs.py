@@ -89,6 +89,45 @@ def layer_params(seed: int, dims: Dims, act: str = "bf16") -> LayerParams:
     )
 
 
+# ------------------------------------------------ weights around the core
+# The hidden size of the layer is not on the pages; 2048 is that of the
+# 80B-A3B model they name (a reading).
+HIDDEN = 2048
+_HX, _HNW, _WQKVZ, _WBA, _WOUT = range(15, 20)
+
+
+@dataclass
+class BlockWeights:
+    """Weights of the layer around the core, in [out_features, in_features]
+    layout, drawn so that the core sees inputs of unit scale:
+    norm_w ~ U(-0.5, 0.5) (the Gemma norm multiplies by 1 + w), the input
+    projections ~ N(0, 1/hidden), out_proj ~ N(0, 1/(h_v d_v))."""
+    hidden: int
+    norm_w: np.ndarray          # [hidden]
+    w_qkvz: np.ndarray          # [c_ch + h_v d_v, hidden]
+    w_ba: np.ndarray            # [2 h_v, hidden]
+    w_out: np.ndarray           # [hidden, h_v d_v]
+
+    def as_dict(self) -> dict:
+        return dict(norm_w=self.norm_w, w_qkvz=self.w_qkvz, w_ba=self.w_ba, w_out=self.w_out)
+
+
+def block_weights(seed: int, dims: Dims, hidden: int = HIDDEN, act: str = "bf16") -> BlockWeights:
+    vd = dims.h_v * dims.d_v
+    return BlockWeights(
+        hidden=hidden,
+        norm_w=uniform((seed, _HNW), (hidden,), -0.5, 0.5, act),
+        w_qkvz=normal((seed, _WQKVZ), (dims.c_ch + vd, hidden), 1.0 / math.sqrt(hidden), act),
+        w_ba=normal((seed, _WBA), (2 * dims.h_v, hidden), 1.0 / math.sqrt(hidden), act),
+        w_out=normal((seed, _WOUT), (hidden, vd), 1.0 / math.sqrt(vd), act),
+    )
+
+
+def block_input(seed: int, i: int, T: int, hidden: int = HIDDEN, act: str = "bf16") -> np.ndarray:
+    """Layer input of sequence (or request) i: [T, hidden] ~ N(0, 1)."""
+    return normal((seed, _HX, i), (T, hidden), 1.0, act)
+
+
 # ---------------------------------------------------------------- tiny case
 @dataclass
 class TinyCase:

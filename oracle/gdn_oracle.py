@@ -245,6 +245,62 @@ def layer_sequence(x, a, b, z, conv_w, conv_b, A_log, dt_bias, norm_w, conv_stat
     return res
 
 
+# ------------------------------------------------- the layer around the core
+# LightLLM #1097 ("Specialized Triton Kernels") lists a Gemma RMSNorm kernel
+# beside the GDN kernels, and the layer's input projections are named
+# in_proj_qkvz and in_proj_ba; the pages give neither formulas nor layouts.
+# Readings:
+#   * the layer input is normalised over the hidden size by the Gemma form of
+#     RMSNorm, whose weight enters as (1 + w): x / sqrt(mean(x^2) + eps) * (1 + w);
+#   * in_proj_qkvz maps it to the packed q | k | v conv input followed by z
+#     (h_v * d_v columns, V head major), in_proj_ba to b followed by a (h_v
+#     columns each), the order of the projections' names;
+#   * out_proj maps the gated-RMSNorm output, flattened over (V head, d_v), to
+#     the hidden size; with residual the layer input is added to it;
+#   * every weight has the [out_features, in_features] layout of a linear layer.
+
+def gemma_rmsnorm(x, w, eps=1e-6):
+    """Gemma-style RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * (1 + w)."""
+    x = _f64(x)
+    rms = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return (x / rms) * (1.0 + _f64(w))
+
+
+def linear(x, w):
+    """x @ w^T for a weight in [out_features, in_features] layout."""
+    return _f64(x) @ _f64(w).T
+
+
+def block_sequence(X, weights, conv_w, conv_b, A_log, dt_bias, norm_w, conv_state0, ssm_state0, dims,
+                   scale=1.0, norm_eps=1e-6, block_eps=1e-6, residual=True, keep_states=False, perturb=None):
+    """One sequence through the whole layer: Gemma RMSNorm -> in_proj_qkvz and
+    in_proj_ba -> the core (layer_sequence) -> out_proj (+ the input).
+
+    X [T, hidden]; weights: dict with norm_w [hidden], w_qkvz [c_ch + h_v d_v,
+    hidden], w_ba [2 h_v, hidden], w_out [hidden, h_v d_v].  perturb, when
+    given, is applied to every activation tensor the layer hands from one
+    kernel to the next (the normalised input, both projections, the conv
+    output inside the core and the core's output), as in layer_sequence.
+    """
+    h_k, h_v, d_k, d_v = dims
+    c_ch = 2 * h_k * d_k + h_v * d_v
+    X = _f64(X)
+    T = X.shape[0]
+    pert = perturb if perturb is not None else (lambda t: t)
+    xn = pert(gemma_rmsnorm(X, weights["norm_w"], block_eps))
+    p = pert(linear(xn, weights["w_qkvz"]))
+    q = pert(linear(xn, weights["w_ba"]))
+    x, z = p[:, :c_ch], p[:, c_ch:].reshape(T, h_v, d_v)
+    b, a = q[:, :h_v], q[:, h_v:]
+    r = layer_sequence(x, a, b, z, conv_w, conv_b, A_log, dt_bias, norm_w, conv_state0, ssm_state0, dims,
+                       scale, norm_eps, keep_states=keep_states, perturb=perturb)
+    o = pert(r["out"].reshape(T, h_v * d_v))
+    y = linear(o, weights["w_out"])
+    if residual:
+        y = y + X
+    return dict(r, xn=xn, x=x, z=z, a=a, b=b, core_out=o, block_out=y)
+
+
 def prefill_batch(x, a, b, z, cu_seqlens, slots, has_init, conv_pool, ssm_pool, params, dims,
                   scale=1.0, norm_eps=1e-6):
     """Packed varlen prefill over whole pools (small cases only).

@@ -271,6 +271,65 @@ def pin_layer_worked_example():
     return err
 
 
+def pin_gemma_rmsnorm_closed_form():
+    """A constant row c 1 normalises to c / sqrt(c^2 + eps) (1 + w); a one-hot
+    row s e_j to s / sqrt(s^2 / n + eps) (1 + w_j) at j and zero elsewhere; a
+    weight of -1 zeroes its column."""
+    n, eps = 6, 1e-6
+    w = np.array([0.25, -0.5, 0.0, 1.0, -1.0, 0.125])
+    err = 0.0
+    for c in (3.0, -0.5):
+        got = O.gemma_rmsnorm(np.full((1, n), c), w, eps)[0]
+        err = max(err, float(np.abs(got - c / math.sqrt(c * c + eps) * (1.0 + w)).max()))
+    s, j = 2.0, 3
+    x = np.zeros((2, n))
+    x[0, j] = s
+    x[1] = np.arange(1.0, n + 1.0)
+    exp0 = np.zeros(n)
+    exp0[j] = s / math.sqrt(s * s / n + eps) * (1.0 + w[j])
+    ms = sum(v * v for v in range(1, n + 1)) / n     # 91 / 6
+    exp1 = np.array([(v + 1) / math.sqrt(ms + eps) * (1.0 + w[v]) for v in range(n)])
+    got = O.gemma_rmsnorm(x, w, eps)
+    return max(err, float(np.abs(got[0] - exp0).max()), float(np.abs(got[1] - exp1).max()), abs(got[1, 4]))
+
+
+def pin_linear_brute_force():
+    """x @ w^T against explicit sums on small integers (exact in fp64), with a
+    non-square weight so that a transposed operand cannot pass."""
+    rng = np.random.default_rng(40)
+    x = rng.integers(-3, 4, (3, 5)).astype(np.float64)
+    w = rng.integers(-3, 4, (4, 5)).astype(np.float64)
+    ref = np.array([[sum(x[t, k] * w[n, k] for k in range(5)) for n in range(4)] for t in range(3)])
+    return float(np.abs(O.linear(x, w) - ref).max())
+
+
+def pin_block_identity_weights():
+    """With selecting projections the layer reduces to the core on its
+    normalised input.  hidden = c_ch + h_v d_v + 2 h_v; in_proj_qkvz takes the
+    first c_ch + h_v d_v columns of the normalised input (conv input, then z),
+    in_proj_ba the last 2 h_v (b, then a); out_proj writes the core output to
+    the first h_v d_v columns and zero elsewhere; the input is added."""
+    rng = np.random.default_rng(41)
+    h_k, h_v, d_k, d_v = dims = (1, 2, 4, 4)
+    c_ch, vd = 2 * h_k * d_k + h_v * d_v, h_v * d_v
+    H, T = c_ch + vd + 2 * h_v, 7
+    eye = np.eye(H)
+    wts = dict(norm_w=rng.uniform(-0.5, 0.5, H), w_qkvz=eye[: c_ch + vd], w_ba=eye[c_ch + vd:],
+               w_out=np.eye(H, vd))
+    X = rng.standard_normal((T, H))
+    conv_w, A_log, dt_bias = 0.5 * rng.standard_normal((c_ch, 4)), rng.uniform(0, 2.7, h_v), rng.uniform(-1, 1, h_v)
+    norm_w, conv0, ssm0 = rng.uniform(0.5, 1.5, d_v), rng.standard_normal((c_ch, 3)), 0.1 * rng.standard_normal(
+        (h_v, d_v, d_k))
+    got = O.block_sequence(X, wts, conv_w, None, A_log, dt_bias, norm_w, conv0, ssm0, dims, 1.0, 1e-6, 1e-6)
+    xn = O.gemma_rmsnorm(X, wts["norm_w"], 1e-6)
+    core = O.layer_sequence(xn[:, :c_ch], xn[:, c_ch + vd + h_v:], xn[:, c_ch + vd: c_ch + vd + h_v],
+                            xn[:, c_ch: c_ch + vd].reshape(T, h_v, d_v), conv_w, None, A_log, dt_bias, norm_w,
+                            conv0, ssm0, dims, 1.0, 1e-6)
+    exp = X.copy()
+    exp[:, :vd] += core["out"].reshape(T, vd)
+    return max(float(np.abs(got["block_out"] - exp).max()), float(np.abs(got["ssm"] - core["ssm"]).max()))
+
+
 PINS = {
     "exact_product_form": (pin_exact_product_form, 1e-12),
     "chunked_equals_recurrent": (pin_chunked_equals_recurrent, 1e-11),
@@ -282,6 +341,9 @@ PINS = {
     "rmsnorm_vs_torch": (pin_rmsnorm_vs_torch, 1e-13),
     "l2norm": (pin_l2norm, 1e-13),
     "layer_worked_example": (pin_layer_worked_example, 1e-12),
+    "gemma_rmsnorm_closed_form": (pin_gemma_rmsnorm_closed_form, 1e-13),
+    "linear_brute_force": (pin_linear_brute_force, 1e-300),   # exact: small integers
+    "block_identity_weights": (pin_block_identity_weights, 1e-12),
 }
 
 
@@ -511,6 +573,15 @@ MUTATIONS = {
     "qkv_split_k_before_q": ("split_qkv", _mutated("split_qkv", "q = y[:, : h_k * d_k]", "q = y[:, h_k * d_k: 2 * h_k * d_k]")),
     "mtp_snapshot_of_next_token": ("decode_batch", _mutated("decode_batch", 'r["ssm_states"][p]', 'r["ssm_states"][-1]')),
     "prefill_state_to_wrong_slot": ("prefill_batch", _mutated("prefill_batch", "ssm_pool[s] = r[\"ssm\"]", "ssm_pool[s - 1] = r[\"ssm\"]")),
+    "gemma_plain_weight": ("gemma_rmsnorm", _mutated("gemma_rmsnorm", "(1.0 + _f64(w))", "_f64(w)")),
+    "gemma_sum_not_mean": ("gemma_rmsnorm", _mutated("gemma_rmsnorm", "np.mean(x * x", "np.sum(x * x")),
+    "linear_transposed_weight": ("linear", lambda x, w: np.asarray(x, np.float64) @ np.asarray(w, np.float64)),
+    "block_a_b_swapped": ("block_sequence", _mutated("block_sequence", "b, a = q[:, :h_v], q[:, h_v:]",
+                                                     "a, b = q[:, :h_v], q[:, h_v:]")),
+    "block_z_before_x": ("block_sequence", _mutated(
+        "block_sequence", "x, z = p[:, :c_ch], p[:, c_ch:].reshape(T, h_v, d_v)",
+        "x, z = p[:, h_v * d_v:], p[:, :h_v * d_v].reshape(T, h_v, d_v)")),
+    "block_no_residual": ("block_sequence", _mutated("block_sequence", "y = y + X", "y = y")),
 }
 
 
