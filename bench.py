@@ -22,8 +22,10 @@ separate calls, pools rotated so states come from HBM) and its padded-bucket
 graph, the 128 x 4-token MTP step (gdn_decode, the two separate calls, the
 commit copy) and its bucket graph, the ~271k-token varlen prefill on the
 seeded inputs of the parity tests, the prefill at one tensor-parallel rank's
-head counts (tp = 2, 4), and the fp64 CPU oracle timed on the host's cores on
-a sample of every workload.
+head counts (tp = 2, 4), the whole layer around the core (Gemma RMSNorm and
+the projections at hidden 2048) for the 4096-token prefill and the 256-request
+decode, and the fp64 CPU oracle timed on the host's cores on a sample of every
+workload.
 """
 from __future__ import annotations
 
@@ -659,6 +661,155 @@ def bench_mtp_bucket(args, torch, gdn, gi):
             "graph_ms_per_step": round(ms, 4), "draft_tokens_per_s": round(live * case.t_step / (ms * 1e-3), 1)}
 
 
+def bench_layer(args, torch, gdn, gi):
+    """The whole layer around the core at hidden 2048 (a reading: the hidden
+    size the pages do not give): Gemma RMSNorm, in_proj_qkvz/ba (one MFMA
+    kernel), gdn_prefill, out_proj with the residual, over the 4096-token
+    single sequence (two rotating copies, as the prefill row), and the same
+    four calls around gdn_decode for 256 requests x 1 token.  Per-call times
+    from HIP events on the launch stream; the projections' MFMA fraction
+    against the dense bf16 peak, and torch's own GEMM (F.linear, hipBLASLt) on
+    the same shapes beside them for reference."""
+    import torch.nn.functional as F
+    hidden = gi.HIDDEN
+    case = gi.prefill_case()
+    d = case.dims
+    dims = gdn.Dims(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_w)
+    dev = torch.device("cuda")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev, torch.bfloat16)
+    T, vd = case.t_total, d.h_v * d.d_v
+    n_in = d.c_ch + vd + 2 * d.h_v
+    W = gi.block_weights(case.seed, d, hidden)
+    wts = gdn.BlockWeights(bf(W.norm_w), bf(W.w_qkvz), bf(W.w_ba), bf(W.w_out))
+    p = case.params
+    conv_w, norm_w = bf(p.conv_w), bf(p.norm_w)
+    A_log, dt_bias = torch.from_numpy(p.A_log).to(dev), torch.from_numpy(p.dt_bias).to(dev)
+    cu = torch.tensor(case.cu_seqlens, dtype=torch.int32, device=dev)
+    slots = torch.zeros(1, dtype=torch.int32, device=dev)
+    has_init = torch.zeros(1, dtype=torch.uint8, device=dev)
+    ws_bytes = gdn.prefill_workspace_size(dims, 0, 1, T, case.chunk)
+    X0 = gi.block_input(case.seed, 0, T, hidden)
+    mk = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    copies = [dict(X=bf(X0), xn=mk(T, hidden), qkv=mk(T, d.c_ch), z=mk(T, d.h_v, d.d_v), b=mk(T, d.h_v),
+                   a=mk(T, d.h_v), o=mk(T, d.h_v, d.d_v), y=mk(T, hidden),
+                   conv_pool=torch.zeros((1, d.c_ch, d.conv_w - 1), dtype=torch.bfloat16, device=dev),
+                   ssm_pool=torch.zeros((1, d.h_v, d.d_v, d.d_k), dtype=torch.float32, device=dev),
+                   ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)) for _ in range(2)]
+
+    def step(k, e=None):
+        c = copies[k % 2]
+        if e: e[0].record()
+        gdn.rmsnorm_gemma(c["X"], wts.norm_w, 1e-6, out=c["xn"])
+        if e: e[1].record()
+        gdn.in_proj(dims, c["xn"], wts.w_qkvz, wts.w_ba, c["qkv"], c["z"], c["b"], c["a"])
+        if e: e[2].record()
+        gdn.prefill(dims, c["qkv"], conv_w, c["a"], c["b"], A_log, dt_bias, cu, slots, c["conv_pool"],
+                    c["ssm_pool"], has_init, case.chunk, 1.0, c["z"], norm_w, 1e-6, o=c["o"], workspace=c["ws"])
+        if e: e[3].record()
+        gdn.out_proj(dims, c["o"].view(T, vd), wts.w_out, c["X"], c["y"])
+        if e: e[4].record()
+
+    steps = max(min(args.steps, 100), 20)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for k in range(4):
+        step(k)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    graphs = [capture_graph(torch, lambda k=k: step(k)) for k in range(2)]
+    for k in range(4):
+        graphs[k % 2].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        graphs[k % 2].replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / steps * 1e3
+    ms = lambda i, j: pct([e[i].elapsed_time(e[j]) for e in evs])
+    t_norm, t_in, t_pre, t_out = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
+
+    def lib_gemm(x, w):
+        """torch's GEMM (F.linear) on the same operands: mean ms of 20 calls."""
+        for _ in range(3):
+            F.linear(x, w)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            F.linear(x, w)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 20
+
+    c = copies[0]
+    w_in = torch.cat([wts.w_qkvz, wts.w_ba])
+    lib_in, lib_out = lib_gemm(c["xn"], w_in), lib_gemm(c["o"].view(T, vd), wts.w_out)
+    fl_in, fl_out = 2.0 * T * hidden * n_in, 2.0 * T * vd * hidden
+    tf = lambda fl, t: fl / (t * 1e-3) / 1e12
+    proj = lambda fl, t, lib: {"algorithmic_flops": fl, "launch_ms": t, "achieved_tflops": round(tf(fl, t["mean"]), 1),
+                               "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tf(fl, t["mean"]) / BF16_PEAK_TFLOPS, 4),
+                               "torch_f_linear_ms": round(lib, 4),
+                               "torch_f_linear_tflops": round(tf(fl, lib), 1)}
+    prefill_row = {
+        "workload": f"layer_prefill_single_{T}", "hidden": hidden, "calls": "gdn_rmsnorm_gemma, gdn_in_proj, "
+        "gdn_prefill, gdn_out_proj (+ residual)", "graph_ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "kernels_ms": {"gdn_rmsnorm_gemma": t_norm, "gdn_in_proj": t_in, "gdn_prefill": t_pre, "gdn_out_proj": t_out},
+        "in_proj": proj(fl_in, t_in, lib_in), "out_proj": proj(fl_out, t_out, lib_out),
+        "rmsnorm_gbs": round(2.0 * T * hidden * 2 / (t_norm["mean"] * 1e-3) / 1e9, 1)}
+    del copies, graphs
+    torch.cuda.empty_cache()
+
+    # decode: 256 requests x 1 token, states in place on a 512-slot pool
+    dc = gi.decode_case()
+    n = dc.n
+    slots_d = torch.from_numpy(dc.slots).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(dc.seed + 1)
+    ssm = torch.randn((dc.n_slots, d.h_v, d.d_v, d.d_k), device=dev, generator=gen) * 0.02
+    conv = torch.randn((dc.n_slots, d.c_ch, d.conv_w - 1), device=dev, generator=gen).to(torch.bfloat16)
+    Xd = bf(np.stack([gi.block_input(dc.seed, i, 1, hidden) for i in range(n)]).reshape(n, hidden))
+    xn, qkv, z, b, a = mk(n, hidden), mk(n, d.c_ch), mk(n, d.h_v, d.d_v), mk(n, d.h_v), mk(n, d.h_v)
+    o, y = mk(n, 1, d.h_v, d.d_v), mk(n, hidden)
+
+    def dstep(e=None):
+        if e: e[0].record()
+        gdn.rmsnorm_gemma(Xd, wts.norm_w, 1e-6, out=xn)
+        if e: e[1].record()
+        gdn.in_proj(dims, xn, wts.w_qkvz, wts.w_ba, qkv, z, b, a)
+        if e: e[2].record()
+        gdn.decode(dims, qkv.view(n, 1, d.c_ch), conv_w, a.view(n, 1, d.h_v), b.view(n, 1, d.h_v), A_log, dt_bias,
+                   slots_d, conv, ssm, None, 1.0, z.view(n, 1, d.h_v, d.d_v), norm_w, 1e-6, o=o)
+        if e: e[3].record()
+        gdn.out_proj(dims, o.view(n, vd), wts.w_out, Xd, y)
+        if e: e[4].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for _ in range(4):
+        dstep()
+    torch.cuda.synchronize()
+    for k in range(steps):
+        dstep(evs[k])
+    torch.cuda.synchronize()
+    g = capture_graph(torch, dstep)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_dec = (time.perf_counter() - t0) / steps * 1e3
+    t_norm, t_in, t_dec, t_out = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
+    w_bytes_in, w_bytes_out = 2.0 * n_in * hidden, 2.0 * hidden * vd
+    gbs = lambda nb, t: round(nb / (t["mean"] * 1e-3) / 1e9, 1)
+    decode_row = {
+        "workload": f"layer_decode_{n}x1", "hidden": hidden, "graph_ms_per_step": round(ms_dec, 4),
+        "tokens_per_s": round(n / (ms_dec * 1e-3), 1),
+        "kernels_ms": {"gdn_rmsnorm_gemma": t_norm, "gdn_in_proj": t_in, "gdn_decode": t_dec, "gdn_out_proj": t_out},
+        "in_proj_weight_gbs": gbs(w_bytes_in + 2.0 * n * (hidden + n_in), t_in),
+        "out_proj_weight_gbs": gbs(w_bytes_out + 2.0 * n * (vd + 2 * hidden), t_out),
+        "torch_f_linear_ms": {"in_proj": round(lib_gemm(xn, w_in), 4), "out_proj": round(lib_gemm(o.view(n, vd),
+                                                                                                   wts.w_out), 4)}}
+    return {"prefill": prefill_row, "decode": decode_row}
+
+
 def cpu_baseline(case2) -> dict:
     """The fp64 oracle, as it stands, on the host's cores: a pool of
     single-threaded worker processes (started before this process touched the
@@ -729,6 +880,7 @@ def main() -> int:
     ap.add_argument("--no-mtp", action="store_true")
     ap.add_argument("--no-tp", action="store_true", help="skip the per-rank (tp = 2, 4) prefill rows")
     ap.add_argument("--no-bucket", action="store_true", help="skip the padded decode and MTP bucket graph rows")
+    ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer rows (norm, projections, core)")
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
     ap.add_argument("--prefill-copies", type=int, default=2,
                     help="copies of the prefill buffers the steps rotate over (2: more than the memory-side cache)")
@@ -771,6 +923,8 @@ def main() -> int:
     mtp = run("mtp 128x4", args.no_mtp, bench_mtp, args, torch, gdn, gi)
     mtp_bucket = run("mtp bucket", args.no_mtp or args.no_bucket, bench_mtp_bucket, args, torch, gdn, gi)
     torch.cuda.empty_cache()
+    layer = run("layer", args.no_layer, bench_layer, args, torch, gdn, gi)
+    torch.cuda.empty_cache()
     var = run("varlen", args.no_varlen, bench_varlen, args, torch, gdn, gi)
     torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth_gbs(torch)
@@ -804,6 +958,7 @@ def main() -> int:
         "mtp_bucket": mtp_bucket,
         "varlen": var,
         "tp_shapes": tp,
+        "layer": layer,
         "device": {**info, "rocminfo": rinfo, "copy_gbs": round(copy_gbs, 1)},
     }
     print(json.dumps(line), flush=True)

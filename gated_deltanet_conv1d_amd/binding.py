@@ -44,6 +44,9 @@ SIGNATURES = {
     "gdn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
                                   _P, _P, _F, _P]),
     "gdn_state_copy": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
+    "gdn_rmsnorm_gemma": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _F, _P, _P]),
+    "gdn_in_proj": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "gdn_out_proj": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P]),
 }
 
 
@@ -82,6 +85,8 @@ def lib(path: Optional[str] = None) -> ctypes.CDLL:
             raise GdnError(f"{path} is not built: run gated_deltanet_conv1d_amd.build.build() first")
         handle = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
+            if path != LIB_PATH and not hasattr(handle, name):
+                continue        # an older variant build: only the calls it has
             fn = getattr(handle, name)
             fn.restype, fn.argtypes = res, args
         _lib = handle
@@ -300,6 +305,55 @@ def state_copy(dims: Dims, state, src, dst, conv_state=None):
                                 _ptr(dst, torch.int32, "dst"), src.shape[0], _stream()), "gdn_state_copy")
 
 
+def rmsnorm_gemma(x, w, eps: float = 1e-6, out=None):
+    """Gemma-form RMSNorm over the last axis (gdn_rmsnorm_gemma): x / rms(x) * (1 + w)."""
+    hidden = x.shape[-1]
+    _shape(w, (hidden,), "w")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().gdn_rmsnorm_gemma(_act(x), x.numel() // hidden if hidden else 0, hidden, _ptr(x, x.dtype, "x"),
+                                   _ptr(w, x.dtype, "w"), eps, _ptr(out, x.dtype, "out"), _stream()),
+           "gdn_rmsnorm_gemma")
+    return out
+
+
+def in_proj(dims: Dims, xn, w_qkvz, w_ba, qkv=None, z=None, b=None, a=None):
+    """The input projections (gdn_in_proj).  xn [T, hidden] bf16.  Returns
+    (qkv [T, c_ch], z [T, h_v, d_v], b [T, h_v], a [T, h_v])."""
+    T, hidden = xn.shape
+    vd = dims.h_v * dims.d_v
+    _shape(w_qkvz, (dims.c_ch + vd, hidden), "w_qkvz")
+    _shape(w_ba, (2 * dims.h_v, hidden), "w_ba")
+    mk = lambda *shape: torch.empty(shape, dtype=xn.dtype, device=xn.device)
+    qkv = mk(T, dims.c_ch) if qkv is None else qkv
+    z = mk(T, dims.h_v, dims.d_v) if z is None else z
+    b = mk(T, dims.h_v) if b is None else b
+    a = mk(T, dims.h_v) if a is None else a
+    _check(lib().gdn_in_proj(ctypes.byref(_cdims(dims)), _act(xn), T, hidden, _ptr(xn, xn.dtype, "xn"),
+                             _ptr(w_qkvz, xn.dtype, "w_qkvz"), _ptr(w_ba, xn.dtype, "w_ba"),
+                             _ptr(qkv, xn.dtype, "qkv"), _ptr(z, xn.dtype, "z"), _ptr(b, xn.dtype, "b"),
+                             _ptr(a, xn.dtype, "a"), _stream()), "gdn_in_proj")
+    return qkv, z, b, a
+
+
+def out_proj(dims: Dims, o, w_out, residual=None, y=None):
+    """y = o w_out^T (+ residual) (gdn_out_proj).  o [T, h_v * d_v] (or
+    [T, h_v, d_v]) bf16; returns y [T, hidden]."""
+    T = o.shape[0]
+    hidden = w_out.shape[0]
+    _shape(w_out, (hidden, dims.h_v * dims.d_v), "w_out")
+    if o.numel() != T * dims.h_v * dims.d_v:
+        raise GdnError(f"o: expected {T} x {dims.h_v * dims.d_v} values, got shape {tuple(o.shape)}")
+    if residual is not None:
+        _shape(residual, (T, hidden), "residual")
+    if y is None:
+        y = torch.empty((T, hidden), dtype=o.dtype, device=o.device)
+    _check(lib().gdn_out_proj(ctypes.byref(_cdims(dims)), _act(o), T, hidden, _ptr(o, o.dtype, "o"),
+                              _ptr(w_out, o.dtype, "w_out"), _ptr(residual, o.dtype, "residual"),
+                              _ptr(y, o.dtype, "y"), _stream()), "gdn_out_proj")
+    return y
+
+
 # ------------------------------------------------------- layer sequences
 def prefill_layer(dims: Dims, x, conv_w, A_log, dt_bias, a, b, cu_seqlens, slots, conv_state, state, has_init=None,
                   chunk: int = 64, scale: float = 1.0, z=None, norm_w=None, norm_eps: float = 1e-6, conv_b=None):
@@ -319,3 +373,46 @@ def decode_layer(dims: Dims, x, conv_w, A_log, dt_bias, a, b, slots, conv_state,
     y = conv1d_update(dims, x, conv_w, conv_state, slots, out_slots, conv_b)
     out = recurrent_decode(dims, y, a, b, A_log, dt_bias, state, slots, out_slots, scale, z, norm_w, norm_eps)
     return out, y
+
+
+class BlockWeights(NamedTuple):
+    """Weights of the layer around the core (device tensors, bf16)."""
+    norm_w: torch.Tensor   # [hidden] Gemma RMSNorm weight (the norm multiplies by 1 + w)
+    w_qkvz: torch.Tensor   # [c_ch + h_v d_v, hidden]
+    w_ba: torch.Tensor     # [2 h_v, hidden]
+    w_out: torch.Tensor    # [hidden, h_v d_v]
+
+
+def block_prefill(dims: Dims, X, wts: BlockWeights, conv_w, A_log, dt_bias, cu_seqlens, slots, conv_state, state,
+                  has_init=None, chunk: int = 64, scale: float = 1.0, norm_w=None, norm_eps: float = 1e-6,
+                  block_eps: float = 1e-6, residual: bool = True, conv_b=None, workspace=None,
+                  intermediates: bool = False):
+    """The whole layer over a packed varlen batch X [T, hidden]: Gemma RMSNorm,
+    the input projections, the single-call prefill and out_proj (+ X).  Four
+    ABI calls; returns y [T, hidden], and with intermediates also a dict of
+    the activations handed between them (xn, qkv, z, b, a, o)."""
+    xn = rmsnorm_gemma(X, wts.norm_w, block_eps)
+    qkv, z, b, a = in_proj(dims, xn, wts.w_qkvz, wts.w_ba)
+    o = prefill(dims, qkv, conv_w, a, b, A_log, dt_bias, cu_seqlens, slots, conv_state, state, has_init, chunk,
+                scale, z, norm_w, norm_eps, conv_b=conv_b, workspace=workspace)
+    y = out_proj(dims, o, wts.w_out, X if residual else None)
+    return (y, dict(xn=xn, qkv=qkv, z=z, b=b, a=a, o=o)) if intermediates else y
+
+
+def block_decode(dims: Dims, X, wts: BlockWeights, conv_w, A_log, dt_bias, slots, conv_state, state,
+                 out_slots=None, scale: float = 1.0, norm_w=None, norm_eps: float = 1e-6, block_eps: float = 1e-6,
+                 residual: bool = True, conv_b=None, intermediates: bool = False):
+    """The whole layer for a decode / MTP step, X [n_seq, t_step, hidden]
+    request-major: Gemma RMSNorm, the input projections, the single-call
+    decode and out_proj (+ X).  Returns y [n_seq, t_step, hidden] (and the
+    intermediates, as block_prefill)."""
+    n_seq, t_step, hidden = X.shape
+    X2 = X.reshape(n_seq * t_step, hidden)
+    xn = rmsnorm_gemma(X2, wts.norm_w, block_eps)
+    qkv, z, b, a = in_proj(dims, xn, wts.w_qkvz, wts.w_ba)
+    o = decode(dims, qkv.view(n_seq, t_step, dims.c_ch), conv_w, a.view(n_seq, t_step, dims.h_v),
+               b.view(n_seq, t_step, dims.h_v), A_log, dt_bias, slots, conv_state, state, out_slots, scale,
+               z.view(n_seq, t_step, dims.h_v, dims.d_v), norm_w, norm_eps, conv_b)
+    y = out_proj(dims, o.view(n_seq * t_step, dims.h_v * dims.d_v), wts.w_out,
+                 X2 if residual else None).view(n_seq, t_step, hidden)
+    return (y, dict(xn=xn, qkv=qkv, z=z, b=b, a=a, o=o)) if intermediates else y

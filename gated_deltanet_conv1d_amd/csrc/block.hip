@@ -1,0 +1,411 @@
+// The layer around the GDN core: the Gemma-form RMSNorm of the layer input
+// and the three linear projections (in_proj_qkvz, in_proj_ba, out_proj).
+//
+// LightLLM #1097 "[model] Support Qwen3next" lists a Gemma RMSNorm kernel next
+// to the GDN kernels ("Specialized Triton Kernels"); the projections are the
+// layer's in_proj_qkvz / in_proj_ba and out_proj.  The Gemma form multiplies
+// by (1 + w):  out = x / sqrt(mean(x^2) + eps) * (1 + w)  per row.
+//
+// Projections.  Y[m, n] = sum_k X[m, k] W[n, k] with bf16 operands, fp32
+// accumulation and one RNE rounding of the result: a dense contraction, so it
+// runs on MFMA (v_mfma_f32_16x16x32_bf16).  Both operands are read along k
+// (X rows, weight rows in [out_features, in_features] layout), 64 k per stage
+// through LDS.  The MFMA's first operand is the weight tile, so each lane's
+// four accumulator values are four consecutive output columns of one row
+// (one 8-byte store).  A workgroup of 4 waves owns a BM x BN output tile; each
+// wave a (BM/WGM) x (BN/WGN) sub-tile held as 16x16 accumulators.  The next
+// stage's global loads are issued into registers before the current stage's
+// MFMAs, so HBM latency hides behind the contraction.
+//
+// LDS rows are 64 bf16 = 128 bytes = 8 chunks of 16 bytes; chunk c of row r
+// sits at position c ^ (r & 7), so the 16 rows a fragment read touches (same
+// logical chunk) fall in 8 distinct chunk positions: no bank conflicts for
+// either the 16-byte stores or the 16-byte fragment reads.
+//
+// Workgroup b runs on XCD b % 8; tiles are numbered so that each XCD takes a
+// contiguous range, and within that range GM m-tiles share each weight tile
+// while it is hot in that XCD's L2.
+//
+// Output columns may be split over up to four destinations (in_proj writes the
+// packed conv input, z, b and a to separate arrays); out_proj may add a
+// residual.
+#include <hip/hip_runtime.h>
+
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace {
+
+// ----------------------------------------------------------- Gemma RMSNorm
+// One wave per row; two passes over the row (the second hits cache).
+template <typename T>
+__global__ __launch_bounds__(256) void gemma_norm_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                          float eps, T* __restrict__ out, int64_t rows,
+                                                          int hidden) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const T* xr = x + row * hidden;
+  T* orow = out + row * hidden;
+  const int nch = hidden >> 3;
+  float ss = 0.0f;
+  for (int c = lane; c < nch; c += 64) {
+    float v[8];
+    load8(xr + c * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)hidden + eps);
+  for (int c = lane; c < nch; c += 64) {
+    float v[8], g[8];
+    load8(xr + c * 8, v);
+    load8(w + c * 8, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * r * (1.0f + g[e]);
+    store8(orow + c * 8, v);
+  }
+}
+
+// ------------------------------------------------------------- projections
+constexpr int kBK = 64;  // k per LDS stage (one 128-byte row per tile row)
+
+struct ProjDev {
+  const bf16* x;
+  int64_t ldx, m;
+  const bf16* w0;  // weight rows [0, n_w0)
+  const bf16* w1;  // weight rows [n_w0, n)
+  int n_w0, n, k;
+  int nseg;
+  int64_t seg_begin[4];
+  bf16* seg_ptr[4];
+  int64_t seg_ld[4];
+  const bf16* res;
+  int64_t ld_res;
+  int tiles_m, tiles_n, per_xcd, group_m;
+};
+
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4): lane l
+// writes bytes [16 l, 16 l + 16) after the wave-uniform LDS address.  Kept out
+// of the kernel templates: a target builtin in a template body leaves the
+// host-side launch stub of its instantiations undefined.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ int swz(int row, int c) { return row * kBK + ((c ^ (row & 7)) << 3); }
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ int seg_of(const ProjDev& p, int64_t n) {
+  int s = 0;
+#pragma unroll
+  for (int q = 1; q < 4; ++q)
+    if (q < p.nseg && n >= p.seg_begin[q]) s = q;
+  return s;
+}
+
+// Writes a wave's accumulators: lane (rl, g) of 16x16 tile (j, i) holds output
+// columns n .. n+3 (n = nb + 16 j + 4 g) of row m = mb + 16 i + rl.  VEC: every
+// segment starts at a multiple of 4 columns with a row stride that is one too,
+// and n is one: four columns always share a segment (one 8-byte store).
+// Otherwise one column at a time.
+template <bool VEC, bool RES, int FN, int FM>
+__device__ __forceinline__ void store_tile(const ProjDev& p, int64_t mb, int nb, int rl, int g,
+                                           const f32x4 (&acc)[FN][FM]) {
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = nb + j * 16 + 4 * g;
+    if (n >= p.n) continue;
+    if constexpr (VEC) {
+      const int s = seg_of(p, n);
+      bf16* base = p.seg_ptr[s] + (n - p.seg_begin[s]);
+      const int64_t ld = p.seg_ld[s];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = mb + i * 16 + rl;
+        if (m >= p.m) continue;
+        float o0 = acc[j][i][0], o1 = acc[j][i][1], o2 = acc[j][i][2], o3 = acc[j][i][3];
+        if constexpr (RES) {
+          const uint2 r = *reinterpret_cast<const uint2*>(p.res + m * p.ld_res + n);
+          o0 += bf_lo(r.x);
+          o1 += bf_hi(r.x);
+          o2 += bf_lo(r.y);
+          o3 += bf_hi(r.y);
+        }
+        const bf16x4 b = {(bf16)o0, (bf16)o1, (bf16)o2, (bf16)o3};
+        *reinterpret_cast<bf16x4*>(base + m * ld) = b;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = mb + i * 16 + rl;
+        if (m >= p.m) continue;
+        for (int e = 0; e < 4; ++e) {
+          const int ne = n + e;
+          if (ne >= p.n) break;
+          const int se = seg_of(p, ne);
+          float o = acc[j][i][e];
+          if constexpr (RES) o += (float)p.res[m * p.ld_res + ne];
+          p.seg_ptr[se][m * p.seg_ld[se] + (ne - p.seg_begin[se])] = (bf16)o;
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int OCC, bool VEC, bool RES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void proj_kernel(ProjDev p) {
+  static_assert(WGM * WGN == 4, "four waves");
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+  constexpr int LX = BM / 32, LW = BN / 32;  // 16-byte chunks per thread per stage
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 32 == 0 && BN % 32 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) bf16 sx[BM * kBK];
+  __shared__ __attribute__((aligned(16))) bf16 sw[BN * kBK];
+
+  // tile order: XCD-contiguous ranges, then groups of group_m m-tiles per n-tile
+  const int b = blockIdx.x;
+  const int64_t lt = (int64_t)(b & 7) * p.per_xcd + (b >> 3);
+  if (lt >= (int64_t)p.tiles_m * p.tiles_n) return;
+  const int64_t span = (int64_t)p.group_m * p.tiles_n;
+  const int grp = (int)(lt / span);
+  const int gm = min(p.group_m, p.tiles_m - grp * p.group_m);
+  const int within = (int)(lt - grp * span);
+  const int mt = grp * p.group_m + within % gm;
+  const int nt = within / gm;
+  const int64_t m0 = (int64_t)mt * BM;
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ch = tid & 7, r0 = tid >> 3;
+  const bf16* xs[LX];
+  const bf16* ws[LW];
+#pragma unroll
+  for (int i = 0; i < LX; ++i) {
+    const int64_t row = m0 + r0 + 32 * i;
+    xs[i] = row < p.m ? p.x + row * p.ldx + ch * 8 : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const int n = n0 + r0 + 32 * i;
+    ws[i] = n < p.n_w0 ? p.w0 + (int64_t)n * p.k + ch * 8
+                       : (n < p.n ? p.w1 + (int64_t)(n - p.n_w0) * p.k + ch * 8 : nullptr);
+  }
+  uint4 rx[LX], rw[LW];
+  auto gload = [&](int k0) {
+    const bool kin = k0 + ch * 8 < p.k;
+#pragma unroll
+    for (int i = 0; i < LX; ++i)
+      rx[i] = (xs[i] && kin) ? *reinterpret_cast<const uint4*>(xs[i] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < LW; ++i)
+      rw[i] = (ws[i] && kin) ? *reinterpret_cast<const uint4*>(ws[i] + k0) : make_uint4(0, 0, 0, 0);
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < LX; ++i) *reinterpret_cast<uint4*>(&sx[swz(r0 + 32 * i, ch)]) = rx[i];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) *reinterpret_cast<uint4*>(&sw[swz(r0 + 32 * i, ch)]) = rw[i];
+  };
+
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int rl = lane & 15, g = lane >> 4;
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int kt_n = (p.k + kBK - 1) / kBK;
+  gload(0);
+  sstore();
+  __syncthreads();
+  for (int kt = 0; kt < kt_n; ++kt) {
+    if (kt + 1 < kt_n) gload((kt + 1) * kBK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + g;
+      bf16x8 fw[FN], fx[FM];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fw[j] = *reinterpret_cast<const bf16x8*>(&sw[swz(wn * WN + j * 16 + rl, c)]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fx[i] = *reinterpret_cast<const bf16x8*>(&sx[swz(wm * WM + i * 16 + rl, c)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx[i], acc[j][i], 0, 0, 0);
+    }
+    __syncthreads();
+    if (kt + 1 < kt_n) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  store_tile<VEC, RES, FN, FM>(p, m0 + wm * WM, n0 + wn * WN, rl, g, acc);
+}
+
+// The same contraction for k a multiple of 64, with the stages moved from HBM
+// straight into LDS (global_load_lds_dwordx4: no staging registers, no LDS
+// store instructions) and two LDS buffers, so the next stage streams in while
+// the MFMAs consume the current one; one barrier per stage.  A wave's load
+// instruction fills one contiguous kilobyte of LDS (lane l: bytes 16 l), i.e.
+// 8 tile rows; lane l takes logical chunk (l % 8) ^ (l / 8) of row l / 8, which
+// realises the swizzled layout above.  Rows past m or n read the last valid
+// row instead (in bounds; their outputs are never stored).  Weight rows from
+// n_w0 on come from the second weight matrix, as in the kernel above.
+template <int BM, int BN, int WGM, int WGN, bool RES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_lds_kernel(ProjDev p) {
+  constexpr bool VEC = true;
+  static_assert(WGM * WGN == 4, "four waves");
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+  constexpr int IX = BM / 32, IW = BN / 32;  // load instructions per wave per stage
+  __shared__ __attribute__((aligned(16))) bf16 sx[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) bf16 sw[2][BN * kBK];
+
+  const int b = blockIdx.x;
+  const int64_t lt = (int64_t)(b & 7) * p.per_xcd + (b >> 3);
+  if (lt >= (int64_t)p.tiles_m * p.tiles_n) return;
+  const int64_t span = (int64_t)p.group_m * p.tiles_n;
+  const int grp = (int)(lt / span);
+  const int gm = min(p.group_m, p.tiles_m - grp * p.group_m);
+  const int within = (int)(lt - grp * span);
+  const int mt = grp * p.group_m + within % gm;
+  const int nt = within / gm;
+  const int64_t m0 = (int64_t)mt * BM;
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane >> 3, lch = (lane & 7) ^ (lane >> 3);
+  auto issue = [&](int k0, int buf) {
+#pragma unroll
+    for (int i = 0; i < IX; ++i) {
+      const int blk = i * 4 + wave;
+      const int64_t row = min(m0 + blk * 8 + lrow, p.m - 1);
+      lds_dma16(p.x + row * p.ldx + k0 + lch * 8, &sx[buf][blk * 8 * kBK]);
+    }
+#pragma unroll
+    for (int i = 0; i < IW; ++i) {
+      const int blk = i * 4 + wave;
+      const int n = min(n0 + blk * 8 + lrow, p.n - 1);
+      const bf16* wrow = n < p.n_w0 ? p.w0 + (int64_t)n * p.k : p.w1 + (int64_t)(n - p.n_w0) * p.k;
+      lds_dma16(wrow + k0 + lch * 8, &sw[buf][blk * 8 * kBK]);
+    }
+  };
+
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int rl = lane & 15, g = lane >> 4;
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int kt_n = p.k / kBK;
+  issue(0, 0);
+  for (int kt = 0; kt < kt_n; ++kt) {
+    const int buf = kt & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of stage kt have landed (vmcnt 0)
+    __syncthreads();                      // ... everyone's, and everyone is done with stage kt - 1
+    if (kt + 1 < kt_n) issue((kt + 1) * kBK, buf ^ 1);
+    const bf16* cx = sx[buf];
+    const bf16* cw = sw[buf];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + g;
+      bf16x8 fx[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fx[i] = *reinterpret_cast<const bf16x8*>(&cx[swz(wm * WM + i * 16 + rl, c)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const bf16x8 fw = *reinterpret_cast<const bf16x8*>(&cw[swz(wn * WN + j * 16 + rl, c)]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fx[i], acc[j][i], 0, 0, 0);
+      }
+    }
+  }
+
+  store_tile<VEC, RES, FN, FM>(p, m0 + wm * WM, n0 + wn * WN, rl, g, acc);
+}
+
+template <int BM, int BN, int WGM, int WGN, bool RES>
+hipError_t run_proj_lds(ProjDev p, hipStream_t st) {
+  p.tiles_m = (int)((p.m + BM - 1) / BM);
+  p.tiles_n = (p.n + BN - 1) / BN;
+  p.group_m = 4;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  p.per_xcd = (int)((tiles + 7) / 8);
+  hipLaunchKernelGGL((proj_lds_kernel<BM, BN, WGM, WGN, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)), dim3(256), 0, st,
+                     p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int OCC, bool VEC, bool RES>
+hipError_t run_proj(ProjDev p, hipStream_t st) {
+  p.tiles_m = (int)((p.m + BM - 1) / BM);
+  p.tiles_n = (p.n + BN - 1) / BN;
+  p.group_m = 4;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  p.per_xcd = (int)((tiles + 7) / 8);
+  hipLaunchKernelGGL((proj_kernel<BM, BN, WGM, WGN, OCC, VEC, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)), dim3(256), 0,
+                     st, p);
+  return hipGetLastError();
+}
+
+int64_t tile_count(int64_t m, int n, int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); }
+
+}  // namespace
+
+hipError_t launch_gemma_norm(const GemmaNormArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  if (a.bf16)
+    hipLaunchKernelGGL(gemma_norm_kernel<bf16>, grid, block, 0, st, (const bf16*)a.x, (const bf16*)a.w, a.eps,
+                       (bf16*)a.out, a.rows, a.hidden);
+  else
+    hipLaunchKernelGGL(gemma_norm_kernel<float>, grid, block, 0, st, (const float*)a.x, (const float*)a.w, a.eps,
+                       (float*)a.out, a.rows, a.hidden);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
+  ProjDev p{};
+  p.x = (const bf16*)a.x;
+  p.ldx = a.ldx;
+  p.m = a.m;
+  p.w0 = (const bf16*)a.w0;
+  p.w1 = (const bf16*)a.w1;
+  p.n_w0 = a.n_w0;
+  p.n = a.n;
+  p.k = a.k;
+  p.nseg = a.nseg;
+  for (int s = 0; s < 4; ++s) {
+    p.seg_begin[s] = s < a.nseg ? a.seg[s].begin : a.n;
+    p.seg_ptr[s] = s < a.nseg ? (bf16*)a.seg[s].ptr : nullptr;
+    p.seg_ld[s] = s < a.nseg ? a.seg[s].ld : 0;
+  }
+  p.res = (const bf16*)a.residual;
+  p.ld_res = a.ld_res;
+  // four output columns per lane store at once when every segment allows it
+  bool vec = a.n % 4 == 0 && (a.residual == nullptr || (a.ld_res % 4 == 0 && ((uintptr_t)a.residual & 7) == 0));
+  for (int s = 0; s < a.nseg; ++s)
+    vec = vec && a.seg[s].begin % 4 == 0 && a.seg[s].ld % 4 == 0 && ((uintptr_t)a.seg[s].ptr & 7) == 0;
+  // one weight matrix and whole 64-deep stages: the direct-to-LDS kernel
+  // (in_proj_qkvz: no residual, 256 x 256 tiles; out_proj: residual, 256 x 128)
+  const bool lds = vec && a.k % kBK == 0;
+  const bool res = a.residual != nullptr;
+  if (lds && !res && a.m >= 1024 && tile_count(a.m, a.n, 256, 256) >= 512)
+    return run_proj_lds<256, 256, 2, 2, false>(p, st);
+  if (lds && a.m >= 1024)
+    return res ? run_proj_lds<256, 128, 2, 2, true>(p, st) : run_proj_lds<256, 128, 2, 2, false>(p, st);
+  if (tile_count(a.m, a.n, 128, 128) >= 256) {
+    if (vec) return res ? run_proj<128, 128, 2, 2, 2, true, true>(p, st) : run_proj<128, 128, 2, 2, 2, true, false>(p, st);
+    return res ? run_proj<128, 128, 2, 2, 2, false, true>(p, st) : run_proj<128, 128, 2, 2, 2, false, false>(p, st);
+  }
+  if (vec) return res ? run_proj<64, 128, 1, 4, 2, true, true>(p, st) : run_proj<64, 128, 1, 4, 2, true, false>(p, st);
+  return res ? run_proj<64, 128, 1, 4, 2, false, true>(p, st) : run_proj<64, 128, 1, 4, 2, false, false>(p, st);
+}
+
+}  // namespace gdn

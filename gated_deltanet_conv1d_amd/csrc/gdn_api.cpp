@@ -225,6 +225,71 @@ int gdn_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step,
   return from_hip(gdn::launch_decode(args, (hipStream_t)stream));
 }
 
+int gdn_rmsnorm_gemma(int32_t act, int64_t rows, int32_t hidden, const void* x, const void* w, float eps, void* out,
+                      void* stream) {
+  GDN_TRY(check_act(act));
+  if (rows < 0 || hidden <= 0 || hidden % 8 != 0 || !(eps >= 0.0f)) return GDN_ERR_SHAPE;
+  if (rows == 0) return GDN_OK;
+  GDN_TRY(need(x, w, out));
+  GDN_TRY(align_ok(x, w, out));
+  gdn::GemmaNormArgs a{act == GDN_BF16, rows, hidden, x, w, eps, out};
+  return from_hip(gdn::launch_gemma_norm(a, (hipStream_t)stream));
+}
+
+int gdn_in_proj(const gdn_dims* dims, int32_t act, int64_t t_total, int32_t hidden, const void* xn,
+                const void* w_qkvz, const void* w_ba, void* qkv, void* z, void* b, void* a, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (act != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (t_total < 0 || hidden <= 0 || hidden % 8 != 0) return GDN_ERR_SHAPE;
+  if (t_total == 0) return GDN_OK;
+  GDN_TRY(need(xn, w_qkvz, w_ba, qkv, z, b, a));
+  GDN_TRY(align_ok(xn, w_qkvz, w_ba, qkv, z, b, a));
+  const int c_ch = s.c_ch(), vd = s.h_v * s.d;
+  gdn::ProjArgs p{};
+  p.m = t_total;
+  p.n = c_ch + vd + 2 * s.h_v;
+  p.k = hidden;
+  p.x = xn;
+  p.ldx = hidden;
+  p.w0 = w_qkvz;
+  p.n_w0 = c_ch + vd;
+  p.w1 = w_ba;
+  p.nseg = 4;
+  p.seg[0] = {0, qkv, c_ch};
+  p.seg[1] = {c_ch, z, vd};
+  p.seg[2] = {c_ch + vd, b, s.h_v};
+  p.seg[3] = {c_ch + vd + s.h_v, a, s.h_v};
+  return from_hip(gdn::launch_proj(p, (hipStream_t)stream));
+}
+
+int gdn_out_proj(const gdn_dims* dims, int32_t act, int64_t t_total, int32_t hidden, const void* o,
+                 const void* w_out, const void* residual, void* y, void* stream) {
+  Shape s;
+  GDN_TRY(check_dims(dims, &s));
+  GDN_TRY(check_act(act));
+  if (act != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (t_total < 0 || hidden <= 0 || hidden % 8 != 0) return GDN_ERR_SHAPE;
+  if (t_total == 0) return GDN_OK;
+  GDN_TRY(need(o, w_out, y));
+  GDN_TRY(align_ok(o, w_out, residual, y));
+  gdn::ProjArgs p{};
+  p.m = t_total;
+  p.n = hidden;
+  p.k = s.h_v * s.d;
+  p.x = o;
+  p.ldx = p.k;
+  p.w0 = w_out;
+  p.n_w0 = hidden;
+  p.w1 = nullptr;
+  p.nseg = 1;
+  p.seg[0] = {0, y, hidden};
+  p.residual = residual;
+  p.ld_res = hidden;
+  return from_hip(gdn::launch_proj(p, (hipStream_t)stream));
+}
+
 int gdn_state_copy(const gdn_dims* dims, int32_t act, float* state, void* conv_state, int32_t n_slots,
                    const int32_t* src, const int32_t* dst, int32_t n, void* stream) {
   Shape s;

@@ -164,4 +164,40 @@ hipError_t launch_chunk_split(const ChunkArgs& a, hipStream_t st);
 // windows included.
 hipError_t launch_prefill_fused(const ChunkArgs& a, hipStream_t st);
 
+// Gemma-form RMSNorm of the layer input (block.hip).
+struct GemmaNormArgs {
+  bool bf16;
+  int64_t rows;
+  int hidden;  // multiple of 8
+  const void* x;
+  const void* w;
+  float eps;
+  void* out;
+};
+hipError_t launch_gemma_norm(const GemmaNormArgs& a, hipStream_t st);
+
+// Y[m, n] = sum_k X[m, k] W[n, k] (+ residual), bf16 in and out, fp32
+// accumulation (block.hip).  Weight rows [0, n_w0) come from w0, [n_w0, n)
+// from w1.  Output column n goes to the segment s with seg[s].begin <= n <
+// seg[s+1].begin, at seg[s].ptr[m * seg[s].ld + n - seg[s].begin].
+struct ProjSeg {
+  int64_t begin;
+  void* ptr;
+  int64_t ld;
+};
+struct ProjArgs {
+  int64_t m;
+  int n, k;  // k a multiple of 8
+  const void* x;
+  int64_t ldx;
+  const void* w0;
+  int n_w0;
+  const void* w1;
+  int nseg;  // 1..4
+  ProjSeg seg[4];
+  const void* residual;  // [m][ld_res] bf16 or NULL; only with one segment
+  int64_t ld_res;
+};
+hipError_t launch_proj(const ProjArgs& a, hipStream_t st);
+
 }  // namespace gdn

@@ -239,6 +239,50 @@ int gdn_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step,
                const int32_t* out_slots, void* o, const void* z, const void* norm_w, float norm_eps, void* stream);
 
 /*
+ * The layer around the core.  LightLLM #1097 "[model] Support Qwen3next" lists
+ * a Gemma RMSNorm kernel next to the GDN kernels ("Specialized Triton
+ * Kernels"); the layer's projections are in_proj_qkvz, in_proj_ba and
+ * out_proj.  The layouts are readings: weights in [out_features][in_features]
+ * order; in_proj_qkvz's outputs are the packed q|k|v conv input followed by z,
+ * in_proj_ba's are b followed by a.  These three calls take bf16 only
+ * (GDN_ERR_UNSUPPORTED for GDN_F32 in the projections); hidden is a positive
+ * multiple of 8.
+ *
+ * gdn_rmsnorm_gemma -- the Gemma form of RMSNorm over the hidden size:
+ *   out[t, :] = x[t, :] / sqrt(mean_j x[t, j]^2 + eps) * (1 + w)
+ *   x, out  act [rows][hidden]   (out may not alias x)
+ *   w       act [hidden]
+ */
+int gdn_rmsnorm_gemma(int32_t act, int64_t rows, int32_t hidden, const void* x, const void* w, float eps, void* out,
+                      void* stream);
+
+/*
+ * gdn_in_proj -- the input projections of the normalised layer input xn, on
+ * MFMA (bf16 operands, fp32 accumulation, each output rounded once):
+ *   P = xn w_qkvz^T:  qkv = P[:, :c_ch]  (the conv input of gdn_prefill /
+ *                     gdn_decode),  z = P[:, c_ch:]
+ *   R = xn w_ba^T:    b = R[:, :h_v],  a = R[:, h_v:]
+ *   xn     bf16 [t_total][hidden]
+ *   w_qkvz bf16 [c_ch + h_v*d_v][hidden]
+ *   w_ba   bf16 [2*h_v][hidden]
+ *   qkv    bf16 [t_total][c_ch];  z bf16 [t_total][h_v][d_v];  b, a bf16 [t_total][h_v]
+ * One kernel.  No output may alias an input.
+ */
+int gdn_in_proj(const gdn_dims* dims, int32_t act, int64_t t_total, int32_t hidden, const void* xn,
+                const void* w_qkvz, const void* w_ba, void* qkv, void* z, void* b, void* a, void* stream);
+
+/*
+ * gdn_out_proj -- y = o w_out^T (+ residual), bf16 operands, fp32 accumulation,
+ * the residual added before the one rounding:
+ *   o        bf16 [t_total][h_v*d_v]   (the gated-RMSNorm output of the core)
+ *   w_out    bf16 [hidden][h_v*d_v]
+ *   residual bf16 [t_total][hidden] or NULL
+ *   y        bf16 [t_total][hidden]    (may equal residual; may not alias o)
+ */
+int gdn_out_proj(const gdn_dims* dims, int32_t act, int64_t t_total, int32_t hidden, const void* o,
+                 const void* w_out, const void* residual, void* y, void* stream);
+
+/*
  * gdn_state_copy -- bitwise pool[dst[i]] <- pool[src[i]] for i < n, for the
  * recurrent state pool and (when conv_state is non-NULL) the conv state pool.
  * This is the MTP commit copy of LightLLM PR #1184 (copy buffers from source

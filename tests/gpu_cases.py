@@ -15,7 +15,15 @@ realisations, rounded, and rounded after a seeded half-ulp nudge:
   (ii)  rows with sens <= tol * mag / 10: err <= tol * mag        (plain)
   (iii) the rows over plain tol number at most the ill-conditioned rows
         (sens > tol * mag / 2), and those are at most ILL_MAX = 10% of the
-        rows of a workload (checked from 200 rows up).
+        rows of a workload (checked from 200 rows up).  The whole layer's
+        output rows are tokens over the hidden size; each mixes every V head,
+        so one ill-conditioned head makes its token row ill-conditioned.
+        There the fraction is checked on the core output's (token, V head)
+        rows, which the same test compares, and not on the token rows.  In
+        the whole layer the core's inputs, the gate inputs a and b among them,
+        are themselves rounded projections, so more rows are ill-conditioned:
+        the oracle alone finds 11.6-15.1% of the core rows of the layer
+        workloads so, and the cap there is ILL_MAX_LAYER = 20%.
 
 sens is the oracle's own measure of the row's conditioning: how far an
 activation-precision rounding of its input moves the exact answer (two
@@ -47,6 +55,7 @@ SENS = 2.0          # bound widening, in units of the oracle's own sensitivity
 WELL = 0.1          # sens <= WELL * tol * mag: the plain tolerance applies
 ILL = 0.5           # sens > ILL * tol * mag: an ill-conditioned row
 ILL_MAX = 0.10      # at most this fraction of rows may be ill-conditioned
+ILL_MAX_LAYER = 0.20  # the same for the core rows inside the whole layer
 DEV = torch.device("cuda:0")
 
 
@@ -94,8 +103,9 @@ def rel(x: np.ndarray, r: np.ndarray) -> float:
 class Score:
     """Accumulates rows under the tolerance rule above."""
 
-    def __init__(self, tol: float):
+    def __init__(self, tol: float, ill_max: float | None = ILL_MAX):
         self.tol = tol
+        self.ill_max = ill_max  # None: rule (iii)'s fraction is checked on other rows
         self.rows = self.well = self.ill = self.over = self.fails = 0
         self.plain = 0.0        # worst plain relative error over all rows
         self.well_plain = 0.0   # worst plain relative error over well-conditioned rows
@@ -149,7 +159,7 @@ class Score:
     def ok(self) -> bool:
         # (the fraction of ill-conditioned rows is a property of a workload:
         # it is checked once a score holds enough rows to estimate it)
-        frac_ok = self.rows < 200 or self.ill <= ILL_MAX * self.rows
+        frac_ok = self.ill_max is None or self.rows < 200 or self.ill <= self.ill_max * self.rows
         return self.fails == 0 and self.over <= self.ill and frac_ok
 
     def __str__(self) -> str:

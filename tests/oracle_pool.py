@@ -165,6 +165,57 @@ def decode_req_check(task):
     return out, st, r["conv_states"]
 
 
+def _block_oracle(case, hidden, X, conv0, ssm0, residual, keep=False):
+    """The whole layer (oracle.block_sequence) on one sequence or request of a
+    case whose layer weights come from the case seed: the exact result and the
+    two activation-precision realisations."""
+    d = case.dims
+    p = case.params
+    w = gi.block_weights(case.seed, d, hidden, case.act).as_dict()
+    f = lambda **pe: O.block_sequence(X, w, p.conv_w, None, p.A_log, p.dt_bias, p.norm_w, conv0, ssm0,
+                                      (d.h_k, d.h_v, d.d_k, d.d_v), 1.0, 1e-6, 1e-6, residual, keep, **pe)
+    return f(), [f(perturb=pe) for pe in perturbations(case.act)]
+
+
+def block_seq_check(task):
+    """The whole layer on sequence i of a prefill case against the device's
+    results: task = (case, hidden, i, residual, out_raw [L, hidden], ssm
+    [h_v, d_v, d_k], conv_raw [c_ch, W-1]) with o_raw [L, h_v, d_v] the core's
+    output.  Returns per-token output stats, per-(token, V head) core-output
+    stats, per-head state stats and per-channel conv-state stats."""
+    case, hidden, i, residual, out_raw, o_raw, ssm, conv_raw = task
+    s = int(case.slots[i])
+    init = bool(case.has_init[i])
+    X = gi.block_input(case.seed, i, int(case.lengths[i]), hidden, case.act)
+    r, rts = _block_oracle(case, hidden, X, case.slot_conv(s) if init else None, case.slot_ssm(s) if init else None,
+                           residual)
+    out = row_stats(from_raw(out_raw), r["block_out"], [rt["block_out"] for rt in rts])
+    dv = case.dims.d_v
+    o = row_stats(from_raw(o_raw), r["core_out"], [rt["core_out"] for rt in rts], n=dv)
+    st = [row_stats(ssm[h], r["ssm"][h], [rt["ssm"][h] for rt in rts], n=r["ssm"][h].size)
+          for h in range(case.dims.h_v)]
+    cv = row_stats(from_raw(conv_raw), r["conv"], [rt["conv"] for rt in rts])
+    return out, o, st, cv
+
+
+def block_req_check(task):
+    """The whole layer on request i of a decode / MTP case: task = (case, hidden,
+    i, out_raw [t_step, hidden], o_raw [t_step, h_v, d_v] (the core's output),
+    ssm [h_v, d_v, d_k] (the state after pos + 1 tokens) or None, pos)."""
+    case, hidden, i, out_raw, o_raw, ssm, pos = task
+    s = int(case.slots[i])
+    X = gi.block_input(case.seed, i, case.t_step, hidden, case.act)
+    r, rts = _block_oracle(case, hidden, X, case.slot_conv(s), case.slot_ssm(s), True, keep=True)
+    out = row_stats(from_raw(out_raw), r["block_out"], [rt["block_out"] for rt in rts])
+    o = row_stats(from_raw(o_raw), r["core_out"], [rt["core_out"] for rt in rts], n=case.dims.d_v)
+    st = None
+    if ssm is not None:
+        ref = r["ssm_states"][pos]
+        st = [row_stats(ssm[h], ref[h], [rt["ssm_states"][pos][h] for rt in rts], n=ref[h].size)
+              for h in range(case.dims.h_v)]
+    return out, o, st
+
+
 # ------------------------------------------- host baselines (timing only)
 def prefill_oracle_heads(task) -> None:
     """The oracle on sequence i of a prefill case for the given V heads (None =

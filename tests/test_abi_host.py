@@ -38,7 +38,7 @@ FAKE = 0x1000  # a 16-byte-aligned non-null address: every call below must fail 
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
         assert n in binding.SIGNATURES, n
@@ -178,3 +178,26 @@ def test_binding_rejects_host_tensors():
         gdn.conv1d_fwd(gdn.Dims(), x, torch.zeros(gdn.Dims().c_ch, 4, dtype=torch.bfloat16),
                        torch.tensor([0, 4], dtype=torch.int32), torch.tensor([0], dtype=torch.int32),
                        torch.zeros(1, gdn.Dims().c_ch, 3, dtype=torch.bfloat16))
+
+
+def test_block_argument_errors(L):
+    F1, F2, F3 = FAKE + 4096, FAKE + 8192, FAKE + 12288
+    assert L.gdn_rmsnorm_gemma(0, 4, 12, FAKE, F1, 1e-6, F2, None) == SHAPE        # hidden % 8
+    assert L.gdn_rmsnorm_gemma(0, -1, 16, FAKE, F1, 1e-6, F2, None) == SHAPE
+    assert L.gdn_rmsnorm_gemma(0, 4, 16, FAKE, F1, -1.0, F2, None) == SHAPE         # eps < 0
+    assert L.gdn_rmsnorm_gemma(0, 0, 16, None, None, 1e-6, None, None) == OK
+    assert L.gdn_rmsnorm_gemma(0, 4, 16, None, F1, 1e-6, F2, None) == NULL
+    assert L.gdn_rmsnorm_gemma(2, 4, 16, FAKE, F1, 1e-6, F2, None) == DTYPE
+    assert L.gdn_rmsnorm_gemma(0, 4, 16, FAKE + 8, F1, 1e-6, F2, None) == ALIGN
+    ptrs = [FAKE, F1, F2, F3, F3 + 4096, F3 + 8192, F3 + 12288]
+    assert L.gdn_in_proj(D(), 1, 8, 2048, *ptrs, None) == UNSUP                      # fp32 projections
+    assert L.gdn_in_proj(D(), 0, 8, 2047, *ptrs, None) == SHAPE
+    assert L.gdn_in_proj(D(), 0, -1, 2048, *ptrs, None) == SHAPE
+    assert L.gdn_in_proj(D(), 0, 0, 2048, *([None] * 7), None) == OK
+    assert L.gdn_in_proj(D(), 0, 8, 2048, *ptrs[:2], None, *ptrs[3:], None) == NULL   # no w_ba
+    assert L.gdn_in_proj(D(d=96), 0, 8, 2048, *ptrs, None) == UNSUP
+    assert L.gdn_out_proj(D(), 0, 8, 2048, FAKE, F1, F2 + 2, F3, None) == ALIGN    # residual
+    assert L.gdn_out_proj(D(), 1, 8, 2048, FAKE, F1, None, F3, None) == UNSUP
+    assert L.gdn_out_proj(D(), 0, 8, 0, FAKE, F1, None, F3, None) == SHAPE
+    assert L.gdn_out_proj(D(), 0, 8, 2048, FAKE, None, None, F3, None) == NULL
+    assert L.gdn_out_proj(D(), 0, 0, 2048, None, None, None, None, None) == OK
