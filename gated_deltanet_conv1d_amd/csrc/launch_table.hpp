@@ -20,13 +20,15 @@ struct ChainShape {
 };
 
 constexpr ChainShape kChainTable[] = {
-    {32, INT64_MAX, 1, 4},
-    {128, INT64_MAX, 2, 3},
-    {INT64_MAX, INT64_MAX, 4, 3},
+    {32, INT64_MAX, 1, 3},
+    {64, INT64_MAX, 2, 3},
+    {256, INT64_MAX, 4, 2},
+    {512, INT64_MAX, 4, 3},
+    {INT64_MAX, INT64_MAX, 4, 2},
 };
 
 // The (ntw, pd) pairs the table uses, each instantiated once per kernel type.
-#define GDN_CHAIN_SHAPES(X) X(1, 4) X(2, 3) X(4, 3)
+#define GDN_CHAIN_SHAPES(X) X(1, 3) X(2, 3) X(4, 2) X(4, 3)
 
 inline ChainShape chain_shape(int64_t chains, int64_t mean_len) {
   for (const ChainShape& s : kChainTable)

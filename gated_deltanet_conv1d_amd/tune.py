@@ -3,16 +3,18 @@
     python -m gated_deltanet_conv1d_amd.tune [--out csrc/launch_table.hpp] [--reps 10]
     python -m gated_deltanet_conv1d_amd.tune --build-only --variants DIR   # compile the candidates (no GPU)
     python -m gated_deltanet_conv1d_amd.tune --time-only --variants DIR    # time prebuilt candidates
+    python -m gated_deltanet_conv1d_amd.tune --from-json FILE              # table from stored timings
 
 For every candidate shape (d_v tiles per chain workgroup, prefetch stages) it
 copies the kernel sources, pins the launch table to that one shape, builds the
 copy (under --variants, default _build/tune/), and times gdn_prefill with it on
 a grid of workloads: n_seq sequences of L tokens each at the 16 QK / 32 V head,
-d = 128 layout, bf16, chunk 64, two copies of every buffer alternated.  Each build runs in its own process (one library per
-process).  The fastest shape per grid cell becomes a row of the launch table
-the library consults at run time (csrc/launch_table.hpp), and the timings are
-written next to it as JSON.  Results do not depend on the shape, so the table
-only moves time.
+d = 128 layout, bf16, chunk 64, two copies of every buffer alternated.  Each
+variant is timed in its own process (one library per process).  For each
+sequence count the shape fastest over its lengths becomes a row of the launch
+table the library consults at run time (csrc/launch_table.hpp), and the
+timings are written next to it as JSON.  Results do not depend on the shape,
+so the table only moves time.
 """
 from __future__ import annotations
 
@@ -156,26 +158,32 @@ def time_variant(lib_path: str, reps: int) -> dict:
 
 
 def choose(times: dict) -> list:
-    """Table rows from {shape: {cell: ms}}: the fastest shape per cell, rows ordered
-    by chain count then length; the last length of a chain count and the last
-    chain count are open-ended."""
-    rows = []
+    """Table rows from {shape: {cell: ms}}: for each sequence count (chain
+    count n * h_v) the shape with the smallest sum over lengths of time / best
+    time of the cell, so one shape serves all lengths of a chain count; runs of
+    chain counts that pick the same shape merge, the last row is open-ended."""
     ns = [n for n in N_SEQ if any(n * L <= MAX_TOKENS for L in LENGTHS)]
-    for i, n in enumerate(ns):
-        Ls = [L for L in LENGTHS if n * L <= MAX_TOKENS]
-        for j, L in enumerate(Ls):
-            cell = f"{n}x{L}"
-            best = min(times, key=lambda s: times[s][cell])
-            ntw, pd = (int(v) for v in best.split(","))
-            rows.append((None if i == len(ns) - 1 else n * H_V, None if j == len(Ls) - 1 else L, ntw, pd))
-    # merge consecutive rows of one chain count that pick the same shape
-    merged = []
-    for r in rows:
-        if merged and merged[-1][0] == r[0] and merged[-1][2:] == r[2:]:
-            merged[-1] = (r[0], r[1], r[2], r[3])
+    picks = []
+    for n in ns:
+        cells = [f"{n}x{L}" for L in LENGTHS if n * L <= MAX_TOKENS]
+        best = {c: min(times[s][c] for s in times) for c in cells}
+        score = {s: sum(times[s][c] / best[c] for c in cells) for s in times}
+        picks.append((n * H_V, min(score, key=score.get)))
+    rows = []
+    for chains, shape in picks:
+        ntw, pd = (int(v) for v in shape.split(","))
+        if rows and rows[-1][2:] == (ntw, pd):
+            rows[-1] = (chains, None, ntw, pd)
         else:
-            merged.append(r)
-    return merged
+            rows.append((chains, None, ntw, pd))
+    rows[-1] = (None, None) + rows[-1][2:]
+    return rows
+
+
+def write_table(out: str, rows) -> None:
+    shapes = sorted({(n, p) for _, _, n, p in rows})
+    with open(out, "w") as f:
+        f.write(table_source(rows, shapes))
 
 
 def main() -> int:
@@ -187,9 +195,20 @@ def main() -> int:
     ap.add_argument("--build-only", action="store_true")
     ap.add_argument("--build-jobs", type=int, default=4, help="variants compiled at once")
     ap.add_argument("--time-only", action="store_true")
+    ap.add_argument("--from-json", help="rewrite the table from the timings stored in this JSON file")
     ap.add_argument("--time", help=argparse.SUPPRESS)       # internal: time one built variant
     ap.add_argument("--time-out", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.from_json:      # rewrite the table from stored timings
+        with open(args.from_json) as f:
+            rec = json.load(f)
+        rows = choose(rec["median_ms"])
+        rec["table"] = [list(r) for r in rows]
+        write_table(args.out, rows)
+        with open(args.json, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"tune: wrote {args.out} ({len(rows)} rows) and {args.json}", file=sys.stderr)
+        return 0
     if args.time:
         with open(args.time_out, "w") as f:
             json.dump(time_variant(args.time, args.reps), f)
@@ -222,11 +241,10 @@ def main() -> int:
             times[f"{ntw},{pd}"] = json.load(f)
         print(f"tune: shape ({ntw}, {pd}) timed in {time.time() - t0:.0f} s", file=sys.stderr, flush=True)
     rows = choose(times)
-    shapes = sorted({(n, p) for _, _, n, p in rows})
-    with open(args.out, "w") as f:
-        f.write(table_source(rows, shapes))
+    write_table(args.out, rows)
     with open(args.json, "w") as f:
-        json.dump({"grid": {"n_seq": N_SEQ, "lengths": LENGTHS, "max_tokens": MAX_TOKENS,
+        json.dump({"command": " ".join(["python -m gated_deltanet_conv1d_amd.tune"] + sys.argv[1:]),
+                   "grid": {"n_seq": N_SEQ, "lengths": LENGTHS, "max_tokens": MAX_TOKENS,
                             "layout": f"h_k {H_K}, h_v {H_V}, d {D}, conv_w {W}, chunk {CHUNK}, bf16"},
                    "median_ms": times, "table": [list(r) for r in rows]}, f, indent=1)
     print(f"tune: wrote {args.out} ({len(rows)} rows) and {args.json}", file=sys.stderr)

@@ -1,0 +1,60 @@
+"""Every row of the chain launch table gives results bitwise equal to those of
+the same sequences run one call each (one sequence is 32 chains: the first
+row's shape).  The shape only moves time: each chain's accumulators see the
+same MFMA order whatever the d_v tiles per workgroup and prefetch depth."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import gated_deltanet_conv1d_amd as gdn
+from tests.gpu_cases import dev, host_raw, i32, log, u8
+from tests.test_launch_table import table_rows
+
+pytestmark = pytest.mark.gpu
+
+ROWS, _ = table_rows()
+D = gdn.Dims(16, 32, 128, 128, 4)
+
+
+def _n_seq(r: int) -> int:
+    """A sequence count whose 32 n chains select row r (and no earlier row)."""
+    lo = ROWS[r - 1][0] if r else 0
+    hi = ROWS[r][0]
+    n = hi // D.h_v if hi is not None else lo // D.h_v + 1
+    assert lo < n * D.h_v and (hi is None or n * D.h_v <= hi)
+    return n
+
+
+@pytest.mark.parametrize("r", range(len(ROWS)))
+def test_table_row_matches_single_sequence_calls(r):
+    n = _n_seq(r)
+    lengths = np.random.default_rng(60 + r).integers(40, 200, n)
+    log(f"launch table row {r} {ROWS[r]}: {n} sequences, {int(lengths.sum())} tokens")
+    case = gi.varlen_case(seed=60 + r, lengths=lengths, n_slots=n, dims=gi.QWEN3_NEXT)
+    p = case.params
+    bf = lambda v: dev(v, torch.bfloat16)
+    f32 = lambda v: dev(v, torch.float32)
+    conv0 = np.stack([case.slot_conv(s) for s in range(n)])
+    ssm0 = np.stack([case.slot_ssm(s) for s in range(n)])
+    xs = [case.seq_x(i) for i in range(n)]
+    a_s, b_s, z_s = [case.seq_a(i) for i in range(n)], [case.seq_b(i) for i in range(n)], [case.seq_z(i) for i in range(n)]
+    common = (bf(p.conv_w),)
+    conv_pool, ssm_pool = bf(conv0), f32(ssm0)
+    out = gdn.prefill(D, bf(np.concatenate(xs)), *common, bf(np.concatenate(a_s)), bf(np.concatenate(b_s)),
+                      f32(p.A_log), f32(p.dt_bias), i32(case.cu_seqlens), i32(case.slots), conv_pool, ssm_pool,
+                      u8(case.has_init), 64, 1.0, bf(np.concatenate(z_s)), bf(p.norm_w))
+    torch.cuda.synchronize()
+    out_b, ssm_b, conv_b = host_raw(out), ssm_pool.cpu().numpy(), host_raw(conv_pool)
+    for i in range(n):
+        s = int(case.slots[i])
+        cp, sp = bf(conv0), f32(ssm0)
+        o1 = gdn.prefill(D, bf(xs[i]), *common, bf(a_s[i]), bf(b_s[i]), f32(p.A_log), f32(p.dt_bias),
+                         i32([0, len(xs[i])]), i32([s]), cp, sp, u8([1]), 64, 1.0, bf(z_s[i]), bf(p.norm_w))
+        torch.cuda.synchronize()
+        lo, hi = case.cu_seqlens[i], case.cu_seqlens[i + 1]
+        assert np.array_equal(host_raw(o1), out_b[lo:hi]), f"sequence {i}: output"
+        assert np.array_equal(sp.cpu().numpy()[s], ssm_b[s]), f"sequence {i}: state"
+        assert np.array_equal(host_raw(cp)[s], conv_b[s]), f"sequence {i}: conv state"
