@@ -12,15 +12,16 @@
 // (X rows, weight rows in [out_features, in_features] layout), 64 k per stage
 // through LDS.  The MFMA's first operand is the weight tile, so each lane's
 // four accumulator values are four consecutive output columns of one row
-// (one 8-byte store).  A workgroup of 4 waves owns a BM x BN output tile; each
-// wave a (BM/WGM) x (BN/WGN) sub-tile held as 16x16 accumulators.  The next
-// stage's global loads are issued into registers before the current stage's
-// MFMAs, so HBM latency hides behind the contraction.
+// (one 8-byte store).  A workgroup owns a BM x BN output tile; each of its
+// waves a (BM/WGM) x (BN/WGN) sub-tile held as 16x16 accumulators.  Two
+// kernels: one stages each 64-deep step through registers (the next step's
+// global loads are issued before the current step's MFMAs, so HBM latency
+// hides behind the contraction; two workgroups per CU), the other moves the
+// steps straight from HBM into LDS.
 //
-// LDS rows are 64 bf16 = 128 bytes = 8 chunks of 16 bytes; chunk c of row r
-// sits at position c ^ (r & 7), so the 16 rows a fragment read touches (same
-// logical chunk) fall in 8 distinct chunk positions: no bank conflicts for
-// either the 16-byte stores or the 16-byte fragment reads.
+// LDS rows are 64 bf16 = 128 bytes = 8 chunks of 16 bytes, stored swizzled
+// (chunk c of row r at a position that depends on r) so that the rows one
+// fragment read touches at one logical chunk spread over the banks.
 //
 // Workgroup b runs on XCD b % 8; tiles are numbered so that each XCD takes a
 // contiguous range, and within that range GM m-tiles share each weight tile
@@ -94,6 +95,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
+// Register-staged kernel: chunk c of row r at c ^ (r % 8).
 __device__ __forceinline__ int swz(int row, int c) { return row * kBK + ((c ^ (row & 7)) << 3); }
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -250,19 +252,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 
 // The same contraction for k a multiple of 64, with the stages moved from HBM
 // straight into LDS (global_load_lds_dwordx4: no staging registers, no LDS
-// store instructions) and two LDS buffers, so the next stage streams in while
+// store instructions), 4 or 8 waves (one or two per SIMD) and two LDS
+// buffers, so the next stage streams in while
 // the MFMAs consume the current one; one barrier per stage.  A wave's load
 // instruction fills one contiguous kilobyte of LDS (lane l: bytes 16 l), i.e.
-// 8 tile rows; lane l takes logical chunk (l % 8) ^ (l / 8) of row l / 8, which
-// realises the swizzled layout above.  Rows past m or n read the last valid
-// row instead (in bounds; their outputs are never stored).  Weight rows from
-// n_w0 on come from the second weight matrix, as in the kernel above.
+// 8 tile rows: lane l writes physical chunk l % 8 of row l / 8 and so fetches
+// the logical chunk that the swizzle puts there.  Rows past m or n read the
+// last valid row instead (in bounds; their outputs are never stored).  Weight
+// rows from n_w0 on come from the second weight matrix, as in the kernel above.
+//
+// The swizzle here is chunk c of row r at c ^ ((r / 2) % 8): the 16 rows a
+// quarter-wave reads at one logical chunk then cover all 64 banks once.
+__device__ __forceinline__ int swz2(int row, int c) { return row * kBK + ((c ^ ((row >> 1) & 7)) << 3); }
+
 template <int BM, int BN, int WGM, int WGN, bool RES>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_lds_kernel(ProjDev p) {
-  constexpr bool VEC = true;
-  static_assert(WGM * WGN == 4, "four waves");
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+void proj_lds_kernel(ProjDev p) {
+  constexpr int NW = WGM * WGN;  // waves: 4 (one per SIMD) or 8 (two per SIMD)
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
-  constexpr int IX = BM / 32, IW = BN / 32;  // load instructions per wave per stage
+  static_assert(FM * 16 == WM && FN * 16 == WN, "wave tile");
+  constexpr int IX = BM / (8 * NW), IW = BN / (8 * NW);  // load instructions per wave per stage
+  static_assert(IX * 8 * NW == BM && IW * 8 * NW == BN, "whole load instructions");
   __shared__ __attribute__((aligned(16))) bf16 sx[2][BM * kBK];
   __shared__ __attribute__((aligned(16))) bf16 sw[2][BN * kBK];
 
@@ -279,31 +290,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int n0 = nt * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane >> 3, lch = (lane & 7) ^ (lane >> 3);
+  const int lrow = lane >> 3;
+  // each lane's row addresses, fixed for the whole k loop (computed once from
+  // scalar copies of the pointers: a per-lane choice between two pointers of
+  // the argument block would otherwise become a per-lane load of the pointer)
+  const bf16* const xbase = p.x;
+  const bf16* const w0 = p.w0;
+  const bf16* const w1 = p.w1;
+  const bf16* xrow[IX];
+  const bf16* wrow[IW];
+  auto lchunk = [&](int blk) { return (lane & 7) ^ (((blk * 8 + lrow) >> 1) & 7); };
+#pragma unroll
+  for (int i = 0; i < IX; ++i) {
+    const int blk = i * NW + wave;
+    const int64_t row = min(m0 + blk * 8 + lrow, p.m - 1);
+    xrow[i] = xbase + row * p.ldx + lchunk(blk) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < IW; ++i) {
+    const int blk = i * NW + wave;
+    const int n = min(n0 + blk * 8 + lrow, p.n - 1);
+    const int64_t off = n < p.n_w0 ? (int64_t)n * p.k : (int64_t)(n - p.n_w0) * p.k;
+    wrow[i] = (n < p.n_w0 ? w0 : w1) + off + lchunk(blk) * 8;
+  }
   auto issue = [&](int k0, int buf) {
 #pragma unroll
-    for (int i = 0; i < IX; ++i) {
-      const int blk = i * 4 + wave;
-      const int64_t row = min(m0 + blk * 8 + lrow, p.m - 1);
-      lds_dma16(p.x + row * p.ldx + k0 + lch * 8, &sx[buf][blk * 8 * kBK]);
-    }
+    for (int i = 0; i < IX; ++i) lds_dma16(xrow[i] + k0, &sx[buf][(i * NW + wave) * 8 * kBK]);
 #pragma unroll
-    for (int i = 0; i < IW; ++i) {
-      const int blk = i * 4 + wave;
-      const int n = min(n0 + blk * 8 + lrow, p.n - 1);
-      const bf16* wrow = n < p.n_w0 ? p.w0 + (int64_t)n * p.k : p.w1 + (int64_t)(n - p.n_w0) * p.k;
-      lds_dma16(wrow + k0 + lch * 8, &sw[buf][blk * 8 * kBK]);
-    }
+    for (int i = 0; i < IW; ++i) lds_dma16(wrow[i] + k0, &sw[buf][(i * NW + wave) * 8 * kBK]);
   };
 
   const int wm = wave % WGM, wn = wave / WGM;
-  const int rl = lane & 15, g = lane >> 4;
   f32x4 acc[FN][FM];
 #pragma unroll
   for (int j = 0; j < FN; ++j)
 #pragma unroll
     for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // fragments: lane l reads row l % 16 at chunk 4 kk + l / 16 (two 32-deep
+  // steps per stage)
+  const int rl = lane & 15, g = lane >> 4;
   const int kt_n = p.k / kBK;
   issue(0, 0);
   for (int kt = 0; kt < kt_n; ++kt) {
@@ -318,17 +344,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int c = kk * 4 + g;
       bf16x8 fx[FM];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fx[i] = *reinterpret_cast<const bf16x8*>(&cx[swz(wm * WM + i * 16 + rl, c)]);
+      for (int i = 0; i < FM; ++i) fx[i] = *reinterpret_cast<const bf16x8*>(&cx[swz2(wm * WM + i * 16 + rl, c)]);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const bf16x8 fw = *reinterpret_cast<const bf16x8*>(&cw[swz(wn * WN + j * 16 + rl, c)]);
+        const bf16x8 fw = *reinterpret_cast<const bf16x8*>(&cw[swz2(wn * WN + j * 16 + rl, c)]);
 #pragma unroll
         for (int i = 0; i < FM; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fx[i], acc[j][i], 0, 0, 0);
       }
     }
   }
 
-  store_tile<VEC, RES, FN, FM>(p, m0 + wm * WM, n0 + wn * WN, rl, g, acc);
+  store_tile<true, RES, FN, FM>(p, m0 + wm * WM, n0 + wn * WN, rl, g, acc);
 }
 
 template <int BM, int BN, int WGM, int WGN, bool RES>
@@ -338,8 +364,8 @@ hipError_t run_proj_lds(ProjDev p, hipStream_t st) {
   p.group_m = 4;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   p.per_xcd = (int)((tiles + 7) / 8);
-  hipLaunchKernelGGL((proj_lds_kernel<BM, BN, WGM, WGN, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)), dim3(256), 0, st,
-                     p);
+  hipLaunchKernelGGL((proj_lds_kernel<BM, BN, WGM, WGN, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)),
+                     dim3(64 * WGM * WGN), 0, st, p);
   return hipGetLastError();
 }
 
@@ -350,8 +376,8 @@ hipError_t run_proj(ProjDev p, hipStream_t st) {
   p.group_m = 4;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   p.per_xcd = (int)((tiles + 7) / 8);
-  hipLaunchKernelGGL((proj_kernel<BM, BN, WGM, WGN, OCC, VEC, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)), dim3(256), 0,
-                     st, p);
+  hipLaunchKernelGGL((proj_kernel<BM, BN, WGM, WGN, OCC, VEC, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)),
+                     dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -392,14 +418,14 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
   bool vec = a.n % 4 == 0 && (a.residual == nullptr || (a.ld_res % 4 == 0 && ((uintptr_t)a.residual & 7) == 0));
   for (int s = 0; s < a.nseg; ++s)
     vec = vec && a.seg[s].begin % 4 == 0 && a.seg[s].ld % 4 == 0 && ((uintptr_t)a.seg[s].ptr & 7) == 0;
-  // one weight matrix and whole 64-deep stages: the direct-to-LDS kernel
-  // (in_proj_qkvz: no residual, 256 x 256 tiles; out_proj: residual, 256 x 128)
+  // Measured on the 4096-token layer (hidden 2048): in_proj_qkvz/ba runs
+  // best as 256 x 256 tiles streamed straight into LDS (8 waves, two per
+  // SIMD), out_proj as 128 x 128 tiles staged through registers (two
+  // workgroups per CU); small m takes 64 x 128 tiles for more workgroups.
   const bool lds = vec && a.k % kBK == 0;
   const bool res = a.residual != nullptr;
   if (lds && !res && a.m >= 1024 && tile_count(a.m, a.n, 256, 256) >= 512)
-    return run_proj_lds<256, 256, 2, 2, false>(p, st);
-  if (lds && a.m >= 1024)
-    return res ? run_proj_lds<256, 128, 2, 2, true>(p, st) : run_proj_lds<256, 128, 2, 2, false>(p, st);
+    return run_proj_lds<256, 256, 2, 4, false>(p, st);
   if (tile_count(a.m, a.n, 128, 128) >= 256) {
     if (vec) return res ? run_proj<128, 128, 2, 2, 2, true, true>(p, st) : run_proj<128, 128, 2, 2, 2, true, false>(p, st);
     return res ? run_proj<128, 128, 2, 2, 2, false, true>(p, st) : run_proj<128, 128, 2, 2, 2, false, false>(p, st);
