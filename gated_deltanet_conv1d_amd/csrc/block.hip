@@ -418,20 +418,31 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
   bool vec = a.n % 4 == 0 && (a.residual == nullptr || (a.ld_res % 4 == 0 && ((uintptr_t)a.residual & 7) == 0));
   for (int s = 0; s < a.nseg; ++s)
     vec = vec && a.seg[s].begin % 4 == 0 && a.seg[s].ld % 4 == 0 && ((uintptr_t)a.seg[s].ptr & 7) == 0;
-  // Measured on the 4096-token layer (hidden 2048): in_proj_qkvz/ba runs
-  // best as 256 x 256 tiles streamed straight into LDS (8 waves, two per
-  // SIMD), out_proj as 128 x 128 tiles staged through registers (two
-  // workgroups per CU); small m takes 64 x 128 tiles for more workgroups.
+  // Measured on the layer's shapes (hidden 2048): at 4096 tokens
+  // in_proj_qkvz/ba runs best as 256 x 256 tiles streamed straight into LDS
+  // (8 waves, two per SIMD) and out_proj as 128 x 128 tiles staged through
+  // registers (two workgroups per CU); at 256 decode rows in_proj takes
+  // 64 x 128 tiles and out_proj 64 x 32.
   const bool lds = vec && a.k % kBK == 0;
   const bool res = a.residual != nullptr;
   if (lds && !res && a.m >= 1024 && tile_count(a.m, a.n, 256, 256) >= 512)
     return run_proj_lds<256, 256, 2, 4, false>(p, st);
-  if (tile_count(a.m, a.n, 128, 128) >= 256) {
-    if (vec) return res ? run_proj<128, 128, 2, 2, 2, true, true>(p, st) : run_proj<128, 128, 2, 2, 2, true, false>(p, st);
-    return res ? run_proj<128, 128, 2, 2, 2, false, true>(p, st) : run_proj<128, 128, 2, 2, 2, false, false>(p, st);
-  }
-  if (vec) return res ? run_proj<64, 128, 1, 4, 2, true, true>(p, st) : run_proj<64, 128, 1, 4, 2, true, false>(p, st);
-  return res ? run_proj<64, 128, 1, 4, 2, false, true>(p, st) : run_proj<64, 128, 1, 4, 2, false, false>(p, st);
+#define GDN_PROJ(BM_, BN_, WGM_, WGN_)                                                              \
+  do {                                                                                               \
+    if (vec)                                                                                         \
+      return res ? run_proj<BM_, BN_, WGM_, WGN_, 2, true, true>(p, st)                               \
+                 : run_proj<BM_, BN_, WGM_, WGN_, 2, true, false>(p, st);                             \
+    return res ? run_proj<BM_, BN_, WGM_, WGN_, 2, false, true>(p, st)                                \
+               : run_proj<BM_, BN_, WGM_, WGN_, 2, false, false>(p, st);                              \
+  } while (0)
+  // otherwise the largest register-staged tile that still gives 256
+  // workgroups: a small m (decode) is bound by per-step overheads of each
+  // workgroup's k loop, so more, smaller tiles run faster there
+  if (tile_count(a.m, a.n, 128, 128) >= 256) GDN_PROJ(128, 128, 2, 2);
+  if (tile_count(a.m, a.n, 64, 128) >= 256) GDN_PROJ(64, 128, 1, 4);
+  if (tile_count(a.m, a.n, 64, 64) >= 256) GDN_PROJ(64, 64, 2, 2);
+  GDN_PROJ(64, 32, 2, 2);
+#undef GDN_PROJ
 }
 
 }  // namespace gdn

@@ -46,11 +46,12 @@ def _small_ints(seed, shape, lo=-2, hi=2, density=0.5):
     return v * (rng.random(shape) < density)
 
 
-# tile choices (in_proj / out_proj): 128 x 128 / 64 x 128 staged through
-# registers; 128 x 128 / 128 x 128; 256 x 256 straight into LDS / 128 x 128;
-# one row; k not a multiple of 64 with 2-column segments (column by column)
-@pytest.mark.parametrize("dims,hidden,T", [(QWEN, 2048, 300), (QWEN, 2048, 1100), (QWEN, 2048, 2600),
-                                           (QWEN, 1024, 1), (SMALL, 24, 37)])
+# tile choices (in_proj / out_proj), staged through registers unless noted:
+# 64 x 128 / 64 x 32; 128 x 128 / 64 x 32; 128 x 128 / 64 x 64; 256 x 256
+# straight into LDS / 128 x 128; one row (64 x 32 / 64 x 32); k not a multiple
+# of 64 with 2-column segments (column by column)
+@pytest.mark.parametrize("dims,hidden,T", [(QWEN, 2048, 256), (QWEN, 2048, 300), (QWEN, 2048, 600),
+                                           (QWEN, 2048, 2600), (QWEN, 1024, 1), (SMALL, 24, 37)])
 def test_projections_exact_on_small_integers(dims, hidden, T):
     log(f"projections: dims {dims} hidden {hidden} T {T}")
     vd = dims.h_v * dims.d_v
