@@ -134,21 +134,43 @@ def counter_traffic(workload: str, kernels) -> float | None:
         return None
 
 
+def chain_shape(chains: int, mean_len: int) -> tuple[int, int]:
+    """(d_v tiles per workgroup, prefetch stages) of the chain pass for a call
+    with this many (sequence, V head) chains: the first matching row of the
+    launch table in csrc/launch_table.hpp."""
+    import re
+    src = open(os.path.join(ROOT, "gated_deltanet_conv1d_amd", "csrc", "launch_table.hpp")).read()
+    body = src[src.index("kChainTable[] = {"):]
+    rows = re.findall(r"\{(\w+), (\w+), (\d+), (\d+)\}", body[:body.index("};")])
+    for mc, ml, ntw, pd in rows:
+        if (mc == "INT64_MAX" or chains <= int(mc)) and (ml == "INT64_MAX" or mean_len <= int(ml)):
+            return int(ntw), int(pd)
+    return int(rows[-1][2]), int(rows[-1][3])
+
+
+_NTW, _PD = chain_shape(32, 4096)   # the single 4096-token sequence: 32 chains
 # kernels one gdn_chunk_prefill call launches on the split path (one sequence:
 # no chunk index kernel)
 CHUNK_SPLIT_KERNELS = ("void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, false, 4, 2>",
-                       "void split::chunk_state_kernel<__bf16, 128, 64, 1, 4>",
+                       f"void split::chunk_state_kernel<__bf16, 128, 64, {_NTW}, {_PD}>",
                        "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, false, 4>")
 # kernels one gdn_prefill call launches (the chain kernel also stores the conv windows)
 PREFILL_KERNELS = ("void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, true, 4, 2>",
-                   "void split::chunk_state_kernel<__bf16, 128, 64, 1, 4>",
+                   f"void split::chunk_state_kernel<__bf16, 128, 64, {_NTW}, {_PD}>",
                    "void split::chunk_out_kernel<__bf16, __bf16, 128, 64, true, 4>")
+# the single-call decode (in place, one token) and MTP draft step kernels
+DECODE_KERNEL = "void decode_fused_kernel<__bf16, 128, 2, 4, false, true, true>"
+MTP_KERNEL = "void decode_fused_kernel<__bf16, 128, 2, 4, true, true, false>"
+# the layer's projection kernels at 4096 tokens (in_proj_qkvz/ba, out_proj with the residual)
+IN_PROJ_KERNEL = "void proj_lds_kernel<256, 256, 2, 4, false>"
+OUT_PROJ_KERNEL = "void proj_kernel<128, 128, 2, 2, 2, true, true>"
 
 
 def counter_mfma(workload: str, kernels) -> dict | None:
     """MFMA utilisation from the committed rocprofv3 counter pass
-    (profiles/<workload>_mfma.json): MFMA-busy cycles over CU-busy cycles of
-    the kernels' dispatches, summed; None when the sources changed since."""
+    (profiles/<workload>_mfma.json): the kernels' MFMA-busy cycles (summed
+    over every SIMD) over their GPU-busy cycles (per XCD) x 1024 SIMDs, summed
+    over the kernels; None when the sources changed since."""
     path = os.path.join(ROOT, "profiles", f"{workload}_mfma.json")
     if not os.path.exists(path):
         return None
@@ -159,10 +181,12 @@ def counter_mfma(workload: str, kernels) -> dict | None:
     per = rec["per_dispatch"]
     try:
         busy = sum(per[k]["mfma_busy_cycles"] for k in kernels)
-        total = sum(per[k]["cu_busy_cycles"] for k in kernels)
+        total = sum(per[k]["gpu_busy_cycles_per_xcd"] * per[k]["simds"] for k in kernels)
+        flops = sum(per[k]["mfma_flops"] for k in kernels)
     except KeyError:
         return None
-    return {"mfma_busy_frac": round(busy / total, 4) if total else None, "counters": rec.get("counters")}
+    return {"mfma_util": round(busy / total, 4) if total else None, "mfma_flops_issued": flops,
+            "counters": rec.get("counters"), "formula": rec.get("util_formula")}
 
 
 def capture_graph(torch, fn):
@@ -184,6 +208,22 @@ def device_info() -> dict:
     import torch
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "cus": p.multi_processor_count, "arch": getattr(p, "gcnArchName", "")}
+
+
+def fill_bandwidth_gbs(torch) -> float:
+    """Measured device write-only bandwidth (a 1 GiB fill: bytes written / time)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        a.fill_(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        a.fill_(1)
+    e1.record()
+    torch.cuda.synchronize()
+    return n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def copy_bandwidth_gbs(torch) -> float:
@@ -441,7 +481,8 @@ def bench_decode(args, torch, gdn, gi):
     nb_rec = decode_algorithmic(case.n, 1, d.h_k, d.h_v, d.d_k, 2, 1)
     gbs = nb_dec / (t_dec["mean"] * 1e-3) / 1e9
     gbs_rec = nb_rec / (t_rec["mean"] * 1e-3) / 1e9
-    return {"workload": "decode_256x1", "call": "gdn_decode", "kernel": "decode_fused_kernel<bf16,128,2,4,false>",
+    return {"workload": "decode_256x1", "call": "gdn_decode", "kernel": DECODE_KERNEL,
+            "traffic": counter_traffic("decode_mtp", (DECODE_KERNEL,)),
             "launch_ms": t_dec, "algorithmic_bytes": nb_dec, "value": round(gbs, 1), "unit": "GB/s",
             "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(case.n / (t_dec["mean"] * 1e-3), 1),
@@ -598,7 +639,8 @@ def bench_mtp(args, torch, gdn, gi):
     gbs = nb_dec / (t_dec["mean"] * 1e-3) / 1e9
     gbs_rec = nb_rec / (t_rec["mean"] * 1e-3) / 1e9
     return {"workload": f"mtp_{case.n}x{case.t_step}", "call": "gdn_decode",
-            "kernel": "decode_fused_kernel<bf16,128,2,4,true>", "launch_ms": t_dec, "algorithmic_bytes": nb_dec,
+            "kernel": MTP_KERNEL, "traffic": counter_traffic("decode_mtp", (MTP_KERNEL,)),
+            "launch_ms": t_dec, "algorithmic_bytes": nb_dec,
             "value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "state_copy_ms": t_copy2, "state_copy_gbs": round(copy_bytes / (t_copy2["mean"] * 1e-3) / 1e9, 1),
             "draft_tokens_per_s": round(case.n * case.t_step / ((t_dec["mean"] + t_copy2["mean"]) * 1e-3), 1),
@@ -746,16 +788,18 @@ def bench_layer(args, torch, gdn, gi):
     lib_in, lib_out = lib_gemm(c["xn"], w_in), lib_gemm(c["o"].view(T, vd), wts.w_out)
     fl_in, fl_out = 2.0 * T * hidden * n_in, 2.0 * T * vd * hidden
     tf = lambda fl, t: fl / (t * 1e-3) / 1e12
-    proj = lambda fl, t, lib: {"algorithmic_flops": fl, "launch_ms": t, "achieved_tflops": round(tf(fl, t["mean"]), 1),
-                               "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tf(fl, t["mean"]) / BF16_PEAK_TFLOPS, 4),
-                               "torch_f_linear_ms": round(lib, 4),
-                               "torch_f_linear_tflops": round(tf(fl, lib), 1)}
+    proj = lambda fl, t, lib, kern: {"kernel": kern, "algorithmic_flops": fl, "launch_ms": t,
+                                     "achieved_tflops": round(tf(fl, t["mean"]), 1), "peak_tflops": BF16_PEAK_TFLOPS,
+                                     "frac": round(tf(fl, t["mean"]) / BF16_PEAK_TFLOPS, 4),
+                                     "traffic": counter_traffic("layer_4096", (kern,)),
+                                     "counters": counter_mfma("layer_4096", (kern,)),
+                                     "torch_f_linear_ms": round(lib, 4), "torch_f_linear_tflops": round(tf(fl, lib), 1)}
     prefill_row = {
         "workload": f"layer_prefill_single_{T}", "hidden": hidden, "calls": "gdn_rmsnorm_gemma, gdn_in_proj, "
         "gdn_prefill, gdn_out_proj (+ residual)", "graph_ms_per_step": round(ms_step, 4),
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "kernels_ms": {"gdn_rmsnorm_gemma": t_norm, "gdn_in_proj": t_in, "gdn_prefill": t_pre, "gdn_out_proj": t_out},
-        "in_proj": proj(fl_in, t_in, lib_in), "out_proj": proj(fl_out, t_out, lib_out),
+        "in_proj": proj(fl_in, t_in, lib_in, IN_PROJ_KERNEL), "out_proj": proj(fl_out, t_out, lib_out, OUT_PROJ_KERNEL),
         "rmsnorm_gbs": round(2.0 * T * hidden * 2 / (t_norm["mean"] * 1e-3) / 1e9, 1)}
     del copies, graphs
     torch.cuda.empty_cache()
@@ -928,6 +972,7 @@ def main() -> int:
     var = run("varlen", args.no_varlen, bench_varlen, args, torch, gdn, gi)
     torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth_gbs(torch)
+    fill_gbs = fill_bandwidth_gbs(torch)
     cpu = run("cpu baseline", args.no_cpu_baseline, cpu_baseline, pre["inputs"]["case"])
     T = pre["T"]
     line = {
@@ -959,7 +1004,7 @@ def main() -> int:
         "varlen": var,
         "tp_shapes": tp,
         "layer": layer,
-        "device": {**info, "rocminfo": rinfo, "copy_gbs": round(copy_gbs, 1)},
+        "device": {**info, "rocminfo": rinfo, "copy_gbs": round(copy_gbs, 1), "fill_gbs": round(fill_gbs, 1)},
     }
     print(json.dumps(line), flush=True)
     return 0
