@@ -25,6 +25,10 @@ realisations, rounded, and rounded after a seeded half-ulp nudge:
         the oracle alone finds 11.6-15.1% of the core rows of the layer
         workloads so, and the cap there is ILL_MAX_LAYER = 20%.
 
+Each score also reports how many rows over plain tol are not ill-conditioned
+and the smallest sens / (tol * mag) among the rows over plain tol, so how far
+a workload leans on the sensitivity term is visible per test.
+
 sens is the oracle's own measure of the row's conditioning: how far an
 activation-precision rounding of its input moves the exact answer (two
 realisations, since one alone understates it on the worst rows).  It is
@@ -107,6 +111,8 @@ class Score:
         self.tol = tol
         self.ill_max = ill_max  # None: rule (iii)'s fraction is checked on other rows
         self.rows = self.well = self.ill = self.over = self.fails = 0
+        self.over_moderate = 0      # rows over plain tol that are not ill-conditioned
+        self.over_min_sens = np.inf  # smallest sens / (tol mag) over the rows over plain tol
         self.plain = 0.0        # worst plain relative error over all rows
         self.well_plain = 0.0   # worst plain relative error over well-conditioned rows
         self.ratio = 0.0        # worst err / bound
@@ -133,6 +139,10 @@ class Score:
         if ill.any():
             self.ill_sens = max(self.ill_sens, float((err[ill] / sens[ill]).max()))
         self.over += int(over.sum())
+        self.over_moderate += int((over & ~ill).sum())
+        if over.any():
+            with np.errstate(divide="ignore", invalid="ignore"):
+                self.over_min_sens = min(self.over_min_sens, float((sens[over] / tolm[over]).min()))
         self.plain = max(self.plain, float(rel_.max()))
         if well.any():
             self.well_plain = max(self.well_plain, float(rel_[well].max()))
@@ -165,7 +175,8 @@ class Score:
     def __str__(self) -> str:
         s = (f"rows {self.rows}: plain worst {self.plain:.2e}, well-conditioned {self.well} worst "
              f"{self.well_plain:.2e}; ill-conditioned {self.ill} (err/sens worst {self.ill_sens:.2f}), over plain tol "
-             f"{self.over}; err/bound worst {self.ratio:.3f}")
+             f"{self.over} (not ill-conditioned {self.over_moderate}, smallest sens/(tol mag) "
+             f"{self.over_min_sens:.2f}); err/bound worst {self.ratio:.3f}")
         return s + (f"; FAILS {self.fails} ({self.first_fail})" if self.fails else "")
 
 
