@@ -21,7 +21,9 @@
 // chunk-parallel.  The prep pass writes the operands as ready-made MFMA
 // fragments:
 //   -W                             (A operand, contraction over d_k)
-//   K^T                            (A operand, contraction over the chunk; raw k)
+//   K^T                            (A operand, contraction over the chunk; raw k,
+//                                   so one copy per QK head, in the unit of
+//                                   its first V head)
 //   scale P                        (A operand, lower triangle; bf16 as hi + lo)
 //   Ut                             (accumulator layout; the chain turns it into U)
 //   f_q = scale e^G r_q            (per token; the output pass reads raw q)
@@ -963,13 +965,17 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
         store_pair<Op>(at<Op>(unit(s), K::W_OFF + (uint32_t)(mt * NPD + sp_w) * PB + lp), frag_from<Op>(wacc[0], -1.f),
                        DVT == 2 ? frag_from<Op>(wacc[DVT - 1], -1.f) : zf);
       }
+      // raw K^T is the same for every V head of the QK head: stored once, in
+      // the unit of the group's first V head, where the chain reads it
+      if ((h0 + s) % (h_v / h_k) == 0) {
 #pragma unroll
-      for (int j = 0; j < DVT; ++j)
+        for (int j = 0; j < DVT; ++j)
 #pragma unroll
-        for (int sp = 0; sp < NPC; ++sp) {
-          store_pair<Op>(at<Op>(unit(s), K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp), Kc[2 * sp][j],
-                         2 * sp + 1 < CT ? Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j] : zf);
-        }
+          for (int sp = 0; sp < NPC; ++sp) {
+            store_pair<Op>(at<Op>(unit(s), K::KT_OFF + (uint32_t)((wave * DVT + j) * NPC + sp) * PB + lp),
+                           Kc[2 * sp][j], 2 * sp + 1 < CT ? Kc[2 * sp + 1 < CT ? 2 * sp + 1 : 0][j] : zf);
+          }
+      }
     }
   }
 }
@@ -998,7 +1004,7 @@ template <typename Op, int D, int C, int NTW, int PD>
 __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
     const int32_t* __restrict__ cstart, unsigned char* __restrict__ ws, float* __restrict__ state,
-    int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v,
+    int32_t n_slots, Op* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v, int32_t kt_group,
     const Op* __restrict__ conv_x, Op* __restrict__ conv_state, int32_t c_ch, int32_t conv_w) {
   using K = Cfg<Op, D, C>;
   using FragT = typename Frag<Op>::type;
@@ -1079,6 +1085,8 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
   // unit of chunk k of this sequence, clamped to the last one: loads past the
   // end re-read it, so every load is unconditional and the wait counts exact
   auto unit_of = [&](int k) { return ws + uniform_i64(((int64_t)(gc0 + min(k, nch - 1)) * h_v + h) * K::UNIT); };
+  // K^T lives in the unit of the QK head's first V head (the same chunk)
+  const int64_t kt_delta = -(int64_t)(h % kt_group) * K::UNIT;
   Pair<Op> wn[PD][UPW][NPD], kt[PD][SM][NPC];
   FragT ut[PD][UPW][NTW];
   f32x4 fk[PD][UPW];
@@ -1096,7 +1104,7 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
       ut[s][i][jt] = *at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + NTW * tile + jt) * PB / 2 + lf);
     } else if (j < NW + NU + NK) {
       const int m = (j - NW - NU) / NPC, sp = (j - NW - NU) % NPC;
-      kt[s][m][sp].load(at<Op>(u, K::KT_OFF + (uint32_t)((SM * wave + m) * NPC + sp) * PB + lp));
+      kt[s][m][sp].load(at<Op>(u + kt_delta, K::KT_OFF + (uint32_t)((SM * wave + m) * NPC + sp) * PB + lp));
     } else if (j < NPIECE - 1) {
       const int i = j - NW - NU - NK;
       const int mt = min(wave + MW * i, CT - 1);
@@ -1405,8 +1413,8 @@ hipError_t launch_chain(const ChunkArgs& a, int64_t groups, const int32_t* cstar
   constexpr int TW = Cfg<Op, D, C>::NT >= NTW ? NTW : Cfg<Op, D, C>::NT;
   hipLaunchKernelGGL((chunk_state_kernel<Op, D, C, TW, PD>), dim3((unsigned)(groups * (Cfg<Op, D, C>::NT / TW))),
                      dim3(kChainThreads<D>), 0, st, a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state,
-                     a.n_slots, (Op*)a.o, a.t_total, a.n_seq, a.s.h_v, conv_x, (Op*)const_cast<void*>(a.conv_state),
-                     a.s.c_ch(), a.s.conv_w);
+                     a.n_slots, (Op*)a.o, a.t_total, a.n_seq, a.s.h_v, a.s.h_v / a.s.h_k, conv_x,
+                     (Op*)const_cast<void*>(a.conv_state), a.s.c_ch(), a.s.conv_w);
   return hipGetLastError();
 }
 
