@@ -470,7 +470,7 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
     const T* __restrict__ qkv, const float* __restrict__ g_in, const float* __restrict__ beta_in,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const int32_t* __restrict__ cstart,
     int32_t n_slots, int32_t n_seq, int64_t t_total, int32_t h_k, int32_t h_v, float scale,
-    unsigned char* __restrict__ ws, ConvIn conv, GateIn gate, const uint8_t* __restrict__ has_init) {
+    unsigned char* __restrict__ ws, ConvIn conv, GateIn gate, const uint8_t* __restrict__ has_init, int32_t q_out) {
   static_assert(sizeof(T) == sizeof(Op), "raw activations are MFMA operands");
   using K = Cfg<Op, D, C>;
   using L = PrepLDS<Op, D, C, FUSE, G>;
@@ -676,6 +676,20 @@ __global__ __launch_bounds__(kThreads<D>) void chunk_prep_kernel(
       }
     }
     __syncthreads();  // r_k visible; q and v rows are read before the A tiles overlay them
+  }
+
+  // ---- for the chain that computes the output itself: the chunk's raw q
+  // rows as A-operand pairs [C/16][D/32], once per QK head, in the S^T area of
+  // the unit of its first V head (that chain writes no S^T)
+  if (q_out && h0 % (h_v / h_k) == 0) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int ib = wave + b * WAVES;
+      if (ib >= CT) break;
+#pragma unroll
+      for (int sp = 0; sp < NPD; ++sp)
+        store_pair<Op>(at<Op>(unit(0), K::H_OFF + (uint32_t)(ib * NPD + sp) * PB + lp), Qb[b][sp][0], Qb[b][sp][1]);
+    }
   }
 
   // ---- Gram work.  Wave w: the P^T tiles of its q blocks ib (pairs of
@@ -1235,6 +1249,322 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_state_kernel(
     }
 }
 
+// ---------------------------------------------------- chain with output
+// Four consecutive activations of a row, raw (8 bytes of bf16, 16 of fp32).
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+  uint2 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void zero() { u = make_uint2(0, 0); }
+  __device__ __forceinline__ void to_f32(float* v) const {
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+};
+template <> struct Raw4<float> {
+  float4 u;
+  __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void zero() { u = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void to_f32(float* v) const {
+    v[0] = u.x;
+    v[1] = u.y;
+    v[2] = u.z;
+    v[3] = u.w;
+  }
+};
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Many chains at once: one workgroup per (sequence, V head) holds all of S^T
+// and computes each chunk's output itself, so neither S^T at the chunk start
+// nor U goes through the workspace and no output pass runs.  Wave w owns the
+// chunk's row tile w (its rows of U and of O) and d_k tiles 2w, 2w + 1 of S^T.
+// Per chunk:
+//   h = bf16(S^T) -> LDS; the chunk's q rows, P, f_q and z are requested; barrier
+//   U = Ut - W S^T for row tile w -> LDS twice (diag(f_k) U for the state
+//   update, U for the output), and O^T = (h as A) x (q as B): the transposed
+//   product, so a lane holds 4 consecutive d_v values of one token; times f_q;
+//   barrier
+//   S^T <- e^{G_n} S^T + K^T diag(f_k) U; O^T += (U as A) x (P as B), P's high
+//   and low parts; the gated RMSNorm over d_v and 8-byte stores.
+// The products, their operands (bf16 S^T, bf16 U) and their order are those of
+// the chain and output kernels.  q is the prep pass's copy of the chunk's q
+// rows, kept with K^T in the unit of the QK head's first V head; the V heads
+// of a QK head run on one XCD.
+template <typename T, typename Op, int D, int C, int PD>
+__global__ __launch_bounds__(kChainThreads<D>) void chunk_chain_out_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
+    const int32_t* __restrict__ cstart, unsigned char* __restrict__ ws, float* __restrict__ state,
+    int32_t n_slots, T* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v, int32_t kt_group,
+    const T* __restrict__ z, const T* __restrict__ norm_w, float norm_eps, const Op* __restrict__ conv_x,
+    Op* __restrict__ conv_state, int32_t c_ch, int32_t conv_w) {
+  static_assert(sizeof(T) == sizeof(Op), "outputs in the activation type");
+  using K = Cfg<Op, D, C>;
+  using FragT = typename Frag<Op>::type;
+  constexpr int NT = K::NT, CT = K::CT, NPD = K::NPD, NPC = K::NPC;
+  constexpr int MW = NPD;                   // waves
+  static_assert(64 * MW == kChainThreads<D>, "one wave per h pair");
+  static_assert(CT <= MW, "one chunk row tile per wave");
+  static_assert(PD >= 2, "a chunk's loads go to a stage other than its own");
+  constexpr int SM = NT >= 2 ? 2 : 1;       // d_k tiles of S^T per wave
+  constexpr uint32_t PB = K::PAIR * sizeof(Op);
+  __shared__ __attribute__((aligned(16))) Op sH[NPD][NT][64 * 8];  // h, pairs
+  __shared__ __attribute__((aligned(16))) Op sU[CT][NT][64 * 4];   // diag(f_k) U, accumulator layout
+  __shared__ __attribute__((aligned(16))) Op sUo[CT][NT][64 * 4];  // U
+  // chain index: the kt_group V heads of a QK head on consecutive slots of one XCD
+  const int xcd = blockIdx.x & 7, qb = blockIdx.x >> 3;
+  const int64_t grp = ((int64_t)(qb / kt_group) * 8 + xcd) * kt_group + qb % kt_group;
+  if (grp >= (int64_t)n_seq * h_v) return;
+  const int n = (int)(grp / h_v), h = (int)(grp % h_v);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int64_t lo = min((int64_t)cu[n], t_total);
+  const int64_t hi = min(max((int64_t)cu[n + 1], lo), t_total);
+  const int32_t slot = slots[n];
+  const int64_t o_ld = (int64_t)h_v * D;
+  if (!slot_ok(slot, n_slots)) {  // padding entry: zero outputs
+    for (int64_t e = tid; e < (hi - lo) * D; e += 64 * MW) o[(lo + e / D) * o_ld + h * D + e % D] = from_f32<T>(0.f);
+    return;
+  }
+  const bool init = has_init == nullptr || has_init[n] != 0;
+  float* st_ptr = state + ((int64_t)slot * h_v + h) * D * D;
+  const int32_t gc0 = first_chunk<C>(cstart, cu, n_seq, t_total, n);
+
+  if (conv_x != nullptr) {
+    // fused-input prefill: the sequence's final conv window, one channel per
+    // thread over the sequence's workgroups (the prep pass read the old ones)
+    const int wm1 = conv_w - 1;
+    const int64_t len = hi - lo;
+    const int stride = 64 * MW * h_v;
+    for (int c = h * 64 * MW + (int)tid; c < c_ch; c += stride) {
+      Op* cs = conv_state + ((int64_t)slot * c_ch + c) * wm1;
+      Op prev[kMaxConvW - 1], nw[kMaxConvW - 1];
+#pragma unroll
+      for (int j = 0; j < kMaxConvW - 1; ++j) prev[j] = j < wm1 && init && len < wm1 ? cs[j] : from_f32<Op>(0.f);
+#pragma unroll
+      for (int j = 0; j < kMaxConvW - 1; ++j) {
+        const int64_t p = len - wm1 + j;
+        Op v = from_f32<Op>(0.f);
+#pragma unroll
+        for (int t = 0; t < kMaxConvW - 1; ++t) v = t == wm1 + (int)p ? prev[t] : v;  // (no register index)
+        nw[j] = j < wm1 && p >= 0 ? conv_x[(lo + p) * c_ch + c] : v;
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxConvW - 1; ++j)
+        if (j < wm1) cs[j] = nw[j];
+    }
+  }
+
+  f32x4 Sacc[SM][NT];
+#pragma unroll
+  for (int m = 0; m < SM; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int mt = SM * wave + m, dv = 16 * j + l16;
+      if (init) {
+        const float4 v = *reinterpret_cast<const float4*>(st_ptr + dv * D + 16 * mt + 4 * g4);
+        Sacc[m][j] = f32x4{v.x, v.y, v.z, v.w};
+      } else {
+        Sacc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+  const uint32_t lp = lane * 8 * sizeof(Op);
+  const uint32_t lf = lane * 4 * sizeof(Op);
+  const int nch = (int)((hi - lo + C - 1) / C);
+  auto unit_of = [&](int k) { return ws + uniform_i64(((int64_t)(gc0 + min(k, nch - 1)) * h_v + h) * K::UNIT); };
+  const int64_t kt_delta = -(int64_t)(h % kt_group) * K::UNIT;  // the QK head's first V head (K^T, q)
+  const int mt = min(wave, CT - 1);  // this wave's chunk row tile (waves past CT keep nothing)
+  const bool rows = wave < CT;
+  Pair<Op> wn[PD][NPD], kt[PD][SM][NPC];
+  FragT ut[PD][NT];
+  f32x4 fk[PD];
+  float egn[PD];
+  constexpr int NW = NPD, NU = NT, NK = SM * NPC, NPIECE = NW + NU + NK + 2;
+  auto piece = [&](int s, const unsigned char* u, int j) {
+    if (j < NW) {
+      wn[s][j].load(at<Op>(u, K::W_OFF + (uint32_t)(mt * NPD + j) * PB + lp));
+    } else if (j < NW + NU) {
+      ut[s][j - NW] = *at<FragT>(u, K::UT_OFF + (uint32_t)(mt * NT + (j - NW)) * PB / 2 + lf);
+    } else if (j < NW + NU + NK) {
+      const int m = (j - NW - NU) / NPC, sp = (j - NW - NU) % NPC;
+      kt[s][m][sp].load(at<Op>(u + kt_delta, K::KT_OFF + (uint32_t)((SM * wave + m) * NPC + sp) * PB + lp));
+    } else if (j < NPIECE - 1) {
+      fk[s] = *at<f32x4>(u, K::FK_OFF + 4 * (16 * mt + 4 * g4));
+    } else {
+      egn[s] = *at<float>(u, K::F_OFF);
+    }
+  };
+  const FragT zf = zero_frag<Op>();
+  auto step = [&](int s, unsigned char* uc, int ls, const unsigned char* ul, int k) {
+    int pc = 0;
+    auto next_load = [&]() {
+      if (pc < NPIECE) {
+        __builtin_amdgcn_sched_barrier(0);
+        piece(ls, ul, pc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      ++pc;
+    };
+    // this chunk's output operands for row tile mt
+    const int64_t c0 = lo + (int64_t)k * C;
+    const int row = 16 * mt + (int)l16;  // this lane's token within the chunk
+    const bool live = rows && c0 + row < hi;
+    Pair<Op> qp[NPD], pa[NPC], pl[NPC];
+#pragma unroll
+    for (int sp = 0; sp < NPD; ++sp) qp[sp].load(at<Op>(uc + kt_delta, K::H_OFF + (uint32_t)(mt * NPD + sp) * PB + lp));
+#pragma unroll
+    for (int sp = 0; sp < NPC; ++sp)
+      if (2 * sp <= mt) {
+        pa[sp].load(at<Op>(uc, K::P_OFF + (uint32_t)(mt * NPC + sp) * PB + lp));
+        if constexpr (K::P_PARTS == 2) pl[sp].load(at<Op>(uc, K::P_OFF + (uint32_t)((CT + mt) * NPC + sp) * PB + lp));
+      }
+    const float fq = *at<float>(uc, K::FQ_OFF + 4 * row);
+    Raw4<T> zr[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (z && live) zr[j].load(z + (c0 + row) * o_ld + h * D + 16 * j + 4 * g4);
+      else zr[j].zero();
+    }
+    // h = S^T at the chunk start: this wave's pairs
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const FragT h0 = frag_from<Op>(Sacc[0][j]), h1 = SM > 1 ? frag_from<Op>(Sacc[SM - 1][j]) : zf;
+      next_load();
+      store_pair<Op>(&sH[wave][j][lane * 8], h0, h1);
+    }
+    next_load();
+    __syncthreads();
+    // U = Ut - W S^T and O^T = h^T q^T for row tile mt, one d_v tile at a time
+    f32x4 Oacc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      f32x4 acc, oac = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = to_f32(ut[s][j][e]);
+#pragma unroll
+      for (int sp = 0; sp < NPD; ++sp) {
+        Pair<Op> hp;
+        hp.load(&sH[sp][j][lane * 8]);
+        FragT b0, b1, q0, q1;
+        hp.split(b0, b1);
+        qp[sp].split(q0, q1);
+        wn[s][sp].mma(acc, b0, b1);
+        mma_k32(oac, b0, b1, q0, q1);
+        next_load();
+      }
+      if (rows) {
+        f32x4 su;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) su[e] = acc[e] * fk[s][e];
+        *reinterpret_cast<FragT*>(&sU[mt][j][lane * 4]) = frag_from<Op>(su);
+        *reinterpret_cast<FragT*>(&sUo[mt][j][lane * 4]) = frag_from<Op>(acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Oacc[j][e] = oac[e] * fq;  // scale e^{G_t} r_q[t] on Q S^T only
+    }
+    // the decay of S^T does not wait for U
+#pragma unroll
+    for (int m = 0; m < SM; ++m)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[m][j][e] *= egn[s];
+    __syncthreads();
+    // S^T <- e^{G_n} S^T + K^T diag(f_k) U; O^T += U^T P^T
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      FragT uf[CT];
+#pragma unroll
+      for (int t = 0; t < CT; ++t) uf[t] = *reinterpret_cast<const FragT*>(&sU[t][j][lane * 4]);
+#pragma unroll
+      for (int sp = 0; sp < NPC; ++sp)
+#pragma unroll
+        for (int m = 0; m < SM; ++m) {
+          kt[s][m][sp].mma(Sacc[m][j], uf[2 * sp], 2 * sp + 1 < CT ? uf[2 * sp + 1] : zf);
+          next_load();
+        }
+      if (rows) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t) uf[t] = *reinterpret_cast<const FragT*>(&sUo[t][j][lane * 4]);
+#pragma unroll
+        for (int sp = 0; sp < NPC; ++sp)
+          if (2 * sp <= mt) {
+            FragT p0, p1;
+            const FragT u1 = 2 * sp + 1 < CT ? uf[2 * sp + 1] : zf;
+            pa[sp].split(p0, p1);
+            mma_k32(Oacc[j], uf[2 * sp], u1, p0, p1);
+            if constexpr (K::P_PARTS == 2) {
+              pl[sp].split(p0, p1);
+              mma_k32(Oacc[j], uf[2 * sp], u1, p0, p1);
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NPIECE; ++j) next_load();  // any left (small shapes)
+    // gated RMSNorm over d_v: this lane's 4 x NT values of its token, the rest
+    // of the row in the lanes of the other three lane groups
+    if (rows) {
+      if (z) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = fmaf(Oacc[j][e], Oacc[j][e], ss);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float rstd = fast_rsq(ss * (1.0f / D) + norm_eps);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          float w[4], zz[4], v[4];
+          load4(norm_w + 16 * j + 4 * g4, w);
+          zr[j].to_f32(zz);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = Oacc[j][e] * rstd * w[e] * fast_silu(zz[e]);
+          if (live) store4(o + (c0 + row) * o_ld + h * D + 16 * j + 4 * g4, v);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          float v[4] = {Oacc[j][0], Oacc[j][1], Oacc[j][2], Oacc[j][3]};
+          if (live) store4(o + (c0 + row) * o_ld + h * D + 16 * j + 4 * g4, v);
+        }
+      }
+    }
+  };
+  if (nch > 0) {
+#pragma unroll
+    for (int s = 0; s < PD - 1; ++s)
+#pragma unroll
+      for (int j = 0; j < NPIECE; ++j) piece(s, unit_of(s), j);
+  }
+  int k = 0;
+  for (; k + PD <= nch; k += PD) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) step(s, unit_of(k + s), (s + PD - 1) % PD, unit_of(k + s + PD - 1), k + s);
+  }
+#pragma unroll
+  for (int s = 0; s < PD - 1; ++s)  // the last nch % PD chunks (uniform over the workgroup)
+    if (k + s < nch) step(s, unit_of(k + s), (s + PD - 1) % PD, unit_of(k + s + PD - 1), k + s);
+
+#pragma unroll
+  for (int m = 0; m < SM; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int mt2 = SM * wave + m, dv = 16 * j + l16;
+      *reinterpret_cast<float4*>(st_ptr + dv * D + 16 * mt2 + 4 * g4) =
+          make_float4(Sacc[m][j][0], Sacc[m][j][1], Sacc[m][j][2], Sacc[m][j][3]);
+    }
+}
+
 // ------------------------------------------------------------------ output
 // Per (chunk, V head): O = diag(f_q) Q h^T + P U (the scale is in f_q and P); with z,
 // out = O / sqrt(mean_dv(O^2) + eps) * w * silu(z).  Wave w computes d_v
@@ -1418,6 +1748,36 @@ hipError_t launch_chain(const ChunkArgs& a, int64_t groups, const int32_t* cstar
   return hipGetLastError();
 }
 
+// The chain that computes the output itself: one workgroup per chain, the
+// kt_group V heads of a QK head on one XCD.
+template <typename T, typename Op, int D, int C, int PD>
+hipError_t launch_chain_out(const ChunkArgs& a, const int32_t* cstart, unsigned char* units, const Op* conv_x,
+                            hipStream_t st) {
+  const int g = a.s.h_v / a.s.h_k;
+  const int64_t chains = (int64_t)a.n_seq * a.s.h_v;
+  const int64_t blocks = (chains + 8 * g - 1) / (8 * g) * 8 * g;
+  hipLaunchKernelGGL((chunk_chain_out_kernel<T, Op, D, C, PD>), dim3((unsigned)blocks), dim3(kChainThreads<D>), 0, st,
+                     a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state, a.n_slots, (T*)a.o, a.t_total,
+                     a.n_seq, a.s.h_v, g, (const T*)a.z, (const T*)a.norm_w, a.norm_eps, conv_x,
+                     (Op*)const_cast<void*>(a.conv_state), a.s.c_ch(), a.s.conv_w);
+  return hipGetLastError();
+}
+
+// A launch-table shape: NTW d_v tiles per chain workgroup, or (NTW = 8, all of
+// d_v at the layer's head dim) the chain that computes the output itself when
+// every chunk row tile has its own wave; else the widest split chain.
+// (bf16 only: the fp32 mode's operands do not fit its registers)
+template <typename Op, int D, int C>
+constexpr bool chain_out_fits(int ntw) {
+  return ntw >= 8 && sizeof(Op) == 2 && Cfg<Op, D, C>::CT <= Cfg<Op, D, C>::NPD;
+}
+template <typename T, typename Op, int D, int C, int NTW, int PD>
+hipError_t launch_shape(const ChunkArgs& a, int64_t groups, const int32_t* cstart, unsigned char* units,
+                        const Op* conv_x, hipStream_t st) {
+  if constexpr (chain_out_fits<Op, D, C>(NTW)) return launch_chain_out<T, Op, D, C, PD>(a, cstart, units, conv_x, st);
+  else return launch_chain<Op, D, C, (NTW >= 8 ? 4 : NTW), PD>(a, groups, cstart, units, conv_x, st);
+}
+
 // workspace: [chunk index][units]
 inline size_t idx_bytes(int32_t n_seq) { return (((size_t)n_seq + 1) * 4 + 255) / 256 * 256; }
 
@@ -1446,6 +1806,12 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t max_chunks = a.t_total / C + a.n_seq;
+  // the chain's launch shape from the measured table (launch_table.hpp): one
+  // d_v tile per workgroup is the most parallel chain, more tiles per
+  // workgroup share each -W and K^T load, which bounds many chains at once;
+  // all of d_v in one workgroup also computes the output (no output pass)
+  const ChainShape shape = chain_shape((int64_t)a.n_seq * a.s.h_v, a.t_total / a.n_seq);
+  const bool chain_out = chain_out_fits<Op, D, C>(shape.ntw);
   if (max_chunks > 0) {
     // two V heads per QK head: one prep workgroup per QK head shares the q/k
     // loads (or convolutions) and the raw Gram products between them
@@ -1456,26 +1822,25 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
     if (pair_fits && a.s.h_v == 2 * a.s.h_k)
       hipLaunchKernelGGL((chunk_prep_kernel<T, Op, D, C, FUSE, W, G2>), dim3((unsigned)(max_chunks * a.s.h_k)),
                          dim3(K::THREADS), 0, st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, cstart,
-                         a.n_slots, a.n_seq, a.t_total, a.s.h_k, a.s.h_v, a.scale, units, ci, gi, a.has_init);
+                         a.n_slots, a.n_seq, a.t_total, a.s.h_k, a.s.h_v, a.scale, units, ci, gi, a.has_init,
+                         (int32_t)chain_out);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<T, Op, D, C, FUSE, W, 1>), dim3((unsigned)(max_chunks * a.s.h_v)),
                          dim3(K::THREADS), 0, st, (const T*)a.qkv, a.g, a.beta, a.cu_seqlens, a.slots, cstart,
-                         a.n_slots, a.n_seq, a.t_total, a.s.h_k, a.s.h_v, a.scale, units, ci, gi, a.has_init);
+                         a.n_slots, a.n_seq, a.t_total, a.s.h_k, a.s.h_v, a.scale, units, ci, gi, a.has_init,
+                         (int32_t)chain_out);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t groups = ((int64_t)a.n_seq * a.s.h_v + 7) / 8 * 8;
   const Op* cx = FUSE ? reinterpret_cast<const Op*>(a.x) : nullptr;
-  // the chain's launch shape from the measured table (launch_table.hpp): one
-  // d_v tile per workgroup is the most parallel chain, more tiles per
-  // workgroup share each -W and K^T load, which bounds many chains at once
-  const ChainShape shape = chain_shape((int64_t)a.n_seq * a.s.h_v, a.t_total / a.n_seq);
   hipError_t ce = hipErrorInvalidValue;
-#define GDN_CHAIN_CASE(NTW_, PD_) \
-  if (shape.ntw == NTW_ && shape.pd == PD_) ce = launch_chain<Op, D, C, NTW_, PD_>(a, groups, cstart, units, cx, st);
+#define GDN_CHAIN_CASE(NTW_, PD_)                   \
+  if (shape.ntw == NTW_ && shape.pd == PD_)          \
+    ce = launch_shape<T, Op, D, C, NTW_, PD_>(a, groups, cstart, units, cx, st);
   GDN_CHAIN_SHAPES(GDN_CHAIN_CASE)
 #undef GDN_CHAIN_CASE
   if (ce != hipSuccess) return ce;
-  if (max_chunks > 0)
+  if (max_chunks > 0 && !chain_out)
     hipLaunchKernelGGL((chunk_out_kernel<T, Op, D, C, FUSE, W>), dim3((unsigned)(max_chunks * a.s.h_v)),
                        dim3(K::THREADS), 0, st, (const T*)a.qkv, a.cu_seqlens, a.slots, cstart, units, a.n_slots,
                        a.n_seq, a.t_total, a.s.h_k, a.s.h_v, (T*)a.o, (const T*)a.z, (const T*)a.norm_w,

@@ -13,8 +13,9 @@ d = 128 layout, bf16, chunk 64, two copies of every buffer alternated.  Each
 variant is timed in its own process (one library per process).  For each
 sequence count the shape fastest over its lengths becomes a row of the launch
 table the library consults at run time (csrc/launch_table.hpp), and the
-timings are written next to it as JSON.  Results do not depend on the shape,
-so the table only moves time.
+timings are written next to it as JSON.  The states do not depend on the
+shape; the outputs of the whole-d_v chain (ntw 8), which computes them
+itself, can differ from the output pass's in the last bit.
 """
 from __future__ import annotations
 
@@ -30,8 +31,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 
-# candidate (ntw, pd): tiles per chain workgroup, register stages of the prefetch
-CANDIDATES = [(1, 2), (1, 3), (1, 4), (1, 5), (1, 6), (2, 2), (2, 3), (2, 4), (4, 2), (4, 3)]
+# candidate (ntw, pd): tiles per chain workgroup, register stages of the
+# prefetch; ntw 8 (all of d_v) is the chain that computes the output itself
+CANDIDATES = [(1, 2), (1, 3), (1, 4), (1, 5), (1, 6), (2, 2), (2, 3), (2, 4), (4, 2), (4, 3), (8, 2), (8, 3)]
 # grid: sequences per batch x tokens per sequence (at most 2^19 tokens per batch)
 N_SEQ = [1, 2, 4, 8, 16, 32, 64]
 LENGTHS = [512, 2048, 8192]
@@ -51,9 +53,12 @@ def table_source(rows, shapes) -> str:
 // A row applies to a call whose number of (sequence, V head) chains is at most
 // max_chains and whose mean sequence length is at most max_len (the first
 // matching row wins).  ntw: 16-wide d_v tiles per chain workgroup (they share
-// each -W and K^T load); pd: register stages of the chunk-operand prefetch.
-// Results do not depend on the shape: every accumulator sees the same MFMA
-// order.
+// each -W and K^T load), 8 = all of d_v in one workgroup, which then also
+// computes the output (no output pass); pd: register stages of the
+// chunk-operand prefetch.  The states do not depend on the shape (every
+// accumulator sees the same MFMA order); the outputs of the whole-d_v chain
+// can differ from the output pass's in the last bit (its products and norm
+// sum run in another order).
 #pragma once
 #include <stdint.h>
 

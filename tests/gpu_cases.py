@@ -95,6 +95,19 @@ def host_raw(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy()
 
 
+def bf16_ulps(a: np.ndarray, b: np.ndarray) -> int:
+    """Largest distance in bf16 units in the last place between two arrays of
+    bf16 bit patterns (uint16): each pattern is mapped to a signed integer
+    that counts representable values from zero (+0 and -0 both to 0), so the
+    distance also holds across a sign change."""
+    def order(v):
+        v = v.astype(np.int32)
+        return np.where(v & 0x8000, -(v & 0x7FFF), v)
+    if a.size == 0:
+        return 0
+    return int(np.abs(order(a) - order(b)).max())
+
+
 def rel(x: np.ndarray, r: np.ndarray) -> float:
     """Plain max-norm relative error ||x - r||_inf / ||r||_inf."""
     if r.size == 0:

@@ -1,7 +1,11 @@
-"""Every row of the chain launch table gives results bitwise equal to those of
-the same sequences run one call each (one sequence is 32 chains: the first
-row's shape).  The shape only moves time: each chain's accumulators see the
-same MFMA order whatever the d_v tiles per workgroup and prefetch depth."""
+"""Every row of the chain launch table gives results equal to those of the
+same sequences run one call each (one sequence is 32 chains: the first row's
+shape).  States and conv states are bitwise equal for every shape: each
+chain's accumulators see the same MFMA order whatever the d_v tiles per
+workgroup and prefetch depth.  Outputs are bitwise equal too, except for the
+whole-d_v chain (ntw 8), which computes them itself with its products and
+norm sum in another order: there every output is within one bf16 unit in the
+last place of the output pass's."""
 from __future__ import annotations
 
 import numpy as np
@@ -10,7 +14,7 @@ import torch
 
 import gdn_inputs as gi
 import gated_deltanet_conv1d_amd as gdn
-from tests.gpu_cases import dev, host_raw, i32, log, u8
+from tests.gpu_cases import bf16_ulps, dev, host_raw, i32, log, u8
 from tests.test_launch_table import table_rows
 
 pytestmark = pytest.mark.gpu
@@ -55,6 +59,9 @@ def test_table_row_matches_single_sequence_calls(r):
                          i32([0, len(xs[i])]), i32([s]), cp, sp, u8([1]), 64, 1.0, bf(z_s[i]), bf(p.norm_w))
         torch.cuda.synchronize()
         lo, hi = case.cu_seqlens[i], case.cu_seqlens[i + 1]
-        assert np.array_equal(host_raw(o1), out_b[lo:hi]), f"sequence {i}: output"
+        if ROWS[r][2] >= 8:
+            assert bf16_ulps(host_raw(o1), out_b[lo:hi]) <= 1, f"sequence {i}: output beyond one unit in the last place"
+        else:
+            assert np.array_equal(host_raw(o1), out_b[lo:hi]), f"sequence {i}: output"
         assert np.array_equal(sp.cpu().numpy()[s], ssm_b[s]), f"sequence {i}: state"
         assert np.array_equal(host_raw(cp)[s], conv_b[s]), f"sequence {i}: conv state"

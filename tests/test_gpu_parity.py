@@ -15,8 +15,9 @@ import torch
 import gdn_inputs as gi
 import gated_deltanet_conv1d_amd as gdn
 from oracle import gdn_oracle as O
-from tests.gpu_cases import (TOL, DevPrefill, Score, act_dtype, compare_prefill, decode_req_check, dev, host, host_raw,
+from tests.gpu_cases import (TOL, DevPrefill, Score, act_dtype, bf16_ulps, compare_prefill, decode_req_check, dev, host, host_raw,
                              i32, log, oracle_prefill_seq, oracle_with_perturbed, rel, run_map, u8)
+from tests.test_launch_table import table_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -293,12 +294,13 @@ def test_deterministic():
 
 
 def test_batch_composition_does_not_change_a_sequence():
-    """One sequence's outputs and final state are bitwise the same whether it
-    runs alone or packed with 3 or 8 more sequences.  With 32 V heads of
-    d=128 these batches give the chain pass 256, 1024 and 2304 (sequence,
-    head, d_v tile) chains, which it runs with 1, 2 and 4 tiles per
-    workgroup: every launch shape of the chain is covered, on both entry
-    points, and the packed runs also meet the oracle on the first sequence."""
+    """One sequence's final state and conv state are bitwise the same whether
+    it runs alone or packed with 3 or 8 more sequences (32, 128 and 288
+    (sequence, V head) chains: the launch table's split shapes and the chain
+    that computes the output itself), on both entry points; its outputs are
+    bitwise the same on the split shapes and within one bf16 unit in the last
+    place on the chain with output (another order of its products and norm
+    sum).  The packed runs also meet the oracle on the first sequence."""
     lengths = np.array([300, 129, 64, 1, 700, 65, 0, 200, 333])
     case = gi.varlen_case(seed=16, lengths=lengths, n_slots=12)
     dp = DevPrefill(case)
@@ -325,10 +327,23 @@ def test_batch_composition_does_not_change_a_sequence():
                 w = compare_prefill(dp, o, seqs=[0], heads=[0, 5, 31])
                 log(f"packed 9: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
                 assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
+    rows, _ = table_rows()
+
+    def whole_dv(n):  # the table's shape for n sequences x 32 V heads
+        for mc, _ml, ntw, _pd in rows:
+            if mc is None or n * 32 <= mc:
+                return ntw >= 8
+
     for key, got in res.items():
         ref = res[(1, False)]
-        for r, g in zip(ref, got):
-            assert torch.equal(r, g), f"sequence 0 differs with {key[0]} sequences (fused={key[1]})"
+        o_r, o_g = ref[0], got[0]
+        if whole_dv(key[0]):
+            assert bf16_ulps(host_raw(o_r), host_raw(o_g)) <= 1, \
+                f"sequence 0 output beyond one unit in the last place with {key[0]} sequences (fused={key[1]})"
+        else:
+            assert torch.equal(o_r, o_g), f"sequence 0 output differs with {key[0]} sequences (fused={key[1]})"
+        for r, g in zip(ref[1:], got[1:]):
+            assert torch.equal(r, g), f"sequence 0 state differs with {key[0]} sequences (fused={key[1]})"
 
 
 def test_many_short_sequences():
