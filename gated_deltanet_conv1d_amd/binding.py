@@ -136,6 +136,14 @@ def _shape(t: torch.Tensor, shape, name: str) -> None:
         raise GdnError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _opt_shape(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """Shape check of an optional argument (a caller-provided output buffer,
+    an optional input): the kernels size every access from the dimensions,
+    so a smaller buffer would be written or read past its end."""
+    if t is not None:
+        _shape(t, shape, name)
+
+
 # ------------------------------------------------------------------ calls
 def conv1d_fwd(dims: Dims, x, w, cu_seqlens, slots, conv_state, has_init=None, bias=None, y=None):
     """Causal conv1d + SiLU over a packed varlen batch; updates conv_state in place."""
@@ -144,6 +152,10 @@ def conv1d_fwd(dims: Dims, x, w, cu_seqlens, slots, conv_state, has_init=None, b
     _shape(x, (t_total, dims.c_ch), "x")
     _shape(w, (dims.c_ch, dims.conv_w), "w")
     _shape(cu_seqlens, (n_seq + 1,), "cu_seqlens")
+    _shape(conv_state, (conv_state.shape[0], dims.c_ch, dims.conv_w - 1), "conv_state")
+    _opt_shape(has_init, (n_seq,), "has_init")
+    _opt_shape(bias, (dims.c_ch,), "bias")
+    _opt_shape(y, (t_total, dims.c_ch), "y")
     if y is None:
         y = torch.empty_like(x)
     _check(lib().gdn_conv1d_fwd(ctypes.byref(_cdims(dims)), act, n_seq, t_total, _ptr(x, x.dtype, "x"),
@@ -159,8 +171,12 @@ def conv1d_update(dims: Dims, x, w, conv_state, slots, out_slots=None, bias=None
     act = _act(x)
     n_seq, t_step = x.shape[0], x.shape[1]
     _shape(x, (n_seq, t_step, dims.c_ch), "x")
-    if out_slots is not None:
-        _shape(out_slots, (n_seq, t_step), "out_slots")
+    _shape(w, (dims.c_ch, dims.conv_w), "w")
+    _shape(conv_state, (conv_state.shape[0], dims.c_ch, dims.conv_w - 1), "conv_state")
+    _shape(slots, (n_seq,), "slots")
+    _opt_shape(out_slots, (n_seq, t_step), "out_slots")
+    _opt_shape(bias, (dims.c_ch,), "bias")
+    _opt_shape(y, (n_seq, t_step, dims.c_ch), "y")
     if y is None:
         y = torch.empty_like(x)
     _check(lib().gdn_conv1d_update(ctypes.byref(_cdims(dims)), act, n_seq, t_step, _ptr(x, x.dtype, "x"),
@@ -176,6 +192,11 @@ def gating(a, b, A_log, dt_bias, g=None, beta=None):
     act = _act(a)
     h_v = a.shape[-1]
     n = a.numel() // h_v
+    _shape(b, a.shape, "b")
+    _shape(A_log, (h_v,), "A_log")
+    _shape(dt_bias, (h_v,), "dt_bias")
+    _opt_shape(g, a.shape, "g")
+    _opt_shape(beta, a.shape, "beta")
     if g is None:
         g = torch.empty(a.shape, dtype=torch.float32, device=a.device)
     if beta is None:
@@ -197,7 +218,14 @@ def chunk_prefill(dims: Dims, qkv, g, beta, cu_seqlens, slots, state, has_init=N
     act = _act(qkv)
     t_total, n_seq = qkv.shape[0], slots.shape[0]
     _shape(qkv, (t_total, dims.c_ch), "qkv")
+    _shape(g, (t_total, dims.h_v), "g")
+    _shape(beta, (t_total, dims.h_v), "beta")
+    _shape(cu_seqlens, (n_seq + 1,), "cu_seqlens")
     _shape(state, (state.shape[0], dims.h_v, dims.d_v, dims.d_k), "state")
+    _opt_shape(has_init, (n_seq,), "has_init")
+    _opt_shape(z, (t_total, dims.h_v, dims.d_v), "z")
+    _opt_shape(norm_w, (dims.d_v,), "norm_w")
+    _opt_shape(o, (t_total, dims.h_v, dims.d_v), "o")
     if o is None:
         o = torch.empty((t_total, dims.h_v, dims.d_v), dtype=qkv.dtype, device=qkv.device)
     ws = chunk_prefill_workspace_size(dims, act, n_seq, t_total, chunk)
@@ -229,8 +257,17 @@ def prefill(dims: Dims, x, conv_w, a, b, A_log, dt_bias, cu_seqlens, slots, conv
     _shape(x, (t_total, dims.c_ch), "x")
     _shape(a, (t_total, dims.h_v), "a")
     _shape(b, (t_total, dims.h_v), "b")
+    _shape(conv_w, (dims.c_ch, dims.conv_w), "conv_w")
+    _shape(A_log, (dims.h_v,), "A_log")
+    _shape(dt_bias, (dims.h_v,), "dt_bias")
+    _shape(cu_seqlens, (n_seq + 1,), "cu_seqlens")
     _shape(conv_state, (conv_state.shape[0], dims.c_ch, dims.conv_w - 1), "conv_state")
     _shape(state, (state.shape[0], dims.h_v, dims.d_v, dims.d_k), "state")
+    _opt_shape(has_init, (n_seq,), "has_init")
+    _opt_shape(conv_b, (dims.c_ch,), "conv_b")
+    _opt_shape(z, (t_total, dims.h_v, dims.d_v), "z")
+    _opt_shape(norm_w, (dims.d_v,), "norm_w")
+    _opt_shape(o, (t_total, dims.h_v, dims.d_v), "o")
     if o is None:
         o = torch.empty((t_total, dims.h_v, dims.d_v), dtype=x.dtype, device=x.device)
     if workspace is None:
@@ -256,8 +293,15 @@ def recurrent_decode(dims: Dims, qkv, a, b, A_log, dt_bias, state, slots, out_sl
     n_seq, t_step = qkv.shape[0], qkv.shape[1]
     _shape(qkv, (n_seq, t_step, dims.c_ch), "qkv")
     _shape(a, (n_seq, t_step, dims.h_v), "a")
-    if out_slots is not None:
-        _shape(out_slots, (n_seq, t_step), "out_slots")
+    _shape(b, (n_seq, t_step, dims.h_v), "b")
+    _shape(A_log, (dims.h_v,), "A_log")
+    _shape(dt_bias, (dims.h_v,), "dt_bias")
+    _shape(state, (state.shape[0], dims.h_v, dims.d_v, dims.d_k), "state")
+    _shape(slots, (n_seq,), "slots")
+    _opt_shape(out_slots, (n_seq, t_step), "out_slots")
+    _opt_shape(z, (n_seq, t_step, dims.h_v, dims.d_v), "z")
+    _opt_shape(norm_w, (dims.d_v,), "norm_w")
+    _opt_shape(o, (n_seq, t_step, dims.h_v, dims.d_v), "o")
     if o is None:
         o = torch.empty((n_seq, t_step, dims.h_v, dims.d_v), dtype=qkv.dtype, device=qkv.device)
     _check(lib().gdn_recurrent_decode(ctypes.byref(_cdims(dims)), act, n_seq, t_step, scale,
@@ -283,8 +327,15 @@ def decode(dims: Dims, x, conv_w, a, b, A_log, dt_bias, slots, conv_state, state
     _shape(a, (n_seq, t_step, dims.h_v), "a")
     _shape(b, (n_seq, t_step, dims.h_v), "b")
     _shape(slots, (n_seq,), "slots")
-    if out_slots is not None:
-        _shape(out_slots, (n_seq, t_step), "out_slots")
+    _shape(A_log, (dims.h_v,), "A_log")
+    _shape(dt_bias, (dims.h_v,), "dt_bias")
+    _shape(conv_state, (conv_state.shape[0], dims.c_ch, dims.conv_w - 1), "conv_state")
+    _shape(state, (state.shape[0], dims.h_v, dims.d_v, dims.d_k), "state")
+    _opt_shape(out_slots, (n_seq, t_step), "out_slots")
+    _opt_shape(conv_b, (dims.c_ch,), "conv_b")
+    _opt_shape(z, (n_seq, t_step, dims.h_v, dims.d_v), "z")
+    _opt_shape(norm_w, (dims.d_v,), "norm_w")
+    _opt_shape(o, (n_seq, t_step, dims.h_v, dims.d_v), "o")
     if o is None:
         o = torch.empty((n_seq, t_step, dims.h_v, dims.d_v), dtype=x.dtype, device=x.device)
     _check(lib().gdn_decode(ctypes.byref(_cdims(dims)), act, n_seq, t_step, scale, _ptr(x, x.dtype, "x"),
@@ -300,6 +351,9 @@ def decode(dims: Dims, x, conv_w, a, b, A_log, dt_bias, slots, conv_state, state
 def state_copy(dims: Dims, state, src, dst, conv_state=None):
     """Bitwise state[dst[i]] <- state[src[i]] (and the conv pool, when given)."""
     act = GDN_BF16 if conv_state is None else _act(conv_state)
+    _shape(state, (state.shape[0], dims.h_v, dims.d_v, dims.d_k), "state")
+    _shape(dst, tuple(src.shape), "dst")
+    _opt_shape(conv_state, (state.shape[0], dims.c_ch, dims.conv_w - 1), "conv_state")
     _check(lib().gdn_state_copy(ctypes.byref(_cdims(dims)), act, _ptr(state, torch.float32, "state"),
                                 _ptr(conv_state, None, "conv_state"), state.shape[0], _ptr(src, torch.int32, "src"),
                                 _ptr(dst, torch.int32, "dst"), src.shape[0], _stream()), "gdn_state_copy")
@@ -309,6 +363,7 @@ def rmsnorm_gemma(x, w, eps: float = 1e-6, out=None):
     """Gemma-form RMSNorm over the last axis (gdn_rmsnorm_gemma): x / rms(x) * (1 + w)."""
     hidden = x.shape[-1]
     _shape(w, (hidden,), "w")
+    _opt_shape(out, x.shape, "out")
     if out is None:
         out = torch.empty_like(x)
     _check(lib().gdn_rmsnorm_gemma(_act(x), x.numel() // hidden if hidden else 0, hidden, _ptr(x, x.dtype, "x"),
@@ -324,6 +379,10 @@ def in_proj(dims: Dims, xn, w_qkvz, w_ba, qkv=None, z=None, b=None, a=None):
     vd = dims.h_v * dims.d_v
     _shape(w_qkvz, (dims.c_ch + vd, hidden), "w_qkvz")
     _shape(w_ba, (2 * dims.h_v, hidden), "w_ba")
+    _opt_shape(qkv, (T, dims.c_ch), "qkv")
+    _opt_shape(z, (T, dims.h_v, dims.d_v), "z")
+    _opt_shape(b, (T, dims.h_v), "b")
+    _opt_shape(a, (T, dims.h_v), "a")
     mk = lambda *shape: torch.empty(shape, dtype=xn.dtype, device=xn.device)
     qkv = mk(T, dims.c_ch) if qkv is None else qkv
     z = mk(T, dims.h_v, dims.d_v) if z is None else z
@@ -344,8 +403,8 @@ def out_proj(dims: Dims, o, w_out, residual=None, y=None):
     _shape(w_out, (hidden, dims.h_v * dims.d_v), "w_out")
     if o.numel() != T * dims.h_v * dims.d_v:
         raise GdnError(f"o: expected {T} x {dims.h_v * dims.d_v} values, got shape {tuple(o.shape)}")
-    if residual is not None:
-        _shape(residual, (T, hidden), "residual")
+    _opt_shape(residual, (T, hidden), "residual")
+    _opt_shape(y, (T, hidden), "y")
     if y is None:
         y = torch.empty((T, hidden), dtype=o.dtype, device=o.device)
     _check(lib().gdn_out_proj(ctypes.byref(_cdims(dims)), _act(o), T, hidden, _ptr(o, o.dtype, "o"),

@@ -201,3 +201,38 @@ def test_block_argument_errors(L):
     assert L.gdn_out_proj(D(), 0, 8, 0, FAKE, F1, None, F3, None) == SHAPE
     assert L.gdn_out_proj(D(), 0, 8, 2048, FAKE, None, None, F3, None) == NULL
     assert L.gdn_out_proj(D(), 0, 0, 2048, None, None, None, None, None) == OK
+
+
+def test_binding_rejects_wrong_output_shapes():
+    """The binding checks caller-provided outputs and optional inputs against
+    the dimensions before any call (the kernels size every access from the
+    dimensions, so a smaller buffer would be written past its end).  CPU
+    tensors: each call must fail on the shape, before the device check."""
+    import torch
+    dims = gdn.Dims(16, 32, 128, 128, 4)
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    T, n, c = 10, 2, dims.c_ch
+    conv, ssm = bf(4, c, 3), f32(4, 32, 128, 128)
+    cases = [
+        ("o", lambda: gdn.prefill(dims, bf(T, c), bf(c, 4), bf(T, 32), bf(T, 32), f32(32), f32(32), i32(n + 1),
+                                  i32(n), conv, ssm, o=bf(T - 1, 32, 128))),
+        ("z", lambda: gdn.prefill(dims, bf(T, c), bf(c, 4), bf(T, 32), bf(T, 32), f32(32), f32(32), i32(n + 1),
+                                  i32(n), conv, ssm, z=bf(T, 32, 64))),
+        ("o", lambda: gdn.decode(dims, bf(n, 1, c), bf(c, 4), bf(n, 1, 32), bf(n, 1, 32), f32(32), f32(32), i32(n),
+                                 conv, ssm, o=bf(n, 1, 32, 127))),
+        ("y", lambda: gdn.conv1d_fwd(dims, bf(T, c), bf(c, 4), i32(n + 1), i32(n), conv, y=bf(T, c - 8))),
+        ("g", lambda: gdn.gating(bf(T, 32), bf(T, 32), f32(32), f32(32), g=f32(T, 16))),
+        ("o", lambda: gdn.chunk_prefill(dims, bf(T, c), f32(T, 32), f32(T, 32), i32(n + 1), i32(n), ssm,
+                                        o=bf(T, 32, 64))),
+        ("o", lambda: gdn.recurrent_decode(dims, bf(n, 2, c), bf(n, 2, 32), bf(n, 2, 32), f32(32), f32(32), ssm,
+                                           i32(n), i32(n, 2), o=bf(n, 1, 32, 128))),
+        ("out", lambda: gdn.rmsnorm_gemma(bf(T, 64), bf(64), out=bf(T, 32))),
+        ("z", lambda: gdn.in_proj(dims, bf(T, 64), bf(c + 4096, 64), bf(64, 64), z=bf(T, 32, 127))),
+        ("y", lambda: gdn.out_proj(dims, bf(T, 4096), bf(64, 4096), y=bf(T - 2, 64))),
+        ("dst", lambda: gdn.state_copy(dims, ssm, i32(3), i32(2))),
+    ]
+    for name, call in cases:
+        with pytest.raises(gdn.GdnError, match=rf"\b{name} has shape"):
+            call()
