@@ -15,6 +15,11 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline int check_act(int32_t act) { return (act == GDN_BF16 || act == GDN_F32) ? GDN_OK : GDN_ERR_DTYPE; }
 
+// Row counts above this are rejected: the workspace bytes (rows / chunk x h_v
+// x ~100 KB) and every element offset stay far inside 64 bits below it.
+constexpr int64_t kMaxRows = (int64_t)1 << 40;
+inline bool rows_ok(int64_t rows) { return rows >= 0 && rows <= kMaxRows; }
+
 // Validate a gdn_dims and turn it into the kernels' Shape.
 int check_dims(const gdn_dims* d, Shape* s) {
   if (!d) return GDN_ERR_NULL;
@@ -81,7 +86,7 @@ int gdn_conv1d_fwd(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_t
   Shape s;
   GDN_TRY(check_dims(dims, &s));
   GDN_TRY(check_act(act));
-  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq < 0 || !rows_ok(t_total) || n_slots < 0) return GDN_ERR_SHAPE;
   if (n_seq == 0 && t_total > 0) return GDN_ERR_SHAPE;
   if (n_seq == 0) return GDN_OK;
   GDN_TRY(need(w, cu_seqlens, slots, conv_state));
@@ -111,7 +116,7 @@ int gdn_conv1d_update(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t 
 int gdn_gating(int32_t act, int64_t n_tokens, int32_t h_v, const void* a, const void* b, const float* A_log,
                const float* dt_bias, float* g, float* beta, void* stream) {
   GDN_TRY(check_act(act));
-  if (n_tokens < 0 || h_v <= 0) return GDN_ERR_SHAPE;
+  if (!rows_ok(n_tokens) || h_v <= 0) return GDN_ERR_SHAPE;
   if (n_tokens == 0) return GDN_OK;
   GDN_TRY(need(a, b, A_log, dt_bias, g, beta));
   gdn::GatingArgs args{act == GDN_BF16, n_tokens, h_v, a, b, A_log, dt_bias, g, beta};
@@ -121,7 +126,7 @@ int gdn_gating(int32_t act, int64_t n_tokens, int32_t h_v, const void* a, const 
 size_t gdn_chunk_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total,
                                         int32_t chunk) {
   Shape s;
-  if (check_dims(dims, &s) != GDN_OK || check_act(act) != GDN_OK || n_seq < 0 || t_total < 0) return 0;
+  if (check_dims(dims, &s) != GDN_OK || check_act(act) != GDN_OK || n_seq < 0 || !rows_ok(t_total)) return 0;
   return gdn::chunk_split_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
 }
 
@@ -133,7 +138,7 @@ int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t 
   Shape s;
   GDN_TRY(check_dims(dims, &s));
   GDN_TRY(check_act(act));
-  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq < 0 || !rows_ok(t_total) || n_slots < 0) return GDN_ERR_SHAPE;
   if (n_seq == 0 && t_total > 0) return GDN_ERR_SHAPE;
   if (!gdn::chunk_supported(s.d, chunk, act == GDN_BF16)) return GDN_ERR_UNSUPPORTED;
   if (n_seq == 0) return GDN_OK;
@@ -151,7 +156,7 @@ int gdn_chunk_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t 
 
 size_t gdn_prefill_workspace_size(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_total, int32_t chunk) {
   Shape s;
-  if (check_dims(dims, &s) != GDN_OK || check_act(act) != GDN_OK || n_seq < 0 || t_total < 0) return 0;
+  if (check_dims(dims, &s) != GDN_OK || check_act(act) != GDN_OK || n_seq < 0 || !rows_ok(t_total)) return 0;
   return gdn::chunk_split_workspace_size(s, act == GDN_BF16, n_seq, t_total, chunk);
 }
 
@@ -163,7 +168,7 @@ int gdn_prefill(const gdn_dims* dims, int32_t act, int32_t n_seq, int64_t t_tota
   Shape s;
   GDN_TRY(check_dims(dims, &s));
   GDN_TRY(check_act(act));
-  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if (n_seq < 0 || !rows_ok(t_total) || n_slots < 0) return GDN_ERR_SHAPE;
   if (n_seq == 0 && t_total > 0) return GDN_ERR_SHAPE;
   if (!gdn::chunk_supported(s.d, chunk, act == GDN_BF16)) return GDN_ERR_UNSUPPORTED;
   if (n_seq == 0) return GDN_OK;
@@ -228,7 +233,7 @@ int gdn_decode(const gdn_dims* dims, int32_t act, int32_t n_seq, int32_t t_step,
 int gdn_rmsnorm_gemma(int32_t act, int64_t rows, int32_t hidden, const void* x, const void* w, float eps, void* out,
                       void* stream) {
   GDN_TRY(check_act(act));
-  if (rows < 0 || hidden <= 0 || hidden % 8 != 0 || !(eps >= 0.0f)) return GDN_ERR_SHAPE;
+  if (!rows_ok(rows) || hidden <= 0 || hidden % 8 != 0 || !(eps >= 0.0f)) return GDN_ERR_SHAPE;
   if (rows == 0) return GDN_OK;
   GDN_TRY(need(x, w, out));
   GDN_TRY(align_ok(x, w, out));
@@ -242,7 +247,7 @@ int gdn_in_proj(const gdn_dims* dims, int32_t act, int64_t t_total, int32_t hidd
   GDN_TRY(check_dims(dims, &s));
   GDN_TRY(check_act(act));
   if (act != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-  if (t_total < 0 || hidden <= 0 || hidden % 8 != 0) return GDN_ERR_SHAPE;
+  if (!rows_ok(t_total) || hidden <= 0 || hidden % 8 != 0) return GDN_ERR_SHAPE;
   if (t_total == 0) return GDN_OK;
   GDN_TRY(need(xn, w_qkvz, w_ba, qkv, z, b, a));
   GDN_TRY(align_ok(xn, w_qkvz, w_ba, qkv, z, b, a));
@@ -270,7 +275,7 @@ int gdn_out_proj(const gdn_dims* dims, int32_t act, int64_t t_total, int32_t hid
   GDN_TRY(check_dims(dims, &s));
   GDN_TRY(check_act(act));
   if (act != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-  if (t_total < 0 || hidden <= 0 || hidden % 8 != 0) return GDN_ERR_SHAPE;
+  if (!rows_ok(t_total) || hidden <= 0 || hidden % 8 != 0) return GDN_ERR_SHAPE;
   if (t_total == 0) return GDN_OK;
   GDN_TRY(need(o, w_out, y));
   GDN_TRY(align_ok(o, w_out, residual, y));

@@ -42,7 +42,10 @@
  *  - Returns GDN_OK or a negative gdn_status.  Argument errors are reported
  *    before anything is enqueued; GDN_ERR_HIP means a launch failed.
  *  - Supported sizes: d_k == d_v in {16, 32, 64, 128}; h_v a multiple of h_k;
- *    conv_w in {2, 3, 4}; chunk in {16, 32, 64}.
+ *    conv_w in {2, 3, 4}; chunk in {16, 32, 64}.  Row counts (t_total, rows)
+ *    above 2^40 are rejected with GDN_ERR_SHAPE (no device holds such a batch;
+ *    below it every size computed from them, workspace bytes included, is
+ *    exact in 64 bits), and the workspace-size queries return 0 for them.
  */
 #ifndef GDN_H
 #define GDN_H
