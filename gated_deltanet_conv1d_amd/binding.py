@@ -44,6 +44,7 @@ SIGNATURES = {
     "gdn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
                                   _P, _P, _F, _P]),
     "gdn_state_copy": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _I32, _P]),
+    "gdn_check_slots": (ctypes.c_int, [_I32, _P, _I32, _P, _I32, _P, _P]),
     "gdn_rmsnorm_gemma": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _F, _P, _P]),
     "gdn_in_proj": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_out_proj": (ctypes.c_int, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P]),
@@ -357,6 +358,20 @@ def state_copy(dims: Dims, state, src, dst, conv_state=None):
     _check(lib().gdn_state_copy(ctypes.byref(_cdims(dims)), act, _ptr(state, torch.float32, "state"),
                                 _ptr(conv_state, None, "conv_state"), state.shape[0], _ptr(src, torch.int32, "src"),
                                 _ptr(dst, torch.int32, "dst"), src.shape[0], _stream()), "gdn_state_copy")
+
+
+def check_slots(n_slots: int, slots, out_slots=None) -> torch.Tensor:
+    """Device check of slot tables (gdn_check_slots): int32 flags over
+    slots.ravel() ++ out_slots.ravel(), 1 = padding other than -1,
+    2 = an in-range slot equal to an earlier entry; all zero means valid."""
+    s = slots.reshape(-1)
+    o = None if out_slots is None else out_slots.reshape(-1)
+    n, n_out = s.numel(), 0 if o is None else o.numel()
+    flags = torch.empty(n + n_out, dtype=torch.int32, device=slots.device)
+    _check(lib().gdn_check_slots(n_slots, _ptr(s, torch.int32, "slots"), n,
+                                 _ptr(o, torch.int32, "out_slots") if n_out else None, n_out,
+                                 _ptr(flags, torch.int32, "flags"), _stream()), "gdn_check_slots")
+    return flags
 
 
 def rmsnorm_gemma(x, w, eps: float = 1e-6, out=None):

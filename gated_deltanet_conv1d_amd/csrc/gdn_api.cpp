@@ -308,4 +308,15 @@ int gdn_state_copy(const gdn_dims* dims, int32_t act, float* state, void* conv_s
   return from_hip(gdn::launch_state_copy(a, (hipStream_t)stream));
 }
 
+int gdn_check_slots(int32_t n_slots, const int32_t* slots, int32_t n, const int32_t* out_slots, int32_t n_out,
+                    int32_t* flags, void* stream) {
+  if (n_slots < 0 || n < 0 || n_out < 0) return GDN_ERR_SHAPE;
+  if (n + (int64_t)n_out == 0) return GDN_OK;
+  GDN_TRY(need(flags));
+  if (n > 0) GDN_TRY(need(slots));
+  if (n_out > 0) GDN_TRY(need(out_slots));
+  gdn::SlotCheckArgs a{n_slots, slots, n, out_slots, n_out, flags};
+  return from_hip(gdn::launch_slot_check(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

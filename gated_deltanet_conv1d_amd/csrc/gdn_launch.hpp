@@ -71,6 +71,16 @@ struct StateCopyArgs {
 };
 hipError_t launch_state_copy(const StateCopyArgs& a, hipStream_t st);
 
+struct SlotCheckArgs {
+  int32_t n_slots;
+  const int32_t* slots;
+  int32_t n;
+  const int32_t* out_slots;
+  int32_t n_out;
+  int32_t* flags;
+};
+hipError_t launch_slot_check(const SlotCheckArgs& a, hipStream_t st);
+
 struct RecurrentArgs {
   Shape s;
   bool bf16;

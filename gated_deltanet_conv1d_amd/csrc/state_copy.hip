@@ -53,7 +53,38 @@ __global__ __launch_bounds__(kThreads) void state_copy_kernel(
   }
 }
 
+// Slot-table check: entry i of the list slots ++ out_slots gets flags[i] =
+// 1 if it is neither -1 nor a slot in [0, n_slots) (padding by another
+// value), | 2 if it is a slot in [0, n_slots) equal to an earlier entry of
+// the list.  One thread per entry scans the entries before it (a debugging
+// aid: quadratic in the list length, which is a few thousand at most).
+__global__ __launch_bounds__(kThreads) void slot_check_kernel(int32_t n_slots, const int32_t* __restrict__ slots,
+                                                              int32_t n, const int32_t* __restrict__ out_slots,
+                                                              int32_t n_out, int32_t* __restrict__ flags) {
+  const int64_t total = (int64_t)n + n_out;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int32_t v = i < n ? slots[i] : out_slots[i - n];
+    int32_t f = (v < -1 || v >= n_slots) ? 1 : 0;
+    if (v >= 0 && v < n_slots)
+      for (int64_t j = 0; j < i; ++j)
+        if ((j < n ? slots[j] : out_slots[j - n]) == v) {
+          f |= 2;
+          break;
+        }
+    flags[i] = f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_slot_check(const SlotCheckArgs& a, hipStream_t st) {
+  const int64_t total = (int64_t)a.n + a.n_out;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(slot_check_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(kThreads), 0, st,
+                     a.n_slots, a.slots, a.n, a.out_slots, a.n_out, a.flags);
+  return hipGetLastError();
+}
 
 hipError_t launch_state_copy(const StateCopyArgs& a, hipStream_t st) {
   if (a.n == 0) return hipSuccess;

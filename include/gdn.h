@@ -296,6 +296,23 @@ int gdn_out_proj(const gdn_dims* dims, int32_t act, int64_t t_total, int32_t hid
 int gdn_state_copy(const gdn_dims* dims, int32_t act, float* state, void* conv_state, int32_t n_slots,
                    const int32_t* src, const int32_t* dst, int32_t n, void* stream);
 
+/*
+ * gdn_check_slots -- a debugging check of a call's slot tables, on the device
+ * (the calls above cannot check them without a host sync: an entry used twice
+ * races, see the conventions).  Over the list L = slots[0..n) followed by
+ * out_slots[0..n_out), writes for each entry i
+ *   flags[i] = (L[i] < -1 || L[i] >= n_slots ? 1 : 0)        padding other than -1
+ *            | (0 <= L[i] < n_slots and L[i] == L[j] for some j < i ? 2 : 0)
+ * so an all-zero flags array means every entry is -1 or a distinct in-range
+ * slot.  For gdn_prefill / gdn_decode pass the call's slots and out_slots;
+ * for gdn_state_copy pass dst, then src if sources must also be distinct.
+ * O((n + n_out)^2) work on one stream; intended for tests and debugging.
+ *   slots int32 [n];  out_slots int32 [n_out] (NULL when n_out == 0)
+ *   flags int32 [n + n_out]   (device, written)
+ */
+int gdn_check_slots(int32_t n_slots, const int32_t* slots, int32_t n, const int32_t* out_slots, int32_t n_out,
+                    int32_t* flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -247,6 +247,18 @@ static void block_checks() {
         stub::last.proj.n == 2048 && stub::last.proj.residual == P(3) && stub::last.proj.ld_res == 2048);
 }
 
+static void slot_checks() {
+  reset();
+  CHECK(gdn_check_slots(-1, I(1), 4, nullptr, 0, reinterpret_cast<int32_t*>(P(2)), nullptr) == GDN_ERR_SHAPE);
+  CHECK(gdn_check_slots(8, I(1), -4, nullptr, 0, reinterpret_cast<int32_t*>(P(2)), nullptr) == GDN_ERR_SHAPE);
+  CHECK(gdn_check_slots(8, I(1), 4, nullptr, 3, reinterpret_cast<int32_t*>(P(2)), nullptr) == GDN_ERR_NULL);
+  CHECK(gdn_check_slots(8, I(1), 4, nullptr, 0, nullptr, nullptr) == GDN_ERR_NULL);
+  CHECK(gdn_check_slots(8, nullptr, 0, nullptr, 0, nullptr, nullptr) == GDN_OK && !stub::last.which);
+  CHECK(gdn_check_slots(8, I(1), 4, I(3), 12, reinterpret_cast<int32_t*>(P(2)), nullptr) == GDN_OK);
+  CHECK(launched("launch_slot_check") && stub::last.slot_check.n == 4 && stub::last.slot_check.n_out == 12 &&
+        stub::last.slot_check.out_slots == I(3) && stub::last.slot_check.n_slots == 8);
+}
+
 static void status_checks() {
   const int codes[] = {GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE,
                        GDN_ERR_HIP, GDN_ERR_ALIGN, GDN_ERR_TOO_LARGE, 12345, -999};
@@ -265,6 +277,7 @@ int main() {
   prefill_checks();
   decode_checks();
   block_checks();
+  slot_checks();
   status_checks();
   std::printf("host API checks: %d run, %d failed\n", n_checks, n_failed);
   return n_failed ? 1 : 0;

@@ -29,6 +29,7 @@ GDN_STUB(launch_chunk_split, ChunkArgs, chunk)
 GDN_STUB(launch_prefill_fused, ChunkArgs, chunk)
 GDN_STUB(launch_gemma_norm, GemmaNormArgs, norm)
 GDN_STUB(launch_proj, ProjArgs, proj)
+GDN_STUB(launch_slot_check, SlotCheckArgs, slot_check)
 #undef GDN_STUB
 
 bool decode_supported(const Shape& s) { return s.h_v == s.h_k || s.h_v == 2 * s.h_k; }

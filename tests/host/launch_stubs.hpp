@@ -14,6 +14,7 @@ struct Record {
   gdn::ChunkArgs chunk{};
   gdn::GemmaNormArgs norm{};
   gdn::ProjArgs proj{};
+  gdn::SlotCheckArgs slot_check{};
 };
 extern Record last;               // the most recent launch (which == nullptr: none)
 extern hipError_t next_result;    // what the next launches return

@@ -193,3 +193,44 @@ def test_block_footprint(T):
     torch.cuda.synchronize()
     for t in (xn, qkv, z, b, a, y):
         assert t.guard_ok() and t.unwritten() == 0
+
+
+def _slot_flags(n_slots, lst):
+    seen, out = set(), []
+    for v in lst:
+        f = 1 if (v < -1 or v >= n_slots) else 0
+        if 0 <= v < n_slots:
+            f |= 2 if v in seen else 0
+            seen.add(v)
+        out.append(f)
+    return np.array(out, np.int32)
+
+
+@pytest.mark.parametrize("case", ["valid", "faulty", "large", "empty"])
+def test_check_slots(case):
+    """gdn_check_slots flags padding other than -1 and repeated in-range slots,
+    exactly as a set scan over the concatenated list does."""
+    rng = np.random.default_rng(54)
+    n_slots = 640
+    if case == "valid":
+        perm = rng.permutation(n_slots).astype(np.int32)
+        slots, out = perm[:128].copy(), perm[128:640].reshape(128, 4).copy()
+        slots[[3, 70]] = -1
+        out[5, 2] = -1
+    elif case == "faulty":
+        slots = np.array([4, 9, 4, -1, -1, 640, -7, 12], np.int32)
+        out = np.array([[9, 13], [12, 2 ** 30], [13, -1]], np.int32)
+    elif case == "large":
+        slots = rng.integers(-3, n_slots + 3, 1024).astype(np.int32)
+        out = rng.integers(-3, n_slots + 3, (1024, 4)).astype(np.int32)
+    else:
+        slots, out = np.zeros(0, np.int32), None
+    flags = gdn.check_slots(n_slots, i32(slots), None if out is None else i32(out))
+    torch.cuda.synchronize()
+    ref = _slot_flags(n_slots, np.concatenate([slots.ravel()] + ([] if out is None else [out.ravel()])).tolist())
+    got = flags.cpu().numpy()
+    assert np.array_equal(got, ref), np.nonzero(got != ref)
+    if case == "valid":
+        assert not got.any()
+    if case == "faulty":
+        assert got.tolist() == [0, 0, 2, 0, 0, 1, 1, 0, 2, 0, 2, 1, 2, 0]
