@@ -84,6 +84,7 @@ struct ProjDev {
   int64_t seg_ld[4];
   const bf16* res;
   int64_t ld_res;
+  int n_begin;  // first output column of this launch (its tiles cover [n_begin, n))
   int tiles_m, tiles_n, per_xcd, group_m;
 };
 
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const int mt = grp * p.group_m + within % gm;
   const int nt = within / gm;
   const int64_t m0 = (int64_t)mt * BM;
-  const int n0 = nt * BN;
+  const int n0 = p.n_begin + nt * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ch = tid & 7, r0 = tid >> 3;
@@ -287,7 +288,7 @@ void proj_lds_kernel(ProjDev p) {
   const int mt = grp * p.group_m + within % gm;
   const int nt = within / gm;
   const int64_t m0 = (int64_t)mt * BM;
-  const int n0 = nt * BN;
+  const int n0 = p.n_begin + nt * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane >> 3;
@@ -360,7 +361,7 @@ void proj_lds_kernel(ProjDev p) {
 template <int BM, int BN, int WGM, int WGN, bool RES>
 hipError_t run_proj_lds(ProjDev p, hipStream_t st) {
   p.tiles_m = (int)((p.m + BM - 1) / BM);
-  p.tiles_n = (p.n + BN - 1) / BN;
+  p.tiles_n = (p.n - p.n_begin + BN - 1) / BN;
   p.group_m = 4;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   p.per_xcd = (int)((tiles + 7) / 8);
@@ -372,7 +373,7 @@ hipError_t run_proj_lds(ProjDev p, hipStream_t st) {
 template <int BM, int BN, int WGM, int WGN, int OCC, bool VEC, bool RES>
 hipError_t run_proj(ProjDev p, hipStream_t st) {
   p.tiles_m = (int)((p.m + BM - 1) / BM);
-  p.tiles_n = (p.n + BN - 1) / BN;
+  p.tiles_n = (p.n - p.n_begin + BN - 1) / BN;
   p.group_m = 4;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   p.per_xcd = (int)((tiles + 7) / 8);
@@ -425,8 +426,18 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
   // 64 x 128 tiles and out_proj 64 x 32.
   const bool lds = vec && a.k % kBK == 0;
   const bool res = a.residual != nullptr;
-  if (lds && !res && a.m >= 1024 && tile_count(a.m, a.n, 256, 256) >= 512)
-    return run_proj_lds<256, 256, 2, 4, false>(p, st);
+  if (lds && !res && a.m >= 1024 && tile_count(a.m, a.n, 256, 256) >= 512) {
+    // A narrow last column tile (in_proj's 2 h_v columns of b and a past
+    // 48 tiles of 256) would cost a whole round of 256 x 256 tiles on its
+    // own: those columns go to a second launch of small register-staged tiles.
+    const int n_full = a.n / 256 * 256;
+    if (n_full == a.n || a.n - n_full > 128) return run_proj_lds<256, 256, 2, 4, false>(p, st);
+    ProjDev rest = p;
+    p.n = n_full;
+    if (hipError_t e = run_proj_lds<256, 256, 2, 4, false>(p, st); e != hipSuccess) return e;
+    rest.n_begin = n_full;
+    return run_proj<64, 32, 2, 2, 2, true, false>(rest, st);
+  }
 #define GDN_PROJ(BM_, BN_, WGM_, WGN_)                                                              \
   do {                                                                                               \
     if (vec)                                                                                         \
