@@ -162,8 +162,10 @@ PREFILL_KERNELS = ("void split::chunk_prep_kernel<__bf16, __bf16, 128, 64, true,
 DECODE_KERNEL = "void decode_fused_kernel<__bf16, 128, 2, 4, false, true, true>"
 MTP_KERNEL = "void decode_fused_kernel<__bf16, 128, 2, 4, true, true, false>"
 # the layer's projection kernels at 4096 tokens (in_proj_qkvz/ba, out_proj with the residual)
-IN_PROJ_KERNEL = "void proj_lds_kernel<256, 256, 2, 4, false>"
-OUT_PROJ_KERNEL = "void proj_kernel<128, 128, 2, 2, 2, true, true>"
+# in_proj at 4096 rows: 48 column tiles of 256 x 256 straight into LDS, then
+# the 64-wide last tile (b and a) as small register-staged tiles
+IN_PROJ_KERNELS = ("void proj_lds_kernel<256, 256, 2, 4, false>", "void proj_kernel<64, 32, 2, 2, 2, true, false>")
+OUT_PROJ_KERNELS = ("void proj_kernel<128, 128, 2, 2, 2, true, true>",)
 
 
 def counter_mfma(workload: str, kernels) -> dict | None:
@@ -788,18 +790,18 @@ def bench_layer(args, torch, gdn, gi):
     lib_in, lib_out = lib_gemm(c["xn"], w_in), lib_gemm(c["o"].view(T, vd), wts.w_out)
     fl_in, fl_out = 2.0 * T * hidden * n_in, 2.0 * T * vd * hidden
     tf = lambda fl, t: fl / (t * 1e-3) / 1e12
-    proj = lambda fl, t, lib, kern: {"kernel": kern, "algorithmic_flops": fl, "launch_ms": t,
-                                     "achieved_tflops": round(tf(fl, t["mean"]), 1), "peak_tflops": BF16_PEAK_TFLOPS,
-                                     "frac": round(tf(fl, t["mean"]) / BF16_PEAK_TFLOPS, 4),
-                                     "traffic": counter_traffic("layer_4096", (kern,)),
-                                     "counters": counter_mfma("layer_4096", (kern,)),
+    proj = lambda fl, t, lib, kerns: {"kernels": list(kerns), "algorithmic_flops": fl, "launch_ms": t,
+                                      "achieved_tflops": round(tf(fl, t["mean"]), 1), "peak_tflops": BF16_PEAK_TFLOPS,
+                                      "frac": round(tf(fl, t["mean"]) / BF16_PEAK_TFLOPS, 4),
+                                      "traffic": counter_traffic("layer_4096", kerns),
+                                      "counters": counter_mfma("layer_4096", kerns),
                                      "torch_f_linear_ms": round(lib, 4), "torch_f_linear_tflops": round(tf(fl, lib), 1)}
     prefill_row = {
         "workload": f"layer_prefill_single_{T}", "hidden": hidden, "calls": "gdn_rmsnorm_gemma, gdn_in_proj, "
         "gdn_prefill, gdn_out_proj (+ residual)", "graph_ms_per_step": round(ms_step, 4),
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "kernels_ms": {"gdn_rmsnorm_gemma": t_norm, "gdn_in_proj": t_in, "gdn_prefill": t_pre, "gdn_out_proj": t_out},
-        "in_proj": proj(fl_in, t_in, lib_in, IN_PROJ_KERNEL), "out_proj": proj(fl_out, t_out, lib_out, OUT_PROJ_KERNEL),
+        "in_proj": proj(fl_in, t_in, lib_in, IN_PROJ_KERNELS), "out_proj": proj(fl_out, t_out, lib_out, OUT_PROJ_KERNELS),
         "rmsnorm_gbs": round(2.0 * T * hidden * 2 / (t_norm["mean"] * 1e-3) / 1e9, 1)}
     del copies, graphs
     torch.cuda.empty_cache()
