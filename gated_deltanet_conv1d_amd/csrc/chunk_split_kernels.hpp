@@ -1318,6 +1318,7 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_chain_out_kernel(
   __shared__ __attribute__((aligned(16))) Op sH[NPD][NT][64 * 8];  // h, pairs
   __shared__ __attribute__((aligned(16))) Op sU[CT][NT][64 * 4];   // diag(f_k) U, accumulator layout
   __shared__ __attribute__((aligned(16))) Op sUo[CT][NT][64 * 4];  // U
+  __shared__ __attribute__((aligned(16))) float sNW[D];             // norm weights
   // chain index: the kt_group V heads of a QK head on consecutive slots of one XCD
   const int xcd = blockIdx.x & 7, qb = blockIdx.x >> 3;
   const int64_t grp = ((int64_t)(qb / kt_group) * 8 + xcd) * kt_group + qb % kt_group;
@@ -1403,6 +1404,10 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_chain_out_kernel(
     }
   };
   const FragT zf = zero_frag<Op>();
+  // the norm weights in LDS (read after the first chunk's barriers): a load
+  // of them in the epilogue would wait for the output stores issued before it
+  if (z)
+    for (int e = (int)tid; e < D; e += 64 * MW) sNW[e] = to_f32(norm_w[e]);
   auto step = [&](int s, unsigned char* uc, int ls, const unsigned char* ul, int k) {
     int pc = 0;
     auto next_load = [&]() {
@@ -1524,11 +1529,10 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_chain_out_kernel(
         const float rstd = fast_rsq(ss * (1.0f / D) + norm_eps);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          float w[4], zz[4], v[4];
-          load4(norm_w + 16 * j + 4 * g4, w);
+          float zz[4], v[4];
           zr[j].to_f32(zz);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = Oacc[j][e] * rstd * w[e] * fast_silu(zz[e]);
+          for (int e = 0; e < 4; ++e) v[e] = Oacc[j][e] * rstd * sNW[16 * j + 4 * g4 + e] * fast_silu(zz[e]);
           if (live) store4(o + (c0 + row) * o_ld + h * D + 16 * j + 4 * g4, v);
         }
       } else {
