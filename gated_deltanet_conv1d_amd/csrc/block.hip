@@ -358,6 +358,132 @@ void proj_lds_kernel(ProjDev p) {
   store_tile<true, RES, FN, FM>(p, m0 + wm * WM, n0 + wn * WN, rl, g, acc);
 }
 
+// Few rows (decode): the contraction of a BM x BN tile is split over k
+// between the four waves (wave w takes the w-th quarter of k), so each wave's
+// serial loop is a quarter as long; every wave holds the whole tile's
+// accumulators and reads its MFMA fragments straight from global memory into
+// registers, PD 64-deep stages in flight, with no LDS staging and no barrier
+// in the loop.  The four partial tiles are then summed through LDS in wave
+// order and stored as the other kernels store theirs.  k is a multiple of 256.
+template <int BM, int BN, int PD, bool RES>
+__global__ __launch_bounds__(256) void proj_splitk_kernel(ProjDev p) {
+  constexpr int FM = BM / 16, FN = BN / 16, T = FM * FN;
+  static_assert(PD >= 2, "stages");
+  __shared__ __attribute__((aligned(16))) f32x4 red[4][T][64];
+
+  const int b = blockIdx.x;
+  const int64_t lt = (int64_t)(b & 7) * p.per_xcd + (b >> 3);
+  if (lt >= (int64_t)p.tiles_m * p.tiles_n) return;
+  const int64_t span = (int64_t)p.group_m * p.tiles_n;
+  const int grp = (int)(lt / span);
+  const int gm = min(p.group_m, p.tiles_m - grp * p.group_m);
+  const int within = (int)(lt - grp * span);
+  const int mt = grp * p.group_m + within % gm;
+  const int nt = within / gm;
+  const int64_t m0 = (int64_t)mt * BM;
+  const int n0 = p.n_begin + nt * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rl = lane & 15, g = lane >> 4;
+  // this lane's rows (clamped to the last valid one: in bounds, never stored)
+  const bf16* const xbase = p.x;
+  const bf16* const w0 = p.w0;
+  const bf16* const w1 = p.w1;
+  const int kq = p.k / 4;                            // this wave's k range [wave kq, wave kq + kq)
+  const bf16* xr[FM];
+  const bf16* wr[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = min(m0 + 16 * i + rl, p.m - 1);
+    xr[i] = xbase + row * p.ldx + wave * kq + 8 * g;
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = min(n0 + 16 * j + rl, p.n - 1);
+    wr[j] = (n < p.n_w0 ? w0 + (int64_t)n * p.k : w1 + (int64_t)(n - p.n_w0) * p.k) + wave * kq + 8 * g;
+  }
+  // stage st, half kk: logical chunk kk * 4 + g of the 64-deep step, as in the
+  // LDS-staged kernels
+  bf16x8 fx[PD][2][FM], fw[PD][2][FN];
+  auto load = [&](int s, int st) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int k = st * kBK + kk * 32;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fx[s][kk][i] = *reinterpret_cast<const bf16x8*>(xr[i] + k);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fw[s][kk][j] = *reinterpret_cast<const bf16x8*>(wr[j] + k);
+    }
+  };
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int ns = kq / kBK;
+#pragma unroll
+  for (int s = 0; s < PD - 1; ++s)
+    if (s < ns) load(s, s);
+  for (int st0 = 0; st0 < ns; st0 += PD) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      const int st = st0 + s;
+      if (st < ns) {  // (uniform)
+        if (st + PD - 1 < ns) load((s + PD - 1) % PD, st + PD - 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[s][kk][j], fx[s][kk][i], acc[j][i], 0, 0, 0);
+      }
+    }
+  }
+  // partial tiles -> LDS; wave w sums tiles w, w + 4, ... over the waves in order
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) red[wave][j * FM + i][lane] = acc[j][i];
+  __syncthreads();
+  for (int t = wave; t < T; t += 4) {
+    f32x4 v = red[0][t][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const f32x4 q = red[w][t][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += q[e];
+    }
+    const int j = t / FM, i = t % FM;
+    const int n = n0 + 16 * j + 4 * g;
+    const int64_t m = m0 + 16 * i + rl;
+    if (n >= p.n || m >= p.m) continue;
+    const int sg = seg_of(p, n);
+    float o0 = v[0], o1 = v[1], o2 = v[2], o3 = v[3];
+    if constexpr (RES) {
+      const uint2 r = *reinterpret_cast<const uint2*>(p.res + m * p.ld_res + n);
+      o0 += bf_lo(r.x);
+      o1 += bf_hi(r.x);
+      o2 += bf_lo(r.y);
+      o3 += bf_hi(r.y);
+    }
+    const bf16x4 o = {(bf16)o0, (bf16)o1, (bf16)o2, (bf16)o3};
+    *reinterpret_cast<bf16x4*>(p.seg_ptr[sg] + (n - p.seg_begin[sg]) + m * p.seg_ld[sg]) = o;
+  }
+}
+
+template <int BM, int BN, int PD, bool RES>
+hipError_t run_proj_splitk(ProjDev p, hipStream_t st) {
+  p.tiles_m = (int)((p.m + BM - 1) / BM);
+  p.tiles_n = (p.n - p.n_begin + BN - 1) / BN;
+  p.group_m = 4;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  p.per_xcd = (int)((tiles + 7) / 8);
+  hipLaunchKernelGGL((proj_splitk_kernel<BM, BN, PD, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)), dim3(256), 0,
+                     st, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN, bool RES>
 hipError_t run_proj_lds(ProjDev p, hipStream_t st) {
   p.tiles_m = (int)((p.m + BM - 1) / BM);
@@ -438,6 +564,11 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
     rest.n_begin = n_full;
     return run_proj<64, 32, 2, 2, 2, true, false>(rest, st);
   }
+  // few rows and few columns (a decode step's out_proj): k split over the
+  // waves; with many columns (in_proj) the LDS-staged tiles below share each
+  // weight stage between the waves and run faster
+  if (vec && a.k % 256 == 0 && a.m <= 512 && tile_count(a.m, a.n, 64, 128) < 256)
+    return res ? run_proj_splitk<64, 32, 3, true>(p, st) : run_proj_splitk<64, 32, 3, false>(p, st);
 #define GDN_PROJ(BM_, BN_, WGM_, WGN_)                                                              \
   do {                                                                                               \
     if (vec)                                                                                         \
