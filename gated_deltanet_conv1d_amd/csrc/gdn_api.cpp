@@ -69,7 +69,7 @@ const char* gdn_status_string(int status) {
     case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
     case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: invalid or inconsistent size";
     case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown activation dtype";
-    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: size not supported by this build";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: size not supported by this library";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: a kernel launch failed";
     case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer not 16-byte aligned";
