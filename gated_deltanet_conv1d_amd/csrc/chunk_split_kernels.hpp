@@ -83,13 +83,15 @@ struct Cfg {
   static constexpr int HALO_OFF = FK_OFF + C * 4;
   static constexpr int UNIT = (HALO_OFF + D * (kMaxConvW - 1) * (int)sizeof(Op) + 255) / 256 * 256;
   // output kernel LDS: raw q rows, then (over them) the fp32 O tile, row-major
-  static constexpr int LD_Q = D + 16;
+  static constexpr int LD_Q = D + 8;
   static constexpr int LD_O = D + 4;
   static constexpr int OUT_BYTES = C * LD_O * 4 > C * LD_Q * (int)sizeof(Op) ? C * LD_O * 4 : C * LD_Q * (int)sizeof(Op);
-  // prep kernel LDS.  Row strides are padded so the 8-byte fragment reads of
-  // a wave (16 rows x 4 column groups) hit distinct banks.
-  static constexpr int LDR = D + 16;   // raw k rows (elements)
-  static constexpr int LDA = C + 16;   // fp32 A, then T in place
+  // prep kernel LDS.  Row strides are padded so that the fragment reads of a
+  // wave (16 rows x 4 column groups) spread over the banks: 68 words per row
+  // of k / q / v (the 16 rows start 4 banks apart), 68 words per row of A
+  // and T.
+  static constexpr int LDR = D + 8;    // raw k rows (elements)
+  static constexpr int LDA = C + 4;    // fp32 A, then T in place
   static constexpr int LDT = C + 8;    // T diag(b e^G r_k) and T diag(b), operand type
 };
 
@@ -1720,8 +1722,14 @@ __global__ __launch_bounds__(kThreads<D>) __attribute__((amdgpu_waves_per_eu(3))
     const int r = (int)(tid / LPR) + k * RPP;
     if (r >= C) break;  // uniform over the LPR lanes of a row
     float v[8];
-    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(sO + r * LD_O + e0);
-    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(sO + r * LD_O + e0 + 4);
+    // (lanes 8..15 of a row take their second half first: the 16 lanes' first
+    // reads then cover 64 distinct banks)
+    const bool hi_first = (tid & 8) != 0;
+    const float4 first = *reinterpret_cast<const float4*>(sO + r * LD_O + e0 + (hi_first ? 4 : 0));
+    const float4 second = *reinterpret_cast<const float4*>(sO + r * LD_O + e0 + (hi_first ? 0 : 4));
+    const float4 lo4 = hi_first ? second : first, hi4 = hi_first ? first : second;
+    v[0] = lo4.x; v[1] = lo4.y; v[2] = lo4.z; v[3] = lo4.w;
+    v[4] = hi4.x; v[5] = hi4.y; v[6] = hi4.z; v[7] = hi4.w;
     const bool live = r < nvalid;
     const int64_t off = (c0 + r) * o_ld + h * D + e0;
     if (z) {
