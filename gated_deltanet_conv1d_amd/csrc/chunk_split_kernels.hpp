@@ -161,11 +161,23 @@ __device__ __forceinline__ int32_t first_chunk(const int32_t* __restrict__ cstar
   return __builtin_amdgcn_readfirstlane(__shfl(seq_scan<C>(cu, n_seq, t_total).excl, n));
 }
 
-// cstart[i] = sum over j < i of ceil(len_j / C), for i = 0..n_seq.  One block.
+// cstart[i] = sum over j < i of ceil(len_j / C), for i = 0..n_seq, and
+// order[0..n_seq): the sequences by chunk count, longest first (ties by
+// index; index order above kOrderSeqs sequences).  One block.
+//
+// The chain with output runs one workgroup per (sequence, V head) for the
+// whole sequence and takes its sequence from order: with lengths spread over a
+// batch, dispatching the long chains first keeps the last round of workgroups
+// from being one long chain started late (on 64 sequences of 128..8192
+// tokens, 256 concurrent chains: 580 chunk steps per slot in index order, 537
+// longest first, 534 ideal).
+constexpr int kOrderSeqs = 1024;
 static __global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t* __restrict__ cu, int32_t n_seq,
                                                            int64_t t_total, int32_t chunk,
-                                                           int32_t* __restrict__ cstart) {
+                                                           int32_t* __restrict__ cstart,
+                                                           int32_t* __restrict__ order) {
   __shared__ int32_t part[1024];
+  __shared__ int32_t cnt[kOrderSeqs];
   const int tid = threadIdx.x;
   const int per = (n_seq + 1023) / 1024;
   const int i0 = min(tid * per, n_seq), i1 = min(i0 + per, n_seq);
@@ -173,10 +185,25 @@ static __global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t*
   for (int i = i0; i < i1; ++i) {
     const int64_t lo = min((int64_t)cu[i], t_total);
     const int64_t hi = min(max((int64_t)cu[i + 1], lo), t_total);
-    s += (int32_t)((hi - lo + chunk - 1) / chunk);
+    const int32_t c = (int32_t)((hi - lo + chunk - 1) / chunk);
+    if (n_seq <= kOrderSeqs) cnt[i] = c;  // (then i == tid)
+    s += c;
   }
   part[tid] = s;
   __syncthreads();
+  if (n_seq <= kOrderSeqs) {
+    if (tid < n_seq) {
+      const int32_t mine = cnt[tid];
+      int32_t rank = 0;
+      for (int j = 0; j < n_seq; ++j) {
+        const int32_t c = cnt[j];
+        rank += c > mine || (c == mine && j < tid);
+      }
+      order[rank] = tid;
+    }
+  } else {
+    for (int i = i0; i < i1; ++i) order[i] = i;
+  }
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
     const int32_t v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
@@ -1303,9 +1330,9 @@ __device__ __forceinline__ void store4(float* p, const float* v) {
 template <typename T, typename Op, int D, int C, int PD>
 __global__ __launch_bounds__(kChainThreads<D>) void chunk_chain_out_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ has_init,
-    const int32_t* __restrict__ cstart, unsigned char* __restrict__ ws, float* __restrict__ state,
-    int32_t n_slots, T* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v, int32_t kt_group,
-    const T* __restrict__ z, const T* __restrict__ norm_w, float norm_eps, const Op* __restrict__ conv_x,
+    const int32_t* __restrict__ cstart, const int32_t* __restrict__ order, unsigned char* __restrict__ ws,
+    float* __restrict__ state, int32_t n_slots, T* __restrict__ o, int64_t t_total, int32_t n_seq, int32_t h_v,
+    int32_t kt_group, const T* __restrict__ z, const T* __restrict__ norm_w, float norm_eps, const Op* __restrict__ conv_x,
     Op* __restrict__ conv_state, int32_t c_ch, int32_t conv_w) {
   static_assert(sizeof(T) == sizeof(Op), "outputs in the activation type");
   using K = Cfg<Op, D, C>;
@@ -1325,7 +1352,8 @@ __global__ __launch_bounds__(kChainThreads<D>) void chunk_chain_out_kernel(
   const int xcd = blockIdx.x & 7, qb = blockIdx.x >> 3;
   const int64_t grp = ((int64_t)(qb / kt_group) * 8 + xcd) * kt_group + qb % kt_group;
   if (grp >= (int64_t)n_seq * h_v) return;
-  const int n = (int)(grp / h_v), h = (int)(grp % h_v);
+  // sequences longest first when the chunk index gives their order
+  const int n = order ? order[grp / h_v] : (int)(grp / h_v), h = (int)(grp % h_v);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const uint32_t tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int64_t lo = min((int64_t)cu[n], t_total);
@@ -1768,8 +1796,9 @@ hipError_t launch_chain_out(const ChunkArgs& a, const int32_t* cstart, unsigned 
   const int g = a.s.h_v / a.s.h_k;
   const int64_t chains = (int64_t)a.n_seq * a.s.h_v;
   const int64_t blocks = (chains + 8 * g - 1) / (8 * g) * 8 * g;
+  const int32_t* order = cstart ? cstart + a.n_seq + 1 : nullptr;
   hipLaunchKernelGGL((chunk_chain_out_kernel<T, Op, D, C, PD>), dim3((unsigned)blocks), dim3(kChainThreads<D>), 0, st,
-                     a.cu_seqlens, a.slots, a.has_init, cstart, units, a.state, a.n_slots, (T*)a.o, a.t_total,
+                     a.cu_seqlens, a.slots, a.has_init, cstart, order, units, a.state, a.n_slots, (T*)a.o, a.t_total,
                      a.n_seq, a.s.h_v, g, (const T*)a.z, (const T*)a.norm_w, a.norm_eps, conv_x,
                      (Op*)const_cast<void*>(a.conv_state), a.s.c_ch(), a.s.conv_w);
   return hipGetLastError();
@@ -1790,8 +1819,8 @@ hipError_t launch_shape(const ChunkArgs& a, int64_t groups, const int32_t* cstar
   else return launch_chain<Op, D, C, (NTW >= 8 ? 4 : NTW), PD>(a, groups, cstart, units, conv_x, st);
 }
 
-// workspace: [chunk index][units]
-inline size_t idx_bytes(int32_t n_seq) { return (((size_t)n_seq + 1) * 4 + 255) / 256 * 256; }
+// workspace: [chunk index: cstart (n_seq + 1), order (n_seq)][units]
+inline size_t idx_bytes(int32_t n_seq) { return ((2 * (size_t)n_seq + 1) * 4 + 255) / 256 * 256; }
 
 template <typename T, typename Op, int D, int C>
 size_t ws_bytes(int32_t n_seq, int64_t t_total, int32_t h_v) {
@@ -1814,7 +1843,7 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   unsigned char* units = reinterpret_cast<unsigned char*>(a.workspace) + idx_bytes(a.n_seq);
   if (cstart) {
     hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.n_seq, a.t_total, (int32_t)C,
-                       cstart);
+                       cstart, cstart + a.n_seq + 1);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t max_chunks = a.t_total / C + a.n_seq;
