@@ -1,9 +1,10 @@
 """GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
 
-Sizes: small multi-chunk cases with ragged tails are checked element by
-element; the full-size workloads are checked element by element where the
-oracle finishes in seconds (single 4096-token prefill, decode, MTP) and on
-sampled sequences/heads otherwise (the ~271k-token varlen batch).
+Sizes: small multi-chunk cases with ragged tails and the full-size workloads
+(single 4096-token prefill, decode, MTP and the ~271k-token varlen batch) are
+all checked element by element: every output row, every final state, every
+conv window.  The varlen batch's oracle runs on a process pool over the
+host's cores.
 """
 from __future__ import annotations
 
