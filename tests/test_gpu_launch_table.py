@@ -37,7 +37,22 @@ def test_table_row_matches_single_sequence_calls(r):
     n = _n_seq(r)
     lengths = np.random.default_rng(60 + r).integers(40, 200, n)
     log(f"launch table row {r} {ROWS[r]}: {n} sequences, {int(lengths.sum())} tokens")
-    case = gi.varlen_case(seed=60 + r, lengths=lengths, n_slots=n, dims=gi.QWEN3_NEXT)
+    _check_batch_against_single_calls(lengths, 60 + r, ROWS[r][2] >= 8)
+
+
+def test_longest_first_chains_match_single_sequence_calls():
+    """More than 8 sequences: the chunk index kernel runs and the chain with
+    output takes its sequences longest first (ties by index).  Lengths with
+    ties, an empty and a one-token sequence; results as one call each."""
+    lengths = np.array([150, 40, 150, 0, 300, 1, 64, 65, 150, 200, 7, 129])
+    assert len(lengths) * D.h_v > ROWS[-2][0]  # the whole-d_v row
+    log(f"longest-first order: {len(lengths)} sequences, {int(lengths.sum())} tokens")
+    _check_batch_against_single_calls(lengths, 70, True)
+
+
+def _check_batch_against_single_calls(lengths, seed, whole_dv):
+    n = len(lengths)
+    case = gi.varlen_case(seed=seed, lengths=lengths, n_slots=n, dims=gi.QWEN3_NEXT)
     p = case.params
     bf = lambda v: dev(v, torch.bfloat16)
     f32 = lambda v: dev(v, torch.float32)
@@ -54,12 +69,16 @@ def test_table_row_matches_single_sequence_calls(r):
     out_b, ssm_b, conv_b = host_raw(out), ssm_pool.cpu().numpy(), host_raw(conv_pool)
     for i in range(n):
         s = int(case.slots[i])
+        if lengths[i] == 0:  # no tokens: the slot's states stay as they were
+            assert np.array_equal(ssm0[s], ssm_b[s]), f"sequence {i}: state of an empty sequence"
+            assert np.array_equal(host_raw(bf(conv0))[s], conv_b[s]), f"sequence {i}: conv state of an empty sequence"
+            continue
         cp, sp = bf(conv0), f32(ssm0)
         o1 = gdn.prefill(D, bf(xs[i]), *common, bf(a_s[i]), bf(b_s[i]), f32(p.A_log), f32(p.dt_bias),
                          i32([0, len(xs[i])]), i32([s]), cp, sp, u8([1]), 64, 1.0, bf(z_s[i]), bf(p.norm_w))
         torch.cuda.synchronize()
         lo, hi = case.cu_seqlens[i], case.cu_seqlens[i + 1]
-        if ROWS[r][2] >= 8:
+        if whole_dv:
             assert bf16_ulps(host_raw(o1), out_b[lo:hi]) <= 1, f"sequence {i}: output beyond one unit in the last place"
         else:
             assert np.array_equal(host_raw(o1), out_b[lo:hi]), f"sequence {i}: output"
