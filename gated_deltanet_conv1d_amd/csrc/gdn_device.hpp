@@ -184,9 +184,12 @@ __device__ __forceinline__ void mma_k32(f32x4& acc, const bf16x4& a0, const bf16
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 // A lone 16-wide block runs as 16x16x32 with a zero upper half, so every bf16
-// MFMA in a dependent chain has the same shape: chains that mixed 16x16x16 and
-// 16x16x32 bf16 MFMAs on one accumulator gave nondeterministic, wrong results
-// on gfx950 with this toolchain, while each shape alone is exact.
+// MFMA in a dependent chain has the same shape.  For a 16x16x16 product that
+// takes a 16x16x32 product's result as its accumulator (or the reverse), this
+// toolchain emits the two back to back with no wait states on gfx950, and the
+// second reads a stale accumulator: such mixed chains came out wrong and
+// different from run to run, and exact once 16 wait states separated the two.
+// One shape per chain needs no waits (the hardware forwards the accumulator).
 __device__ __forceinline__ void mma_k16(f32x4& acc, const bf16x4& a, const bf16x4& b) {
   const bf16x4 zero = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
   mma_k32(acc, a, zero, b, zero);
