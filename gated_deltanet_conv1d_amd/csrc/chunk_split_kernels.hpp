@@ -32,14 +32,18 @@
 // K'^T U with K' = diag(f_k) K runs as K^T (diag(f_k) U): k enters exactly as
 // the bf16 conv output, and the one rounding is that of the scaled U.
 //
-//   chunk_index_kernel  first global chunk of every sequence (block scan; only
-//                       with more than 8 sequences, else each wave scans)
+//   chunk_index_kernel  first global chunk of every sequence (block scan) and
+//                       the sequences longest first; only with more than 8
+//                       sequences, else each wave scans
 //   chunk_prep_kernel   per (chunk, V head, or both V heads of a QK head when
 //                       h_v = 2 h_k): q/k L2 norm, gates, Gram, T and the
 //                       operand fragments above
 //   chunk_state_kernel  per (sequence, V head, d_v tile): the chunk loop; in
 //                       the single-call prefill also the final conv windows
 //   chunk_out_kernel    per (chunk, V head): O, gated RMSNorm over d_v, store
+//   chunk_chain_out_kernel  many chains: per (sequence, V head), the chunk
+//                       loop over all of d_v that also computes the output
+//                       (then no output pass runs)
 #pragma once
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
