@@ -71,18 +71,26 @@ def round_act(act: str):
 
 def perturbations(act: str):
     """Two activation-precision realisations of a conv output: rounded to the
-    activation type, and rounded after a seeded random relative nudge of half
-    a unit in the last place (a second, equally valid rounding of the same
-    values).  The larger change of the oracle's result under the two is its
-    sensitivity: one realisation alone can understate how far rounding moves
-    an ill-conditioned row."""
+    activation type, and rounded after a seeded random relative nudge (a
+    second, equally valid realisation of the same values).  The larger change
+    of the oracle's result under the two is its sensitivity: one realisation
+    alone can understate how far rounding moves an ill-conditioned row.
+
+    The nudge is the working precision of the path: half a unit in the last
+    place for bf16, whose operand rounding dominates every other error there;
+    for fp32, sqrt(128) 2^-24, the typical relative rounding of a length-128
+    fp32 dot product (the contractions over d_k = 128 run in fp32, and the
+    conv output and gates come from hardware exp2 and reciprocal, several
+    units in the last place from the exact values), so half an fp32 unit
+    would understate what the fp32 arithmetic does to a row that amplifies
+    input perturbations several hundred times."""
     rnd = round_act(act)
-    half_ulp = 2.0 ** -9 if act == "bf16" else 2.0 ** -25
+    nudge = 2.0 ** -9 if act == "bf16" else np.sqrt(128.0) * 2.0 ** -24
 
     def nudged(y):
         y = np.asarray(y, np.float64)
         xi = np.random.default_rng(20251).uniform(-1.0, 1.0, y.shape)
-        return rnd(y * (1.0 + half_ulp * xi))
+        return rnd(y * (1.0 + nudge * xi))
 
     return [rnd, nudged]
 

@@ -369,6 +369,32 @@ def test_many_short_sequences():
     assert torch.equal(out_f, ref[0]) and torch.equal(dp.ssm_pool, ref[1]) and torch.equal(dp.conv_pool, ref[2])
 
 
+def test_many_chains_fp32():
+    """The fp32 mode above 128 chains: the launch table picks the whole-d_v
+    chain, which the fp32 operands do not fit, so the widest split chain runs
+    (with the chunk index, more than 8 sequences).  40 sequences of 0..150
+    tokens at d = 128, chunk 32, 4 V heads (160 chains): every output, state
+    and conv window against the oracle, and both entry points equal."""
+    rng = np.random.default_rng(19)
+    lengths = rng.integers(0, 151, size=40)
+    case = gi.varlen_case(seed=19, dims=gi.Dims(2, 4, 128, 128, 4), act="f32", lengths=lengths, n_slots=48,
+                          chunk=32)
+    assert case.n_seq * case.dims.h_v > 128
+    dp = DevPrefill(case)
+    conv0, ssm0 = dp.conv_pool.clone(), dp.ssm_pool.clone()
+    out, *_ = dp.run()
+    torch.cuda.synchronize()
+    w = compare_prefill(dp, out)
+    log(f"fp32, 160 chains: out [{w['out']}] ssm [{w['ssm']}] conv {w['conv']:.1e}")
+    assert w["out"].ok() and w["ssm"].ok() and w["conv"] == 0.0
+    ref = (out.clone(), dp.ssm_pool.clone(), dp.conv_pool.clone())
+    dp.conv_pool.copy_(conv0)
+    dp.ssm_pool.copy_(ssm0)
+    out_f = dp.run_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, ref[0]) and torch.equal(dp.ssm_pool, ref[1]) and torch.equal(dp.conv_pool, ref[2])
+
+
 def test_state_copy_bitwise_and_skips():
     dims = gdn.Dims(2, 4, 64, 64, 4)
     g = torch.Generator(device="cuda").manual_seed(0)
