@@ -33,9 +33,19 @@ def _capture(fn):
     return graph
 
 
-def test_prefill_graph_replays_match_eager():
+# 4 sequences: no chunk index, the split chain and the output pass; 40 (160
+# chains): the chunk index with the longest-first order and the chain that
+# computes the output itself
+PREFILL_BATCHES = {"4 sequences": [77, 190, 64, 1],
+                   "40 sequences": list(np.random.default_rng(22).integers(0, 101, 40))}
+
+
+@pytest.mark.parametrize("single_call", [False, True])
+@pytest.mark.parametrize("batch", list(PREFILL_BATCHES))
+def test_prefill_graph_replays_match_eager(batch, single_call):
     dims = gi.Dims(2, 4, 128, 128, 4)
-    case = gi.varlen_case(seed=21, dims=dims, lengths=np.array([77, 190, 64, 1]), n_slots=6)
+    lengths = np.array(PREFILL_BATCHES[batch])
+    case = gi.varlen_case(seed=21, dims=dims, lengths=lengths, n_slots=len(lengths) + 2)
     dp = DevPrefill(case)
     d = dp.dims
     T = case.t_total
@@ -44,10 +54,15 @@ def test_prefill_graph_replays_match_eager():
     g = torch.empty((T, d.h_v), dtype=torch.float32, device="cuda")
     beta = torch.empty_like(g)
     o = torch.empty((T, d.h_v, d.d_v), dtype=dp.x.dtype, device="cuda")
-    ws = torch.empty(gdn.chunk_prefill_workspace_size(d, 0, case.n_seq, T, case.chunk), dtype=torch.uint8,
+    ws = torch.empty(max(gdn.chunk_prefill_workspace_size(d, 0, case.n_seq, T, case.chunk),
+                         gdn.prefill_workspace_size(d, 0, case.n_seq, T, case.chunk)), dtype=torch.uint8,
                      device="cuda")
 
     def step():
+        if single_call:
+            gdn.prefill(d, dp.x, dp.conv_w, dp.a, dp.b, dp.A_log, dp.dt_bias, dp.cu, dp.slots, dp.conv_pool,
+                        dp.ssm_pool, dp.has_init, case.chunk, 1.0, dp.z, dp.norm_w, 1e-6, o=o, workspace=ws)
+            return
         gdn.conv1d_fwd(d, dp.x, dp.conv_w, dp.cu, dp.slots, dp.conv_pool, dp.has_init, y=y)
         gdn.gating(dp.a, dp.b, dp.A_log, dp.dt_bias, g=g, beta=beta)
         gdn.chunk_prefill(d, y, g, beta, dp.cu, dp.slots, dp.ssm_pool, dp.has_init, case.chunk, 1.0, dp.z,
