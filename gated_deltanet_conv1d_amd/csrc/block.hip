@@ -96,6 +96,29 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
+// Four 16-byte fragments from LDS, waited for inside the asm block, so their
+// registers hold the data when it ends.  Written in asm for the direct-to-LDS
+// kernel: the compiler cannot tell an LDS read of the current stage from the
+// destinations of the next stage's direct-to-LDS loads, and before such a
+// read it waits for every load in flight (vmcnt 0), which leaves the next
+// stage's loads no MFMA work to overlap.  Stage order is kept by the kernel's
+// own wait and barrier at the top of each stage.
+__device__ __forceinline__ uint32_t lds_addr(const bf16* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16*)p;
+}
+__device__ __forceinline__ void lds_read4(const bf16* p0, const bf16* p1, const bf16* p2, const bf16* p3,
+                                          bf16x8& o0, bf16x8& o1, bf16x8& o2, bf16x8& o3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2)), "v"(lds_addr(p3))
+      : "memory");
+}
+
 // Register-staged kernel: chunk c of row r at c ^ (r % 8).
 __device__ __forceinline__ int swz(int row, int c) { return row * kBK + ((c ^ (row & 7)) << 3); }
 
@@ -273,6 +296,7 @@ void proj_lds_kernel(ProjDev p) {
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
   static_assert(FM * 16 == WM && FN * 16 == WN, "wave tile");
+  static_assert(FM % 4 == 0 && FN % 4 == 0, "fragments read four at a time");
   constexpr int IX = BM / (8 * NW), IW = BN / (8 * NW);  // load instructions per wave per stage
   static_assert(IX * 8 * NW == BM && IW * 8 * NW == BN, "whole load instructions");
   __shared__ __attribute__((aligned(16))) bf16 sx[2][BM * kBK];
@@ -343,15 +367,17 @@ void proj_lds_kernel(ProjDev p) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c = kk * 4 + g;
-      bf16x8 fx[FM];
+      bf16x8 fx[FM], fw[FN];
+      auto xp = [&](int i) { return &cx[swz2(wm * WM + i * 16 + rl, c)]; };
+      auto wp = [&](int j) { return &cw[swz2(wn * WN + j * 16 + rl, c)]; };
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fx[i] = *reinterpret_cast<const bf16x8*>(&cx[swz2(wm * WM + i * 16 + rl, c)]);
+      for (int i = 0; i < FM; i += 4) lds_read4(xp(i), xp(i + 1), xp(i + 2), xp(i + 3), fx[i], fx[i + 1], fx[i + 2], fx[i + 3]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const bf16x8 fw = *reinterpret_cast<const bf16x8*>(&cw[swz2(wn * WN + j * 16 + rl, c)]);
+      for (int j = 0; j < FN; j += 4) lds_read4(wp(j), wp(j + 1), wp(j + 2), wp(j + 3), fw[j], fw[j + 1], fw[j + 2], fw[j + 3]);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fx[i], acc[j][i], 0, 0, 0);
-      }
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx[i], acc[j][i], 0, 0, 0);
     }
   }
 
