@@ -377,9 +377,17 @@ __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int
       for (int k = 0; k < RB; ++k) store8(base + dst[p] + (rb * RB + k) * ldr + 8 * cg, zero);
       continue;
     }
-    // from here every window position lies in [seq_lo - (W-1), c0 + nvalid).
-    // All RB + W - 1 rows are loaded first, unconditionally (an out-of-window
-    // row re-reads row c0, which is always in range), so the loads overlap.
+    // the 8 channels' taps are 8W consecutive weights: W vector loads, issued
+    // before the rows, so that waiting for them does not wait for every row
+    // (loads retire in issue order) and row k's outputs need only rows up to
+    // k + W - 1.  From here every window position lies in
+    // [seq_lo - (W-1), c0 + nvalid).  All RB + W - 1 rows are loaded,
+    // unconditionally (an out-of-window row re-reads row c0, which is always
+    // in range), so the loads overlap.
+    Raw8<T> wr[W], br;
+#pragma unroll
+    for (int j = 0; j < W; ++j) wr[j].load(wt + (int64_t)ch * W + 8 * j);
+    if (bias) br.load(bias + ch);
     constexpr int NR = RB + W - 1;
     const int64_t p0 = c0 + rb * RB - (W - 1);  // position of window row 0
     Raw8<T> raw[NR];
@@ -389,24 +397,17 @@ __device__ __forceinline__ void stage_conv(const ConvIn& ci, int c_ch, const int
       const bool in_x = pos >= ci.seq_lo && pos < c0 + nvalid;
       raw[k].load(x + (in_x ? pos : c0) * c_ch + ch);
     }
-    // the 8 channels' taps are 8W consecutive weights: W vector loads
     float w[W][8], b[8];
     {
       float wf[W * 8];
 #pragma unroll
-      for (int j = 0; j < W; ++j) {
-        Raw8<T> r;
-        r.load(wt + (int64_t)ch * W + 8 * j);
-        r.to_f32(wf + 8 * j);
-      }
+      for (int j = 0; j < W; ++j) wr[j].to_f32(wf + 8 * j);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < W; ++j) w[j][i] = wf[i * W + j];
       if (bias) {
-        Raw8<T> r;
-        r.load(bias + ch);
-        r.to_f32(b);
+        br.to_f32(b);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) b[i] = 0.0f;
