@@ -441,9 +441,17 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(ONE && 
     for (int k = 0; k < FL::CPT; ++k) {
       const int lc = tid + k * FL::THREADS;
       if (lc < NCH) {
-        for (int tt = 0; tt < nt; ++tt) {
+        // the block's inputs of this channel, all requested before the first
+        // is used (one memory latency, not one per token)
+        T xin[FL::TB];
+#pragma unroll
+        for (int tt = 0; tt < FL::TB; ++tt)
+          if (tt < nt) xin[tt] = x[((int64_t)i * t_step + t0 + tt) * c_ch + ch[k]];
+#pragma unroll
+        for (int tt = 0; tt < FL::TB; ++tt) {
+          if (tt >= nt) break;
           const int64_t row = (int64_t)i * t_step + t0 + tt;
-          const T xv = x[row * c_ch + ch[k]];
+          const T xv = xin[tt];
           float acc = bias[k];
 #pragma unroll
           for (int j = 0; j < W - 1; ++j) acc = fmaf(wt[k][j], win[k][j], acc);
