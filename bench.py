@@ -164,8 +164,8 @@ MTP_KERNEL = "void decode_fused_kernel<__bf16, 128, 2, 4, true, true, false>"
 # the layer's projection kernels at 4096 tokens (in_proj_qkvz/ba, out_proj with the residual)
 # in_proj at 4096 rows: 48 column tiles of 256 x 256 straight into LDS, then
 # the 64-wide last tile (b and a) as small register-staged tiles
-IN_PROJ_KERNELS = ("void proj_lds_kernel<256, 256, 2, 4, false>", "void proj_kernel<64, 32, 2, 2, 2, true, false>")
-OUT_PROJ_KERNELS = ("void proj_kernel<128, 128, 2, 2, 2, true, true>",)
+IN_PROJ_KERNELS = ("void proj_lds_kernel<256, 256, 2, 4, false, 2>", "void proj_kernel<64, 32, 2, 2, 2, true, false>")
+OUT_PROJ_KERNELS = ("void proj_lds_kernel<128, 256, 2, 4, true, 3>",)
 
 
 def counter_mfma(workload: str, kernels) -> dict | None:

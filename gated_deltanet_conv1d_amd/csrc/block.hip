@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 // quarter-wave reads at one logical chunk then cover all 64 banks once.
 __device__ __forceinline__ int swz2(int row, int c) { return row * kBK + ((c ^ ((row >> 1) & 7)) << 3); }
 
-template <int BM, int BN, int WGM, int WGN, bool RES>
+template <int BM, int BN, int WGM, int WGN, bool RES, int NBUF = 2>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 void proj_lds_kernel(ProjDev p) {
   constexpr int NW = WGM * WGN;  // waves: 4 (one per SIMD) or 8 (two per SIMD)
@@ -299,8 +299,15 @@ void proj_lds_kernel(ProjDev p) {
   static_assert(FM % 4 == 0 && FN % 4 == 0, "fragments read four at a time");
   constexpr int IX = BM / (8 * NW), IW = BN / (8 * NW);  // load instructions per wave per stage
   static_assert(IX * 8 * NW == BM && IW * 8 * NW == BN, "whole load instructions");
-  __shared__ __attribute__((aligned(16))) bf16 sx[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) bf16 sw[2][BN * kBK];
+  // NBUF LDS buffers: NBUF - 1 stages in flight while one is consumed; a
+  // wave's loads of stage kt have landed once at most the later stages' loads
+  // are outstanding (loads retire in issue order; no other memory operation
+  // is issued in the k loop)
+  static_assert(NBUF >= 2 && (NBUF - 2) * (IX + IW) < 64, "stages in flight");
+  constexpr int VM_LATER = (NBUF - 2) * (IX + IW);
+  constexpr int WAIT_KT = 0x0F70 | (VM_LATER & 15) | ((VM_LATER >> 4) << 14);  // vmcnt(VM_LATER)
+  __shared__ __attribute__((aligned(16))) bf16 sx[NBUF][BM * kBK];
+  __shared__ __attribute__((aligned(16))) bf16 sw[NBUF][BN * kBK];
 
   const int b = blockIdx.x;
   const int64_t lt = (int64_t)(b & 7) * p.per_xcd + (b >> 3);
@@ -356,12 +363,23 @@ void proj_lds_kernel(ProjDev p) {
   // steps per stage)
   const int rl = lane & 15, g = lane >> 4;
   const int kt_n = p.k / kBK;
-  issue(0, 0);
+  // stages 0 .. NBUF-2 up front; no load is ever issued past the end of k,
+  // so none is in flight when the workgroup ends
+#pragma unroll
+  for (int q = 0; q < NBUF - 1; ++q)
+    if (q < kt_n) issue(q * kBK, q);
   for (int kt = 0; kt < kt_n; ++kt) {
-    const int buf = kt & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of stage kt have landed (vmcnt 0)
-    __syncthreads();                      // ... everyone's, and everyone is done with stage kt - 1
-    if (kt + 1 < kt_n) issue((kt + 1) * kBK, buf ^ 1);
+    const int buf = kt % NBUF;
+    // this wave's loads of stage kt have landed: with all NBUF - 2 later
+    // stages issued, at most their loads are outstanding; near the end, none
+    if (kt + NBUF - 2 < kt_n) __builtin_amdgcn_s_waitcnt(WAIT_KT);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    // ... everyone's, and everyone is done reading stage kt - 1 (the asm reads
+    // retire before their block ends).  A bare barrier: __syncthreads' fence
+    // would also wait for the later stages' loads (it counts direct-to-LDS
+    // loads as pending LDS writes) and drain the pipeline
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + NBUF - 1 < kt_n) issue((kt + NBUF - 1) * kBK, (kt + NBUF - 1) % NBUF);
     const bf16* cx = sx[buf];
     const bf16* cw = sw[buf];
 #pragma unroll
@@ -510,14 +528,14 @@ hipError_t run_proj_splitk(ProjDev p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, bool RES>
+template <int BM, int BN, int WGM, int WGN, bool RES, int NBUF = 2>
 hipError_t run_proj_lds(ProjDev p, hipStream_t st) {
   p.tiles_m = (int)((p.m + BM - 1) / BM);
   p.tiles_n = (p.n - p.n_begin + BN - 1) / BN;
   p.group_m = 4;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   p.per_xcd = (int)((tiles + 7) / 8);
-  hipLaunchKernelGGL((proj_lds_kernel<BM, BN, WGM, WGN, RES>), dim3((unsigned)(8 * (int64_t)p.per_xcd)),
+  hipLaunchKernelGGL((proj_lds_kernel<BM, BN, WGM, WGN, RES, NBUF>), dim3((unsigned)(8 * (int64_t)p.per_xcd)),
                      dim3(64 * WGM * WGN), 0, st, p);
   return hipGetLastError();
 }
@@ -573,9 +591,10 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
     vec = vec && a.seg[s].begin % 4 == 0 && a.seg[s].ld % 4 == 0 && ((uintptr_t)a.seg[s].ptr & 7) == 0;
   // Measured on the layer's shapes (hidden 2048): at 4096 tokens
   // in_proj_qkvz/ba runs best as 256 x 256 tiles streamed straight into LDS
-  // (8 waves, two per SIMD) and out_proj as 128 x 128 tiles staged through
-  // registers (two workgroups per CU); at 256 decode rows in_proj takes
-  // 64 x 128 tiles and out_proj 64 x 32.
+  // (8 waves, two per SIMD, two LDS buffers) and out_proj (k = 4096: 64
+  // stages) as 128 x 256 tiles streamed into three LDS buffers, two stages in
+  // flight; at 256 decode rows in_proj takes 64 x 128 tiles and out_proj
+  // 64 x 32.
   const bool lds = vec && a.k % kBK == 0;
   const bool res = a.residual != nullptr;
   if (lds && !res && a.m >= 1024 && tile_count(a.m, a.n, 256, 256) >= 512) {
@@ -590,6 +609,8 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t st) {
     rest.n_begin = n_full;
     return run_proj<64, 32, 2, 2, 2, true, false>(rest, st);
   }
+  if (lds && res && a.m >= 1024 && tile_count(a.m, a.n, 128, 256) >= 256)
+    return run_proj_lds<128, 256, 2, 4, true, 3>(p, st);
   // few rows and few columns (a decode step's out_proj): k split over the
   // waves; with many columns (in_proj) the LDS-staged tiles below share each
   // weight stage between the waves and run faster
