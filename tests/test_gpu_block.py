@@ -49,11 +49,14 @@ def _small_ints(seed, shape, lo=-2, hi=2, density=0.5):
 # kernel and tile choices (in_proj / out_proj): 64 x 128 staged through LDS /
 # 64 x 32 split over k; 128 x 128 / 64 x 32 split over k (a partial last row
 # tile); 128 x 128 / 64 x 64; 256 x 256 straight into LDS plus the 64-wide
-# last column tile as 64 x 32 / 128 x 128; one row (64 x 32 split over k, the
-# four output segments / the same); k not a multiple of 64 with 2-column
-# segments (column by column)
+# last column tile as 64 x 32 / 128 x 128; 256 x 256 plus the last column
+# tile / 128 x 256 with three LDS buffers, at 4096 rows and with a partial
+# last row tile at 4100; one row (64 x 32 split over k, the four output
+# segments / the same); k not a multiple of 64 with 2-column segments (column
+# by column)
 @pytest.mark.parametrize("dims,hidden,T", [(QWEN, 2048, 256), (QWEN, 2048, 300), (QWEN, 2048, 600),
-                                           (QWEN, 2048, 2600), (QWEN, 1024, 1), (SMALL, 24, 37)])
+                                           (QWEN, 2048, 2600), (QWEN, 2048, 4096), (QWEN, 2048, 4100),
+                                           (QWEN, 1024, 1), (SMALL, 24, 37)])
 def test_projections_exact_on_small_integers(dims, hidden, T):
     log(f"projections: dims {dims} hidden {hidden} T {T}")
     vd = dims.h_v * dims.d_v
